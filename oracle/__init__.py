@@ -1,0 +1,177 @@
+"""CPU oracle for the GDN / KDA recurrent-state decode step (FP32, uniform INT8, DAMP).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()`` and by the CPU
+baseline leg of ``bench.py``. The GPU library and its binding never import it, and it imports
+nothing from them. The arithmetic lives in ``oracle.c`` (see its header for the sources and the
+precision policy); this module only builds/loads that library and marshals numpy arrays.
+
+Logical state representation of ``n`` units of a ``D x D`` state (rows = key channels):
+    fp32:       S  float32 [n, D, D]
+    quantized:  mask uint8 [n, D] (1 = FP16 row), h uint16 [n, D, D] (binary16 bits),
+                c int8 [n, D, D], s float32 [n, D]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build() -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` next to it (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        Lg = ctypes.c_long
+        L.oracle_f16_from_f32_n.argtypes = [P, P, Lg]
+        L.oracle_f32_from_f16_n.argtypes = [P, P, Lg]
+        L.oracle_quant_row.argtypes = [I, P, P, P]
+        L.oracle_quantize.argtypes = [I, Lg, P, P, P, P, P, I]
+        L.oracle_quantize.restype = I
+        L.oracle_dequantize.argtypes = [I, Lg, P, P, P, P, P, I]
+        L.oracle_dequantize.restype = I
+        L.oracle_step.argtypes = [I, Lg, I, P, P, P, P, P, P, P, P, P, I, P, P, I]
+        L.oracle_step.restype = I
+        L.oracle_select_rows.argtypes = [I, I, Lg, P, P, I, P, P]
+        L.oracle_select_rows.restype = I
+        _lib = L
+    return _lib
+
+
+def default_threads() -> int:
+    n = os.environ.get("OMP_NUM_THREADS")
+    if n and n.isdigit() and int(n) > 0:
+        return int(n)
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def f16_from_f32(x) -> np.ndarray:
+    x = _c(x, np.float32)
+    h = np.empty(x.shape, np.uint16)
+    lib().oracle_f16_from_f32_n(_p(x), _p(h), x.size)
+    return h
+
+
+def f32_from_f16(h) -> np.ndarray:
+    h = _c(h, np.uint16)
+    x = np.empty(h.shape, np.float32)
+    lib().oracle_f32_from_f16_n(_p(h), _p(x), h.size)
+    return x
+
+
+def quant_row(x) -> tuple[np.ndarray, np.float32]:
+    x = _c(x, np.float32)
+    c = np.empty(x.shape, np.int8)
+    s = np.zeros(1, np.float32)
+    lib().oracle_quant_row(x.size, _p(x), _p(c), _p(s))
+    return c, s[0]
+
+
+def quantize(mask, S, nthreads: int | None = None):
+    """fp32 states ``S[n, D, D]`` -> logical quantized representation ``(h, c, s)``."""
+    S = _c(S, np.float32)
+    n, D, _ = S.shape
+    mask = _c(np.broadcast_to(mask, (n, D)), np.uint8)
+    h = np.empty((n, D, D), np.uint16)
+    c = np.empty((n, D, D), np.int8)
+    s = np.empty((n, D), np.float32)
+    rc = lib().oracle_quantize(D, n, _p(mask), _p(S), _p(h), _p(c), _p(s),
+                               nthreads or default_threads())
+    assert rc == 0
+    return h, c, s
+
+
+def dequantize(mask, h, c, s, nthreads: int | None = None) -> np.ndarray:
+    h = _c(h, np.uint16)
+    c = _c(c, np.int8)
+    s = _c(s, np.float32)
+    n, D, _ = c.shape
+    mask = _c(np.broadcast_to(mask, (n, D)), np.uint8)
+    S = np.empty((n, D, D), np.float32)
+    rc = lib().oracle_dequantize(D, n, _p(mask), _p(h), _p(c), _p(s), _p(S),
+                                 nthreads or default_threads())
+    assert rc == 0
+    return S
+
+
+def _vecs(q, k, v, alpha, beta, n, D):
+    q = _c(q, np.float32).reshape(n, D)
+    k = _c(k, np.float32).reshape(n, D)
+    v = _c(v, np.float32).reshape(n, D)
+    alpha = _c(alpha, np.float32)
+    per_key = 1 if alpha.size == n * D and D != 1 else 0
+    alpha = alpha.reshape(n, D) if per_key else alpha.reshape(n)
+    beta = _c(beta, np.float32).reshape(n)
+    return q, k, v, alpha, per_key, beta
+
+
+def step_fp32(S, q, k, v, alpha, beta, nthreads: int | None = None) -> np.ndarray:
+    """One step on fp32 states ``S[n, D, D]`` (updated in place); returns the readout [n, D].
+    ``alpha`` is [n] (GDN) or [n, D] (KDA)."""
+    assert S.dtype == np.float32 and S.flags.c_contiguous
+    n, D, _ = S.shape
+    q, k, v, alpha, per_key, beta = _vecs(q, k, v, alpha, beta, n, D)
+    out = np.empty((n, D), np.float32)
+    rc = lib().oracle_step(D, n, 0, None, _p(S), None, None, None, _p(q), _p(k), _p(v),
+                           _p(alpha), per_key, _p(beta), _p(out), nthreads or default_threads())
+    assert rc == 0
+    return out
+
+
+def step_quant(mask, h, c, s, q, k, v, alpha, beta, nthreads: int | None = None) -> np.ndarray:
+    """One step on the quantized representation (``h, c, s`` updated in place); returns the
+    readout [n, D]. Uniform INT8 is ``mask`` all zero."""
+    for a, t in ((h, np.uint16), (c, np.int8), (s, np.float32)):
+        assert a.dtype == t and a.flags.c_contiguous
+    n, D, _ = c.shape
+    mask = _c(np.broadcast_to(mask, (n, D)), np.uint8)
+    q, k, v, alpha, per_key, beta = _vecs(q, k, v, alpha, beta, n, D)
+    out = np.empty((n, D), np.float32)
+    rc = lib().oracle_step(D, n, 1, _p(mask), None, _p(h), _p(c), _p(s), _p(q), _p(k), _p(v),
+                           _p(alpha), per_key, _p(beta), _p(out), nthreads or default_threads())
+    assert rc == 0
+    return out
+
+
+def select_rows(S, abar, r: int):
+    """Row selection for ``S[n_slots, H, D, D]`` with mean decay ``abar[H, D]``.
+    Returns ``(rows int32 [H, r] ascending, score float64 [H, D])``."""
+    S = _c(S, np.float32)
+    n_slots, H, D, _ = S.shape
+    abar = _c(np.broadcast_to(abar, (H, D)), np.float64)
+    rows = np.empty((H, r), np.int32)
+    score = np.empty((H, D), np.float64)
+    rc = lib().oracle_select_rows(D, H, n_slots, _p(S), _p(abar), r, _p(rows), _p(score))
+    assert rc == 0
+    return rows, score

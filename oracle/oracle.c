@@ -1,0 +1,274 @@
+/*
+ * oracle.c -- CPU oracle for the GDN / KDA recurrent-state decode step in FP32, uniform INT8
+ * and DAMP's FP16 + INT8 layout.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h): loaded by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg, never by the GPU library or its Python binding.
+ *
+ * Arithmetic policy. The pages do not fix the precision of the step's intermediate values, so
+ * every real-valued quantity of the step (reconstructed state, decayed state, projection,
+ * delta, new state, readout) is computed in binary64, in the order the step defines it, with
+ * plain loops (no blocking, fusion or reordering). The new state X is rounded once to binary32,
+ * the working precision of the recurrent state (the DAMP abstract: states are commonly kept in
+ * FP32). Every quantization decision (binary16 rounding, the INT8 scale and the INT8 codes) is
+ * taken on that binary32 X, in binary32, which is also the precision the GPU kernels use.
+ *
+ * Build: gcc -O2 -std=c11 -fopenmp -fPIC -shared -ffp-contract=off -fno-fast-math.
+ * -ffp-contract=off keeps every a*b+c as two rounded operations, so the binary32 division
+ * and nearbyintf below are exactly the IEEE operations.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------------------------
+ * IEEE 754 binary16, written from the format definition (1 sign bit, 5 exponent bits with bias
+ * 15, 10 fraction bits; subnormals have spacing 2^-24; the largest finite value is 65504).
+ * Round to nearest, ties to even. Binary32 -> binary64 is exact and scaling by a power of two
+ * is exact, so the rounding is done on an exact integer multiple count with nearbyint().
+ * ---------------------------------------------------------------------------------------- */
+uint16_t oracle_f16_from_f32(float xf) {
+  uint32_t u;
+  memcpy(&u, &xf, sizeof u);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  if (isnan(xf)) return (uint16_t)(sign | 0x7e00u);
+  const double a = fabs((double)xf);
+  /* 65520 = 65504 + half of the last binade's spacing (32); at or above it, RNE overflows. */
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u);
+  if (a == 0.0) return sign;
+  int e2;
+  (void)frexp(a, &e2); /* a = f * 2^e2 with f in [0.5, 1): a lies in [2^(e2-1), 2^e2) */
+  const int E = e2 - 1;
+  if (E < -14) {
+    /* subnormal range: value = n * 2^-24, n in [0, 1024]; n = 1024 encodes 2^-14 exactly */
+    const double n = nearbyint(ldexp(a, 24));
+    return (uint16_t)(sign | (uint16_t)n);
+  }
+  /* normal range: value = n * 2^(E-10), n in [1024, 2048]; n = 2048 carries into E + 1 */
+  const double n = nearbyint(ldexp(a, 10 - E));
+  const uint32_t bits = ((uint32_t)(E + 15) << 10) + (uint32_t)n - 1024u;
+  return (uint16_t)(sign | bits);
+}
+
+float oracle_f32_from_f16(uint16_t h) {
+  const int sign = (h >> 15) & 1;
+  const int ex = (h >> 10) & 0x1f;
+  const int fr = h & 0x3ff;
+  double v;
+  if (ex == 0x1f)
+    v = fr ? NAN : INFINITY;
+  else if (ex == 0)
+    v = ldexp((double)fr, -24);
+  else
+    v = ldexp((double)(1024 + fr), ex - 25);
+  return (float)(sign ? -v : v);
+}
+
+void oracle_f16_from_f32_n(const float* x, uint16_t* h, long n) {
+  for (long i = 0; i < n; ++i) h[i] = oracle_f16_from_f32(x[i]);
+}
+
+void oracle_f32_from_f16_n(const uint16_t* h, float* x, long n) {
+  for (long i = 0; i < n; ++i) x[i] = oracle_f32_from_f16(h[i]);
+}
+
+/* ------------------------------------------------------------------------------------------
+ * INT8 row requantization. The pages name only "INT8" for the non-pivot rows (DAMP abstract);
+ * the rule used here is symmetric, one fp32 scale per row, scale = row absmax / 127, codes
+ * rounded half-to-even and limited to [-127, 127] (code -128 is never produced).
+ * ---------------------------------------------------------------------------------------- */
+void oracle_quant_row(int D, const float* x, int8_t* c, float* s) {
+  float m = 0.0f;
+  for (int j = 0; j < D; ++j) {
+    const float a = fabsf(x[j]);
+    if (a > m) m = a;
+  }
+  if (m == 0.0f) {
+    *s = 0.0f;
+    memset(c, 0, (size_t)D);
+    return;
+  }
+  const float sc = m / 127.0f; /* binary32 division, round to nearest even */
+  for (int j = 0; j < D; ++j) {
+    const float t = x[j] / sc;   /* binary32 division */
+    float r = nearbyintf(t);     /* default rounding mode: to nearest, ties to even */
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    c[j] = (int8_t)r;
+  }
+  *s = sc;
+}
+
+/* Reconstructed value of entry (i, j) of a quantized unit, exact in binary64: an 8-bit code
+ * times a 24-bit significand fits in 53 bits, and binary16 widens exactly.
+ * (Table C2 step 1 of the STEPQuant page: integer codes and scales, or FP16 for pivot units.) */
+static double recon(int D, const uint8_t* mask, const uint16_t* h, const int8_t* c,
+                    const float* s, int i, int j) {
+  if (mask[i]) return (double)oracle_f32_from_f16(h[(long)i * D + j]);
+  return (double)c[(long)i * D + j] * (double)s[i];
+}
+
+int oracle_quantize(int D, long n_units, const uint8_t* mask, const float* S, uint16_t* h,
+                    int8_t* c, float* s, int nthreads) {
+  if (D <= 0 || n_units < 0 || !mask || !S || !h || !c || !s) return -1;
+  const long DD = (long)D * D;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+  for (long u = 0; u < n_units; ++u) {
+    for (int i = 0; i < D; ++i) {
+      const float* row = S + u * DD + (long)i * D;
+      if (mask[u * D + i]) {
+        for (int j = 0; j < D; ++j) h[u * DD + (long)i * D + j] = oracle_f16_from_f32(row[j]);
+        memset(c + u * DD + (long)i * D, 0, (size_t)D);
+        s[u * D + i] = 0.0f;
+      } else {
+        for (int j = 0; j < D; ++j) h[u * DD + (long)i * D + j] = 0;
+        oracle_quant_row(D, row, c + u * DD + (long)i * D, s + u * D + i);
+      }
+    }
+  }
+  return 0;
+}
+
+int oracle_dequantize(int D, long n_units, const uint8_t* mask, const uint16_t* h,
+                      const int8_t* c, const float* s, float* S, int nthreads) {
+  if (D <= 0 || n_units < 0 || !mask || !S || !h || !c || !s) return -1;
+  const long DD = (long)D * D;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+  for (long u = 0; u < n_units; ++u)
+    for (int i = 0; i < D; ++i)
+      for (int j = 0; j < D; ++j)
+        S[u * DD + (long)i * D + j] =
+            (float)recon(D, mask + u * D, h + u * DD, c + u * DD, s + u * D, i, j);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * One decode step of one unit, in the order of Table C2 on the STEPQuant page:
+ *   1. reconstruct S_hat from codes and scales, or from FP16 for pivot rows (fp32 format: the
+ *      stored values);
+ *   2. X = D_t S_hat + beta k (v^T - k^T D_t S_hat), with D_t = alpha I (GDN) or diag(alpha)
+ *      (KDA; the table's KDA remark and the DAMP abstract's per-key-channel decay);
+ *   3. readout y = X^T q, taken from X before requantization;
+ *   6. store: FP16 for pivot rows, INT8 codes + scale for the rest (DAMP abstract), or fp32.
+ * Steps 4-5 of that table (STEPQuant's dual-axis fitting) are not part of DAMP.
+ * work holds D*D + D doubles.
+ * ---------------------------------------------------------------------------------------- */
+static void step_unit(int D, int fmt, const uint8_t* mask, float* S32, uint16_t* h, int8_t* c,
+                      float* s, const float* q, const float* k, const float* v,
+                      const float* alpha, int per_key, float beta, float* out, double* work,
+                      float* rowbuf) {
+  double* X = work;       /* D x D */
+  double* u = work + (long)D * D; /* D: k^T D_t S_hat */
+
+  /* steps 1 and 2a: S' = D_t S_hat, held in X */
+  for (int i = 0; i < D; ++i) {
+    const double a = (double)(per_key ? alpha[i] : alpha[0]);
+    for (int j = 0; j < D; ++j) {
+      const double sh = fmt == 0 ? (double)S32[(long)i * D + j] : recon(D, mask, h, c, s, i, j);
+      X[(long)i * D + j] = a * sh;
+    }
+  }
+  /* step 2b: u_j = sum_i k_i S'_ij, i ascending */
+  for (int j = 0; j < D; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < D; ++i) acc += (double)k[i] * X[(long)i * D + j];
+    u[j] = acc;
+  }
+  /* step 2c: X_ij = S'_ij + k_i * beta * (v_j - u_j) */
+  for (int i = 0; i < D; ++i)
+    for (int j = 0; j < D; ++j)
+      X[(long)i * D + j] += (double)k[i] * ((double)beta * ((double)v[j] - u[j]));
+  /* step 3: y_j = sum_i q_i X_ij from the unquantized X */
+  for (int j = 0; j < D; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < D; ++i) acc += (double)q[i] * X[(long)i * D + j];
+    out[j] = (float)acc;
+  }
+  /* step 6: round X once to binary32, then store in the unit's format */
+  for (int i = 0; i < D; ++i) {
+    for (int j = 0; j < D; ++j) rowbuf[j] = (float)X[(long)i * D + j];
+    if (fmt == 0) {
+      memcpy(S32 + (long)i * D, rowbuf, sizeof(float) * (size_t)D);
+    } else if (mask[i]) {
+      for (int j = 0; j < D; ++j) h[(long)i * D + j] = oracle_f16_from_f32(rowbuf[j]);
+    } else {
+      oracle_quant_row(D, rowbuf, c + (long)i * D, s + i);
+    }
+  }
+}
+
+int oracle_step(int D, long n_units, int fmt, const uint8_t* mask, float* S32, uint16_t* h,
+                int8_t* c, float* s, const float* q, const float* k, const float* v,
+                const float* alpha, int per_key, const float* beta, float* out, int nthreads) {
+  if (D <= 0 || n_units < 0 || (fmt != 0 && fmt != 1)) return -1;
+  if (!q || !k || !v || !alpha || !beta || !out) return -1;
+  if (fmt == 0 && !S32) return -1;
+  if (fmt == 1 && (!mask || !h || !c || !s)) return -1;
+  const long DD = (long)D * D;
+  int bad = 0;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+  {
+    double* work = (double*)malloc(sizeof(double) * (size_t)(DD + D));
+    float* rowbuf = (float*)malloc(sizeof(float) * (size_t)D);
+    if (!work || !rowbuf) {
+#pragma omp atomic write
+      bad = 1;
+    }
+#pragma omp for schedule(static)
+    for (long un = 0; un < n_units; ++un) {
+      if (!work || !rowbuf) continue;
+      step_unit(D, fmt, fmt ? mask + un * D : NULL, fmt ? NULL : S32 + un * DD,
+                fmt ? h + un * DD : NULL, fmt ? c + un * DD : NULL, fmt ? s + un * D : NULL,
+                q + un * D, k + un * D, v + un * D, per_key ? alpha + un * D : alpha + un,
+                per_key, beta[un], out + un * D, work, rowbuf);
+    }
+    free(work);
+    free(rowbuf);
+  }
+  return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * Offline selection of high-risk key rows. The DAMP abstract ranks key channels by
+ * quantization-error energy together with decay-based error retention and fixes the choice
+ * offline. Here error energy is read as the row's mean square (the energy an INT8 row with a
+ * row absmax scale spreads its error over) and retention as the geometric-series factor
+ * 1/(1 - abar) of a gate that multiplies the state by abar each step.
+ * ---------------------------------------------------------------------------------------- */
+int oracle_select_rows(int D, int H, long n_slots, const float* S, const double* abar, int r,
+                       int32_t* rows, double* score) {
+  if (D <= 0 || H <= 0 || n_slots <= 0 || r < 0 || r > D || !S || !abar || !rows || !score)
+    return -1;
+  const long DD = (long)D * D;
+  for (int hh = 0; hh < H; ++hh) {
+    for (int i = 0; i < D; ++i) {
+      double e = 0.0;
+      for (long sl = 0; sl < n_slots; ++sl) {
+        const float* row = S + (sl * H + hh) * DD + (long)i * D;
+        double ms = 0.0;
+        for (int j = 0; j < D; ++j) ms += (double)row[j] * (double)row[j];
+        e += ms / (double)D;
+      }
+      e /= (double)n_slots;
+      score[(long)hh * D + i] = e / (1.0 - abar[(long)hh * D + i]);
+    }
+    /* r rounds of "take the largest remaining score, lower index on ties" */
+    char* taken = (char*)calloc((size_t)D, 1);
+    if (!taken) return -1;
+    for (int t = 0; t < r; ++t) {
+      int best = -1;
+      for (int i = 0; i < D; ++i) {
+        if (taken[i]) continue;
+        if (best < 0 || score[(long)hh * D + i] > score[(long)hh * D + best]) best = i;
+      }
+      taken[best] = 1;
+    }
+    int n = 0;
+    for (int i = 0; i < D; ++i)
+      if (taken[i]) rows[(long)hh * r + n++] = i;
+    free(taken);
+  }
+  return 0;
+}
