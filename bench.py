@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Throughput of the DAMP decode step on one MI355X.
+
+Workload (default): the serving pool -- 4,096 request slots x 32 GDN heads of 128 x 128 states
+in the DAMP layout (24 FP16 key rows per head, INT8 + fp32 row scale for the other 104), of
+which 1,024 random slots are active; each step updates 1,024 x 32 = 32,768 (slot, head) states
+with bf16 q, k, v and fp32 alpha, beta, cycling through 4 pre-made input sets. The touched
+state (654 MB read + written per step) is larger than the 256 MB Infinity Cache.
+
+A step = one damp_decode_step launch over the batch (reconstruct, decay, delta update, readout,
+requantize). Timing: HIP events recorded on the stream the kernels are launched on, around
+exactly --steps launches after --warmup untimed ones, with device synchronisation on both sides.
+
+Prints ONE JSON line. value = (slot, head) state updates per second. roofline.achieved uses the
+algorithmic bytes of one update (state block read + written, q/k/v, alpha, beta, readout, slot
+index) times the updates per launch, divided by the average launch time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD published peak
+TRAFFIC_PER_LAUNCH_BYTES = None  # filled from the committed rocprofv3 counter summary, or null
+
+
+def alg_bytes_per_update(fmt: str, d: int = 128, r: int = 24, per_key: bool = False,
+                         qkv_bytes: int = 2) -> int:
+    """Bytes one (slot, head) update must move: the state block in and out, q/k/v, the gate
+    (scalar or per key), beta, the fp32 readout and the 4-byte slot index (shared by the
+    heads of a slot: counted per unit as 4/H, rounded into the total below)."""
+    if fmt == "damp":
+        state = 2 * r * d + (d - r) * d + 4 * (d - r)
+    elif fmt == "int8":
+        state = d * d + 4 * d
+    else:
+        state = 4 * d * d
+    vecs = 3 * qkv_bytes * d + (4 * d if per_key else 4) + 4 + 4 * d + 4
+    return 2 * state + vecs
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-baselines", action="store_true",
+                   help="skip the in-library fp32 / uniform-INT8 comparison runs")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--only", choices=["damp", "fp32", "int8"], default=None,
+                   help="time only this format (for profiling)")
+    return p.parse_args()
+
+
+def make_inputs(torch, synth, dev):
+    sets = []
+    for i in range(4):
+        inp = synth.pool4096_step(i)
+        bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
+        sets.append((bf(inp.q_bits), bf(inp.k_bits), bf(inp.v_bits),
+                     torch.from_numpy(inp.alpha).to(dev), torch.from_numpy(inp.beta).to(dev)))
+    return sets
+
+
+def fill_states(torch, fn, slots_dev, H, d, dev, chunk=128, seed=1003):
+    """Active slots get S ~ N(0, 0.1) from a seeded device generator, written by ``fn``
+    (S_chunk [c, H, d, d], slot_idx_chunk) in chunks."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    for i in range(0, slots_dev.numel(), chunk):
+        sl = slots_dev[i:i + chunk]
+        S = torch.randn((sl.numel(), H, d, d), generator=g, device=dev, dtype=torch.float32)
+        S.mul_(0.1)
+        fn(S, sl)
+    torch.cuda.synchronize()
+
+
+def time_launches(torch, launch, steps, warmup):
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per launch
+
+
+def cpu_baseline(seconds: float):
+    """The oracle timed on this host's cores on a bounded sample of the same workload: the
+    first 64 active slots (x 32 heads = 2,048 updates per call) of the pool, DAMP format."""
+    import oracle
+    from quantized_delta_rule_gdn_amd import synth
+    w = synth.POOL4096
+    n_slots = 64
+    S = synth.pool4096_states(0, n_slots).reshape(n_slots * w.heads, w.d, w.d)
+    rows = synth.pool4096_rows()
+    mask = np.broadcast_to(synth.rows_to_mask(rows, w.d), (n_slots, w.heads, w.d)).reshape(-1, w.d)
+    h, c, s = oracle.quantize(mask, S)
+    inp = synth.pool4096_step(0)
+    n = n_slots * w.heads
+    vec = (inp.q[:n_slots].reshape(n, w.d), inp.k[:n_slots].reshape(n, w.d),
+           inp.v[:n_slots].reshape(n, w.d), inp.alpha[:n_slots].reshape(n),
+           inp.beta[:n_slots].reshape(n))
+    threads = oracle.default_threads()
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.step_quant(mask, h, c, s, *vec, nthreads=threads)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": calls * n / el, "unit": "state-updates/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{calls} oracle steps of 2,048 (slot, head) DAMP updates (first 64 active "
+                      f"slots of the pool workload) in {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (every unit is "
+              "independent; a multi-GPU run would shard slots or heads with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from quantized_delta_rule_gdn_amd import lib, synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = synth.POOL4096
+    H, d, r = w.heads, w.d, w.fp16_rows
+    slots = torch.from_numpy(synth.pool4096_slots()).to(dev)
+    B = slots.numel()
+    units = B * H
+    sets = make_inputs(torch, synth, dev)
+    out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    results = {}
+
+    def run(fmt):
+        if fmt == "damp":
+            st = lib.DampState(w.pool_slots, H, d, synth.pool4096_rows(), device=dev)
+            st.pool.zero_()
+            fill_states(torch, st.quantize, slots, H, d, dev)
+            launch = lambda i: st.decode_step(slots, *sets[i % 4], out)
+            keep = st
+        elif fmt == "fp32":
+            pool = torch.zeros((w.pool_slots, H, d, d), dtype=torch.float32, device=dev)
+            fill_states(torch, lambda S, sl: pool.index_copy_(0, sl.long(), S), slots, H, d, dev)
+            launch = lambda i: lib.fp32_decode_step(pool, slots, *sets[i % 4], out)
+            keep = pool
+        else:
+            codes = torch.zeros((w.pool_slots, H, d, d), dtype=torch.int8, device=dev)
+            scales = torch.zeros((w.pool_slots, H, d), dtype=torch.float32, device=dev)
+            fill_states(torch, lambda S, sl: lib.uniform_int8_quantize(codes, scales, S, sl),
+                        slots, H, d, dev)
+            launch = lambda i: lib.uniform_int8_decode_step(codes, scales, slots, *sets[i % 4], out)
+            keep = (codes, scales)
+        ms = time_launches(torch, launch, args.steps, args.warmup)
+        del keep
+        torch.cuda.empty_cache()
+        ab = alg_bytes_per_update(fmt, d, r) * units
+        return {"ms_per_step": ms, "updates_per_s": units / (ms * 1e-3),
+                "alg_bytes_per_launch": ab, "gbs": ab / (ms * 1e-3) / 1e9}
+
+    fmts = [args.only] if args.only else (["damp"] if args.no_baselines else ["damp", "fp32", "int8"])
+    for f in fmts:
+        results[f] = run(f)
+        print(f"# {f}: {results[f]['ms_per_step'] * 1e3:.1f} us/step, "
+              f"{results[f]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+
+    main_fmt = args.only or "damp"
+    m = results[main_fmt]
+    line = {
+        "metric": "state-updates/s (slot·head·token) + achieved HBM GB/s vs peak, 1 MI355X",
+        "value": m["updates_per_s"],
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+fp16+int8" if main_fmt == "damp" else ("f32" if main_fmt == "fp32" else "f32+int8"),
+        "data": "synthetic: seeded N(0, 0.1) states, unit-norm bf16 q/k, N(0,1) bf16 v, "
+                "sigmoid gates; no model weights",
+        "config": {"workload": "pool4096: GDN decode step, 4096-slot DAMP pool x 32 heads x "
+                               "128x128, 1024 active random slots, 24 FP16 rows/head, bf16 qkv",
+                   "format": main_fmt, "slots_active": B, "heads": H, "d": d,
+                   "fp16_rows": r, "global_batch": B, "seq_len": 1},
+        "roofline": {"bound": "hbm", "achieved": m["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": m["gbs"] / PEAK_HBM_GBS, "traffic": TRAFFIC_PER_LAUNCH_BYTES},
+    }
+    if "fp32" in results and "damp" in results:
+        line["baselines"] = {f: {"ms_per_step": v["ms_per_step"], "updates_per_s": v["updates_per_s"],
+                                 "gbs": v["gbs"], "frac": v["gbs"] / PEAK_HBM_GBS}
+                             for f, v in results.items() if f != "damp"}
+        line["speedup_vs_fp32"] = results["fp32"]["ms_per_step"] / results["damp"]["ms_per_step"]
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * damp.h -- C ABI of libdamp.so: the per-token decode update of Gated DeltaNet (GDN) and Kimi
+ * Delta Attention (KDA) recurrent states on AMD Instinct MI355X (gfx950), with the state held
+ * in DAMP's mixed-precision layout, plus the FP32-state and uniform-INT8-state updates the
+ * DAMP pages compare against.
+ *
+ * Sources (web pages):
+ *  [C2]   "STEPQuant: When and Where Errors Matter in Delta-Rule Recurrent State Quantization"
+ *         (thelatestinai.com listing), appendix Table C2, one persistent decode step: inputs
+ *         are the compressed state, q_t, k_t, v_t, the gate D_t, beta_t and a frozen precision
+ *         map; (1) reconstruct the previous state from integer codes and scales, or FP16 for
+ *         pivot units; (2) X = D_t S_hat + beta_t k_t (v_t^T - k_t^T D_t S_hat); (3) emit
+ *         y_t = X^T q_t before requantization; (6) pack codes and scales, store pivots in FP16,
+ *         keep the old representation valid until its readers finish.
+ *  [DAMP] "DAMP: Decay-Aware Mixed-Precision Recurrent-State Quantization", abstract (arXiv v1
+ *         on news.chathome.org; later version on mlsanity.com): high-risk key channels chosen
+ *         offline are kept in FP16, the remaining key channels in INT8, under a fixed storage
+ *         budget; states are otherwise FP32; the update is memory-bandwidth bound; the gate is
+ *         a scalar per head (GDN) or one decay per key channel (KDA).
+ *
+ * Notation. A "unit" is one (slot, head) state S of d_k x d_v floats; row i is key channel i,
+ * column j is value dimension j. D_t = alpha * I (GDN, one alpha per unit) or diag(alpha)
+ * (KDA, alpha[d_k] per unit). The library neither normalises q or k nor scales q; callers do
+ * that before the call. Supported sizes: d_k == d_v in {16, 32, 64, 128}; anything else
+ * returns DAMP_ERR_UNSUPPORTED.
+ *
+ * INT8 rows (the pages only say "INT8"; this rule is the library's): symmetric, one fp32 scale
+ * per row, scale = fl32(max_j |X_ij| / 127), code = round-half-to-even of fl32(X_ij / scale),
+ * codes in [-127, 127]; an all-zero row has scale 0 and codes 0. FP16 rows: IEEE binary16,
+ * round to nearest even. Reconstruction: code * scale, or the binary16 value.
+ *
+ * Execution model. Every call that takes a `stream` (a hipStream_t, e.g. torch's
+ * torch.cuda.current_stream().cuda_stream; NULL = the default stream) only validates its
+ * arguments on the host and enqueues work: it returns before the GPU has run. The return value
+ * covers host-side validation and launch errors; a fault inside a kernel surfaces at the next
+ * synchronisation of that stream (as a HIP error of the caller's runtime). States are updated
+ * in place: within one call each listed slot must appear once (duplicates race; the result is
+ * undefined), and only listed slots are read or written. With the environment variable
+ * DAMP_DEBUG=1 the step calls copy slot_idx to the host first (synchronising the stream) and
+ * return DAMP_ERR_SLOT_INDEX for an index outside [0, num_slots) or a repeated one.
+ *
+ * Pointers. "dev" pointers are device (HBM) addresses, "host" pointers host memory. The caller
+ * owns every array it passes. No call keeps a pointer after it returns except damp_state_alloc,
+ * whose handle keeps `pool` (which must outlive the handle). No exception crosses this ABI;
+ * every non-OK status stores a message retrievable with damp_last_error().
+ */
+#ifndef DAMP_H
+#define DAMP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum damp_status {
+  DAMP_OK = 0,
+  DAMP_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, misaligned pointer, bad enum */
+  DAMP_ERR_UNSUPPORTED = -2,      /* a size the kernels are not built for */
+  DAMP_ERR_OUT_OF_MEMORY = -3,    /* the library's small device allocation failed */
+  DAMP_ERR_SLOT_INDEX = -4,       /* DAMP_DEBUG=1 only: slot index out of range or repeated */
+  DAMP_ERR_HIP = -5               /* a HIP runtime call or kernel launch failed */
+} damp_status;
+
+/* Gate form ([C2] step 2, "For KDA" remark; [DAMP]). */
+typedef enum damp_decay {
+  DAMP_DECAY_SCALAR = 0,  /* GDN: alpha is [B][H] */
+  DAMP_DECAY_PER_KEY = 1  /* KDA: alpha is [B][H][d_k] */
+} damp_decay;
+
+/* Element type of q, k, v. beta, alpha and the readout are always fp32. */
+typedef enum damp_dtype { DAMP_F32 = 0, DAMP_BF16 = 1 } damp_dtype;
+
+/* Shape of a DAMP state pool: num_slots request slots x num_heads heads, each a d_k x d_v
+ * state with num_fp16_rows FP16 key rows per head (the same rows for every slot: the frozen
+ * precision map of [C2] / [DAMP]) and d_k - num_fp16_rows INT8 rows. */
+typedef struct damp_layout {
+  int32_t num_slots;
+  int32_t num_heads;
+  int32_t d_k;
+  int32_t d_v;
+  int32_t num_fp16_rows;
+} damp_layout;
+
+/* Opaque host handle: the layout, the per-head row map and the pool pointer. */
+typedef struct damp_state damp_state;
+
+/* ---------------------------------------------------------------------------------------
+ * DAMP pool layout. The pool is an array of blocks, block (slot, head) at byte offset
+ * (slot * num_heads + head) * damp_block_bytes(layout). With r = num_fp16_rows, D = d_k = d_v:
+ *   [0, 2 r D)                        the r FP16 key rows, r x D binary16, ascending key index
+ *   [2 r D, 2 r D + (D - r) D)        the D - r INT8 key rows, (D - r) x D int8, ascending key index
+ *   [.., + 4 (D - r))                 the fp32 scales of the INT8 rows, same order
+ *   zero padding up to a multiple of 256 bytes (never read or written by the kernels)
+ * At D = 128, r = 24: 6,144 + 13,312 + 416 = 19,872 data bytes (9.70 bits per state value,
+ * 69.7% below FP32), block stride 19,968 bytes.
+ * ------------------------------------------------------------------------------------- */
+
+/* Bytes of one block (the block stride), or 0 for an invalid or unsupported layout. */
+size_t damp_block_bytes(const damp_layout* layout);
+
+/* Data bytes of one block, without the padding (what a step reads and writes), or 0. */
+size_t damp_block_data_bytes(const damp_layout* layout);
+
+/* Device bytes a pool needs: num_slots * num_heads * damp_block_bytes, or 0 if invalid. */
+size_t damp_state_bytes(const damp_layout* layout);
+
+/* Bind a caller-owned device pool to a layout and a frozen row map.
+ *   fp16_rows  host int32 [num_heads][num_fp16_rows]: the FP16 key rows of each head, strictly
+ *              ascending, each in [0, d_k). May be NULL when num_fp16_rows == 0.
+ *   pool       dev, >= damp_state_bytes(layout) bytes (pool_bytes says how many), 256-byte
+ *              aligned. Not initialised or touched by this call.
+ *   out        receives the handle; *out is set to NULL on failure.
+ * Allocates a small device copy of the row map (num_heads * d_k int32) and copies it with a
+ * synchronous hipMemcpy on the current device. Errors: INVALID_ARGUMENT (null pointer, bad
+ * size, unsorted/duplicate/out-of-range row, pool too small or misaligned), UNSUPPORTED (d_k),
+ * OUT_OF_MEMORY, HIP. */
+damp_status damp_state_alloc(const damp_layout* layout, const int32_t* fp16_rows, void* pool,
+                             size_t pool_bytes, damp_state** out);
+
+/* Release the handle and its row-map copy (not the pool). NULL is accepted. Synchronises
+ * nothing: the caller must not free while work that uses the handle is still queued. */
+damp_status damp_state_free(damp_state* state);
+
+/* Layout of a handle (copied to *layout). */
+damp_status damp_state_layout(const damp_state* state, damp_layout* layout);
+
+/* Pack fp32 states into the pool ([C2] step 6 with the rule above):
+ *   S        dev fp32 [n][num_heads][d_k][d_v], key rows in their original order
+ *   slot_idx dev int32 [n]: block slot of S[i]; distinct, in [0, num_slots)
+ * n == 0 is a no-op. Errors: INVALID_ARGUMENT, SLOT_INDEX (debug), HIP. */
+damp_status damp_state_quantize(damp_state* state, const float* S, const int32_t* slot_idx,
+                                int32_t n, void* stream);
+
+/* Reconstruct fp32 states from the pool ([C2] step 1): S[i] = state of slot slot_idx[i],
+ * code * scale (one fp32 rounding) for INT8 rows, the binary16 value for FP16 rows, in the
+ * original key-row order. Does not modify the pool. */
+damp_status damp_state_dequantize(const damp_state* state, float* S, const int32_t* slot_idx,
+                                  int32_t n, void* stream);
+
+/* One decode step of B requests on a DAMP pool, fused in one kernel ([C2] steps 1, 2, 3, 6):
+ * for each b < B and head h, unit (slot_idx[b], h):
+ *   reconstruct S_hat, S' = D_t S_hat, u = S'^T k, delta = beta (v - u),
+ *   X = S' + k delta^T, out = X^T q (from X, before requantization), requantize X in place.
+ *   slot_idx dev int32 [B], distinct, in [0, num_slots)
+ *   q, k, v  dev [B][num_heads][d] of qkv_dtype (fp32 or bf16), contiguous
+ *   alpha    dev fp32 [B][num_heads] (DAMP_DECAY_SCALAR) or [B][num_heads][d_k] (PER_KEY)
+ *   beta     dev fp32 [B][num_heads]
+ *   out      dev fp32 [B][num_heads][d_v], 16-byte aligned
+ * B == 0 is a no-op. Errors: INVALID_ARGUMENT, SLOT_INDEX (debug), HIP. */
+damp_status damp_decode_step(damp_state* state, const int32_t* slot_idx, int32_t B,
+                             const void* q, const void* k, const void* v, damp_dtype qkv_dtype,
+                             const float* alpha, damp_decay decay, const float* beta,
+                             float* out, void* stream);
+
+/* The same step on an FP32 state pool (the reference format of the DAMP speedups):
+ *   pool dev fp32 [num_slots][num_heads][d_k][d_v], 16-byte aligned. Other arguments as in
+ *   damp_decode_step. No requantization: X is stored as fp32. */
+damp_status fp32_decode_step(float* pool, int32_t num_slots, int32_t num_heads, int32_t d_k,
+                             int32_t d_v, const int32_t* slot_idx, int32_t B, const void* q,
+                             const void* k, const void* v, damp_dtype qkv_dtype,
+                             const float* alpha, damp_decay decay, const float* beta,
+                             float* out, void* stream);
+
+/* The same step on a uniform-INT8 state (every key row INT8 with its own fp32 scale):
+ *   codes  dev int8 [num_slots][num_heads][d_k][d_v], 16-byte aligned
+ *   scales dev fp32 [num_slots][num_heads][d_k], 16-byte aligned
+ * Bit-identical to damp_decode_step with num_fp16_rows = 0 on the same values. */
+damp_status uniform_int8_decode_step(int8_t* codes, float* scales, int32_t num_slots,
+                                     int32_t num_heads, int32_t d_k, int32_t d_v,
+                                     const int32_t* slot_idx, int32_t B, const void* q,
+                                     const void* k, const void* v, damp_dtype qkv_dtype,
+                                     const float* alpha, damp_decay decay, const float* beta,
+                                     float* out, void* stream);
+
+/* Pack fp32 states S[n][num_heads][d][d] into the uniform-INT8 arrays at slot_idx[n]. */
+damp_status uniform_int8_quantize(int8_t* codes, float* scales, int32_t num_slots,
+                                  int32_t num_heads, int32_t d_k, int32_t d_v, const float* S,
+                                  const int32_t* slot_idx, int32_t n, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). The string
+ * is owned by the library and valid until the thread's next call. */
+const char* damp_last_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int32_t damp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DAMP_H */

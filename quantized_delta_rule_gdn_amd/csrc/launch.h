@@ -1,0 +1,55 @@
+// launch.h -- interface between the C-ABI host layer (damp_api.hip) and the gfx950 kernels
+// (step_kernels.hip). Internal to libdamp.so; not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace damp {
+
+enum Fmt : int { FMT_F32 = 0, FMT_Q = 1 };  // fp32 state / FP16 + INT8 rows (DAMP, uniform INT8)
+
+// Where one unit's (slot, head) state lives. Unit u = slot * H + head.
+//   FMT_F32: fp32 rows at hbase + u * hstride (d x d floats, key rows in original order)
+//   FMT_Q:   storage row p < r is FP16 at hbase + u * hstride + 2 p d,
+//            storage row p >= r is INT8 at cbase + u * cstride + (p - r) d,
+//            with its fp32 scale at sbase + u * sstride + 4 (p - r);
+//            rowmap[head * d + p] = the key row held in storage row p (nullptr = identity).
+struct StateRef {
+  uint8_t* hbase;
+  uint8_t* cbase;
+  uint8_t* sbase;
+  int64_t hstride;
+  int64_t cstride;
+  int64_t sstride;
+  int32_t r;
+  const int32_t* rowmap;
+};
+
+struct StepArgs {
+  StateRef st;
+  const int32_t* slot_idx;  // [B]
+  int32_t B;
+  int32_t H;
+  const void* q;            // [B][H][d], fp32 or bf16
+  const void* k;
+  const void* v;
+  const float* alpha;       // [B][H] or [B][H][d]
+  const float* beta;        // [B][H]
+  float* out;               // [B][H][d]
+};
+
+struct PackArgs {
+  StateRef st;
+  const int32_t* slot_idx;  // [n]
+  int32_t n;
+  int32_t H;
+  float* S;                 // [n][H][d][d] fp32, key rows in original order
+};
+
+// Each returns hipSuccess or the launch error. d must be 16, 32, 64 or 128 (checked by caller).
+hipError_t launch_step(int fmt, int d, int per_key, int bf16, const StepArgs& a, hipStream_t s);
+hipError_t launch_quantize(int d, const PackArgs& a, hipStream_t s);
+hipError_t launch_dequantize(int d, const PackArgs& a, hipStream_t s);
+
+}  // namespace damp

@@ -1,0 +1,292 @@
+"""ctypes binding of libdamp.so (include/damp.h). Argument marshalling only.
+
+Torch tensors provide device memory and the stream; every computation runs in the library's
+HIP kernels. There is no fallback: if ``libdamp.so`` is missing or cannot be loaded, every call
+raises. Shapes, dtypes, devices and contiguity are checked here so that the kernels never see
+an array smaller than the sizes passed to them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdamp.so")
+
+DAMP_OK = 0
+DAMP_ERR_INVALID_ARGUMENT = -1
+DAMP_ERR_UNSUPPORTED = -2
+DAMP_ERR_OUT_OF_MEMORY = -3
+DAMP_ERR_SLOT_INDEX = -4
+DAMP_ERR_HIP = -5
+
+DAMP_DECAY_SCALAR = 0
+DAMP_DECAY_PER_KEY = 1
+DAMP_F32 = 0
+DAMP_BF16 = 1
+
+EXPORTS = (
+    "damp_block_bytes", "damp_block_data_bytes", "damp_state_bytes", "damp_state_alloc",
+    "damp_state_free", "damp_state_layout", "damp_state_quantize", "damp_state_dequantize",
+    "damp_decode_step", "fp32_decode_step", "uniform_int8_decode_step", "uniform_int8_quantize",
+    "damp_last_error", "damp_abi_version",
+)
+
+
+class DampError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"damp status {status}: {message}")
+        self.status = status
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("num_slots", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("num_fp16_rows", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libdamp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m quantized_delta_rule_gdn_amd.build`"
+                          " or __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    LP = ctypes.POINTER(Layout)
+    sig = {
+        "damp_block_bytes": ([LP], SZ),
+        "damp_block_data_bytes": ([LP], SZ),
+        "damp_state_bytes": ([LP], SZ),
+        "damp_state_alloc": ([LP, P, P, SZ, ctypes.POINTER(P)], ctypes.c_int),
+        "damp_state_free": ([P], ctypes.c_int),
+        "damp_state_layout": ([P, LP], ctypes.c_int),
+        "damp_state_quantize": ([P, P, P, I32, P], ctypes.c_int),
+        "damp_state_dequantize": ([P, P, P, I32, P], ctypes.c_int),
+        "damp_decode_step": ([P, P, I32, P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, P],
+                             ctypes.c_int),
+        "fp32_decode_step": ([P, I32, I32, I32, I32, P, I32, P, P, P, ctypes.c_int, P,
+                              ctypes.c_int, P, P, P], ctypes.c_int),
+        "uniform_int8_decode_step": ([P, P, I32, I32, I32, I32, P, I32, P, P, P, ctypes.c_int, P,
+                                      ctypes.c_int, P, P, P], ctypes.c_int),
+        "uniform_int8_quantize": ([P, P, I32, I32, I32, I32, P, P, I32, P], ctypes.c_int),
+        "damp_last_error": ([], ctypes.c_char_p),
+        "damp_abi_version": ([], I32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return load().damp_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != DAMP_OK:
+        raise DampError(status, last_error())
+
+
+def layout(num_slots: int, num_heads: int, d: int, num_fp16_rows: int) -> Layout:
+    return Layout(num_slots, num_heads, d, d, num_fp16_rows)
+
+
+def block_bytes(num_slots: int, num_heads: int, d: int, num_fp16_rows: int) -> int:
+    return load().damp_block_bytes(ctypes.byref(layout(num_slots, num_heads, d, num_fp16_rows)))
+
+
+def block_data_bytes(num_slots: int, num_heads: int, d: int, num_fp16_rows: int) -> int:
+    return load().damp_block_data_bytes(ctypes.byref(layout(num_slots, num_heads, d,
+                                                            num_fp16_rows)))
+
+
+def state_bytes(num_slots: int, num_heads: int, d: int, num_fp16_rows: int) -> int:
+    return load().damp_state_bytes(ctypes.byref(layout(num_slots, num_heads, d, num_fp16_rows)))
+
+
+# ------------------------------------------------------------------------------------------
+# torch marshalling
+# ------------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t) -> int:
+    return t.data_ptr()
+
+
+def _need(t, name, dtype, shape, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _step_vectors(slot_idx, q, k, v, alpha, beta, out, H, d):
+    torch = _torch()
+    if slot_idx.dim() != 1:
+        raise ValueError("slot_idx must be 1-D")
+    B = slot_idx.shape[0]
+    dev = slot_idx.device
+    _need(slot_idx, "slot_idx", torch.int32, (B,), dev)
+    if q.dtype == torch.bfloat16:
+        dt = DAMP_BF16
+    elif q.dtype == torch.float32:
+        dt = DAMP_F32
+    else:
+        raise TypeError(f"q/k/v dtype {q.dtype} is not float32 or bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype, (B, H, d), dev)
+    if alpha.dim() == 3:
+        decay = DAMP_DECAY_PER_KEY
+        _need(alpha, "alpha", torch.float32, (B, H, d), dev)
+    else:
+        decay = DAMP_DECAY_SCALAR
+        _need(alpha, "alpha", torch.float32, (B, H), dev)
+    _need(beta, "beta", torch.float32, (B, H), dev)
+    _need(out, "out", torch.float32, (B, H, d), dev)
+    return B, dt, decay
+
+
+class DampState:
+    """A DAMP state pool bound to its frozen per-head FP16 row map.
+
+    ``pool`` (uint8 device tensor of ``state_bytes`` bytes) is allocated here unless given.
+    ``fp16_rows`` is an int array [num_heads, r] of ascending key rows per head."""
+
+    def __init__(self, num_slots: int, num_heads: int, d: int, fp16_rows, pool=None,
+                 device=None):
+        torch = _torch()
+        rows = np.ascontiguousarray(np.asarray(fp16_rows, dtype=np.int32).reshape(num_heads, -1))
+        r = rows.shape[1]
+        self.num_slots, self.num_heads, self.d, self.r = num_slots, num_heads, d, r
+        self.fp16_rows = rows
+        self._layout = layout(num_slots, num_heads, d, r)
+        nbytes = load().damp_state_bytes(ctypes.byref(self._layout))
+        if nbytes == 0:
+            raise DampError(DAMP_ERR_INVALID_ARGUMENT, "invalid or unsupported layout")
+        self.nbytes = nbytes
+        self.block_bytes = load().damp_block_bytes(ctypes.byref(self._layout))
+        self.block_data_bytes = load().damp_block_data_bytes(ctypes.byref(self._layout))
+        if pool is None:
+            pool = torch.empty(nbytes, dtype=torch.uint8,
+                               device=device if device is not None else "cuda")
+        _need(pool, "pool", torch.uint8, (pool.numel(),))
+        if pool.numel() < nbytes:
+            raise ValueError(f"pool has {pool.numel()} bytes, {nbytes} needed")
+        self.pool = pool
+        h = ctypes.c_void_p()
+        with torch.cuda.device(pool.device):
+            _check(load().damp_state_alloc(ctypes.byref(self._layout),
+                                           rows.ctypes.data_as(ctypes.c_void_p) if r else None,
+                                           _ptr(pool), pool.numel(), ctypes.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _check(load().damp_state_free(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def blocks(self):
+        """The pool as uint8 [num_slots, num_heads, block_bytes] (a view)."""
+        return self.pool[: self.nbytes].view(self.num_slots, self.num_heads, self.block_bytes)
+
+    def quantize(self, S, slot_idx, stream=None) -> None:
+        torch = _torch()
+        n = slot_idx.shape[0]
+        _need(slot_idx, "slot_idx", torch.int32, (n,), self.pool.device)
+        _need(S, "S", torch.float32, (n, self.num_heads, self.d, self.d), self.pool.device)
+        _check(load().damp_state_quantize(self._h, _ptr(S), _ptr(slot_idx), n, _stream(stream)))
+
+    def dequantize(self, slot_idx, S=None, stream=None):
+        torch = _torch()
+        n = slot_idx.shape[0]
+        _need(slot_idx, "slot_idx", torch.int32, (n,), self.pool.device)
+        if S is None:
+            S = torch.empty((n, self.num_heads, self.d, self.d), dtype=torch.float32,
+                            device=self.pool.device)
+        _need(S, "S", torch.float32, (n, self.num_heads, self.d, self.d), self.pool.device)
+        _check(load().damp_state_dequantize(self._h, _ptr(S), _ptr(slot_idx), n, _stream(stream)))
+        return S
+
+    def decode_step(self, slot_idx, q, k, v, alpha, beta, out, stream=None) -> None:
+        B, dt, decay = _step_vectors(slot_idx, q, k, v, alpha, beta, out, self.num_heads, self.d)
+        if slot_idx.device != self.pool.device:
+            raise ValueError("slot_idx and the pool are on different devices")
+        _check(load().damp_decode_step(self._h, _ptr(slot_idx), B, _ptr(q), _ptr(k), _ptr(v),
+                                       dt, _ptr(alpha), decay, _ptr(beta), _ptr(out),
+                                       _stream(stream)))
+
+
+def fp32_decode_step(pool, slot_idx, q, k, v, alpha, beta, out, stream=None) -> None:
+    """Decode step on an fp32 state pool [num_slots, H, d, d]."""
+    torch = _torch()
+    if pool.dim() != 4:
+        raise ValueError("pool must be [num_slots, H, d, d]")
+    S_, H, d, d2 = pool.shape
+    _need(pool, "pool", torch.float32, (S_, H, d, d2), slot_idx.device)
+    B, dt, decay = _step_vectors(slot_idx, q, k, v, alpha, beta, out, H, d)
+    _check(load().fp32_decode_step(_ptr(pool), S_, H, d, d2, _ptr(slot_idx), B, _ptr(q),
+                                   _ptr(k), _ptr(v), dt, _ptr(alpha), decay, _ptr(beta),
+                                   _ptr(out), _stream(stream)))
+
+
+def uniform_int8_decode_step(codes, scales, slot_idx, q, k, v, alpha, beta, out,
+                             stream=None) -> None:
+    """Decode step on a uniform-INT8 state: codes int8 [num_slots, H, d, d], scales fp32
+    [num_slots, H, d]."""
+    torch = _torch()
+    if codes.dim() != 4:
+        raise ValueError("codes must be [num_slots, H, d, d]")
+    S_, H, d, d2 = codes.shape
+    _need(codes, "codes", torch.int8, (S_, H, d, d2), slot_idx.device)
+    _need(scales, "scales", torch.float32, (S_, H, d), slot_idx.device)
+    B, dt, decay = _step_vectors(slot_idx, q, k, v, alpha, beta, out, H, d)
+    _check(load().uniform_int8_decode_step(_ptr(codes), _ptr(scales), S_, H, d, d2,
+                                           _ptr(slot_idx), B, _ptr(q), _ptr(k), _ptr(v), dt,
+                                           _ptr(alpha), decay, _ptr(beta), _ptr(out),
+                                           _stream(stream)))
+
+
+def uniform_int8_quantize(codes, scales, S, slot_idx, stream=None) -> None:
+    torch = _torch()
+    S_, H, d, d2 = codes.shape
+    n = slot_idx.shape[0]
+    _need(codes, "codes", torch.int8, (S_, H, d, d2), slot_idx.device)
+    _need(scales, "scales", torch.float32, (S_, H, d), slot_idx.device)
+    _need(slot_idx, "slot_idx", torch.int32, (n,), codes.device)
+    _need(S, "S", torch.float32, (n, H, d, d2), codes.device)
+    _check(load().uniform_int8_quantize(_ptr(codes), _ptr(scales), S_, H, d, d2, _ptr(S),
+                                        _ptr(slot_idx), n, _stream(stream)))

@@ -1,0 +1,143 @@
+"""CPU-only checks of the C-ABI library: it loads without a GPU, exports every entry point the
+header declares, reports the documented storage accounting, and rejects bad arguments on the
+host (before any HIP call) with the documented status codes."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from quantized_delta_rule_gdn_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "damp.h")
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_0-9]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = lib.load()
+    declared = _header_functions()
+    assert len(declared) >= 14
+    assert set(declared) == set(lib.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.damp_abi_version() == (1 << 16)
+
+
+def test_block_accounting_d128():
+    assert lib.block_data_bytes(1, 1, 128, 24) == 6144 + 13312 + 416 == 19872
+    assert lib.block_bytes(1, 1, 128, 24) == 19968
+    assert lib.block_data_bytes(1, 1, 128, 0) == 16384 + 512       # uniform INT8 + row scales
+    assert lib.block_data_bytes(1, 1, 128, 128) == 32768            # all FP16 = 16 bits/value
+    assert lib.state_bytes(4096, 32, 128, 24) == 4096 * 32 * 19968
+    bits = 8 * lib.block_data_bytes(1, 1, 128, 24) / 128 ** 2
+    assert abs(bits - 9.703125) < 1e-12
+    assert abs((1 - bits / 32) - 0.6967773) < 1e-6
+
+
+def test_bits_accounting_matches_page_identities():
+    """bits/value -> compression and storage reduction, as printed on the pages."""
+    g = json.load(open(os.path.join(GOLD, "page_identities.json")))
+    for case in g["cases"]:
+        if "reduction_pct" in case:
+            assert round(100 * (1 - case["bits"] / 32), 1) == case["reduction_pct"]
+        if "compression" in case:
+            # both numbers are printed rounded (bits to 3 decimals, compression to 2): the
+            # identity compression = 32 / bits must hold for some value in both intervals
+            b, c = case["bits"], case["compression"]
+            lo, hi = 32 / (c + 0.005), 32 / (c - 0.005)
+            assert max(lo, b - 0.0005) <= min(hi, b + 0.0005)
+            assert abs(32 / b - c) < 0.006
+    # with fp32 row scales, r FP16 rows per 128x128 head give 9.9 bits/value at r ~ 27
+    r_for_9_9 = min(range(129), key=lambda r: abs(8 * lib.block_data_bytes(1, 1, 128, r) / 128 ** 2 - 9.9))
+    assert r_for_9_9 == 27
+
+
+@pytest.mark.parametrize("d,r", [(0, 0), (128, 129), (128, -1), (100, 4), (256, 8), (48, 0)])
+def test_invalid_layouts_report_zero_bytes(d, r):
+    assert lib.state_bytes(4, 2, d, r) == 0
+
+
+def _alloc(layout, rows, pool, nbytes):
+    L = lib.load()
+    h = ctypes.c_void_p()
+    rows_p = rows.ctypes.data_as(ctypes.c_void_p) if rows is not None else None
+    st = L.damp_state_alloc(ctypes.byref(layout) if layout is not None else None, rows_p, pool,
+                            nbytes, ctypes.byref(h))
+    return st, h
+
+
+def test_alloc_rejects_bad_arguments_on_host():
+    L = lib.load()
+    good_rows = np.array([[0, 5], [1, 7]], np.int32)
+    lay = lib.layout(4, 2, 16, 2)
+    need = lib.state_bytes(4, 2, 16, 2)
+    fake_pool = 0x100000  # never dereferenced: every case fails validation first
+    cases = [
+        (None, good_rows, fake_pool, need, lib.DAMP_ERR_INVALID_ARGUMENT, "layout is NULL"),
+        (lib.layout(4, 2, 100, 2), good_rows, fake_pool, 1 << 30, lib.DAMP_ERR_UNSUPPORTED, "supported"),
+        (lib.layout(4, 2, 16, 17), good_rows, fake_pool, need, lib.DAMP_ERR_INVALID_ARGUMENT, "num_fp16_rows"),
+        (lay, None, fake_pool, need, lib.DAMP_ERR_INVALID_ARGUMENT, "fp16_rows is NULL"),
+        (lay, good_rows, None, need, lib.DAMP_ERR_INVALID_ARGUMENT, "pool is NULL"),
+        (lay, good_rows, fake_pool + 16, need, lib.DAMP_ERR_INVALID_ARGUMENT, "aligned"),
+        (lay, good_rows, fake_pool, need - 1, lib.DAMP_ERR_INVALID_ARGUMENT, "needed"),
+        (lay, np.array([[5, 0], [1, 7]], np.int32), fake_pool, need, lib.DAMP_ERR_INVALID_ARGUMENT, "ascending"),
+        (lay, np.array([[0, 16], [1, 7]], np.int32), fake_pool, need, lib.DAMP_ERR_INVALID_ARGUMENT, "outside"),
+        (lay, np.array([[3, 3], [1, 7]], np.int32), fake_pool, need, lib.DAMP_ERR_INVALID_ARGUMENT, "ascending"),
+    ]
+    for layout, rows, pool, nbytes, want, msg in cases:
+        st, h = _alloc(layout, rows, pool, nbytes)
+        assert st == want, (st, want, lib.last_error())
+        assert msg in lib.last_error()
+        assert not h.value
+
+
+def test_step_entry_points_reject_bad_arguments_on_host():
+    L = lib.load()
+    fp = ctypes.c_void_p(0x100000)
+    ok = ctypes.c_void_p(0x200000)
+    # unsupported size
+    st = L.fp32_decode_step(fp, 4, 2, 48, 48, ok, 1, ok, ok, ok, lib.DAMP_F32, ok, 0, ok, ok, None)
+    assert st == lib.DAMP_ERR_UNSUPPORTED
+    st = L.uniform_int8_decode_step(fp, fp, 4, 2, 128, 64, ok, 1, ok, ok, ok, lib.DAMP_F32, ok, 0,
+                                    ok, ok, None)
+    assert st == lib.DAMP_ERR_UNSUPPORTED
+    # negative batch, bad enums, null pointers, misaligned output
+    assert L.fp32_decode_step(fp, 4, 2, 16, 16, ok, -1, ok, ok, ok, 0, ok, 0, ok, ok, None) == \
+        lib.DAMP_ERR_INVALID_ARGUMENT
+    assert L.fp32_decode_step(fp, 4, 2, 16, 16, ok, 1, ok, ok, ok, 7, ok, 0, ok, ok, None) == \
+        lib.DAMP_ERR_INVALID_ARGUMENT
+    assert L.fp32_decode_step(fp, 4, 2, 16, 16, ok, 1, ok, ok, ok, 0, ok, 3, ok, ok, None) == \
+        lib.DAMP_ERR_INVALID_ARGUMENT
+    assert L.fp32_decode_step(fp, 4, 2, 16, 16, ok, 1, None, ok, ok, 0, ok, 0, ok, ok, None) == \
+        lib.DAMP_ERR_INVALID_ARGUMENT
+    assert L.fp32_decode_step(fp, 4, 2, 16, 16, ok, 1, ok, ok, ok, 0, ok, 0, ok,
+                              ctypes.c_void_p(0x200004), None) == lib.DAMP_ERR_INVALID_ARGUMENT
+    assert "16-byte" in lib.last_error()
+    assert L.fp32_decode_step(None, 4, 2, 16, 16, ok, 1, ok, ok, ok, 0, ok, 0, ok, ok, None) == \
+        lib.DAMP_ERR_INVALID_ARGUMENT
+    assert L.fp32_decode_step(fp, 0, 2, 16, 16, ok, 1, ok, ok, ok, 0, ok, 0, ok, ok, None) == \
+        lib.DAMP_ERR_INVALID_ARGUMENT
+    # B == 0 is a no-op that needs no GPU
+    assert L.fp32_decode_step(fp, 4, 2, 16, 16, None, 0, None, None, None, 0, None, 0, None, None,
+                              None) == lib.DAMP_OK
+    assert L.uniform_int8_decode_step(None, None, 4, 2, 16, 16, None, 0, None, None, None, 0, None,
+                                      0, None, None, None) == lib.DAMP_OK
+    # NULL handles
+    assert L.damp_decode_step(None, ok, 1, ok, ok, ok, 0, ok, 0, ok, ok, None) == \
+        lib.DAMP_ERR_INVALID_ARGUMENT
+    assert L.damp_state_quantize(None, ok, ok, 1, None) == lib.DAMP_ERR_INVALID_ARGUMENT
+    assert L.damp_state_dequantize(None, ok, ok, 1, None) == lib.DAMP_ERR_INVALID_ARGUMENT
+    assert L.damp_state_free(None) == lib.DAMP_OK
+    assert L.uniform_int8_quantize(fp, fp, 4, 2, 16, 16, ok, ok, -2, None) == \
+        lib.DAMP_ERR_INVALID_ARGUMENT

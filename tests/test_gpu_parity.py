@@ -1,0 +1,238 @@
+"""GPU parity: the HIP decode step (through the C ABI) against the CPU oracle, from identical
+input states, for the DAMP, fp32 and uniform-INT8 formats. Tolerances: see gpu_common."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+import oracle  # noqa: E402
+import layout_ref  # noqa: E402
+from gpu_common import (DampPool, check_fp32_state, check_quant, check_readout,  # noqa: E402
+                        fp32_state_bound, gpu_fp32_step, gpu_int8_step, ref_vectors, step_tensors,
+                        to_dev)
+from quantized_delta_rule_gdn_amd import lib, synth  # noqa: E402
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _random_case(seed, B, H, D, r, decay, dtype, outliers=True):
+    rng = np.random.default_rng(seed)
+    S = synth.normal_states(rng, (B, H, D, D), 0.1)
+    if outliers:   # a few heavy key rows and value columns per head
+        for h in range(H):
+            S[:, h, rng.choice(D, max(1, D // 32), replace=False), :] *= 8
+            S[:, h, :, rng.choice(D, max(1, D // 32), replace=False)] *= 5
+    rows = synth.random_rows(rng, H, D, r)
+    inp = synth.step_inputs(rng, B, H, D, decay, dtype)
+    return rows, S, inp
+
+
+def _damp_ref_and_gpu(rows, S, inp, slots, num_slots):
+    B, H, D, _ = S.shape
+    mask = synth.rows_to_mask(rows, D)
+    maskn = np.broadcast_to(mask, (B, H, D)).reshape(B * H, D)
+    h, c, s = oracle.quantize(maskn, S.reshape(B * H, D, D))
+    pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D),
+                    slots, num_slots)
+    out = pool.step(inp)
+    got = pool.logical()
+    ref_out = oracle.step_quant(maskn, h, c, s, *ref_vectors(inp, B, H, D))
+    ref = (h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D))
+    return mask, out, got, ref_out.reshape(B, H, D), ref, pool
+
+
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("D,r,B,H,decay,dtype", [
+    (16, 0, 1, 2, synth.GDN, "fp32"),
+    (16, 5, 3, 2, synth.KDA, "bf16"),
+    (32, 3, 5, 3, synth.GDN, "bf16"),
+    (64, 8, 7, 4, synth.KDA, "fp32"),
+    (128, 0, 3, 4, synth.GDN, "bf16"),
+    (128, 24, 37, 4, synth.GDN, "bf16"),
+    (128, 27, 9, 3, synth.KDA, "bf16"),
+    (128, 1, 2, 2, synth.GDN, "fp32"),
+    (128, 128, 2, 2, synth.KDA, "bf16"),
+])
+def test_damp_step_sizes_and_edges(D, r, B, H, decay, dtype):
+    _log(f"damp step D={D} r={r} B={B} H={H} decay={decay} dtype={dtype}")
+    rows, S, inp = _random_case(D * 1000 + r * 10 + B, B, H, D, r, decay, dtype)
+    num_slots = 2 * B + 3
+    slots = np.random.default_rng(B).choice(num_slots, B, replace=False)
+    mask, out, got, ref_out, ref, pool = _damp_ref_and_gpu(rows, S, inp, slots, num_slots)
+    check_readout(out, ref_out)
+    _log(str(check_quant(mask, got, ref)))
+    # untouched slots keep their sentinel bytes
+    other = np.setdiff1d(np.arange(num_slots), slots)
+    blk = pool.state.blocks()[torch.from_numpy(other).long().cuda()]
+    assert bool((blk == 0xA5).all())
+
+
+@pytest.mark.parametrize("D,B,H,decay,dtype", [(16, 2, 2, synth.GDN, "fp32"),
+                                               (64, 3, 2, synth.KDA, "bf16"),
+                                               (128, 11, 4, synth.GDN, "bf16"),
+                                               (128, 5, 3, synth.KDA, "fp32")])
+def test_fp32_step_within_error_bound(D, B, H, decay, dtype):
+    _log(f"fp32 step D={D} B={B} H={H}")
+    rows, S, inp = _random_case(7 + D + B, B, H, D, 0, decay, dtype)
+    slots = np.arange(B)[::-1].copy()
+    out, Sg = gpu_fp32_step(S, inp, slots, B + 1)
+    Sr = S.reshape(B * H, D, D).copy()
+    q, k, v, a, b = ref_vectors(inp, B, H, D)
+    ref_out = oracle.step_fp32(Sr, q, k, v, a, b)
+    check_readout(out, ref_out)
+    bound = fp32_state_bound(S.reshape(B * H, D, D), a, k, v, b, Sr)
+    err = check_fp32_state(Sg.reshape(B * H, D, D), Sr, bound)
+    _log(f"fp32 state max abs err {err:.3g}")
+
+
+def test_uniform_int8_equals_damp_without_fp16_rows():
+    """Same values in the two layouts give bit-identical results (same kernel arithmetic)."""
+    B, H, D = 6, 4, 128
+    rows, S, inp = _random_case(99, B, H, D, 0, synth.KDA, "bf16")
+    mask, out_d, got_d, ref_out, ref, _ = _damp_ref_and_gpu(rows, S, inp, np.arange(B), B)
+    # the same pre-step values in the uniform-INT8 arrays
+    h0, c0, s0 = oracle.quantize(np.zeros((B * H, D), np.uint8), S.reshape(B * H, D, D))
+    out_i, c_i, s_i = gpu_int8_step(c0.reshape(B, H, D, D), s0.reshape(B, H, D), inp,
+                                    np.arange(B), B)
+    assert np.array_equal(out_i, out_d)
+    assert np.array_equal(c_i, got_d[1])
+    assert np.array_equal(s_i, got_d[2])
+    check_readout(out_i, ref_out)
+
+
+def test_constant_kda_gate_equals_gdn_gate_bitwise():
+    B, H, D, r = 4, 4, 128, 24
+    rows, S, inp = _random_case(5, B, H, D, r, synth.GDN, "bf16")
+    _, out_g, got_g, _, _, _ = _damp_ref_and_gpu(rows, S, inp, np.arange(B), B)
+    inp_k = synth.StepInputs(inp.q, inp.k, inp.v,
+                             np.repeat(inp.alpha[:, :, None], D, axis=2).copy(), inp.beta,
+                             inp.dtype, inp.q_bits, inp.k_bits, inp.v_bits)
+    _, out_k, got_k, _, _, _ = _damp_ref_and_gpu(rows, S, inp_k, np.arange(B), B)
+    assert np.array_equal(out_g, out_k)
+    for a, b in zip(got_g, got_k):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("D,r", [(16, 2), (128, 24), (128, 0), (64, 13)])
+def test_quantize_and_dequantize_kernels_bit_exact(D, r):
+    """Packing from fp32 takes the same binary32 decisions as the oracle: bit-identical."""
+    n, H = 5, 3
+    rng = np.random.default_rng(D + r)
+    S = synth.normal_states(rng, (n, H, D, D), 0.1)
+    S[0, 0, 3] = 0.0                     # an all-zero row
+    S[1, 1, 5, 7] = 127.0                # absmax 127 -> scale exactly 1 ...
+    S[1, 1, 5, :7] = np.arange(7) + 0.5  # ... and exact .5 ties
+    rows = synth.random_rows(rng, H, D, r)
+    mask = synth.rows_to_mask(rows, D)
+    maskn = np.broadcast_to(mask, (n, H, D)).reshape(n * H, D)
+    h, c, s = oracle.quantize(maskn, S.reshape(n * H, D, D))
+    num_slots = n + 2
+    slots = np.array([2, 0, 6, 3, 5], np.int32)
+    st = lib.DampState(num_slots, H, D, rows)
+    st.pool.fill_(0xA5)
+    st.quantize(to_dev(S), to_dev(slots))
+    blocks = st.blocks()[torch.from_numpy(slots).long().cuda()].cpu().numpy()
+    hg, cg, sg = layout_ref.unpack(rows, blocks, D)
+    m = np.broadcast_to(mask, (n, H, D)).astype(bool)
+    assert np.array_equal(hg[m], h.reshape(n, H, D, D)[m])
+    assert np.array_equal(cg[~m], c.reshape(n, H, D, D)[~m])
+    assert np.array_equal(sg[~m], s.reshape(n, H, D)[~m])
+    # padding and untouched slots stay as they were
+    stride, data = layout_ref.block_stride(D, r), layout_ref.block_data_bytes(D, r)
+    assert np.all(blocks[:, :, data:stride] == 0xA5)
+    Sd = st.dequantize(to_dev(slots)).cpu().numpy()
+    Sr = oracle.dequantize(maskn, h, c, s).reshape(n, H, D, D)
+    assert np.array_equal(Sd, Sr)
+
+
+def test_uniform_int8_quantize_bit_exact():
+    n, H, D = 3, 2, 128
+    S = synth.normal_states(np.random.default_rng(3), (n, H, D, D), 0.1)
+    h, c, s = oracle.quantize(np.zeros((n * H, D), np.uint8), S.reshape(n * H, D, D))
+    codes = torch.zeros((n + 1, H, D, D), dtype=torch.int8, device="cuda")
+    scales = torch.zeros((n + 1, H, D), dtype=torch.float32, device="cuda")
+    slots = np.array([1, 3, 0], np.int32)
+    lib.uniform_int8_quantize(codes, scales, to_dev(S), to_dev(slots))
+    sl = torch.from_numpy(slots).long().cuda()
+    assert np.array_equal(codes[sl].cpu().numpy(), c.reshape(n, H, D, D))
+    assert np.array_equal(scales[sl].cpu().numpy(), s.reshape(n, H, D))
+
+
+def test_zero_batch_is_a_no_op():
+    rows = np.zeros((2, 0), np.int32)
+    st = lib.DampState(3, 2, 16, rows)
+    st.pool.fill_(7)
+    e = torch.empty((0, 2, 16), dtype=torch.float32, device="cuda")
+    st.decode_step(torch.empty(0, dtype=torch.int32, device="cuda"), e, e, e,
+                   torch.empty((0, 2), device="cuda"), torch.empty((0, 2), device="cuda"), e)
+    torch.cuda.synchronize()
+    assert bool((st.pool == 7).all())
+
+
+def test_tiny_workload_every_step_from_identical_state():
+    """1 slot, 2 GDN heads, D = 16, 2 FP16 rows per head, 8 steps: at every step the GPU starts
+    from the oracle's state, for DAMP, fp32 and uniform INT8."""
+    rows, S0, steps = synth.tiny()
+    H, D = 2, 16
+    mask = synth.rows_to_mask(rows, D)
+    h, c, s = oracle.quantize(mask, S0.reshape(H, D, D))
+    S32 = S0.reshape(H, D, D).copy()
+    z = np.zeros((H, D), np.uint8)
+    hi, ci, si = oracle.quantize(z, S0.reshape(H, D, D))
+    for t, st in enumerate(steps):
+        _log(f"tiny step {t}")
+        pool = DampPool(rows, h.reshape(1, H, D, D), c.reshape(1, H, D, D), s.reshape(1, H, D),
+                        [0], 1)
+        out = pool.step(st)
+        got = pool.logical()
+        ref_out = oracle.step_quant(mask, h, c, s, *ref_vectors(st, 1, H, D))
+        check_readout(out, ref_out)
+        check_quant(mask, got, (h.reshape(1, H, D, D), c.reshape(1, H, D, D), s.reshape(1, H, D)))
+        # fp32 format
+        S_in = S32.copy()
+        o32, Sg = gpu_fp32_step(S_in.reshape(1, H, D, D), st, [0], 1)
+        q, k, v, a, b = ref_vectors(st, 1, H, D)
+        r32 = oracle.step_fp32(S32, q, k, v, a, b)
+        check_readout(o32, r32)
+        check_fp32_state(Sg.reshape(H, D, D), S32, fp32_state_bound(S_in, a, k, v, b, S32))
+        # uniform INT8
+        oi, cg, sg = gpu_int8_step(ci.reshape(1, H, D, D).copy(), si.reshape(1, H, D).copy(), st,
+                                   [0], 1)
+        ri = oracle.step_quant(z, hi, ci, si, q, k, v, a, b)
+        check_readout(oi, ri)
+        check_quant(np.zeros((1, H, D), np.uint8), (np.zeros_like(cg, np.uint16), cg, sg),
+                    (hi.reshape(1, H, D, D), ci.reshape(1, H, D, D), si.reshape(1, H, D)))
+
+
+def test_debug_mode_rejects_bad_slots(monkeypatch):
+    """DAMP_DEBUG=1 validates slot indices on the host before launching anything."""
+    import subprocess
+    import sys
+    import os
+    code = r"""
+import numpy as np, torch
+from quantized_delta_rule_gdn_amd import lib
+st = lib.DampState(4, 2, 16, np.zeros((2, 0), np.int32))
+st.pool.zero_()
+q = torch.zeros((2, 2, 16), device='cuda'); a = torch.full((2, 2), 0.5, device='cuda')
+out = torch.empty((2, 2, 16), device='cuda')
+for bad in ([0, 4], [1, 1], [-1, 0]):
+    try:
+        st.decode_step(torch.tensor(bad, dtype=torch.int32, device='cuda'), q, q, q, a, a, out)
+        raise SystemExit('accepted %r' % (bad,))
+    except lib.DampError as e:
+        assert e.status == lib.DAMP_ERR_SLOT_INDEX, e
+st.decode_step(torch.tensor([3, 0], dtype=torch.int32, device='cuda'), q, q, q, a, a, out)
+torch.cuda.synchronize()
+print('ok')
+"""
+    env = dict(os.environ, DAMP_DEBUG="1")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
