@@ -58,7 +58,23 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", choices=["damp", "fp32", "int8"], default=None,
                    help="time only this format (for profiling)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="instead of the step, run a plain device copy of MIB MiB --steps times "
+                        "(the reference kernel of known size for HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib: int, steps: int) -> None:
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.ones(mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.zeros_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": mib << 20, "bytes_written": mib << 20,
+                      "launches": steps}), flush=True)
 
 
 def make_inputs(torch, synth, dev):
@@ -137,6 +153,9 @@ def main():
               "independent; a multi-GPU run would shard slots or heads with no exchange)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     import torch
     from quantized_delta_rule_gdn_amd import lib, synth
 

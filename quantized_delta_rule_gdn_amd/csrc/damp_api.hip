@@ -18,7 +18,7 @@ struct damp_state {
   damp_layout layout;
   uint8_t* pool;
   size_t block_bytes;
-  int32_t* rowmap_dev;  // [num_heads][d]: storage row -> key row
+  uint8_t* rowmap_dev;  // [num_heads][d]: storage row -> key row
 };
 
 namespace {
@@ -141,6 +141,7 @@ damp::StateRef damp_ref(const damp_state* s) {
   ref.hstride = ref.cstride = ref.sstride = static_cast<int64_t>(s->block_bytes);
   ref.r = L.num_fp16_rows;
   ref.rowmap = s->rowmap_dev;
+  ref.contiguous = 1;
   return ref;
 }
 
@@ -154,6 +155,7 @@ damp::StateRef int8_ref(int8_t* codes, float* scales, int32_t d) {
   ref.sstride = static_cast<int64_t>(d) * 4;
   ref.r = 0;
   ref.rowmap = nullptr;
+  ref.contiguous = 0;
   return ref;
 }
 
@@ -175,6 +177,11 @@ damp_status run_step(int fmt, const damp::StateRef& ref, int32_t d, int32_t H, i
   a.alpha = alpha;
   a.beta = beta;
   a.out = out;
+  // the persistent kernel stages q/k/v (and a per-key gate) with 16-byte LDS loads
+  a.grid = (fmt == damp::FMT_Q && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&
+            (decay == DAMP_DECAY_SCALAR || aligned(alpha, 16)))
+               ? -1
+               : 0;
   return launched(damp::launch_step(fmt, d, decay == DAMP_DECAY_PER_KEY, dt == DAMP_BF16, a, s),
                   "decode step");
 }
@@ -220,7 +227,7 @@ damp_status damp_state_alloc(const damp_layout* L, const int32_t* fp16_rows, voi
   if (pool_bytes < need)
     return fail(DAMP_ERR_INVALID_ARGUMENT, "pool_bytes %zu < %zu needed", pool_bytes, need);
   // storage order per head: the r FP16 rows ascending, then the remaining rows ascending
-  std::vector<int32_t> map(static_cast<size_t>(H) * d);
+  std::vector<uint8_t> map(static_cast<size_t>(H) * d);
   std::vector<unsigned char> isfp16(static_cast<size_t>(d));
   for (int32_t h = 0; h < H; ++h) {
     std::fill(isfp16.begin(), isfp16.end(), 0);
@@ -231,25 +238,25 @@ damp_status damp_state_alloc(const damp_layout* L, const int32_t* fp16_rows, voi
       if (j > 0 && row <= fp16_rows[static_cast<size_t>(h) * r + j - 1])
         return fail(DAMP_ERR_INVALID_ARGUMENT, "fp16_rows[%d] must be strictly ascending", h);
       isfp16[static_cast<size_t>(row)] = 1;
-      map[static_cast<size_t>(h) * d + j] = row;
+      map[static_cast<size_t>(h) * d + j] = static_cast<uint8_t>(row);
     }
     int32_t p = r;
     for (int32_t i = 0; i < d; ++i)
-      if (!isfp16[static_cast<size_t>(i)]) map[static_cast<size_t>(h) * d + p++] = i;
+      if (!isfp16[static_cast<size_t>(i)]) map[static_cast<size_t>(h) * d + p++] = static_cast<uint8_t>(i);
   }
   damp_state* s = new (std::nothrow) damp_state{};
   if (!s) return fail(DAMP_ERR_OUT_OF_MEMORY, "host allocation of the handle failed");
   s->layout = *L;
   s->pool = static_cast<uint8_t*>(pool);
   s->block_bytes = round_up(data_bytes(L), kBlockAlign);
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->rowmap_dev), sizeof(int32_t) * map.size());
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->rowmap_dev), map.size());
   if (e != hipSuccess) {
     delete s;
     (void)hipGetLastError();
     return fail(e == hipErrorOutOfMemory ? DAMP_ERR_OUT_OF_MEMORY : DAMP_ERR_HIP,
                 "hipMalloc of the row map: %s", hipGetErrorString(e));
   }
-  e = hipMemcpy(s->rowmap_dev, map.data(), sizeof(int32_t) * map.size(), hipMemcpyHostToDevice);
+  e = hipMemcpy(s->rowmap_dev, map.data(), map.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(s->rowmap_dev);
     delete s;

@@ -15,6 +15,7 @@ enum Fmt : int { FMT_F32 = 0, FMT_Q = 1 };  // fp32 state / FP16 + INT8 rows (DA
 //            storage row p >= r is INT8 at cbase + u * cstride + (p - r) d,
 //            with its fp32 scale at sbase + u * sstride + 4 (p - r);
 //            rowmap[head * d + p] = the key row held in storage row p (nullptr = identity).
+//   contiguous: the three regions of a unit are adjacent (DAMP pool blocks).
 struct StateRef {
   uint8_t* hbase;
   uint8_t* cbase;
@@ -23,11 +24,13 @@ struct StateRef {
   int64_t cstride;
   int64_t sstride;
   int32_t r;
-  const int32_t* rowmap;
+  const uint8_t* rowmap;
+  int32_t contiguous;
 };
 
 struct StepArgs {
   StateRef st;
+  int32_t grid;             // persistent launch: < 0 = choose the grid, 0 = one workgroup per unit
   const int32_t* slot_idx;  // [B]
   int32_t B;
   int32_t H;

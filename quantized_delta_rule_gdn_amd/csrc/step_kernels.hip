@@ -20,9 +20,13 @@
 // fully coalesced. Column sums over key rows use the gfx950 cross-row lane swaps
 // (v_permlane16_swap / v_permlane32_swap) inside a wave and LDS across waves; the row absmax for
 // requantization is a DPP butterfly inside the 16 lanes of a row. No MFMA: each unit is a
-// matrix-vector update at ~4 flop/byte, far below the fp32 ridge; the kernel is HBM-bound.
+// matrix-vector update at ~4 flop/byte, far below the fp32 ridge; the kernel is HBM-bound, and
+// its VALU work per state element is kept to about ten instructions so that it stays so
+// (CDNA4 issues one wave64 VALU instruction per SIMD every 4 cycles).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <cstdlib>
 
 #include "launch.h"
 
@@ -38,6 +42,10 @@ struct Geo {
   static constexpr int RPL = D / RPS;                          // row steps (rows) per lane
   static_assert(D % 16 == 0 && RPL * RPS == D, "unsupported d");
 };
+
+// Kind of one stored row.
+// K_MIX: a wave's row step holding both kinds (the FP16 / INT8 boundary when r % 4 != 0).
+enum Kind : int { K_F32 = 0, K_F16 = 1, K_I8 = 2, K_MIX = 3 };
 
 // ---- raw byte movement: N bytes per lane as 32-bit words ----------------------------------
 template <int N>
@@ -128,19 +136,31 @@ __device__ __forceinline__ float sum_row_slots(float x) {
 // Max over the 16 lanes of a row: DPP quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
 // row_mirror. Exact (max is order-free); every lane of the row ends with the row max.
 __device__ __forceinline__ float max_row16(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true)));
   return x;
 }
 
-// INT8 code of x for a row scale s (s > 0) with inv = fl(1/s): round-half-to-even of the
-// binary32 quotient fl(x / s), as the row rule defines it. The fast estimate y = fl(x * inv)
-// is within 2^-23 relative (|y| <= 127.5, so within 1.6e-5 absolute) of x/s, and fl(x/s) is
-// within 3.9e-6 of x/s; when y is farther than 2^-15 from a half-integer, fl(x/s) rounds to
-// the same integer as y, otherwise the exact division is taken (a few cases per million).
-__device__ __forceinline__ int32_t int8_code(float x, float s, float inv) {
+// ---- the INT8 row rule --------------------------------------------------------------------
+// scale = fl(m / 127). q = fl(m * fl(1/127)) followed by one residual correction gives the
+// correctly rounded quotient: checked against IEEE division for every binary32 significand at
+// exponents from 2^-120 to 2^127, which covers every finite non-negative m the rule meets.
+constexpr float kInv127 = 1.0f / 127.0f;
+
+__device__ __forceinline__ float div127(float m) {
+  const float q = m * kInv127;
+  const float r = fmaf(-q, 127.0f, m);
+  return fmaf(r, kInv127, q);
+}
+
+// Exact code: round-half-to-even of the binary32 quotient fl(x / s) (s > 0, inv = fl(1/s)).
+// The estimate y = fl(x * inv) is within 2^-23 relative (|y| <= 127.5: 1.6e-5 absolute) of
+// x/s, and fl(x/s) within 3.9e-6 of it, so unless y is within 2^-15 of a half-integer both
+// round to the same integer; otherwise the IEEE division decides. Used where the input is
+// the caller's fp32 state (pack), so that packing is bit-identical to the rule.
+__device__ __forceinline__ int32_t int8_code_exact(float x, float s, float inv) {
   const float y = x * inv;
   float n = rintf(y);
   if (fabsf(y - n) > 0.5f - 0x1p-15f) n = rintf(__fdiv_rn(x, s));
@@ -148,281 +168,919 @@ __device__ __forceinline__ int32_t int8_code(float x, float s, float inv) {
   return static_cast<int32_t>(n);
 }
 
-// ---- requantize-and-store of the lane's RPL x CPL values (shared by step and pack) -------
-template <int D, int FMT>
-__device__ __forceinline__ void store_state(const StateRef& st, int64_t unit, int w, int rs,
-                                            int cg, float (&X)[Geo<D>::RPL][Geo<D>::CPL]) {
-  using G = Geo<D>;
-  constexpr int CPL = G::CPL;
-  const int r = FMT == FMT_Q ? st.r : 0;
-#pragma unroll
-  for (int t = 0; t < G::RPL; ++t) {
-    const int p = t * G::RPS + w * 4 + rs;
-    if constexpr (FMT == FMT_F32) {
-      uint32_t wd[CPL];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) wd[c] = __float_as_uint(X[t][c]);
-      store_bytes<CPL * 4>(st.hbase + unit * st.hstride + (int64_t(p) * D + cg * CPL) * 4, wd);
-    } else {
-      if (p < r) {
-        uint32_t wd[Words<CPL * 2>::W];
-#pragma unroll
-        for (int i = 0; i < Words<CPL * 2>::W; ++i) wd[i] = 0;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) wd[c >> 1] |= float_to_half_bits(X[t][c]) << (16 * (c & 1));
-        store_bytes<CPL * 2>(st.hbase + unit * st.hstride + (int64_t(p) * D + cg * CPL) * 2, wd);
-      } else {
-        float m = 0.0f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) m = fmaxf(m, fabsf(X[t][c]));
-        m = max_row16(m);
-        const float s = m > 0.0f ? __fdiv_rn(m, 127.0f) : 0.0f;
-        const float inv = m > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
-        uint32_t wd[Words<CPL>::W];
-#pragma unroll
-        for (int i = 0; i < Words<CPL>::W; ++i) wd[i] = 0;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const int32_t code = m > 0.0f ? int8_code(X[t][c], s, inv) : 0;
-          wd[c >> 2] |= (static_cast<uint32_t>(code) & 0xFFu) << (8 * (c & 3));
-        }
-        store_bytes<CPL>(st.cbase + unit * st.cstride + int64_t(p - r) * D + cg * CPL, wd);
-        if (cg == 0)
-          reinterpret_cast<float*>(st.sbase + unit * st.sstride)[p - r] = s;
-      }
-    }
+// Fast code inside the step: round-half-to-even of x * rcp(s), with v_rcp_f32 (1 ulp) and the
+// rounding done by one fma against 1.5 * 2^23 (the integer lands in the low mantissa bits, so
+// the low byte is the two's-complement code). |x * rcp(s)| <= 127 (1 + 2^-22) < 127.5, so no
+// clamp is needed. It can differ from the exact rule only where x/s lies within ~2e-5 of a
+// half-integer (a few codes per 100,000, by one); the step's X itself differs from the
+// oracle's by a few fp32 ulps, which moves codes at the same places.
+__device__ __forceinline__ uint32_t int8_code_fast_bits(float x, float inv) {
+  return __float_as_uint(fmaf(x, inv, 0x1.8p23f));
+}
+
+// Pack the low bytes of four words: v_perm_b32 picks byte 0 of each source.
+__device__ __forceinline__ uint32_t pack4_low_bytes(uint32_t f0, uint32_t f1, uint32_t f2,
+                                                    uint32_t f3) {
+  const uint32_t lo = __builtin_amdgcn_perm(f1, f0, 0x0c0c0400u);  // f0.b0, f1.b0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(f3, f2, 0x04000c0cu);  // 0, 0, f2.b0, f3.b0
+  return lo | hi;
+}
+
+// ---- one lane's part of one stored row: load, decode, requantize + store ----------------
+// State traffic goes through raw buffer instructions: one scalar resource per region of the
+// unit (base, byte size), a 32-bit per-lane offset, and hardware range checking (an offset
+// past the region reads 0 and drops the write).
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor word 3 for raw byte access
+// Cache policy of the state traffic: non-temporal ("nt"). Every state byte is read once and
+// written once per step, so keeping it out of the caches' normal replacement matters: on MI355X
+// a streaming copy runs ~6 TB/s with nt and ~3.7-5.3 TB/s without.
+constexpr int kNT = 2;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kRsrcWord3);
+}
+
+template <int N>
+__device__ __forceinline__ void buf_load(rsrc_t rs, uint32_t off, uint32_t soff, uint32_t* w) {
+  if constexpr (N == 32) {
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, off, soff, kNT);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, soff, kNT);
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+    w[4] = b[0]; w[5] = b[1]; w[6] = b[2]; w[7] = b[3];
+  } else if constexpr (N == 16) {
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, off, soff, kNT);
+    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
+  } else if constexpr (N == 8) {
+    const auto a = __builtin_amdgcn_raw_buffer_load_b64(rs, off, soff, kNT);
+    w[0] = a[0]; w[1] = a[1];
+  } else if constexpr (N == 4) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, soff, kNT);
+  } else if constexpr (N == 2) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, soff, kNT);
+  } else {
+    static_assert(N == 1, "bad width");
+    w[0] = __builtin_amdgcn_raw_buffer_load_b8(rs, off, soff, kNT);
   }
 }
 
-// Raw words a lane holds for one storage row before decoding.
-template <int D, int FMT>
-struct RawRow {
-  static constexpr int W = FMT == FMT_F32 ? Geo<D>::CPL : Words<Geo<D>::CPL * 2>::W;
+template <int N>
+__device__ __forceinline__ void buf_store(rsrc_t rs, uint32_t off, uint32_t soff, const uint32_t* w) {
+  using v4 = __attribute__((ext_vector_type(4))) unsigned int;
+  using v2 = __attribute__((ext_vector_type(2))) unsigned int;
+  if constexpr (N == 32) {
+    __builtin_amdgcn_raw_buffer_store_b128(v4{w[0], w[1], w[2], w[3]}, rs, off, soff, kNT);
+    __builtin_amdgcn_raw_buffer_store_b128(v4{w[4], w[5], w[6], w[7]}, rs, off + 16, soff, kNT);
+  } else if constexpr (N == 16) {
+    __builtin_amdgcn_raw_buffer_store_b128(v4{w[0], w[1], w[2], w[3]}, rs, off, soff, kNT);
+  } else if constexpr (N == 8) {
+    __builtin_amdgcn_raw_buffer_store_b64(v2{w[0], w[1]}, rs, off, soff, kNT);
+  } else if constexpr (N == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32(w[0], rs, off, soff, kNT);
+  } else if constexpr (N == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[0]), rs, off, soff, kNT);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(w[0]), rs, off, soff, kNT);
+  }
+}
+
+// The unit's three regions (FP16 rows or the fp32 state; INT8 rows; INT8 row scales), each
+// a resource plus the region's byte offset inside it. With ONE (a contiguous DAMP block and no
+// mixed row step, so no access relies on region range checks) a single resource spans the
+// block and the regions are offsets into it: fewer scalar registers.
+struct UnitPtr {
+  rsrc_t h;
+  rsrc_t c;
+  rsrc_t s;
+  uint32_t coff;
+  uint32_t soff;
+  int r;
 };
 
-template <int D, int FMT>
-__device__ __forceinline__ void load_state(const StateRef& st, int64_t unit, int w, int rs, int cg,
-                                           uint32_t (&raw)[Geo<D>::RPL][RawRow<D, FMT>::W]) {
-  using G = Geo<D>;
-  constexpr int CPL = G::CPL;
-  const int r = FMT == FMT_Q ? st.r : 0;
-#pragma unroll
-  for (int t = 0; t < G::RPL; ++t) {
-    const int p = t * G::RPS + w * 4 + rs;
-    if constexpr (FMT == FMT_F32) {
-      load_bytes<CPL * 4>(st.hbase + unit * st.hstride + (int64_t(p) * D + cg * CPL) * 4, raw[t]);
-    } else {
-      if (p < r)
-        load_bytes<CPL * 2>(st.hbase + unit * st.hstride + (int64_t(p) * D + cg * CPL) * 2, raw[t]);
-      else
-        load_bytes<CPL>(st.cbase + unit * st.cstride + int64_t(p - r) * D + cg * CPL, raw[t]);
+template <int D, int FMT, bool ONE = false>
+__device__ __forceinline__ UnitPtr unit_ptr(const StateRef& st, int64_t unit) {
+  const uint32_t r = FMT == FMT_Q ? static_cast<uint32_t>(st.r) : 0u;
+  if constexpr (ONE) {
+    const rsrc_t blk = make_rsrc(st.hbase + unit * st.hstride, 2 * r * D + (D - r) * D + 4 * (D - r));
+    return UnitPtr{blk, blk, blk, 2 * r * D, 2 * r * D + (D - r) * D, static_cast<int>(r)};
+  }
+  const uint32_t hbytes = FMT == FMT_F32 ? D * D * 4 : 2 * r * D;
+  return UnitPtr{make_rsrc(st.hbase + unit * st.hstride, hbytes),
+                 make_rsrc(st.cbase + unit * st.cstride, (D - r) * D),
+                 make_rsrc(st.sbase + unit * st.sstride, (D - r) * 4), 0u, 0u, static_cast<int>(r)};
+}
+
+// Byte offset of one lane's part of a storage row inside its region, split into a per-lane part
+// (voff) and a wave-uniform part (soff, an unsigned scalar register of the instruction).
+struct Loc {
+  uint32_t voff;
+  uint32_t soff;
+};
+
+// Storage row p = p0 + rs (p0: the wave's first row of this row step), value columns
+// cg*CPL .. cg*CPL + CPL - 1. MIX: the wave's 4 rows mix FP16 and INT8 rows (r % 4 != 0), so
+// the INT8 row index p - r is formed per lane.
+template <int D, int KIND>
+struct Row {
+  static constexpr int CPL = Geo<D>::CPL;
+  static constexpr int BYTES = KIND == K_F32 ? CPL * 4 : (KIND == K_F16 ? CPL * 2 : CPL);
+  static constexpr int W = Words<BYTES>::W;
+  static constexpr int E = KIND == K_F32 ? 4 : (KIND == K_F16 ? 2 : 1);  // bytes per value
+
+  // MIX: the whole offset goes in voff, which the buffer range check covers, so an access to
+  // a row of the other kind falls outside this region (the INT8 index p - r wraps to a huge
+  // unsigned value; an FP16 offset of an INT8 row is past the FP16 region) and is discarded.
+  template <bool MIX>
+  __device__ static __forceinline__ Loc loc(const UnitPtr& u, int p0, int rs, int cg) {
+    if constexpr (KIND == K_I8) {
+      if constexpr (MIX)
+        return Loc{static_cast<uint32_t>((p0 + rs - u.r) * D + cg * CPL), 0u};
+      return Loc{static_cast<uint32_t>(rs * D + cg * CPL), u.coff + static_cast<uint32_t>((p0 - u.r) * D)};
     }
+    if constexpr (MIX) return Loc{static_cast<uint32_t>(((p0 + rs) * D + cg * CPL) * E), 0u};
+    return Loc{static_cast<uint32_t>((rs * D + cg * CPL) * E), static_cast<uint32_t>(p0 * D * E)};
+  }
+
+  // scale of the INT8 row (4 bytes per row)
+  template <bool MIX>
+  __device__ static __forceinline__ Loc scale_loc(const UnitPtr& u, int p0, int rs) {
+    if constexpr (MIX) return Loc{static_cast<uint32_t>((p0 + rs - u.r) * 4), 0u};
+    return Loc{static_cast<uint32_t>(rs * 4), u.soff + static_cast<uint32_t>((p0 - u.r) * 4)};
+  }
+
+  __device__ static __forceinline__ rsrc_t region(const UnitPtr& u) {
+    return KIND == K_I8 ? u.c : u.h;
+  }
+
+  __device__ static __forceinline__ void load(const UnitPtr& u, Loc l, uint32_t* raw) {
+    buf_load<BYTES>(region(u), l.voff, l.soff, raw);
+  }
+
+  __device__ static __forceinline__ float decode(const uint32_t* w, int c) {
+    if constexpr (KIND == K_F32) return __uint_as_float(w[c]);
+    if constexpr (KIND == K_F16) return half_bits_to_float(w[c >> 1] >> (16 * (c & 1)));
+    return static_cast<float>(static_cast<int8_t>(w[c >> 2] >> (8 * (c & 3))));
+  }
+
+  // EXACT selects int8_code_exact (pack kernel) instead of the fast code (step kernel).
+  // sc_lds: when given, the INT8 row scale goes to sc_lds[p] (the caller writes the unit's
+  // scales to memory later with one coalesced store) instead of a 4-byte store per row.
+  template <bool EXACT, bool MIX>
+  __device__ static __forceinline__ void store(const UnitPtr& u, int p0, int rs, int cg,
+                                               const float* x, float* sc_lds = nullptr) {
+    uint32_t wd[W];
+    if constexpr (KIND == K_F32) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) wd[c] = __float_as_uint(x[c]);
+    } else if constexpr (KIND == K_F16) {
+#pragma unroll
+      for (int i = 0; i < W; ++i) wd[i] = 0;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) wd[c >> 1] |= float_to_half_bits(x[c]) << (16 * (c & 1));
+    } else {
+      float m = fabsf(x[0]);
+#pragma unroll
+      for (int c = 1; c < CPL; ++c) m = fmaxf(m, fabsf(x[c]));
+      m = max_row16(m);
+      const float s = div127(m);
+      if constexpr (EXACT) {
+        const float inv = m > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < W; ++i) wd[i] = 0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int32_t code = m > 0.0f ? int8_code_exact(x[c], s, inv) : 0;
+          wd[c >> 2] |= (static_cast<uint32_t>(code) & 0xFFu) << (8 * (c & 3));
+        }
+      } else {
+        const float inv = m > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
+        uint32_t f[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) f[c] = int8_code_fast_bits(x[c], inv);
+        if constexpr (CPL >= 4) {
+#pragma unroll
+          for (int i = 0; i < CPL / 4; ++i)
+            wd[i] = pack4_low_bytes(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+        } else if constexpr (CPL == 2) {
+          wd[0] = __builtin_amdgcn_perm(f[1], f[0], 0x0c0c0400u);
+        } else {
+          wd[0] = f[0] & 0xFFu;
+        }
+      }
+      if (cg == 0) {
+        if (sc_lds) {
+          sc_lds[p0 + rs] = s;
+        } else {
+          const uint32_t sb = __float_as_uint(s);
+          const Loc sl = scale_loc<MIX>(u, p0, rs);
+          buf_store<4>(u.s, sl.voff, sl.soff, &sb);
+        }
+      }
+    }
+    const Loc l = loc<MIX>(u, p0, rs, cg);
+    buf_store<BYTES>(region(u), l.voff, l.soff, wd);
+  }
+};
+
+// Dispatch one row step on the row kind. p0 = first storage row of the wave's 4 rows
+// (wave-uniform, so the FP16 / INT8 choice is a scalar branch unless r is not a multiple of
+// 4, where one row step of one wave mixes both kinds and branches per lane).
+// R4: r % 4 == 0, so no row step mixes kinds (a separate kernel instance without the mixed
+// path, which would otherwise cost ~35 VGPRs and an occupancy level; the host launches it only
+// when r % 4 == 0, which makes the third case unreachable).
+template <int FMT, bool R4, typename F>
+__device__ __forceinline__ void by_kind(int p0, int r, F&& f) {
+  if constexpr (FMT == FMT_F32) {
+    f.template operator()<K_F32>();
+  } else {
+    if (p0 + 4 <= r)
+      f.template operator()<K_F16>();
+    else if (p0 >= r)
+      f.template operator()<K_I8>();
+    else if (!R4)
+      f.template operator()<K_MIX>();
   }
 }
 
-// Element c of a raw row: fp32 bits, binary16 bits, or an int8 code.
-template <int FMT>
-__device__ __forceinline__ float raw_fp(const uint32_t* w, int c, bool fp16) {
-  if constexpr (FMT == FMT_F32) {
-    return __uint_as_float(w[c]);
+// The same, for one of the per-kind operations below: K_MIX runs both the FP16 and the INT8
+// form with MIX offsets (each lane's access of the other kind is discarded by the range check).
+template <int D, int K, typename F>
+__device__ __forceinline__ void each_kind(F&& f) {
+  if constexpr (K == K_MIX) {
+    f.template operator()<K_F16, true>();
+    f.template operator()<K_I8, true>();
   } else {
-    if (fp16) return half_bits_to_float(w[c >> 1] >> (16 * (c & 1)));
-    return static_cast<float>(static_cast<int8_t>(w[c >> 2] >> (8 * (c & 3))));
+    f.template operator()<K, false>();
+  }
+}
+
+template <int D, int FMT>
+constexpr int raw_words() {
+  return FMT == FMT_F32 ? Row<D, K_F32>::W : Row<D, K_F16>::W;  // FP16 rows are the widest
+}
+
+// Column sums over the key rows, shared by the step kernels. Every lane writes its CPL partial
+// sums of u = S'^T k and p = S'^T q (over its RPL rows) to LDS; thread j then adds the 4*NW
+// partials of column j in a fixed order, forms delta_j = beta (v_j - u_j) (left in sv[j]) and
+// the readout y_j = p_j + (q.k) delta_j. (q.k is summed over row slots with lane swaps.)
+template <int D>
+__device__ __forceinline__ void finish_columns(float (*redu)[D], float (*redp)[D], float* redqk,
+                                               float* sv, float* pu, float* pp, float pqk,
+                                               float beta, float* out_row, int tid, int w, int rs,
+                                               int lane, int cg) {
+  using G = Geo<D>;
+  constexpr int CPL = G::CPL, NW = G::NW;
+  store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(&redu[w * 4 + rs][cg * CPL]),
+                       reinterpret_cast<const uint32_t*>(pu));
+  store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(&redp[w * 4 + rs][cg * CPL]),
+                       reinterpret_cast<const uint32_t*>(pp));
+  pqk = sum_row_slots(pqk);
+  if (lane == 0) redqk[w] = pqk;
+  __syncthreads();
+  for (int j = tid; j < D; j += G::NT) {
+    float uu = redu[0][j], pv = redp[0][j];
+#pragma unroll
+    for (int k = 1; k < 4 * NW; ++k) {
+      uu += redu[k][j];
+      pv += redp[k][j];
+    }
+    float qk = redqk[0];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) qk += redqk[w2];
+    const float dj = beta * (sv[j] - uu);
+    sv[j] = dj;
+    out_row[j] = fmaf(qk, dj, pv);
+  }
+  __syncthreads();
+}
+
+// Write the INT8 row scales gathered in sc_lds[r .. D) with consecutive lanes (coalesced).
+template <int D>
+__device__ __forceinline__ void flush_scales(const UnitPtr& u, const float* sc_lds, int r, int tid) {
+  __syncthreads();
+  for (int i = r + tid; i < D; i += Geo<D>::NT) {
+    const uint32_t sb = __float_as_uint(sc_lds[i]);
+    buf_store<4>(u.s, static_cast<uint32_t>(i - r) * 4u, u.soff, &sb);
   }
 }
 
 // ---- the decode step -----------------------------------------------------------------------
-template <int D, int FMT, int PER_KEY, int BF16>
+template <int D, int FMT, int PER_KEY, int BF16, bool R4>
 __global__ __launch_bounds__(Geo<D>::NT) void step_kernel(const StepArgs a) {
   using G = Geo<D>;
-  constexpr int CPL = G::CPL, RPL = G::RPL, NW = G::NW;
-  __shared__ float sk[D], sq[D], sv[D], sa[D], ssc[D];
-  __shared__ float red[NW][2 * D + 1];
+  constexpr int CPL = G::CPL, RPL = G::RPL, NW = G::NW, RW = raw_words<D, FMT>();
+  __shared__ float4 srow[D];  // per storage row: {row multiplier a_i * scale_i, k_i, q_i, -}
+  __shared__ float sv[D];     // v, then delta
+  __shared__ float redu[4 * NW][D], redp[4 * NW][D], redqk[NW];
+  __shared__ float ssc[D];    // new INT8 row scales, storage order
 
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, rs = lane >> 4, cg = lane & 15;
-  const int bh = blockIdx.x;  // b * H + head
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, rs = lane >> 4, cg = lane & 15;
+  const int bh = __builtin_amdgcn_workgroup_id_x();  // b * H + head
   const int b = bh / a.H;
   const int head = bh - b * a.H;
   const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
   const int r = FMT == FMT_Q ? a.st.r : 0;
+  const UnitPtr up = unit_ptr<D, FMT>(a.st, unit);
 
   // (1) issue every state load of this lane first, so the whole block is in flight
-  uint32_t raw[RPL][RawRow<D, FMT>::W];
-  load_state<D, FMT>(a.st, unit, w, rs, cg, raw);
+  uint32_t raw[RPL][RW];
+#pragma unroll
+  for (int t = 0; t < RPL; ++t) {
+    const int p0 = t * G::RPS + w * 4, p = p0 + rs;
+    by_kind<FMT, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
+      if constexpr (K == K_MIX) {
+        // both loads; the one outside its region reads zeros, so OR-ing merges them
+        uint32_t w8[Row<D, K_I8>::W];
+        Row<D, K_F16>::load(up, Row<D, K_F16>::template loc<true>(up, p0, rs, cg), raw[t]);
+        Row<D, K_I8>::load(up, Row<D, K_I8>::template loc<true>(up, p0, rs, cg), w8);
+#pragma unroll
+        for (int i = 0; i < Row<D, K_I8>::W; ++i) raw[t][i] |= w8[i];
+      } else {
+        Row<D, K>::load(up, Row<D, K>::template loc<false>(up, p0, rs, cg), raw[t]);
+      }
+    });
+  }
 
-  // (2) stage k, q, v, the gate and the (gate-folded) row scales in LDS, in storage-row order
+  // (2) stage per-row scalars (storage order) and v in LDS. The row multiplier folds the gate
+  //     into the INT8 row scale: S'_ij = code_ij * (scale_i * a_i).
   const int64_t vec = int64_t(bh) * D;
   for (int i = tid; i < D; i += G::NT) {
     const int src = a.st.rowmap ? a.st.rowmap[head * D + i] : i;
-    sk[i] = load_in<BF16>(a.k, vec + src);
-    sq[i] = load_in<BF16>(a.q, vec + src);
-    sv[i] = load_in<BF16>(a.v, vec + i);
     const float g = PER_KEY ? a.alpha[vec + src] : a.alpha[bh];
-    sa[i] = g;
+    float mul = g;
     if constexpr (FMT == FMT_Q)
-      ssc[i] = i >= r ? reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[i - r] * g
-                      : 0.0f;
+      if (i >= r) mul = reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[i - r] * g;
+    srow[i] = make_float4(mul, load_in<BF16>(a.k, vec + src), load_in<BF16>(a.q, vec + src), 0.0f);
+    sv[i] = load_in<BF16>(a.v, vec + i);
   }
   __syncthreads();
 
   // (3) reconstruct + decay, partial u = S'^T k, p = S'^T q over this lane's rows
   float S[RPL][CPL];
-  float kr[RPL];
   float pu[CPL], pp[CPL], pqk = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) pu[c] = pp[c] = 0.0f;
 #pragma unroll
   for (int t = 0; t < RPL; ++t) {
-    const int p = t * G::RPS + w * 4 + rs;
-    const float kp = sk[p], qp = sq[p];
-    kr[t] = kp;
-    const bool fp16 = p < r;
-    const float mul = (FMT == FMT_Q && !fp16) ? ssc[p] : sa[p];
+    const int p0 = t * G::RPS + w * 4, p = p0 + rs;
+    const float4 rw = srow[p];
+    by_kind<FMT, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
+      if constexpr (K == K_MIX) {
+        const bool f16 = p < r;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          S[t][c] = (f16 ? Row<D, K_F16>::decode(raw[t], c) : Row<D, K_I8>::decode(raw[t], c)) * rw.x;
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) S[t][c] = Row<D, K>::decode(raw[t], c) * rw.x;
+      }
+    });
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      S[t][c] = raw_fp<FMT>(raw[t], c, fp16) * mul;
-      pu[c] = fmaf(kp, S[t][c], pu[c]);
-      pp[c] = fmaf(qp, S[t][c], pp[c]);
+      pu[c] = fmaf(rw.y, S[t][c], pu[c]);
+      pp[c] = fmaf(rw.z, S[t][c], pp[c]);
     }
-    pqk = fmaf(qp, kp, pqk);
+    pqk = fmaf(rw.z, rw.y, pqk);
   }
 
-  // (4) finish the column reductions: row slots in the wave, then waves through LDS
+  // (4) column reductions, delta and the readout y = p + (q.k) delta (one thread per column)
+  finish_columns<D>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + vec, tid, w, rs, lane, cg);
+
+  // (5) rank-1 write X = S' + k delta^T
+  float dl[CPL];
+  load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    pu[c] = sum_row_slots(pu[c]);
-    pp[c] = sum_row_slots(pp[c]);
+  for (int t = 0; t < RPL; ++t) {
+    const float kp = srow[t * G::RPS + w * 4 + rs].y;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) S[t][c] = fmaf(kp, dl[c], S[t][c]);
   }
-  pqk = sum_row_slots(pqk);
-  if constexpr (NW > 1) {
-    if (rs == 0) {
+
+  // (6) requantize in place
+#pragma unroll
+  for (int t = 0; t < RPL; ++t) {
+    const int p0 = t * G::RPS + w * 4, p = p0 + rs;
+    by_kind<FMT, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
+      each_kind<D, K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
+        Row<D, K2>::template store<false, MIX>(up, p0, rs, cg, S[t], ssc);
+      });
+    });
+  }
+  if constexpr (FMT == FMT_Q) flush_scales<D>(up, ssc, r, tid);
+}
+
+// ---- the decode step for the quantized formats, two passes over the compressed state --------
+// The state stays in VGPRs in its stored (compressed) form, ~20 registers per lane at d = 128,
+// instead of 64 fp32 registers: pass 1 decodes it into the column sums u = S'^T k and
+// p = S'^T q (with the row multiplier folded into k and q per row), pass 2 decodes it again to
+// form X = S' + k delta^T row step by row step, requantize and store. The second decode costs
+// about one VALU instruction per element; the registers it frees raise the number of resident
+// workgroups per CU from 4 to 7-8, i.e. about twice the bytes in flight to HBM.
+//
+// PLAN_SMALL: r % 4 == 0 and r <= 2 * RPS, so only the first two row steps can hold FP16 rows
+// and every later row step is INT8 at compile time (its raw words are half as many).
+enum Plan : int { PLAN_SMALL = 0, PLAN_R4 = 1, PLAN_ANY = 2 };
+
+template <int PLAN, typename F>
+__device__ __forceinline__ void by_plan(int t, int p0, int r, F&& f) {
+  if (PLAN == PLAN_SMALL && t >= 2) {
+    f.template operator()<K_I8>();
+  } else if (p0 + 4 <= r) {
+    f.template operator()<K_F16>();
+  } else if (PLAN != PLAN_ANY || p0 >= r) {
+    f.template operator()<K_I8>();
+  } else {
+    f.template operator()<K_MIX>();
+  }
+}
+
+template <int D, int PER_KEY, int BF16, int PLAN>
+__global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q2(const StepArgs a) {
+  using G = Geo<D>;
+  constexpr int CPL = G::CPL, RPL = G::RPL, NW = G::NW, RW = Words<CPL * 2>::W;
+  __shared__ float4 srow[D];  // per storage row: {row multiplier a_i * scale_i (or a_i), k_i, q_i, -}
+  __shared__ float sv[D];     // v, then delta
+  __shared__ float redu[4 * NW][D], redp[4 * NW][D], redqk[NW];
+  __shared__ float ssc[D];    // new INT8 row scales, storage order
+
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, rs = lane >> 4, cg = lane & 15;
+  const int bh = __builtin_amdgcn_workgroup_id_x();  // b * H + head
+  const int b = bh / a.H;
+  const int head = bh - b * a.H;
+  const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
+  const int r = a.st.r;
+  constexpr bool ONE = PLAN != PLAN_ANY;
+  const UnitPtr up = a.st.contiguous ? unit_ptr<D, FMT_Q, ONE>(a.st, unit) : unit_ptr<D, FMT_Q>(a.st, unit);
+
+  // (1) issue every state load of this lane first, so the whole block is in flight
+  uint32_t raw[RPL][RW];
+#pragma unroll
+  for (int t = 0; t < RPL; ++t) {
+    const int p0 = t * G::RPS + w * 4;
+    by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
+      if constexpr (K == K_MIX) {
+        // both loads; the one outside its region reads zeros, so OR-ing merges them
+        uint32_t w8[Row<D, K_I8>::W];
+        Row<D, K_F16>::load(up, Row<D, K_F16>::template loc<true>(up, p0, rs, cg), raw[t]);
+        Row<D, K_I8>::load(up, Row<D, K_I8>::template loc<true>(up, p0, rs, cg), w8);
+#pragma unroll
+        for (int i = 0; i < Row<D, K_I8>::W; ++i) raw[t][i] |= w8[i];
+      } else {
+        Row<D, K>::load(up, Row<D, K>::template loc<false>(up, p0, rs, cg), raw[t]);
+      }
+    });
+  }
+
+  // (2) per-row scalars (storage order) and v in LDS
+  const int64_t vec = int64_t(bh) * D;
+  for (int i = tid; i < D; i += G::NT) {
+    const int src = a.st.rowmap ? a.st.rowmap[head * D + i] : i;
+    const float g = PER_KEY ? a.alpha[vec + src] : a.alpha[bh];
+    const float mul = i >= r ? reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[i - r] * g : g;
+    srow[i] = make_float4(mul, load_in<BF16>(a.k, vec + src), load_in<BF16>(a.q, vec + src), 0.0f);
+    sv[i] = load_in<BF16>(a.v, vec + i);
+  }
+  __syncthreads();
+
+  // decoded value c of the lane's row step t (code, binary16 value)
+  auto decode = [&]<int K>(int t, int p, int c) __attribute__((always_inline)) -> float {
+    if constexpr (K == K_MIX)
+      return p < r ? Row<D, K_F16>::decode(raw[t], c) : Row<D, K_I8>::decode(raw[t], c);
+    else
+      return Row<D, K>::decode(raw[t], c);
+  };
+
+  // (3) pass 1: u_j += (k_i mul_i) c_ij, p_j += (q_i mul_i) c_ij over the lane's rows
+  float pu[CPL], pp[CPL], pqk = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) pu[c] = pp[c] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < RPL; ++t) {
+    const int p0 = t * G::RPS + w * 4, p = p0 + rs;
+    const float4 rw = srow[p];
+    const float kk = rw.y * rw.x, qq = rw.z * rw.x;
+    by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        red[w][cg * CPL + c] = pu[c];
-        red[w][D + cg * CPL + c] = pp[c];
+        const float x = decode.template operator()<K>(t, p, c);
+        pu[c] = fmaf(kk, x, pu[c]);
+        pp[c] = fmaf(qq, x, pp[c]);
       }
-      if (cg == 0) red[w][2 * D] = pqk;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      float uu = red[0][cg * CPL + c], vv = red[0][D + cg * CPL + c];
-#pragma unroll
-      for (int w2 = 1; w2 < NW; ++w2) {
-        uu += red[w2][cg * CPL + c];
-        vv += red[w2][D + cg * CPL + c];
-      }
-      pu[c] = uu;
-      pp[c] = vv;
-    }
-    float qk = red[0][2 * D];
-#pragma unroll
-    for (int w2 = 1; w2 < NW; ++w2) qk += red[w2][2 * D];
-    pqk = qk;
+    });
+    pqk = fmaf(rw.z, rw.y, pqk);
   }
 
-  // (5) delta, readout y = p + (q.k) delta, rank-1 write X = S' + k delta^T
-  const float beta = a.beta[bh];
+  // (4) column reductions, delta and the readout (one thread per column)
+  finish_columns<D>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + vec, tid, w, rs, lane, cg);
   float dl[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) dl[c] = beta * (sv[cg * CPL + c] - pu[c]);
-  if (w == 0 && rs == 0) {
-    uint32_t o[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) o[c] = __float_as_uint(fmaf(pqk, dl[c], pp[c]));
-    store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(a.out + vec + cg * CPL), o);
-  }
+  load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));
+
+  // The raw words pass through an empty asm statement, so the compiler cannot reuse pass 1's
+  // decoded values (which would keep 64 fp32 registers alive across the reduction).
 #pragma unroll
   for (int t = 0; t < RPL; ++t)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) S[t][c] = fmaf(kr[t], dl[c], S[t][c]);
+    for (int i = 0; i < RW; ++i) asm volatile("" : "+v"(raw[t][i]));
 
-  // (6) requantize in place
-  store_state<D, FMT>(a.st, unit, w, rs, cg, S);
+  // (5) pass 2: X = mul_i c_ij + k_i delta_j, requantize and store, one row step at a time
+#pragma unroll
+  for (int t = 0; t < RPL; ++t) {
+    const int p0 = t * G::RPS + w * 4, p = p0 + rs;
+    const float4 rw = srow[p];
+    by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
+      float X[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) X[c] = fmaf(rw.y, dl[c], decode.template operator()<K>(t, p, c) * rw.x);
+      each_kind<D, K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
+        Row<D, K2>::template store<false, MIX>(up, p0, rs, cg, X, ssc);
+      });
+    });
+  }
+  flush_scales<D>(up, ssc, r, tid);
 }
 
-// ---- pack: fp32 states (original key order) -> state format ---------------------------------
-template <int D, int FMT>
+// ---- the decode step, persistent and prefetching (quantized formats) -----------------------
+// Each workgroup loops over units u = g, g + G, ... (G workgroups, a few per CU). While unit u is
+// being computed, everything unit u + G needs (its state block, q, k, v, gate, beta and the
+// head's row map) is already streaming from HBM straight into LDS through buffer loads with
+// the LDS bit set (16 bytes per lane on gfx950), so every CU keeps ~20 KB per workgroup in
+// flight while it computes instead of alternating load and compute phases.
+//
+// Dynamic LDS of one workgroup (offsets from PfLayout, 16-byte aligned):
+//   blk  the unit's regions as stored: FP16 rows | INT8 rows | scales
+//   q, k, v (bf16 or fp32), alpha (scalar or per key), beta, row map (bytes)
+struct PfLayout {
+  uint32_t h, c, s, q, k, v, a, b, map, total;
+  __host__ __device__ PfLayout(int D, int r, int bf16, int per_key) {
+    const uint32_t e = bf16 ? 2u : 4u;
+    auto up = [](uint32_t x) { return (x + 15u) & ~15u; };
+    h = 0;
+    c = up(2u * r * D);
+    s = c + up(uint32_t(D - r) * D);
+    q = s + up(4u * (D - r));
+    k = q + up(e * D);
+    v = k + up(e * D);
+    a = v + up(e * D);
+    b = a + (per_key ? up(4u * D) : 16u);
+    map = b + 16u;
+    total = map + up(uint32_t(D));
+  }
+};
+
+#define DAMP_LDS(x) ((__attribute__((address_space(3))) void*)(x))
+
+// Copy a region of `bytes` (a multiple of 16, at most MAXB) to LDS with buffer->LDS loads:
+// lane l of wave w moves bytes [c*NT*16 + w*1024 + l*16, +16) of chunk c. Lanes past the end
+// are masked off (not just range-checked), so nothing beyond `bytes` is written in LDS.
+__device__ __forceinline__ void dma16(rsrc_t rs, uint8_t* lds_wave, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, DAMP_LDS(lds_wave), 16, off, 0, 0, kNT);
+}
+
+template <int NT, uint32_t MAXB>
+__device__ __forceinline__ void dma_region(rsrc_t rs, uint8_t* lds, uint32_t bytes, int w, int lane) {
+  constexpr uint32_t CH = NT * 16;
+  constexpr int NCH = int((MAXB + CH - 1) / CH);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const uint32_t wbase = uint32_t(c) * CH + uint32_t(w) * 1024u;
+    if (wbase >= bytes) break;
+    const uint32_t off = wbase + uint32_t(lane) * 16u;
+    if (off < bytes) dma16(rs, lds + wbase, off);
+  }
+}
+
+// A short vector (<= 1 KiB: one wave's share), moved by wave `who` only; 4 bytes: lane 0.
+__device__ __forceinline__ void dma_vec(rsrc_t rs, uint8_t* lds, uint32_t bytes, int w, int who,
+                                        int lane) {
+  if (w != who) return;
+  if (bytes == 4) {
+    if (lane == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, DAMP_LDS(lds), 4, 0, 0, 0, kNT);
+  } else if (uint32_t(lane) * 16u < bytes) {
+    dma16(rs, lds, uint32_t(lane) * 16u);
+  }
+}
+
+template <int D, int PER_KEY, int BF16, bool R4, bool CONTIG>
+__global__ __launch_bounds__(Geo<D>::NT) void step_kernel_pf(const StepArgs a) {
+  using G = Geo<D>;
+  constexpr int CPL = G::CPL, RPL = G::RPL, NW = G::NW, NT = G::NT;
+  constexpr uint32_t E = BF16 ? 2u : 4u;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ float4 srow[D];  // per storage row: {a_i * scale_i (or a_i), k_i, q_i, -}
+  __shared__ float sv[D];     // v, then delta
+  __shared__ float redu[4 * NW][D], redp[4 * NW][D], redqk[NW];
+  __shared__ float ssc[D];    // new INT8 row scales, storage order
+
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int w0 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, rs = lane >> 4, cg = lane & 15;
+  const int total = a.B * a.H;
+  const int gsz = a.grid;
+
+  // queue everything unit `bh` needs into LDS (CONTIG: the unit's regions are one block)
+  constexpr uint32_t kMaxBlock = 2u * D * D;  // all rows FP16
+  auto prefetch = [&](int bh, int w, int r) __attribute__((always_inline)) {
+    const PfLayout L(D, r, BF16, PER_KEY);
+    const int b = bh / a.H, head = bh - b * a.H;
+    const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
+    if constexpr (CONTIG) {
+      dma_region<NT, kMaxBlock>(make_rsrc(a.st.hbase + unit * a.st.hstride, L.q), lds, L.q, w, lane);
+    } else {  // uniform INT8: codes and scales in separate arrays (no FP16 rows)
+      dma_region<NT, D * D>(make_rsrc(a.st.cbase + unit * a.st.cstride, uint32_t(D) * D), lds + L.c,
+                            uint32_t(D) * D, w, lane);
+      dma_vec(make_rsrc(a.st.sbase + unit * a.st.sstride, 4u * D), lds + L.s, 4u * D, w, 0, lane);
+    }
+    const int64_t vec = int64_t(bh) * D;
+    dma_vec(make_rsrc(static_cast<const uint8_t*>(a.q) + vec * E, E * D), lds + L.q, E * D, w, 0 % NW, lane);
+    dma_vec(make_rsrc(static_cast<const uint8_t*>(a.k) + vec * E, E * D), lds + L.k, E * D, w, 1 % NW, lane);
+    dma_vec(make_rsrc(static_cast<const uint8_t*>(a.v) + vec * E, E * D), lds + L.v, E * D, w, 2 % NW, lane);
+    if constexpr (PER_KEY)
+      dma_vec(make_rsrc(a.alpha + vec, 4u * D), lds + L.a, 4u * D, w, 3 % NW, lane);
+    else
+      dma_vec(make_rsrc(a.alpha + bh, 4u), lds + L.a, 4u, w, 3 % NW, lane);
+    dma_vec(make_rsrc(a.beta + bh, 4u), lds + L.b, 4u, w, 1 % NW, lane);
+    if (a.st.rowmap)
+      dma_vec(make_rsrc(a.st.rowmap + head * D, uint32_t(D)), lds + L.map, uint32_t(D), w, 2 % NW, lane);
+  };
+
+  int bh = __builtin_amdgcn_workgroup_id_x();
+  if (bh < total) prefetch(bh, w0, a.st.r);
+  for (; bh < total; bh += gsz) {
+    // The wave index and r are re-read as opaque scalars every unit, so the many cheap values
+    // derived from them (LDS chunk bases, row offsets) are recomputed per unit rather than held
+    // across the loop in scalar registers (which would spill).
+    int w = w0, r = a.st.r;
+    asm volatile("" : "+s"(w), "+s"(r));
+    const PfLayout L(D, r, BF16, PER_KEY);
+    const int b = bh / a.H, head = bh - b * a.H;
+    const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
+    const UnitPtr up = unit_ptr<D, FMT_Q, CONTIG && R4>(a.st, unit);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's buffer->LDS loads have landed
+    __syncthreads();                     // ... and every other wave's
+
+    // (2) per-row scalars in storage order; the row multiplier folds the gate into the scale
+    for (int i = tid; i < D; i += NT) {
+      const int src = a.st.rowmap ? lds[L.map + i] : i;
+      const float g = PER_KEY ? reinterpret_cast<const float*>(lds + L.a)[src]
+                              : reinterpret_cast<const float*>(lds + L.a)[0];
+      const float mul = i >= r ? reinterpret_cast<const float*>(lds + L.s)[i - r] * g : g;
+      float kv, qv, vv;
+      if constexpr (BF16) {
+        kv = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(lds + L.k)[src]) << 16);
+        qv = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(lds + L.q)[src]) << 16);
+        vv = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(lds + L.v)[i]) << 16);
+      } else {
+        kv = reinterpret_cast<const float*>(lds + L.k)[src];
+        qv = reinterpret_cast<const float*>(lds + L.q)[src];
+        vv = reinterpret_cast<const float*>(lds + L.v)[i];
+      }
+      srow[i] = make_float4(mul, kv, qv, 0.0f);
+      sv[i] = vv;
+    }
+    const float beta = reinterpret_cast<const float*>(lds + L.b)[0];
+    __syncthreads();
+
+    // (3) reconstruct + decay from LDS, partial u = S'^T k, p = S'^T q
+    float S[RPL][CPL];
+    float pu[CPL], pp[CPL], pqk = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) pu[c] = pp[c] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < RPL; ++t) {
+      const int p0 = t * G::RPS + w * 4, p = p0 + rs;
+      const float4 rw = srow[p];
+      by_kind<FMT_Q, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
+        uint32_t raw[Words<CPL * 2>::W];
+        if constexpr (K == K_MIX) {
+          const bool f16 = p < r;
+          if (f16) load_bytes<CPL * 2>(lds + L.h + (p * D + cg * CPL) * 2, raw);
+          else load_bytes<CPL>(lds + L.c + (p - r) * D + cg * CPL, raw);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+            S[t][c] = (f16 ? Row<D, K_F16>::decode(raw, c) : Row<D, K_I8>::decode(raw, c)) * rw.x;
+        } else {
+          if constexpr (K == K_F16) load_bytes<CPL * 2>(lds + L.h + (p * D + cg * CPL) * 2, raw);
+          else load_bytes<CPL>(lds + L.c + (p - r) * D + cg * CPL, raw);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) S[t][c] = Row<D, K>::decode(raw, c) * rw.x;
+        }
+      });
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        pu[c] = fmaf(rw.y, S[t][c], pu[c]);
+        pp[c] = fmaf(rw.z, S[t][c], pp[c]);
+      }
+      pqk = fmaf(rw.z, rw.y, pqk);
+    }
+    __syncthreads();  // the staged block and vectors are consumed: refill for the next unit
+    if (bh + gsz < total) prefetch(bh + gsz, w, r);
+
+    // (4) column reductions, delta and the readout (one thread per column)
+    finish_columns<D>(redu, redp, redqk, sv, pu, pp, pqk, beta, a.out + int64_t(bh) * D, tid, w, rs,
+                      lane, cg);
+    float dl[CPL];
+    load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));
+    // rank-1 write X = S' + k delta^T
+#pragma unroll
+    for (int t = 0; t < RPL; ++t) {
+      const float kp = srow[t * G::RPS + w * 4 + rs].y;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) S[t][c] = fmaf(kp, dl[c], S[t][c]);
+    }
+    // (6) requantize in place
+#pragma unroll
+    for (int t = 0; t < RPL; ++t) {
+      const int p0 = t * G::RPS + w * 4;
+      by_kind<FMT_Q, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
+        each_kind<D, K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
+          Row<D, K2>::template store<false, MIX>(up, p0, rs, cg, S[t], ssc);
+        });
+      });
+    }
+    flush_scales<D>(up, ssc, r, tid);
+  }
+}
+
+// ---- pack: fp32 states (original key order) -> quantized format (exact rule) -------------
+template <int D, bool R4>
 __global__ __launch_bounds__(Geo<D>::NT) void quantize_kernel(const PackArgs a) {
   using G = Geo<D>;
   constexpr int CPL = G::CPL;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, rs = lane >> 4, cg = lane & 15;
-  const int ih = blockIdx.x;  // i * H + head
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, rs = lane >> 4, cg = lane & 15;
+  const int ih = __builtin_amdgcn_workgroup_id_x();  // i * H + head
   const int i = ih / a.H;
   const int head = ih - i * a.H;
   const int64_t unit = int64_t(a.slot_idx[i]) * a.H + head;
-  float X[G::RPL][CPL];
+  const int r = a.st.r;
+  const UnitPtr up = unit_ptr<D, FMT_Q>(a.st, unit);
 #pragma unroll
   for (int t = 0; t < G::RPL; ++t) {
-    const int p = t * G::RPS + w * 4 + rs;
+    const int p0 = t * G::RPS + w * 4, p = p0 + rs;
     const int src = a.st.rowmap ? a.st.rowmap[head * D + p] : p;
     uint32_t wd[CPL];
     load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(a.S + (int64_t(ih) * D + src) * D + cg * CPL), wd);
+    float x[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) X[t][c] = __uint_as_float(wd[c]);
+    for (int c = 0; c < CPL; ++c) x[c] = __uint_as_float(wd[c]);
+    by_kind<FMT_Q, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
+      each_kind<D, K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
+        Row<D, K2>::template store<true, MIX>(up, p0, rs, cg, x);
+      });
+    });
   }
-  store_state<D, FMT>(a.st, unit, w, rs, cg, X);
 }
 
-// ---- unpack: state format -> fp32 states (original key order) ------------------------------
-template <int D, int FMT>
+// ---- unpack: quantized format -> fp32 states (original key order) -----------------------
+template <int D, bool R4>
 __global__ __launch_bounds__(Geo<D>::NT) void dequantize_kernel(const PackArgs a) {
   using G = Geo<D>;
   constexpr int CPL = G::CPL;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, rs = lane >> 4, cg = lane & 15;
-  const int ih = blockIdx.x;
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, rs = lane >> 4, cg = lane & 15;
+  const int ih = __builtin_amdgcn_workgroup_id_x();
   const int i = ih / a.H;
   const int head = ih - i * a.H;
   const int64_t unit = int64_t(a.slot_idx[i]) * a.H + head;
-  const int r = FMT == FMT_Q ? a.st.r : 0;
-  uint32_t raw[G::RPL][RawRow<D, FMT>::W];
-  load_state<D, FMT>(a.st, unit, w, rs, cg, raw);
+  const int r = a.st.r;
+  const UnitPtr up = unit_ptr<D, FMT_Q>(a.st, unit);
 #pragma unroll
   for (int t = 0; t < G::RPL; ++t) {
-    const int p = t * G::RPS + w * 4 + rs;
+    const int p0 = t * G::RPS + w * 4, p = p0 + rs;
     const int src = a.st.rowmap ? a.st.rowmap[head * D + p] : p;
-    const bool fp16 = p < r;
-    const float sc = (FMT == FMT_Q && !fp16)
-                         ? reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[p - r]
-                         : 1.0f;
     uint32_t wd[CPL];
+    const bool f16 = p < r;
+    const float sc = f16 ? 1.0f : reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[p - r];
+    by_kind<FMT_Q, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
+      each_kind<D, K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
+        uint32_t raw[Row<D, K2>::W];
+        Row<D, K2>::load(up, Row<D, K2>::template loc<MIX>(up, p0, rs, cg), raw);
+        if (K2 == K_F16 ? f16 : !f16) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) wd[c] = __float_as_uint(raw_fp<FMT>(raw[t], c, fp16) * sc);
+          for (int c = 0; c < CPL; ++c) wd[c] = __float_as_uint(Row<D, K2>::decode(raw, c) * sc);
+        }
+      });
+    });
     store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(a.S + (int64_t(ih) * D + src) * D + cg * CPL), wd);
   }
 }
 
+// Workgroups of a persistent launch: every CU filled to the kernel's occupancy (cached per
+// device, kernel instance and LDS size), never more than there are units.
+template <typename Kernel>
+int persistent_grid(Kernel kernel, int threads, uint32_t lds_bytes, int units) {
+  constexpr int kMaxDev = 64;
+  static int cus[kMaxDev] = {};
+  static int cached_lds[kMaxDev] = {};
+  static int cached_blocks[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  if (cached_lds[dev] != int(lds_bytes)) {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, threads, lds_bytes) != hipSuccess)
+      return 0;
+    cached_blocks[dev] = blocks;
+    cached_lds[dev] = int(lds_bytes);
+  }
+  const long long g = static_cast<long long>(cus[dev]) * cached_blocks[dev];
+  return g <= 0 ? 0 : int(g < units ? g : units);
+}
+
+// The persistent variant measured slower than one workgroup per unit on MI355X (its
+// per-iteration wait also covers the previous unit's stores: gfx9 counts loads and stores on
+// one in-order counter), so it runs only when DAMP_PERSISTENT=1.
+bool persistent_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("DAMP_PERSISTENT");
+    return e && e[0] && e[0] != '0';
+  }();
+  return on;
+}
+
+// DAMP_SINGLE_PASS=1 selects the one-pass quantized kernel (state decoded once into fp32
+// registers) instead of the two-pass one, for comparison.
+bool single_pass_q() {
+  static const bool on = [] {
+    const char* e = std::getenv("DAMP_SINGLE_PASS");
+    return e && e[0] && e[0] != '0';
+  }();
+  return on;
+}
+
 template <int D>
-hipError_t step_d(int fmt, int per_key, int bf16, const StepArgs& a, hipStream_t s) {
+hipError_t step_d(int fmt, int per_key, int bf16, StepArgs a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H));
   const dim3 block(Geo<D>::NT);
-#define DAMP_LAUNCH(F, K, T) \
-  hipLaunchKernelGGL((step_kernel<D, F, K, T>), grid, block, 0, s, a)
+  const bool r4 = a.st.r % 4 == 0;
+  const int units = a.B * a.H;
+#define DAMP_LAUNCH(F, K, T, R) \
+  hipLaunchKernelGGL((step_kernel<D, F, K, T, R>), grid, block, 0, s, a)
+#define DAMP_LAUNCH_PF2(K, T, R, C)                                                        \
+  do {                                                                                     \
+    const uint32_t lds = PfLayout(D, a.st.r, T, K).total;                                  \
+    a.grid = persistent_grid(step_kernel_pf<D, K, T, R, C>, Geo<D>::NT, lds, units);       \
+    if (a.grid > 0)                                                                        \
+      hipLaunchKernelGGL((step_kernel_pf<D, K, T, R, C>), dim3(a.grid), block, lds, s, a); \
+    else                                                                                   \
+      DAMP_LAUNCH(FMT_Q, K, T, R);                                                         \
+  } while (0)
+#define DAMP_LAUNCH_PF(K, T, R) \
+  do { if (a.st.contiguous) DAMP_LAUNCH_PF2(K, T, R, true); else DAMP_LAUNCH_PF2(K, T, R, false); } while (0)
+#define DAMP_LAUNCH_Q2(K, T, P) \
+  hipLaunchKernelGGL((step_kernel_q2<D, K, T, P>), grid, block, 0, s, a)
+#define DAMP_LAUNCH_Q(K, T)                                                                      \
+  do {                                                                                           \
+    if (a.grid != 0) { if (r4) DAMP_LAUNCH_PF(K, T, true); else DAMP_LAUNCH_PF(K, T, false); }   \
+    else if (single_pass_q()) { if (r4) DAMP_LAUNCH(FMT_Q, K, T, true); else DAMP_LAUNCH(FMT_Q, K, T, false); } \
+    else if (r4 && a.st.r <= 2 * Geo<D>::RPS) DAMP_LAUNCH_Q2(K, T, PLAN_SMALL);                  \
+    else if (r4) DAMP_LAUNCH_Q2(K, T, PLAN_R4);                                                  \
+    else DAMP_LAUNCH_Q2(K, T, PLAN_ANY);                                                         \
+  } while (0)
   if (fmt == FMT_F32) {
-    if (per_key) { if (bf16) DAMP_LAUNCH(FMT_F32, 1, 1); else DAMP_LAUNCH(FMT_F32, 1, 0); }
-    else         { if (bf16) DAMP_LAUNCH(FMT_F32, 0, 1); else DAMP_LAUNCH(FMT_F32, 0, 0); }
+    if (per_key) { if (bf16) DAMP_LAUNCH(FMT_F32, 1, 1, true); else DAMP_LAUNCH(FMT_F32, 1, 0, true); }
+    else         { if (bf16) DAMP_LAUNCH(FMT_F32, 0, 1, true); else DAMP_LAUNCH(FMT_F32, 0, 0, true); }
   } else {
-    if (per_key) { if (bf16) DAMP_LAUNCH(FMT_Q, 1, 1); else DAMP_LAUNCH(FMT_Q, 1, 0); }
-    else         { if (bf16) DAMP_LAUNCH(FMT_Q, 0, 1); else DAMP_LAUNCH(FMT_Q, 0, 0); }
+    if (!persistent_enabled()) a.grid = 0;
+    if (per_key) { if (bf16) DAMP_LAUNCH_Q(1, 1); else DAMP_LAUNCH_Q(1, 0); }
+    else         { if (bf16) DAMP_LAUNCH_Q(0, 1); else DAMP_LAUNCH_Q(0, 0); }
   }
+#undef DAMP_LAUNCH_Q
+#undef DAMP_LAUNCH_Q2
+#undef DAMP_LAUNCH_PF
+#undef DAMP_LAUNCH_PF2
 #undef DAMP_LAUNCH
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t quant_d(const PackArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((quantize_kernel<D, FMT_Q>), dim3(unsigned(a.n) * unsigned(a.H)),
-                     dim3(Geo<D>::NT), 0, s, a);
+  const dim3 grid(unsigned(a.n) * unsigned(a.H)), block(Geo<D>::NT);
+  if (a.st.r % 4 == 0)
+    hipLaunchKernelGGL((quantize_kernel<D, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((quantize_kernel<D, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t dequant_d(const PackArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((dequantize_kernel<D, FMT_Q>), dim3(unsigned(a.n) * unsigned(a.H)),
-                     dim3(Geo<D>::NT), 0, s, a);
+  const dim3 grid(unsigned(a.n) * unsigned(a.H)), block(Geo<D>::NT);
+  if (a.st.r % 4 == 0)
+    hipLaunchKernelGGL((dequantize_kernel<D, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((dequantize_kernel<D, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
