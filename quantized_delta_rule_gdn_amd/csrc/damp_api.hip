@@ -177,11 +177,6 @@ damp_status run_step(int fmt, const damp::StateRef& ref, int32_t d, int32_t H, i
   a.alpha = alpha;
   a.beta = beta;
   a.out = out;
-  // the persistent kernel stages q/k/v (and a per-key gate) with 16-byte LDS loads
-  a.grid = (fmt == damp::FMT_Q && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&
-            (decay == DAMP_DECAY_SCALAR || aligned(alpha, 16)))
-               ? -1
-               : 0;
   return launched(damp::launch_step(fmt, d, decay == DAMP_DECAY_PER_KEY, dt == DAMP_BF16, a, s),
                   "decode step");
 }

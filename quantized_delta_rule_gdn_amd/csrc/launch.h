@@ -30,7 +30,6 @@ struct StateRef {
 
 struct StepArgs {
   StateRef st;
-  int32_t grid;             // persistent launch: < 0 = choose the grid, 0 = one workgroup per unit
   const int32_t* slot_idx;  // [B]
   int32_t B;
   int32_t H;

@@ -26,8 +26,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <cstdlib>
-
 #include "launch.h"
 
 namespace damp {
@@ -386,26 +384,39 @@ struct Row {
 // Dispatch one row step on the row kind. p0 = first storage row of the wave's 4 rows
 // (wave-uniform, so the FP16 / INT8 choice is a scalar branch unless r is not a multiple of
 // 4, where one row step of one wave mixes both kinds and branches per lane).
-// R4: r % 4 == 0, so no row step mixes kinds (a separate kernel instance without the mixed
-// path, which would otherwise cost ~35 VGPRs and an occupancy level; the host launches it only
-// when r % 4 == 0, which makes the third case unreachable).
-template <int FMT, bool R4, typename F>
-__device__ __forceinline__ void by_kind(int p0, int r, F&& f) {
-  if constexpr (FMT == FMT_F32) {
+// ---- row plans ------------------------------------------------------------------------------
+// Which kind each row step of a wave holds. A wave's row step covers storage rows p0..p0+3, so
+// with r % 4 == 0 every row step is all-FP16 or all-INT8 (a scalar branch); otherwise the one
+// row step that straddles r mixes both (K_MIX). The plans are separate kernel instances so the
+// common cases carry no code (and no registers) for the mixed one.
+//   PLAN_F32:   fp32 state
+//   PLAN_SMALL: r % 4 == 0 and r <= 2 * RPS: only the first two row steps can hold FP16 rows,
+//               every later row step is INT8 at compile time (its raw words are half as many)
+//   PLAN_R4:    r % 4 == 0
+//   PLAN_ANY:   any r
+enum Plan : int { PLAN_F32 = 0, PLAN_SMALL = 1, PLAN_R4 = 2, PLAN_ANY = 3 };
+
+template <int PLAN, typename F>
+__device__ __forceinline__ void by_plan(int t, int p0, int r, F&& f) {
+  if constexpr (PLAN == PLAN_F32) {
     f.template operator()<K_F32>();
   } else {
-    if (p0 + 4 <= r)
-      f.template operator()<K_F16>();
-    else if (p0 >= r)
+    if (PLAN == PLAN_SMALL && t >= 2) {
       f.template operator()<K_I8>();
-    else if (!R4)
+    } else if (p0 + 4 <= r) {
+      f.template operator()<K_F16>();
+    } else if (PLAN != PLAN_ANY || p0 >= r) {
+      f.template operator()<K_I8>();
+    } else {
       f.template operator()<K_MIX>();
+    }
   }
 }
 
-// The same, for one of the per-kind operations below: K_MIX runs both the FP16 and the INT8
-// form with MIX offsets (each lane's access of the other kind is discarded by the range check).
-template <int D, int K, typename F>
+// A per-kind operation for one of the kinds above: K_MIX runs both the FP16 and the INT8 form
+// with MIX offsets (each lane's access of the other kind falls outside its region and is
+// discarded by the buffer range check).
+template <int K, typename F>
 __device__ __forceinline__ void each_kind(F&& f) {
   if constexpr (K == K_MIX) {
     f.template operator()<K_F16, true>();
@@ -415,9 +426,47 @@ __device__ __forceinline__ void each_kind(F&& f) {
   }
 }
 
-template <int D, int FMT>
-constexpr int raw_words() {
-  return FMT == FMT_F32 ? Row<D, K_F32>::W : Row<D, K_F16>::W;  // FP16 rows are the widest
+// Load the lane's part of row step t into raw (K_MIX: both loads; the one outside its region
+// reads zeros, so OR-ing merges them).
+template <int D, int K>
+__device__ __forceinline__ void load_row_step(const UnitPtr& up, int p0, int rs, int cg, uint32_t* raw) {
+  if constexpr (K == K_MIX) {
+    uint32_t w8[Row<D, K_I8>::W];
+    Row<D, K_F16>::load(up, Row<D, K_F16>::template loc<true>(up, p0, rs, cg), raw);
+    Row<D, K_I8>::load(up, Row<D, K_I8>::template loc<true>(up, p0, rs, cg), w8);
+#pragma unroll
+    for (int i = 0; i < Row<D, K_I8>::W; ++i) raw[i] |= w8[i];
+  } else {
+    Row<D, K>::load(up, Row<D, K>::template loc<false>(up, p0, rs, cg), raw);
+  }
+}
+
+// Decoded value c of a lane's raw row (storage row p; K_MIX decides per lane).
+template <int D, int K>
+__device__ __forceinline__ float decode_row(const uint32_t* raw, int c, int p, int r) {
+  if constexpr (K == K_MIX)
+    return p < r ? Row<D, K_F16>::decode(raw, c) : Row<D, K_I8>::decode(raw, c);
+  else
+    return Row<D, K>::decode(raw, c);
+}
+
+// Per-row scalars of the unit in storage order: srow[i] = {m_i, k_i, q_i, -} with the row
+// multiplier m_i = a_i * scale_i for INT8 rows and a_i otherwise (the gate folded into the
+// scale: S'_ij = code_ij * m_i), and v in sv.
+template <int D, int PER_KEY, int BF16, bool Q>
+__device__ __forceinline__ void stage_rows(const StepArgs& a, int64_t unit, int bh, int head, int r,
+                                           int tid, float4* srow, float* sv) {
+  const int64_t vec = int64_t(bh) * D;
+  for (int i = tid; i < D; i += Geo<D>::NT) {
+    const int src = a.st.rowmap ? a.st.rowmap[head * D + i] : i;
+    const float g = PER_KEY ? a.alpha[vec + src] : a.alpha[bh];
+    float mul = g;
+    if constexpr (Q)
+      if (i >= r) mul = reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[i - r] * g;
+    srow[i] = make_float4(mul, load_in<BF16>(a.k, vec + src), load_in<BF16>(a.q, vec + src), 0.0f);
+    sv[i] = load_in<BF16>(a.v, vec + i);
+  }
+  __syncthreads();
 }
 
 // Column sums over the key rows, shared by the step kernels. Every lane writes its CPL partial
@@ -465,15 +514,16 @@ __device__ __forceinline__ void flush_scales(const UnitPtr& u, const float* sc_l
   }
 }
 
-// ---- the decode step -----------------------------------------------------------------------
-template <int D, int FMT, int PER_KEY, int BF16, bool R4>
-__global__ __launch_bounds__(Geo<D>::NT) void step_kernel(const StepArgs a) {
+// ---- the decode step, fp32 state ---------------------------------------------------------
+// The state is read once into VGPRs (64 fp32 per lane at d = 128), decayed, reduced, updated
+// and written back.
+template <int D, int PER_KEY, int BF16>
+__global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) {
   using G = Geo<D>;
-  constexpr int CPL = G::CPL, RPL = G::RPL, NW = G::NW, RW = raw_words<D, FMT>();
-  __shared__ float4 srow[D];  // per storage row: {row multiplier a_i * scale_i, k_i, q_i, -}
-  __shared__ float sv[D];     // v, then delta
+  constexpr int CPL = G::CPL, RPL = G::RPL, NW = G::NW;
+  __shared__ float4 srow[D];
+  __shared__ float sv[D];  // v, then delta
   __shared__ float redu[4 * NW][D], redp[4 * NW][D], redqk[NW];
-  __shared__ float ssc[D];    // new INT8 row scales, storage order
 
   const int tid = __builtin_amdgcn_workitem_id_x();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -482,64 +532,28 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel(const StepArgs a) {
   const int b = bh / a.H;
   const int head = bh - b * a.H;
   const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
-  const int r = FMT == FMT_Q ? a.st.r : 0;
-  const UnitPtr up = unit_ptr<D, FMT>(a.st, unit);
+  const UnitPtr up = unit_ptr<D, FMT_F32>(a.st, unit);
 
   // (1) issue every state load of this lane first, so the whole block is in flight
-  uint32_t raw[RPL][RW];
-#pragma unroll
-  for (int t = 0; t < RPL; ++t) {
-    const int p0 = t * G::RPS + w * 4, p = p0 + rs;
-    by_kind<FMT, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
-      if constexpr (K == K_MIX) {
-        // both loads; the one outside its region reads zeros, so OR-ing merges them
-        uint32_t w8[Row<D, K_I8>::W];
-        Row<D, K_F16>::load(up, Row<D, K_F16>::template loc<true>(up, p0, rs, cg), raw[t]);
-        Row<D, K_I8>::load(up, Row<D, K_I8>::template loc<true>(up, p0, rs, cg), w8);
-#pragma unroll
-        for (int i = 0; i < Row<D, K_I8>::W; ++i) raw[t][i] |= w8[i];
-      } else {
-        Row<D, K>::load(up, Row<D, K>::template loc<false>(up, p0, rs, cg), raw[t]);
-      }
-    });
-  }
-
-  // (2) stage per-row scalars (storage order) and v in LDS. The row multiplier folds the gate
-  //     into the INT8 row scale: S'_ij = code_ij * (scale_i * a_i).
-  const int64_t vec = int64_t(bh) * D;
-  for (int i = tid; i < D; i += G::NT) {
-    const int src = a.st.rowmap ? a.st.rowmap[head * D + i] : i;
-    const float g = PER_KEY ? a.alpha[vec + src] : a.alpha[bh];
-    float mul = g;
-    if constexpr (FMT == FMT_Q)
-      if (i >= r) mul = reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[i - r] * g;
-    srow[i] = make_float4(mul, load_in<BF16>(a.k, vec + src), load_in<BF16>(a.q, vec + src), 0.0f);
-    sv[i] = load_in<BF16>(a.v, vec + i);
-  }
-  __syncthreads();
-
-  // (3) reconstruct + decay, partial u = S'^T k, p = S'^T q over this lane's rows
   float S[RPL][CPL];
+#pragma unroll
+  for (int t = 0; t < RPL; ++t)
+    Row<D, K_F32>::load(up, Row<D, K_F32>::template loc<false>(up, t * G::RPS + w * 4, rs, cg),
+                        reinterpret_cast<uint32_t*>(S[t]));
+
+  // (2) per-row scalars and v
+  stage_rows<D, PER_KEY, BF16, false>(a, unit, bh, head, 0, tid, srow, sv);
+
+  // (3) decay, partial u = S'^T k, p = S'^T q over this lane's rows
   float pu[CPL], pp[CPL], pqk = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) pu[c] = pp[c] = 0.0f;
 #pragma unroll
   for (int t = 0; t < RPL; ++t) {
-    const int p0 = t * G::RPS + w * 4, p = p0 + rs;
-    const float4 rw = srow[p];
-    by_kind<FMT, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
-      if constexpr (K == K_MIX) {
-        const bool f16 = p < r;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-          S[t][c] = (f16 ? Row<D, K_F16>::decode(raw[t], c) : Row<D, K_I8>::decode(raw[t], c)) * rw.x;
-      } else {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) S[t][c] = Row<D, K>::decode(raw[t], c) * rw.x;
-      }
-    });
+    const float4 rw = srow[t * G::RPS + w * 4 + rs];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
+      S[t][c] *= rw.x;
       pu[c] = fmaf(rw.y, S[t][c], pu[c]);
       pp[c] = fmaf(rw.z, S[t][c], pp[c]);
     }
@@ -547,61 +561,34 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel(const StepArgs a) {
   }
 
   // (4) column reductions, delta and the readout y = p + (q.k) delta (one thread per column)
-  finish_columns<D>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + vec, tid, w, rs, lane, cg);
-
-  // (5) rank-1 write X = S' + k delta^T
+  finish_columns<D>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + int64_t(bh) * D, tid,
+                    w, rs, lane, cg);
   float dl[CPL];
   load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));
+
+  // (5) X = S' + k delta^T, stored in place
 #pragma unroll
   for (int t = 0; t < RPL; ++t) {
-    const float kp = srow[t * G::RPS + w * 4 + rs].y;
+    const int p0 = t * G::RPS + w * 4;
+    const float kp = srow[p0 + rs].y;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) S[t][c] = fmaf(kp, dl[c], S[t][c]);
-  }
-
-  // (6) requantize in place
-#pragma unroll
-  for (int t = 0; t < RPL; ++t) {
-    const int p0 = t * G::RPS + w * 4, p = p0 + rs;
-    by_kind<FMT, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
-      each_kind<D, K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
-        Row<D, K2>::template store<false, MIX>(up, p0, rs, cg, S[t], ssc);
-      });
-    });
-  }
-  if constexpr (FMT == FMT_Q) flush_scales<D>(up, ssc, r, tid);
-}
-
-// ---- the decode step for the quantized formats, two passes over the compressed state --------
-// The state stays in VGPRs in its stored (compressed) form, ~20 registers per lane at d = 128,
-// instead of 64 fp32 registers: pass 1 decodes it into the column sums u = S'^T k and
-// p = S'^T q (with the row multiplier folded into k and q per row), pass 2 decodes it again to
-// form X = S' + k delta^T row step by row step, requantize and store. The second decode costs
-// about one VALU instruction per element; the registers it frees raise the number of resident
-// workgroups per CU from 4 to 7-8, i.e. about twice the bytes in flight to HBM.
-//
-// PLAN_SMALL: r % 4 == 0 and r <= 2 * RPS, so only the first two row steps can hold FP16 rows
-// and every later row step is INT8 at compile time (its raw words are half as many).
-enum Plan : int { PLAN_SMALL = 0, PLAN_R4 = 1, PLAN_ANY = 2 };
-
-template <int PLAN, typename F>
-__device__ __forceinline__ void by_plan(int t, int p0, int r, F&& f) {
-  if (PLAN == PLAN_SMALL && t >= 2) {
-    f.template operator()<K_I8>();
-  } else if (p0 + 4 <= r) {
-    f.template operator()<K_F16>();
-  } else if (PLAN != PLAN_ANY || p0 >= r) {
-    f.template operator()<K_I8>();
-  } else {
-    f.template operator()<K_MIX>();
+    Row<D, K_F32>::template store<false, false>(up, p0, rs, cg, S[t]);
   }
 }
 
+// ---- the decode step, quantized state (DAMP, uniform INT8): two passes over the codes ------
+// The state stays in VGPRs in its stored, compressed form (~20 registers per lane at d = 128
+// with PLAN_SMALL) rather than as 64 fp32 registers: pass 1 decodes it into the column sums
+// u = S'^T k and p = S'^T q (the row multiplier folded into k and q per row), pass 2 decodes it
+// again row step by row step to form X = S' + k delta^T, requantize and store. The second
+// decode costs about one VALU instruction per element; the registers it frees let 7 workgroups
+// share a CU instead of 4, which is what keeps enough bytes in flight to HBM.
 template <int D, int PER_KEY, int BF16, int PLAN>
-__global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q2(const StepArgs a) {
+__global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q(const StepArgs a) {
   using G = Geo<D>;
   constexpr int CPL = G::CPL, RPL = G::RPL, NW = G::NW, RW = Words<CPL * 2>::W;
-  __shared__ float4 srow[D];  // per storage row: {row multiplier a_i * scale_i (or a_i), k_i, q_i, -}
+  __shared__ float4 srow[D];
   __shared__ float sv[D];     // v, then delta
   __shared__ float redu[4 * NW][D], redp[4 * NW][D], redqk[NW];
   __shared__ float ssc[D];    // new INT8 row scales, storage order
@@ -614,8 +601,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q2(const StepArgs a) {
   const int head = bh - b * a.H;
   const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
   const int r = a.st.r;
-  constexpr bool ONE = PLAN != PLAN_ANY;
-  const UnitPtr up = a.st.contiguous ? unit_ptr<D, FMT_Q, ONE>(a.st, unit) : unit_ptr<D, FMT_Q>(a.st, unit);
+  // one buffer resource over a contiguous block unless a row step mixes kinds
+  const UnitPtr up = (PLAN != PLAN_ANY && a.st.contiguous) ? unit_ptr<D, FMT_Q, true>(a.st, unit)
+                                                           : unit_ptr<D, FMT_Q>(a.st, unit);
 
   // (1) issue every state load of this lane first, so the whole block is in flight
   uint32_t raw[RPL][RW];
@@ -623,39 +611,14 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q2(const StepArgs a) {
   for (int t = 0; t < RPL; ++t) {
     const int p0 = t * G::RPS + w * 4;
     by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
-      if constexpr (K == K_MIX) {
-        // both loads; the one outside its region reads zeros, so OR-ing merges them
-        uint32_t w8[Row<D, K_I8>::W];
-        Row<D, K_F16>::load(up, Row<D, K_F16>::template loc<true>(up, p0, rs, cg), raw[t]);
-        Row<D, K_I8>::load(up, Row<D, K_I8>::template loc<true>(up, p0, rs, cg), w8);
-#pragma unroll
-        for (int i = 0; i < Row<D, K_I8>::W; ++i) raw[t][i] |= w8[i];
-      } else {
-        Row<D, K>::load(up, Row<D, K>::template loc<false>(up, p0, rs, cg), raw[t]);
-      }
+      load_row_step<D, K>(up, p0, rs, cg, raw[t]);
     });
   }
 
-  // (2) per-row scalars (storage order) and v in LDS
-  const int64_t vec = int64_t(bh) * D;
-  for (int i = tid; i < D; i += G::NT) {
-    const int src = a.st.rowmap ? a.st.rowmap[head * D + i] : i;
-    const float g = PER_KEY ? a.alpha[vec + src] : a.alpha[bh];
-    const float mul = i >= r ? reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[i - r] * g : g;
-    srow[i] = make_float4(mul, load_in<BF16>(a.k, vec + src), load_in<BF16>(a.q, vec + src), 0.0f);
-    sv[i] = load_in<BF16>(a.v, vec + i);
-  }
-  __syncthreads();
+  // (2) per-row scalars and v
+  stage_rows<D, PER_KEY, BF16, true>(a, unit, bh, head, r, tid, srow, sv);
 
-  // decoded value c of the lane's row step t (code, binary16 value)
-  auto decode = [&]<int K>(int t, int p, int c) __attribute__((always_inline)) -> float {
-    if constexpr (K == K_MIX)
-      return p < r ? Row<D, K_F16>::decode(raw[t], c) : Row<D, K_I8>::decode(raw[t], c);
-    else
-      return Row<D, K>::decode(raw[t], c);
-  };
-
-  // (3) pass 1: u_j += (k_i mul_i) c_ij, p_j += (q_i mul_i) c_ij over the lane's rows
+  // (3) pass 1: u_j += (k_i m_i) c_ij, p_j += (q_i m_i) c_ij over the lane's rows
   float pu[CPL], pp[CPL], pqk = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) pu[c] = pp[c] = 0.0f;
@@ -667,7 +630,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q2(const StepArgs a) {
     by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        const float x = decode.template operator()<K>(t, p, c);
+        const float x = decode_row<D, K>(raw[t], c, p, r);
         pu[c] = fmaf(kk, x, pu[c]);
         pp[c] = fmaf(qq, x, pp[c]);
       }
@@ -675,19 +638,20 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q2(const StepArgs a) {
     pqk = fmaf(rw.z, rw.y, pqk);
   }
 
-  // (4) column reductions, delta and the readout (one thread per column)
-  finish_columns<D>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + vec, tid, w, rs, lane, cg);
+  // (4) column reductions, delta and the readout y = p + (q.k) delta (one thread per column)
+  finish_columns<D>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + int64_t(bh) * D, tid,
+                    w, rs, lane, cg);
   float dl[CPL];
   load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));
 
-  // The raw words pass through an empty asm statement, so the compiler cannot reuse pass 1's
-  // decoded values (which would keep 64 fp32 registers alive across the reduction).
+  // The raw words pass through an empty asm statement, so the compiler cannot keep pass 1's
+  // decoded values (64 fp32 registers) alive across the reduction instead of decoding again.
 #pragma unroll
   for (int t = 0; t < RPL; ++t)
 #pragma unroll
     for (int i = 0; i < RW; ++i) asm volatile("" : "+v"(raw[t][i]));
 
-  // (5) pass 2: X = mul_i c_ij + k_i delta_j, requantize and store, one row step at a time
+  // (5) pass 2: X = m_i c_ij + k_i delta_j, requantize and store, one row step at a time
 #pragma unroll
   for (int t = 0; t < RPL; ++t) {
     const int p0 = t * G::RPS + w * 4, p = p0 + rs;
@@ -695,8 +659,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q2(const StepArgs a) {
     by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
       float X[CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) X[c] = fmaf(rw.y, dl[c], decode.template operator()<K>(t, p, c) * rw.x);
-      each_kind<D, K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
+      for (int c = 0; c < CPL; ++c) X[c] = fmaf(rw.y, dl[c], decode_row<D, K>(raw[t], c, p, r) * rw.x);
+      each_kind<K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
         Row<D, K2>::template store<false, MIX>(up, p0, rs, cg, X, ssc);
       });
     });
@@ -704,210 +668,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q2(const StepArgs a) {
   flush_scales<D>(up, ssc, r, tid);
 }
 
-// ---- the decode step, persistent and prefetching (quantized formats) -----------------------
-// Each workgroup loops over units u = g, g + G, ... (G workgroups, a few per CU). While unit u is
-// being computed, everything unit u + G needs (its state block, q, k, v, gate, beta and the
-// head's row map) is already streaming from HBM straight into LDS through buffer loads with
-// the LDS bit set (16 bytes per lane on gfx950), so every CU keeps ~20 KB per workgroup in
-// flight while it computes instead of alternating load and compute phases.
-//
-// Dynamic LDS of one workgroup (offsets from PfLayout, 16-byte aligned):
-//   blk  the unit's regions as stored: FP16 rows | INT8 rows | scales
-//   q, k, v (bf16 or fp32), alpha (scalar or per key), beta, row map (bytes)
-struct PfLayout {
-  uint32_t h, c, s, q, k, v, a, b, map, total;
-  __host__ __device__ PfLayout(int D, int r, int bf16, int per_key) {
-    const uint32_t e = bf16 ? 2u : 4u;
-    auto up = [](uint32_t x) { return (x + 15u) & ~15u; };
-    h = 0;
-    c = up(2u * r * D);
-    s = c + up(uint32_t(D - r) * D);
-    q = s + up(4u * (D - r));
-    k = q + up(e * D);
-    v = k + up(e * D);
-    a = v + up(e * D);
-    b = a + (per_key ? up(4u * D) : 16u);
-    map = b + 16u;
-    total = map + up(uint32_t(D));
-  }
-};
-
-#define DAMP_LDS(x) ((__attribute__((address_space(3))) void*)(x))
-
-// Copy a region of `bytes` (a multiple of 16, at most MAXB) to LDS with buffer->LDS loads:
-// lane l of wave w moves bytes [c*NT*16 + w*1024 + l*16, +16) of chunk c. Lanes past the end
-// are masked off (not just range-checked), so nothing beyond `bytes` is written in LDS.
-__device__ __forceinline__ void dma16(rsrc_t rs, uint8_t* lds_wave, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, DAMP_LDS(lds_wave), 16, off, 0, 0, kNT);
-}
-
-template <int NT, uint32_t MAXB>
-__device__ __forceinline__ void dma_region(rsrc_t rs, uint8_t* lds, uint32_t bytes, int w, int lane) {
-  constexpr uint32_t CH = NT * 16;
-  constexpr int NCH = int((MAXB + CH - 1) / CH);
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const uint32_t wbase = uint32_t(c) * CH + uint32_t(w) * 1024u;
-    if (wbase >= bytes) break;
-    const uint32_t off = wbase + uint32_t(lane) * 16u;
-    if (off < bytes) dma16(rs, lds + wbase, off);
-  }
-}
-
-// A short vector (<= 1 KiB: one wave's share), moved by wave `who` only; 4 bytes: lane 0.
-__device__ __forceinline__ void dma_vec(rsrc_t rs, uint8_t* lds, uint32_t bytes, int w, int who,
-                                        int lane) {
-  if (w != who) return;
-  if (bytes == 4) {
-    if (lane == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, DAMP_LDS(lds), 4, 0, 0, 0, kNT);
-  } else if (uint32_t(lane) * 16u < bytes) {
-    dma16(rs, lds, uint32_t(lane) * 16u);
-  }
-}
-
-template <int D, int PER_KEY, int BF16, bool R4, bool CONTIG>
-__global__ __launch_bounds__(Geo<D>::NT) void step_kernel_pf(const StepArgs a) {
-  using G = Geo<D>;
-  constexpr int CPL = G::CPL, RPL = G::RPL, NW = G::NW, NT = G::NT;
-  constexpr uint32_t E = BF16 ? 2u : 4u;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ float4 srow[D];  // per storage row: {a_i * scale_i (or a_i), k_i, q_i, -}
-  __shared__ float sv[D];     // v, then delta
-  __shared__ float redu[4 * NW][D], redp[4 * NW][D], redqk[NW];
-  __shared__ float ssc[D];    // new INT8 row scales, storage order
-
-  const int tid = __builtin_amdgcn_workitem_id_x();
-  const int w0 = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, rs = lane >> 4, cg = lane & 15;
-  const int total = a.B * a.H;
-  const int gsz = a.grid;
-
-  // queue everything unit `bh` needs into LDS (CONTIG: the unit's regions are one block)
-  constexpr uint32_t kMaxBlock = 2u * D * D;  // all rows FP16
-  auto prefetch = [&](int bh, int w, int r) __attribute__((always_inline)) {
-    const PfLayout L(D, r, BF16, PER_KEY);
-    const int b = bh / a.H, head = bh - b * a.H;
-    const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
-    if constexpr (CONTIG) {
-      dma_region<NT, kMaxBlock>(make_rsrc(a.st.hbase + unit * a.st.hstride, L.q), lds, L.q, w, lane);
-    } else {  // uniform INT8: codes and scales in separate arrays (no FP16 rows)
-      dma_region<NT, D * D>(make_rsrc(a.st.cbase + unit * a.st.cstride, uint32_t(D) * D), lds + L.c,
-                            uint32_t(D) * D, w, lane);
-      dma_vec(make_rsrc(a.st.sbase + unit * a.st.sstride, 4u * D), lds + L.s, 4u * D, w, 0, lane);
-    }
-    const int64_t vec = int64_t(bh) * D;
-    dma_vec(make_rsrc(static_cast<const uint8_t*>(a.q) + vec * E, E * D), lds + L.q, E * D, w, 0 % NW, lane);
-    dma_vec(make_rsrc(static_cast<const uint8_t*>(a.k) + vec * E, E * D), lds + L.k, E * D, w, 1 % NW, lane);
-    dma_vec(make_rsrc(static_cast<const uint8_t*>(a.v) + vec * E, E * D), lds + L.v, E * D, w, 2 % NW, lane);
-    if constexpr (PER_KEY)
-      dma_vec(make_rsrc(a.alpha + vec, 4u * D), lds + L.a, 4u * D, w, 3 % NW, lane);
-    else
-      dma_vec(make_rsrc(a.alpha + bh, 4u), lds + L.a, 4u, w, 3 % NW, lane);
-    dma_vec(make_rsrc(a.beta + bh, 4u), lds + L.b, 4u, w, 1 % NW, lane);
-    if (a.st.rowmap)
-      dma_vec(make_rsrc(a.st.rowmap + head * D, uint32_t(D)), lds + L.map, uint32_t(D), w, 2 % NW, lane);
-  };
-
-  int bh = __builtin_amdgcn_workgroup_id_x();
-  if (bh < total) prefetch(bh, w0, a.st.r);
-  for (; bh < total; bh += gsz) {
-    // The wave index and r are re-read as opaque scalars every unit, so the many cheap values
-    // derived from them (LDS chunk bases, row offsets) are recomputed per unit rather than held
-    // across the loop in scalar registers (which would spill).
-    int w = w0, r = a.st.r;
-    asm volatile("" : "+s"(w), "+s"(r));
-    const PfLayout L(D, r, BF16, PER_KEY);
-    const int b = bh / a.H, head = bh - b * a.H;
-    const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
-    const UnitPtr up = unit_ptr<D, FMT_Q, CONTIG && R4>(a.st, unit);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's buffer->LDS loads have landed
-    __syncthreads();                     // ... and every other wave's
-
-    // (2) per-row scalars in storage order; the row multiplier folds the gate into the scale
-    for (int i = tid; i < D; i += NT) {
-      const int src = a.st.rowmap ? lds[L.map + i] : i;
-      const float g = PER_KEY ? reinterpret_cast<const float*>(lds + L.a)[src]
-                              : reinterpret_cast<const float*>(lds + L.a)[0];
-      const float mul = i >= r ? reinterpret_cast<const float*>(lds + L.s)[i - r] * g : g;
-      float kv, qv, vv;
-      if constexpr (BF16) {
-        kv = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(lds + L.k)[src]) << 16);
-        qv = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(lds + L.q)[src]) << 16);
-        vv = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(lds + L.v)[i]) << 16);
-      } else {
-        kv = reinterpret_cast<const float*>(lds + L.k)[src];
-        qv = reinterpret_cast<const float*>(lds + L.q)[src];
-        vv = reinterpret_cast<const float*>(lds + L.v)[i];
-      }
-      srow[i] = make_float4(mul, kv, qv, 0.0f);
-      sv[i] = vv;
-    }
-    const float beta = reinterpret_cast<const float*>(lds + L.b)[0];
-    __syncthreads();
-
-    // (3) reconstruct + decay from LDS, partial u = S'^T k, p = S'^T q
-    float S[RPL][CPL];
-    float pu[CPL], pp[CPL], pqk = 0.0f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) pu[c] = pp[c] = 0.0f;
-#pragma unroll
-    for (int t = 0; t < RPL; ++t) {
-      const int p0 = t * G::RPS + w * 4, p = p0 + rs;
-      const float4 rw = srow[p];
-      by_kind<FMT_Q, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
-        uint32_t raw[Words<CPL * 2>::W];
-        if constexpr (K == K_MIX) {
-          const bool f16 = p < r;
-          if (f16) load_bytes<CPL * 2>(lds + L.h + (p * D + cg * CPL) * 2, raw);
-          else load_bytes<CPL>(lds + L.c + (p - r) * D + cg * CPL, raw);
-#pragma unroll
-          for (int c = 0; c < CPL; ++c)
-            S[t][c] = (f16 ? Row<D, K_F16>::decode(raw, c) : Row<D, K_I8>::decode(raw, c)) * rw.x;
-        } else {
-          if constexpr (K == K_F16) load_bytes<CPL * 2>(lds + L.h + (p * D + cg * CPL) * 2, raw);
-          else load_bytes<CPL>(lds + L.c + (p - r) * D + cg * CPL, raw);
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) S[t][c] = Row<D, K>::decode(raw, c) * rw.x;
-        }
-      });
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        pu[c] = fmaf(rw.y, S[t][c], pu[c]);
-        pp[c] = fmaf(rw.z, S[t][c], pp[c]);
-      }
-      pqk = fmaf(rw.z, rw.y, pqk);
-    }
-    __syncthreads();  // the staged block and vectors are consumed: refill for the next unit
-    if (bh + gsz < total) prefetch(bh + gsz, w, r);
-
-    // (4) column reductions, delta and the readout (one thread per column)
-    finish_columns<D>(redu, redp, redqk, sv, pu, pp, pqk, beta, a.out + int64_t(bh) * D, tid, w, rs,
-                      lane, cg);
-    float dl[CPL];
-    load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));
-    // rank-1 write X = S' + k delta^T
-#pragma unroll
-    for (int t = 0; t < RPL; ++t) {
-      const float kp = srow[t * G::RPS + w * 4 + rs].y;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) S[t][c] = fmaf(kp, dl[c], S[t][c]);
-    }
-    // (6) requantize in place
-#pragma unroll
-    for (int t = 0; t < RPL; ++t) {
-      const int p0 = t * G::RPS + w * 4;
-      by_kind<FMT_Q, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
-        each_kind<D, K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
-          Row<D, K2>::template store<false, MIX>(up, p0, rs, cg, S[t], ssc);
-        });
-      });
-    }
-    flush_scales<D>(up, ssc, r, tid);
-  }
-}
-
 // ---- pack: fp32 states (original key order) -> quantized format (exact rule) -------------
-template <int D, bool R4>
+template <int D, int PLAN>
 __global__ __launch_bounds__(Geo<D>::NT) void quantize_kernel(const PackArgs a) {
   using G = Geo<D>;
   constexpr int CPL = G::CPL;
@@ -924,13 +686,11 @@ __global__ __launch_bounds__(Geo<D>::NT) void quantize_kernel(const PackArgs a) 
   for (int t = 0; t < G::RPL; ++t) {
     const int p0 = t * G::RPS + w * 4, p = p0 + rs;
     const int src = a.st.rowmap ? a.st.rowmap[head * D + p] : p;
-    uint32_t wd[CPL];
-    load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(a.S + (int64_t(ih) * D + src) * D + cg * CPL), wd);
     float x[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) x[c] = __uint_as_float(wd[c]);
-    by_kind<FMT_Q, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
-      each_kind<D, K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
+    load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(a.S + (int64_t(ih) * D + src) * D + cg * CPL),
+                        reinterpret_cast<uint32_t*>(x));
+    by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
+      each_kind<K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
         Row<D, K2>::template store<true, MIX>(up, p0, rs, cg, x);
       });
     });
@@ -938,7 +698,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void quantize_kernel(const PackArgs a) 
 }
 
 // ---- unpack: quantized format -> fp32 states (original key order) -----------------------
-template <int D, bool R4>
+template <int D, int PLAN>
 __global__ __launch_bounds__(Geo<D>::NT) void dequantize_kernel(const PackArgs a) {
   using G = Geo<D>;
   constexpr int CPL = G::CPL;
@@ -955,112 +715,48 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequantize_kernel(const PackArgs a
   for (int t = 0; t < G::RPL; ++t) {
     const int p0 = t * G::RPS + w * 4, p = p0 + rs;
     const int src = a.st.rowmap ? a.st.rowmap[head * D + p] : p;
-    uint32_t wd[CPL];
-    const bool f16 = p < r;
-    const float sc = f16 ? 1.0f : reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[p - r];
-    by_kind<FMT_Q, R4>(p0, r, [&]<int K>() __attribute__((always_inline)) {
-      each_kind<D, K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
-        uint32_t raw[Row<D, K2>::W];
-        Row<D, K2>::load(up, Row<D, K2>::template loc<MIX>(up, p0, rs, cg), raw);
-        if (K2 == K_F16 ? f16 : !f16) {
+    const float sc = p < r ? 1.0f : reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[p - r];
+    float x[CPL];
+    by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
+      uint32_t raw[Words<CPL * 2>::W];
+      load_row_step<D, K>(up, p0, rs, cg, raw);
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) wd[c] = __float_as_uint(Row<D, K2>::decode(raw, c) * sc);
-        }
-      });
+      for (int c = 0; c < CPL; ++c) x[c] = decode_row<D, K>(raw, c, p, r) * sc;
     });
-    store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(a.S + (int64_t(ih) * D + src) * D + cg * CPL), wd);
+    store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(a.S + (int64_t(ih) * D + src) * D + cg * CPL),
+                         reinterpret_cast<const uint32_t*>(x));
   }
 }
 
-// Workgroups of a persistent launch: every CU filled to the kernel's occupancy (cached per
-// device, kernel instance and LDS size), never more than there are units.
-template <typename Kernel>
-int persistent_grid(Kernel kernel, int threads, uint32_t lds_bytes, int units) {
-  constexpr int kMaxDev = 64;
-  static int cus[kMaxDev] = {};
-  static int cached_lds[kMaxDev] = {};
-  static int cached_blocks[kMaxDev] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
-  }
-  if (cached_lds[dev] != int(lds_bytes)) {
-    int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, threads, lds_bytes) != hipSuccess)
-      return 0;
-    cached_blocks[dev] = blocks;
-    cached_lds[dev] = int(lds_bytes);
-  }
-  const long long g = static_cast<long long>(cus[dev]) * cached_blocks[dev];
-  return g <= 0 ? 0 : int(g < units ? g : units);
+// ---- launchers -------------------------------------------------------------------------------
+template <int D, int PER_KEY, int BF16>
+void launch_step_q(const StepArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 block(Geo<D>::NT);
+  // PLAN_SMALL covers the usual layouts (r <= 32 FP16 rows at d = 128); any other r takes the
+  // general instance (an r % 4 == 0 instance of the step kept its raw words in scratch).
+  const int r = a.st.r;
+  if (r % 4 == 0 && r <= 2 * Geo<D>::RPS)
+    hipLaunchKernelGGL((step_kernel_q<D, PER_KEY, BF16, PLAN_SMALL>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((step_kernel_q<D, PER_KEY, BF16, PLAN_ANY>), grid, block, 0, s, a);
 }
 
-// The persistent variant measured slower than one workgroup per unit on MI355X (its
-// per-iteration wait also covers the previous unit's stores: gfx9 counts loads and stores on
-// one in-order counter), so it runs only when DAMP_PERSISTENT=1.
-bool persistent_enabled() {
-  static const bool on = [] {
-    const char* e = std::getenv("DAMP_PERSISTENT");
-    return e && e[0] && e[0] != '0';
-  }();
-  return on;
-}
-
-// DAMP_SINGLE_PASS=1 selects the one-pass quantized kernel (state decoded once into fp32
-// registers) instead of the two-pass one, for comparison.
-bool single_pass_q() {
-  static const bool on = [] {
-    const char* e = std::getenv("DAMP_SINGLE_PASS");
-    return e && e[0] && e[0] != '0';
-  }();
-  return on;
+template <int D, int PER_KEY, int BF16>
+void launch_step_dt(int fmt, const StepArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H));
+  if (fmt == FMT_F32)
+    hipLaunchKernelGGL((step_kernel_f32<D, PER_KEY, BF16>), grid, dim3(Geo<D>::NT), 0, s, a);
+  else
+    launch_step_q<D, PER_KEY, BF16>(a, grid, s);
 }
 
 template <int D>
-hipError_t step_d(int fmt, int per_key, int bf16, StepArgs a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H));
-  const dim3 block(Geo<D>::NT);
-  const bool r4 = a.st.r % 4 == 0;
-  const int units = a.B * a.H;
-#define DAMP_LAUNCH(F, K, T, R) \
-  hipLaunchKernelGGL((step_kernel<D, F, K, T, R>), grid, block, 0, s, a)
-#define DAMP_LAUNCH_PF2(K, T, R, C)                                                        \
-  do {                                                                                     \
-    const uint32_t lds = PfLayout(D, a.st.r, T, K).total;                                  \
-    a.grid = persistent_grid(step_kernel_pf<D, K, T, R, C>, Geo<D>::NT, lds, units);       \
-    if (a.grid > 0)                                                                        \
-      hipLaunchKernelGGL((step_kernel_pf<D, K, T, R, C>), dim3(a.grid), block, lds, s, a); \
-    else                                                                                   \
-      DAMP_LAUNCH(FMT_Q, K, T, R);                                                         \
-  } while (0)
-#define DAMP_LAUNCH_PF(K, T, R) \
-  do { if (a.st.contiguous) DAMP_LAUNCH_PF2(K, T, R, true); else DAMP_LAUNCH_PF2(K, T, R, false); } while (0)
-#define DAMP_LAUNCH_Q2(K, T, P) \
-  hipLaunchKernelGGL((step_kernel_q2<D, K, T, P>), grid, block, 0, s, a)
-#define DAMP_LAUNCH_Q(K, T)                                                                      \
-  do {                                                                                           \
-    if (a.grid != 0) { if (r4) DAMP_LAUNCH_PF(K, T, true); else DAMP_LAUNCH_PF(K, T, false); }   \
-    else if (single_pass_q()) { if (r4) DAMP_LAUNCH(FMT_Q, K, T, true); else DAMP_LAUNCH(FMT_Q, K, T, false); } \
-    else if (r4 && a.st.r <= 2 * Geo<D>::RPS) DAMP_LAUNCH_Q2(K, T, PLAN_SMALL);                  \
-    else if (r4) DAMP_LAUNCH_Q2(K, T, PLAN_R4);                                                  \
-    else DAMP_LAUNCH_Q2(K, T, PLAN_ANY);                                                         \
-  } while (0)
-  if (fmt == FMT_F32) {
-    if (per_key) { if (bf16) DAMP_LAUNCH(FMT_F32, 1, 1, true); else DAMP_LAUNCH(FMT_F32, 1, 0, true); }
-    else         { if (bf16) DAMP_LAUNCH(FMT_F32, 0, 1, true); else DAMP_LAUNCH(FMT_F32, 0, 0, true); }
+hipError_t step_d(int fmt, int per_key, int bf16, const StepArgs& a, hipStream_t s) {
+  if (per_key) {
+    if (bf16) launch_step_dt<D, 1, 1>(fmt, a, s); else launch_step_dt<D, 1, 0>(fmt, a, s);
   } else {
-    if (!persistent_enabled()) a.grid = 0;
-    if (per_key) { if (bf16) DAMP_LAUNCH_Q(1, 1); else DAMP_LAUNCH_Q(1, 0); }
-    else         { if (bf16) DAMP_LAUNCH_Q(0, 1); else DAMP_LAUNCH_Q(0, 0); }
+    if (bf16) launch_step_dt<D, 0, 1>(fmt, a, s); else launch_step_dt<D, 0, 0>(fmt, a, s);
   }
-#undef DAMP_LAUNCH_Q
-#undef DAMP_LAUNCH_Q2
-#undef DAMP_LAUNCH_PF
-#undef DAMP_LAUNCH_PF2
-#undef DAMP_LAUNCH
   return hipGetLastError();
 }
 
@@ -1068,9 +764,9 @@ template <int D>
 hipError_t quant_d(const PackArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.n) * unsigned(a.H)), block(Geo<D>::NT);
   if (a.st.r % 4 == 0)
-    hipLaunchKernelGGL((quantize_kernel<D, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<D, PLAN_R4>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((quantize_kernel<D, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<D, PLAN_ANY>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -1078,9 +774,9 @@ template <int D>
 hipError_t dequant_d(const PackArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.n) * unsigned(a.H)), block(Geo<D>::NT);
   if (a.st.r % 4 == 0)
-    hipLaunchKernelGGL((dequantize_kernel<D, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((dequantize_kernel<D, PLAN_R4>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((dequantize_kernel<D, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((dequantize_kernel<D, PLAN_ANY>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
