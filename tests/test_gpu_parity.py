@@ -236,3 +236,39 @@ print('ok')
     r = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("case", ["identity", "full_forget", "zero_rows", "tiny", "large", "zero_v_beta1"])
+def test_degenerate_inputs(case):
+    """Degenerate steps against the oracle: alpha = 1 with beta = 0 (the state must come back
+    unchanged), alpha = 0 (the state is replaced by beta k v^T), all-zero rows (scale 0), very
+    small and large magnitudes, and v = 0 with beta = 1 (the key direction is erased)."""
+    B, H, D, r = 4, 3, 128, 24
+    rows, S, inp = _random_case(77, B, H, D, r, synth.GDN, "bf16")
+    if case == "identity":
+        inp.alpha[:] = 1.0
+        inp.beta[:] = 0.0
+    elif case == "full_forget":
+        inp.alpha[:] = 0.0
+    elif case == "zero_rows":
+        S[:, :, ::3, :] = 0.0
+        S[0] = 0.0
+    elif case == "tiny":
+        S *= np.float32(1e-30)
+    elif case == "large":
+        S *= np.float32(500.0)
+    elif case == "zero_v_beta1":
+        inp = synth.StepInputs(inp.q, inp.k, np.zeros_like(inp.v), inp.alpha,
+                               np.ones_like(inp.beta), inp.dtype, inp.q_bits, inp.k_bits,
+                               np.zeros_like(inp.v_bits))
+    mask, out, got, ref_out, ref, _ = _damp_ref_and_gpu(rows, S, inp, np.arange(B), B)
+    check_readout(out, ref_out)
+    stats = check_quant(mask, got, ref)
+    _log(f"{case}: {stats}")
+    if case == "identity":
+        # the oracle's state came back unchanged; the GPU's codes equal the input codes exactly
+        m = np.broadcast_to(mask, (B, H, D)).reshape(B * H, D)
+        h0, c0, s0 = oracle.quantize(m, S.reshape(B * H, D, D))
+        f = m.astype(bool)
+        assert np.array_equal(got[1].reshape(B * H, D, D)[~f], c0[~f])
+        assert np.array_equal(got[0].reshape(B * H, D, D)[f], h0[f])

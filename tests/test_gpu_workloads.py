@@ -1,0 +1,236 @@
+"""GPU parity on the named workloads at their full sizes, from identical input states.
+
+* gdn64:    64 slots x 32 GDN heads, d = 128; state warmed by 256 fp32 oracle steps from zero,
+            24 FP16 rows per head chosen by the oracle's score, then one bf16 step; DAMP, fp32 and
+            uniform INT8.
+* kda256:   256 slots x 32 KDA heads with lognormal value-column multipliers, 24 FP16 rows by
+            score with per-channel mean gates, 4 INT8 rows per head scaled x20; one step.
+* pool4096: the benchmark's configuration: a 4,096-slot DAMP pool, 1,024 random active slots,
+            one step with the benchmark's first input set; every active unit compared, every
+            inactive block checked bit-identical.
+* drift:    the 64-slot state run for 2,048 steps in all three formats on the GPU; the oracle runs
+            the same steps for a sample of units, and at sampled steps the GPU restarts from the
+            oracle's state for one step (identical-input parity). The per-step readout error of
+            the quantized formats against fp32 is reported (no page gives values to pin it).
+"""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+import oracle  # noqa: E402
+import layout_ref  # noqa: E402
+from gpu_common import (SENTINEL, DampPool, check_fp32_state, check_quant, check_readout,  # noqa: E402
+                        fp32_state_bound, gpu_fp32_step, gpu_int8_step, ref_vectors,
+                        step_tensors, to_dev)
+from quantized_delta_rule_gdn_amd import lib, synth  # noqa: E402
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def gdn64_warm():
+    """Warmed fp32 state [64*32, 128, 128], per-head mean gate, FP16 rows [32, 24]."""
+    w = synth.GDN64
+    n = w.batch * w.heads
+    S = np.zeros((n, w.d, w.d), np.float32)
+    gate_sum = np.zeros(w.heads)
+    for t in range(synth.GDN64_WARMUP_STEPS):
+        inp = synth.gdn64_warmup(t)
+        oracle.step_fp32(S, *ref_vectors(inp, w.batch, w.heads, w.d))
+        gate_sum += inp.alpha.astype(np.float64).sum(axis=0)
+    abar = gate_sum / (synth.GDN64_WARMUP_STEPS * w.batch)
+    rows, _ = oracle.select_rows(S.reshape(w.batch, w.heads, w.d, w.d),
+                                 np.repeat(abar[:, None], w.d, axis=1), w.fp16_rows)
+    _log(f"gdn64 warmed: |S| mean {np.abs(S).mean():.3g}, max {np.abs(S).max():.3g}")
+    return S, abar, rows
+
+
+def test_gdn64_all_formats(gdn64_warm):
+    S, _, rows = gdn64_warm
+    w = synth.GDN64
+    B, H, D = w.batch, w.heads, w.d
+    inp = synth.gdn64_step()
+    vecs = ref_vectors(inp, B, H, D)
+    slots = np.arange(B)
+    # DAMP
+    mask = synth.rows_to_mask(rows, D)
+    maskn = np.broadcast_to(mask, (B, H, D)).reshape(B * H, D)
+    h, c, s = oracle.quantize(maskn, S)
+    pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), slots, B)
+    out = pool.step(inp)
+    got = pool.logical()
+    ref_out = oracle.step_quant(maskn, h, c, s, *vecs)
+    check_readout(out, ref_out)
+    _log(f"gdn64 DAMP: {check_quant(mask, got, (h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D)))}")
+    # fp32
+    S32 = S.copy()
+    o32, Sg = gpu_fp32_step(S.reshape(B, H, D, D), inp, slots, B)
+    r32 = oracle.step_fp32(S32, *vecs)
+    check_readout(o32, r32)
+    err = check_fp32_state(Sg.reshape(B * H, D, D), S32, fp32_state_bound(S, vecs[3], vecs[1], vecs[2], vecs[4], S32))
+    _log(f"gdn64 fp32: state max abs err {err:.3g}")
+    # uniform INT8
+    z = np.zeros((B * H, D), np.uint8)
+    hi, ci, si = oracle.quantize(z, S)
+    oi, cg, sg = gpu_int8_step(ci.reshape(B, H, D, D), si.reshape(B, H, D), inp, slots, B)
+    ri = oracle.step_quant(z, hi, ci, si, *vecs)
+    check_readout(oi, ri)
+    _log(f"gdn64 INT8: {check_quant(np.zeros((1, H, D), np.uint8), (np.zeros_like(cg, np.uint16), cg, sg), (hi.reshape(B, H, D, D), ci.reshape(B, H, D, D), si.reshape(B, H, D)))}")
+
+
+def test_kda256_damp():
+    w = synth.KDA256
+    B, H, D, r = w.batch, w.heads, w.d, w.fp16_rows
+    S0, _, inp = synth.kda256()
+    # rows by score with per-channel mean gate (alpha is in original key order)
+    abar = inp.alpha.astype(np.float64).mean(axis=0)          # [H, D]
+    rows, _ = oracle.select_rows(S0, abar, r)
+    mask = synth.rows_to_mask(rows, D)
+    int8_rows = np.stack([np.flatnonzero(mask[h] == 0) for h in range(H)])
+    out_rows = synth.kda256_outlier_rows(int8_rows)
+    for h in range(H):
+        S0[:, h, out_rows[h], :] *= np.float32(synth.KDA256_OUTLIER_GAIN)
+    n = B * H
+    maskn = np.broadcast_to(mask, (B, H, D)).reshape(n, D)
+    h_, c, s = oracle.quantize(maskn, S0.reshape(n, D, D))
+    del S0
+    pool = DampPool(rows, h_.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D),
+                    np.arange(B), B)
+    out = pool.step(inp)
+    got = pool.logical()
+    ref_out = oracle.step_quant(maskn, h_, c, s, *ref_vectors(inp, B, H, D))
+    check_readout(out, ref_out)
+    _log(f"kda256 DAMP: {check_quant(mask, got, (h_.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D)))}")
+
+
+def test_pool4096_full_size():
+    """The benchmark's launch: 1,024 of 4,096 slots, 32 heads, d = 128, r = 24, bf16 inputs."""
+    w = synth.POOL4096
+    B, H, D, r = w.batch, w.heads, w.d, w.fp16_rows
+    slots = synth.pool4096_slots()
+    rows = synth.pool4096_rows()
+    mask = synth.rows_to_mask(rows, D)
+    st = lib.DampState(w.pool_slots, H, D, rows)
+    st.pool.fill_(SENTINEL)
+    blocks = st.blocks()
+    inp = synth.pool4096_step(0)
+    refs = []
+    chunk = 128
+    for i in range(0, B, chunk):   # quantize with the oracle, pack, upload, slot chunk by chunk
+        S = synth.pool4096_states(i, chunk).reshape(chunk * H, D, D)
+        maskn = np.broadcast_to(mask, (chunk, H, D)).reshape(chunk * H, D)
+        h, c, s = oracle.quantize(maskn, S)
+        del S
+        blocks[torch.from_numpy(slots[i:i + chunk]).long().cuda()] = to_dev(
+            layout_ref.pack(rows, h.reshape(chunk, H, D, D), c.reshape(chunk, H, D, D),
+                            s.reshape(chunk, H, D)))
+        refs.append((h, c, s))
+    torch.cuda.synchronize()
+    _log("pool4096 uploaded")
+    q, k, v, a, b = step_tensors(inp)
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    st.decode_step(to_dev(slots), q, k, v, a, b, out)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    inactive = torch.ones(w.pool_slots, dtype=torch.bool, device="cuda")
+    inactive[torch.from_numpy(slots).long().cuda()] = False
+    assert bool((blocks[inactive] == SENTINEL).all()), "an inactive slot was written"
+    stats = []
+    for j, i in enumerate(range(0, B, chunk)):
+        h, c, s = refs[j]
+        n = chunk * H
+        maskn = np.broadcast_to(mask, (chunk, H, D)).reshape(n, D)
+        vecs = tuple(x[i:i + chunk] for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta))
+        ref_out = oracle.step_quant(maskn, h, c, s, *(x.reshape(n, -1) if x.ndim == 3 else x.reshape(n)
+                                                       for x in vecs))
+        check_readout(out[i:i + chunk], ref_out)
+        got = layout_ref.unpack(rows, blocks[torch.from_numpy(slots[i:i + chunk]).long().cuda()].cpu().numpy(), D)
+        stats.append(check_quant(mask, got, (h.reshape(chunk, H, D, D), c.reshape(chunk, H, D, D),
+                                             s.reshape(chunk, H, D))))
+    eq = min(x["code_eq_frac"] for x in stats)
+    _log(f"pool4096: min code_eq_frac over chunks {eq:.6f}, max fp16 ulp "
+         f"{max(x['fp16_max_ulp'] for x in stats)}, max scale rel {max(x['scale_max_rel'] for x in stats):.3g}")
+
+
+# ------------------------------------------------------------------------------------------
+DRIFT_SAMPLE_SLOTS = (0, 41)        # oracle free-runs these slots' 32 heads
+DRIFT_CHECK_STEPS = (0, 700, 2047)  # identical-input parity at these steps
+
+
+def test_drift_2048_steps(gdn64_warm):
+    S_warm, _, rows = gdn64_warm
+    w = synth.DRIFT
+    B, H, D, T = w.batch, w.heads, w.d, w.steps
+    mask = synth.rows_to_mask(rows, D)
+    maskn = np.broadcast_to(mask, (B, H, D)).reshape(B * H, D)
+    z = np.zeros((B * H, D), np.uint8)
+    # GPU states, all 64 slots
+    h, c, s = oracle.quantize(maskn, S_warm)
+    damp = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), np.arange(B), B)
+    hi, ci, si = oracle.quantize(z, S_warm)
+    codes = to_dev(ci.reshape(B, H, D, D))
+    scales = to_dev(si.reshape(B, H, D))
+    pool32 = to_dev(S_warm.reshape(B, H, D, D))
+    slot_dev = to_dev(np.arange(B, dtype=np.int32))
+    # oracle states for the sampled units
+    sel = np.concatenate([np.arange(sl * H, (sl + 1) * H) for sl in DRIFT_SAMPLE_SLOTS])
+    n = len(sel)
+    o_S = S_warm[sel].copy()
+    o_q = [x[sel].copy() for x in (h, c, s)]
+    o_i = [x[sel].copy() for x in (hi, ci, si)]
+    msel = maskn[sel]
+    zsel = z[sel]
+    outs = {f: torch.empty((B, H, D), dtype=torch.float32, device="cuda") for f in ("f32", "q", "i8")}
+    err_q, err_i, dev32 = [], [], []
+    for t in range(T):
+        inp = synth.drift_step(t)
+        vecs = ref_vectors(inp, B, H, D)
+        vs = tuple(x[sel] for x in vecs)
+        if t in DRIFT_CHECK_STEPS:   # identical-input parity from the oracle's states
+            _log(f"drift step {t}: identical-input check")
+            sl = np.arange(len(DRIFT_SAMPLE_SLOTS))
+            sub = synth.StepInputs(*(x[list(DRIFT_SAMPLE_SLOTS)] for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
+                                   inp.dtype, *(x[list(DRIFT_SAMPLE_SLOTS)] for x in (inp.q_bits, inp.k_bits, inp.v_bits)))
+            ns = len(DRIFT_SAMPLE_SLOTS)
+            p = DampPool(rows, *(x.reshape(ns, H, D, D) for x in o_q[:2]), o_q[2].reshape(ns, H, D), sl, ns)
+            go = p.step(sub)
+            gq = p.logical()
+        # advance the oracle's sampled units
+        r32 = oracle.step_fp32(o_S, *vs)
+        rq = oracle.step_quant(msel, *o_q, *vs)
+        oracle.step_quant(zsel, *o_i, *vs)
+        if t in DRIFT_CHECK_STEPS:
+            check_readout(go, rq)
+            check_quant(mask, gq, tuple(x.reshape(len(DRIFT_SAMPLE_SLOTS), H, *x.shape[1:]) for x in o_q))
+        # the GPU runs all units in all three formats
+        q, k, v, a, b = step_tensors(inp)
+        lib.fp32_decode_step(pool32, slot_dev, q, k, v, a, b, outs["f32"])
+        damp.state.decode_step(slot_dev, q, k, v, a, b, outs["q"])
+        lib.uniform_int8_decode_step(codes, scales, slot_dev, q, k, v, a, b, outs["i8"])
+        o32 = outs["f32"].cpu().numpy().reshape(B * H, D)
+        oq = outs["q"].cpu().numpy().reshape(B * H, D)
+        oi = outs["i8"].cpu().numpy().reshape(B * H, D)
+        assert np.isfinite(oq).all() and np.isfinite(oi).all() and np.isfinite(o32).all()
+        nrm = np.linalg.norm(o32)
+        err_q.append(np.linalg.norm(oq - o32) / nrm)
+        err_i.append(np.linalg.norm(oi - o32) / nrm)
+        dev32.append(np.linalg.norm(o32[sel] - r32) / np.linalg.norm(r32))
+    err_q, err_i, dev32 = map(np.array, (err_q, err_i, dev32))
+    _log(f"drift: DAMP rel readout err vs fp32 mean {err_q.mean():.3e} max {err_q.max():.3e}; "
+         f"uniform INT8 mean {err_i.mean():.3e} max {err_i.max():.3e}; "
+         f"GPU fp32 vs oracle max {dev32.max():.3e}")
+    out_dir = os.environ.get("DAMP_DRIFT_OUT")
+    if out_dir:
+        os.makedirs(out_dir, exist_ok=True)
+        np.savez(os.path.join(out_dir, "drift_curves.npz"), damp=err_q, int8=err_i, fp32_dev=dev32)
+    assert dev32.max() < 1e-4          # the fp32 recurrence stays on the double-accumulated one
+    assert err_q.mean() < err_i.mean()  # FP16 high-risk rows cut the INT8 drift
