@@ -28,8 +28,29 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD published peak
-TRAFFIC_PER_LAUNCH_BYTES = None  # filled from the committed rocprofv3 counter summary, or null
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "damp_step_pool4096_hbm_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "quantized_delta_rule_gdn_amd", "csrc", "step_kernels.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the DAMP step from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each calibrated on a copy of known size), or None when the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            line = line.strip()
+            if line and not line.startswith("#") and "=" in line:
+                key, val = (x.strip() for x in line.split("=", 1))
+                kv[key] = val
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256") != sha:
+        return None
+    return int(kv["traffic_bytes_per_launch"])
 
 
 def alg_bytes_per_update(fmt: str, d: int = 128, r: int = 24, per_key: bool = False,
@@ -223,7 +244,8 @@ def main():
                    "format": main_fmt, "slots_active": B, "heads": H, "d": d,
                    "fp16_rows": r, "global_batch": B, "seq_len": 1},
         "roofline": {"bound": "hbm", "achieved": m["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": m["gbs"] / PEAK_HBM_GBS, "traffic": TRAFFIC_PER_LAUNCH_BYTES},
+                     "frac": m["gbs"] / PEAK_HBM_GBS,
+                     "traffic": measured_traffic() if main_fmt == "damp" else None},
     }
     if "fp32" in results and "damp" in results:
         line["baselines"] = {f: {"ms_per_step": v["ms_per_step"], "updates_per_s": v["updates_per_s"],

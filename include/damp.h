@@ -26,8 +26,13 @@
  *
  * INT8 rows (the pages only say "INT8"; this rule is the library's): symmetric, one fp32 scale
  * per row, scale = fl32(max_j |X_ij| / 127), code = round-half-to-even of fl32(X_ij / scale),
- * codes in [-127, 127]; an all-zero row has scale 0 and codes 0. FP16 rows: IEEE binary16,
- * round to nearest even. Reconstruction: code * scale, or the binary16 value.
+ * codes in [-127, 127]; an all-zero row has scale 0 and codes 0. damp_state_quantize and
+ * uniform_int8_quantize follow this rule bit for bit. Inside the decode steps the code is the
+ * round-half-to-even of X_ij * rcp(scale) (hardware reciprocal, 1 ulp), which can differ by one
+ * from the rule where X_ij / scale lies within ~2e-5 of a half-integer (a few codes in 10^5).
+ * FP16 rows: IEEE binary16, round to nearest even. Reconstruction: code * scale, or the
+ * binary16 value. Rows whose absmax is below ~1e-36 (subnormal scales) are outside the range
+ * the rule is supported for.
  *
  * Execution model. Every call that takes a `stream` (a hipStream_t, e.g. torch's
  * torch.cuda.current_stream().cuda_stream; NULL = the default stream) only validates its
@@ -112,7 +117,7 @@ size_t damp_state_bytes(const damp_layout* layout);
  *   pool       dev, >= damp_state_bytes(layout) bytes (pool_bytes says how many), 256-byte
  *              aligned. Not initialised or touched by this call.
  *   out        receives the handle; *out is set to NULL on failure.
- * Allocates a small device copy of the row map (num_heads * d_k int32) and copies it with a
+ * Allocates a small device copy of the row map (num_heads * d_k bytes) and copies it with a
  * synchronous hipMemcpy on the current device. Errors: INVALID_ARGUMENT (null pointer, bad
  * size, unsorted/duplicate/out-of-range row, pool too small or misaligned), UNSUPPORTED (d_k),
  * OUT_OF_MEMORY, HIP. */
