@@ -1,11 +1,14 @@
 #!/usr/bin/env python3
 """Throughput of the DAMP decode step on one MI355X.
 
-Workload (default): the serving pool -- 4,096 request slots x 32 GDN heads of 128 x 128 states
-in the DAMP layout (24 FP16 key rows per head, INT8 + fp32 row scale for the other 104), of
-which 1,024 random slots are active; each step updates 1,024 x 32 = 32,768 (slot, head) states
-with bf16 q, k, v and fp32 alpha, beta, cycling through 4 pre-made input sets. The touched
-state (654 MB read + written per step) is larger than the 256 MB Infinity Cache.
+Workload (default, --workload pool4096): the serving pool -- 4,096 request slots x 32 GDN heads
+of 128 x 128 states in the DAMP layout (24 FP16 key rows per head, INT8 + fp32 row scale for the
+other 104), of which 1,024 random slots are active; each step updates 1,024 x 32 = 32,768
+(slot, head) states with bf16 q, k, v and fp32 alpha, beta, cycling through 4 pre-made input
+sets. The touched state (654 MB read + written per step) is larger than the 256 MB Infinity
+Cache. Other workloads (--workload gdn64 | kda256 | drift) have 64 or 256 contiguous slots whose
+state fits in that cache: gdn64 and kda256 rotate over enough copies of the pool that each launch
+finds its state in HBM (cold), drift reruns the same 64 slots (warm, labelled so).
 
 A step = one damp_decode_step launch over the batch (reconstruct, decay, delta update, readout,
 requantize). Timing: HIP events recorded on the stream the kernels are launched on, around
@@ -79,6 +82,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", choices=["damp", "fp32", "int8"], default=None,
                    help="time only this format (for profiling)")
+    p.add_argument("--workload", choices=["pool4096", "gdn64", "kda256", "drift"],
+                   default="pool4096")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the step, run a plain device copy of MIB MiB --steps times "
                         "(the reference kernel of known size for HBM byte counters)")
@@ -96,16 +101,6 @@ def copy_calibration(mib: int, steps: int) -> None:
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": mib << 20, "bytes_written": mib << 20,
                       "launches": steps}), flush=True)
-
-
-def make_inputs(torch, synth, dev):
-    sets = []
-    for i in range(4):
-        inp = synth.pool4096_step(i)
-        bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
-        sets.append((bf(inp.q_bits), bf(inp.k_bits), bf(inp.v_bits),
-                     torch.from_numpy(inp.alpha).to(dev), torch.from_numpy(inp.beta).to(dev)))
-    return sets
 
 
 def fill_states(torch, fn, slots_dev, H, d, dev, chunk=128, seed=1003):
@@ -167,6 +162,33 @@ def cpu_baseline(seconds: float):
                       f"slots of the pool workload) in {el:.1f} s"}
 
 
+WORKLOADS = ("pool4096", "gdn64", "kda256", "drift")
+COLD_BYTES = 1 << 30  # rotate copies until this much state lies between two uses of one copy
+
+
+def workload_setup(name, synth, torch, dev):
+    """Slot sets (one per pool copy), FP16 rows, input sets and a description."""
+    if name == "pool4096":
+        w = synth.POOL4096
+        active = synth.pool4096_slots()
+        rows = synth.pool4096_rows()
+        sets = [synth.pool4096_step(i) for i in range(4)]
+        return w, [active], w.pool_slots, rows, sets, True, (
+            "pool4096: GDN decode step, 4096-slot DAMP pool x 32 heads x 128x128, 1024 active "
+            "random slots, 24 FP16 rows/head, bf16 qkv")
+    w = {"gdn64": synth.GDN64, "kda256": synth.KDA256, "drift": synth.DRIFT}[name]
+    rng = np.random.default_rng([w.seed, 7])
+    rows = synth.random_rows(rng, w.heads, w.d, w.fp16_rows)
+    sets = [synth.step_inputs(rng, w.batch, w.heads, w.d, w.decay, "bf16") for _ in range(4)]
+    blk = 2 * w.fp16_rows * w.d + (w.d - w.fp16_rows) * w.d + 4 * (w.d - w.fp16_rows)
+    copies = 1 if name == "drift" else -(-COLD_BYTES // (w.batch * w.heads * blk))
+    slot_sets = [np.arange(c * w.batch, (c + 1) * w.batch, dtype=np.int32) for c in range(copies)]
+    desc = {"gdn64": "gdn64: GDN decode step, 64 slots x 32 heads x 128x128, 24 FP16 rows/head, bf16 qkv",
+            "kda256": "kda256: KDA decode step (per-key gate), 256 slots x 32 heads x 128x128, 24 FP16 rows/head, bf16 qkv",
+            "drift": "drift: GDN decode step repeated on the same 64 slots x 32 heads x 128x128, 24 FP16 rows/head, bf16 qkv"}[name]
+    return w, slot_sets, copies * w.batch, rows, sets, copies > 1, desc
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -182,45 +204,51 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    w = synth.POOL4096
+    w, slot_sets_np, pool_slots, rows, inputs, cold, desc = workload_setup(args.workload, synth, torch, dev)
     H, d, r = w.heads, w.d, w.fp16_rows
-    slots = torch.from_numpy(synth.pool4096_slots()).to(dev)
-    B = slots.numel()
+    per_key = w.decay == synth.KDA
+    slot_sets = [torch.from_numpy(x).to(dev) for x in slot_sets_np]
+    all_slots = torch.cat(slot_sets)
+    B = slot_sets[0].numel()
     units = B * H
-    sets = make_inputs(torch, synth, dev)
+    bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
+    sets = [(bf(i.q_bits), bf(i.k_bits), bf(i.v_bits), torch.from_numpy(i.alpha).to(dev),
+             torch.from_numpy(i.beta).to(dev)) for i in inputs]
     out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    R = len(slot_sets)
     results = {}
 
     def run(fmt):
         if fmt == "damp":
-            st = lib.DampState(w.pool_slots, H, d, synth.pool4096_rows(), device=dev)
+            st = lib.DampState(pool_slots, H, d, rows, device=dev)
             st.pool.zero_()
-            fill_states(torch, st.quantize, slots, H, d, dev)
-            launch = lambda i: st.decode_step(slots, *sets[i % 4], out)
+            fill_states(torch, st.quantize, all_slots, H, d, dev)
+            launch = lambda i: st.decode_step(slot_sets[i % R], *sets[i % 4], out)
             keep = st
         elif fmt == "fp32":
-            pool = torch.zeros((w.pool_slots, H, d, d), dtype=torch.float32, device=dev)
-            fill_states(torch, lambda S, sl: pool.index_copy_(0, sl.long(), S), slots, H, d, dev)
-            launch = lambda i: lib.fp32_decode_step(pool, slots, *sets[i % 4], out)
+            pool = torch.zeros((pool_slots, H, d, d), dtype=torch.float32, device=dev)
+            fill_states(torch, lambda S, sl: pool.index_copy_(0, sl.long(), S), all_slots, H, d, dev)
+            launch = lambda i: lib.fp32_decode_step(pool, slot_sets[i % R], *sets[i % 4], out)
             keep = pool
         else:
-            codes = torch.zeros((w.pool_slots, H, d, d), dtype=torch.int8, device=dev)
-            scales = torch.zeros((w.pool_slots, H, d), dtype=torch.float32, device=dev)
+            codes = torch.zeros((pool_slots, H, d, d), dtype=torch.int8, device=dev)
+            scales = torch.zeros((pool_slots, H, d), dtype=torch.float32, device=dev)
             fill_states(torch, lambda S, sl: lib.uniform_int8_quantize(codes, scales, S, sl),
-                        slots, H, d, dev)
-            launch = lambda i: lib.uniform_int8_decode_step(codes, scales, slots, *sets[i % 4], out)
+                        all_slots, H, d, dev)
+            launch = lambda i: lib.uniform_int8_decode_step(codes, scales, slot_sets[i % R],
+                                                            *sets[i % 4], out)
             keep = (codes, scales)
         ms = time_launches(torch, launch, args.steps, args.warmup)
         del keep
         torch.cuda.empty_cache()
-        ab = alg_bytes_per_update(fmt, d, r) * units
+        ab = alg_bytes_per_update(fmt, d, r, per_key) * units
         return {"ms_per_step": ms, "updates_per_s": units / (ms * 1e-3),
                 "alg_bytes_per_launch": ab, "gbs": ab / (ms * 1e-3) / 1e9}
 
     fmts = [args.only] if args.only else (["damp"] if args.no_baselines else ["damp", "fp32", "int8"])
     for f in fmts:
         results[f] = run(f)
-        print(f"# {f}: {results[f]['ms_per_step'] * 1e3:.1f} us/step, "
+        print(f"# {args.workload} {f}: {results[f]['ms_per_step'] * 1e3:.1f} us/step, "
               f"{results[f]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
     main_fmt = args.only or "damp"
@@ -239,13 +267,13 @@ def main():
         "dtype": "f32+fp16+int8" if main_fmt == "damp" else ("f32" if main_fmt == "fp32" else "f32+int8"),
         "data": "synthetic: seeded N(0, 0.1) states, unit-norm bf16 q/k, N(0,1) bf16 v, "
                 "sigmoid gates; no model weights",
-        "config": {"workload": "pool4096: GDN decode step, 4096-slot DAMP pool x 32 heads x "
-                               "128x128, 1024 active random slots, 24 FP16 rows/head, bf16 qkv",
-                   "format": main_fmt, "slots_active": B, "heads": H, "d": d,
-                   "fp16_rows": r, "global_batch": B, "seq_len": 1},
+        "config": {"workload": desc, "format": main_fmt, "slots_active": B, "heads": H, "d": d,
+                   "fp16_rows": r, "global_batch": B, "seq_len": 1,
+                   "state_cache": "cold (HBM)" if (cold or args.workload == "pool4096") else "warm (Infinity Cache)",
+                   "pool_copies": R},
         "roofline": {"bound": "hbm", "achieved": m["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": m["gbs"] / PEAK_HBM_GBS,
-                     "traffic": measured_traffic() if main_fmt == "damp" else None},
+                     "traffic": measured_traffic() if (main_fmt == "damp" and args.workload == "pool4096") else None},
     }
     if "fp32" in results and "damp" in results:
         line["baselines"] = {f: {"ms_per_step": v["ms_per_step"], "updates_per_s": v["updates_per_s"],

@@ -452,19 +452,40 @@ __device__ __forceinline__ float decode_row(const uint32_t* raw, int c, int p, i
 
 // Per-row scalars of the unit in storage order: srow[i] = {m_i, k_i, q_i, -} with the row
 // multiplier m_i = a_i * scale_i for INT8 rows and a_i otherwise (the gate folded into the
-// scale: S'_ij = code_ij * m_i), and v in sv.
+// scale: S'_ij = code_ij * m_i), and v in sv. Every global load here is independent of the
+// others (k, q and the gate are read in key order, the row map in parallel) and the
+// permutation to storage order goes through LDS (tmp: 3 * D floats), so the staging costs one
+// memory round trip rather than a row-map load followed by dependent k / q loads.
 template <int D, int PER_KEY, int BF16, bool Q>
 __device__ __forceinline__ void stage_rows(const StepArgs& a, int64_t unit, int bh, int head, int r,
-                                           int tid, float4* srow, float* sv) {
+                                           int tid, float4* srow, float* sv, float* tmp) {
   const int64_t vec = int64_t(bh) * D;
-  for (int i = tid; i < D; i += Geo<D>::NT) {
-    const int src = a.st.rowmap ? a.st.rowmap[head * D + i] : i;
-    const float g = PER_KEY ? a.alpha[vec + src] : a.alpha[bh];
-    float mul = g;
-    if constexpr (Q)
-      if (i >= r) mul = reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[i - r] * g;
-    srow[i] = make_float4(mul, load_in<BF16>(a.k, vec + src), load_in<BF16>(a.q, vec + src), 0.0f);
-    sv[i] = load_in<BF16>(a.v, vec + i);
+  constexpr int PER = (D + Geo<D>::NT - 1) / Geo<D>::NT;
+  int src[PER];
+  float sc[PER];
+#pragma unroll
+  for (int n = 0; n < PER; ++n) {
+    const int i = tid + n * Geo<D>::NT;
+    if (i < D) {
+      src[n] = a.st.rowmap ? a.st.rowmap[head * D + i] : i;
+      sc[n] = 1.0f;
+      if constexpr (Q)
+        if (i >= r) sc[n] = reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[i - r];
+      tmp[i] = load_in<BF16>(a.k, vec + i);
+      tmp[D + i] = load_in<BF16>(a.q, vec + i);
+      if constexpr (PER_KEY) tmp[2 * D + i] = a.alpha[vec + i];
+      sv[i] = load_in<BF16>(a.v, vec + i);
+    }
+  }
+  const float g0 = PER_KEY ? 0.0f : a.alpha[bh];
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < PER; ++n) {
+    const int i = tid + n * Geo<D>::NT;
+    if (i < D) {
+      const float g = PER_KEY ? tmp[2 * D + src[n]] : g0;
+      srow[i] = make_float4(sc[n] * g, tmp[src[n]], tmp[D + src[n]], 0.0f);
+    }
   }
   __syncthreads();
 }
@@ -542,7 +563,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
                         reinterpret_cast<uint32_t*>(S[t]));
 
   // (2) per-row scalars and v
-  stage_rows<D, PER_KEY, BF16, false>(a, unit, bh, head, 0, tid, srow, sv);
+  stage_rows<D, PER_KEY, BF16, false>(a, unit, bh, head, 0, tid, srow, sv, &redu[0][0]);
 
   // (3) decay, partial u = S'^T k, p = S'^T q over this lane's rows
   float pu[CPL], pp[CPL], pqk = 0.0f;
@@ -616,7 +637,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q(const StepArgs a) {
   }
 
   // (2) per-row scalars and v
-  stage_rows<D, PER_KEY, BF16, true>(a, unit, bh, head, r, tid, srow, sv);
+  stage_rows<D, PER_KEY, BF16, true>(a, unit, bh, head, r, tid, srow, sv, &redu[0][0]);
 
   // (3) pass 1: u_j += (k_i m_i) c_ij, p_j += (q_i m_i) c_ij over the lane's rows
   float pu[CPL], pp[CPL], pqk = 0.0f;

@@ -197,6 +197,14 @@ def kda256(slots: int | None = None):
     return S0, col_mult, inp
 
 
+def kda256_step() -> StepInputs:
+    """The step inputs of the KDA workload alone (the same draws kda256() returns)."""
+    w = KDA256
+    col_mult = np.random.default_rng([w.seed, 0]).lognormal(0.0, 1.0, (w.heads, w.d))
+    return step_inputs(np.random.default_rng([w.seed, 2]), w.batch, w.heads, w.d, KDA, "bf16",
+                       col_mult.astype(np.float32))
+
+
 def kda256_outlier_rows(int8_rows: np.ndarray) -> np.ndarray:
     """Given, per head, the key rows that are stored in INT8 (int [H, D - r]), draw 4 of them
     per head as outlier rows (scaled x20 by the caller, so that INT8 scales see outliers).
