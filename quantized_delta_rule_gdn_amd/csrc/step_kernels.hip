@@ -31,13 +31,15 @@
 namespace damp {
 namespace {
 
-template <int D>
+template <int D, int NW_ = (D >= 128 ? 4 : (D >= 64 ? 2 : 1))>
 struct Geo {
-  static constexpr int NW = D >= 128 ? 4 : (D >= 64 ? 2 : 1);  // waves per workgroup
+  static constexpr int NW = NW_;                               // waves per workgroup
   static constexpr int NT = NW * 64;                           // threads per workgroup
   static constexpr int CPL = D / 16;                           // value columns per lane
   static constexpr int RPS = NW * 4;                           // storage rows per row step
   static constexpr int RPL = D / RPS;                          // row steps (rows) per lane
+  // row steps that may hold FP16 rows in PLAN_SMALL (at least the first two; D / 4 rows)
+  static constexpr int T16 = (D / 4) / RPS > 2 ? (D / 4) / RPS : 2;
   static_assert(D % 16 == 0 && RPL * RPS == D, "unsupported d");
 };
 
@@ -223,17 +225,32 @@ __device__ __forceinline__ void buf_load(rsrc_t rs, uint32_t off, uint32_t soff,
   }
 }
 
+// A store of more than 64 bits of data reads its data registers after it issues, so a VALU
+// instruction right behind it must not overwrite them. The compiler inserts that wait only when
+// the instruction's soffset is a constant; with an SGPR soffset it does not, and on gfx950 the
+// overwrite then reaches memory (seen as corrupted first dwords of 16-byte row chunks when a
+// conversion was scheduled directly after the store). guard_store keeps the data registers
+// live across an s_nop of two wait states issued after the store.
+using v4u = __attribute__((ext_vector_type(4))) unsigned int;
+using v2u = __attribute__((ext_vector_type(2))) unsigned int;
+
+__device__ __forceinline__ void guard_store(v4u data) { asm volatile("s_nop 1" ::"v"(data)); }
+__device__ __forceinline__ void guard_store2(v4u a, v4u b) { asm volatile("s_nop 1" ::"v"(a), "v"(b)); }
+
 template <int N>
 __device__ __forceinline__ void buf_store(rsrc_t rs, uint32_t off, uint32_t soff, const uint32_t* w) {
-  using v4 = __attribute__((ext_vector_type(4))) unsigned int;
-  using v2 = __attribute__((ext_vector_type(2))) unsigned int;
   if constexpr (N == 32) {
-    __builtin_amdgcn_raw_buffer_store_b128(v4{w[0], w[1], w[2], w[3]}, rs, off, soff, kNT);
-    __builtin_amdgcn_raw_buffer_store_b128(v4{w[4], w[5], w[6], w[7]}, rs, off + 16, soff, kNT);
+    const v4u a{w[0], w[1], w[2], w[3]}, b{w[4], w[5], w[6], w[7]};
+    // back to back, then one guard: the two halves of the lane's 32 bytes stay one clause
+    __builtin_amdgcn_raw_buffer_store_b128(a, rs, off, soff, kNT);
+    __builtin_amdgcn_raw_buffer_store_b128(b, rs, off + 16, soff, kNT);
+    guard_store2(a, b);
   } else if constexpr (N == 16) {
-    __builtin_amdgcn_raw_buffer_store_b128(v4{w[0], w[1], w[2], w[3]}, rs, off, soff, kNT);
+    const v4u a{w[0], w[1], w[2], w[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(a, rs, off, soff, kNT);
+    guard_store(a);
   } else if constexpr (N == 8) {
-    __builtin_amdgcn_raw_buffer_store_b64(v2{w[0], w[1]}, rs, off, soff, kNT);
+    __builtin_amdgcn_raw_buffer_store_b64(v2u{w[0], w[1]}, rs, off, soff, kNT);
   } else if constexpr (N == 4) {
     __builtin_amdgcn_raw_buffer_store_b32(w[0], rs, off, soff, kNT);
   } else if constexpr (N == 2) {
@@ -257,8 +274,8 @@ struct UnitPtr {
 };
 
 template <int D, int FMT, bool ONE = false>
-__device__ __forceinline__ UnitPtr unit_ptr(const StateRef& st, int64_t unit) {
-  const uint32_t r = FMT == FMT_Q ? static_cast<uint32_t>(st.r) : 0u;
+__device__ __forceinline__ UnitPtr unit_ptr(const StateRef& st, int64_t unit, int r_rows) {
+  const uint32_t r = FMT == FMT_Q ? static_cast<uint32_t>(r_rows) : 0u;
   if constexpr (ONE) {
     const rsrc_t blk = make_rsrc(st.hbase + unit * st.hstride, 2 * r * D + (D - r) * D + 4 * (D - r));
     return UnitPtr{blk, blk, blk, 2 * r * D, 2 * r * D + (D - r) * D, static_cast<int>(r)};
@@ -322,9 +339,9 @@ struct Row {
   }
 
   // EXACT selects int8_code_exact (pack kernel) instead of the fast code (step kernel).
-  // sc_lds: when given, the INT8 row scale goes to sc_lds[p] (the caller writes the unit's
-  // scales to memory later with one coalesced store) instead of a 4-byte store per row.
-  template <bool EXACT, bool MIX>
+  // SC_LDS: the INT8 row scale goes to sc_lds[p] (the caller writes the unit's scales to memory
+  // later with one coalesced store) instead of a 4-byte store per row.
+  template <bool EXACT, bool MIX, bool SC_LDS = false>
   __device__ static __forceinline__ void store(const UnitPtr& u, int p0, int rs, int cg,
                                                const float* x, float* sc_lds = nullptr) {
     uint32_t wd[W];
@@ -367,7 +384,7 @@ struct Row {
         }
       }
       if (cg == 0) {
-        if (sc_lds) {
+        if constexpr (SC_LDS) {
           sc_lds[p0 + rs] = s;
         } else {
           const uint32_t sb = __float_as_uint(s);
@@ -390,18 +407,28 @@ struct Row {
 // row step that straddles r mixes both (K_MIX). The plans are separate kernel instances so the
 // common cases carry no code (and no registers) for the mixed one.
 //   PLAN_F32:   fp32 state
-//   PLAN_SMALL: r % 4 == 0 and r <= 2 * RPS: only the first two row steps can hold FP16 rows,
-//               every later row step is INT8 at compile time (its raw words are half as many)
+//   PLAN_SMALL: r % 4 == 0 and r <= T16 * RPS: only the first T16 row steps can hold FP16
+//               rows, every later row step is INT8 at compile time (its raw words are half as
+//               many)
 //   PLAN_R4:    r % 4 == 0
 //   PLAN_ANY:   any r
-enum Plan : int { PLAN_F32 = 0, PLAN_SMALL = 1, PLAN_R4 = 2, PLAN_ANY = 3 };
+//   PLAN_FIXED: r = T * RPS fixed at compile time: row steps 0 .. T-1 are FP16, the rest INT8,
+//               so after unrolling no row step branches on its kind
+enum Plan : int { PLAN_F32 = 0, PLAN_SMALL = 1, PLAN_R4 = 2, PLAN_ANY = 3, PLAN_FIXED = 4 };
 
-template <int PLAN, typename F>
+// T: PLAN_SMALL's T16, or PLAN_FIXED's FP16 row step count.
+template <int PLAN, int T = 2, typename F>
 __device__ __forceinline__ void by_plan(int t, int p0, int r, F&& f) {
+  constexpr int T16 = T;
   if constexpr (PLAN == PLAN_F32) {
     f.template operator()<K_F32>();
+  } else if constexpr (PLAN == PLAN_FIXED) {
+    if (t < T)
+      f.template operator()<K_F16>();
+    else
+      f.template operator()<K_I8>();
   } else {
-    if (PLAN == PLAN_SMALL && t >= 2) {
+    if (PLAN == PLAN_SMALL && t >= T16) {
       f.template operator()<K_I8>();
     } else if (p0 + 4 <= r) {
       f.template operator()<K_F16>();
@@ -456,16 +483,16 @@ __device__ __forceinline__ float decode_row(const uint32_t* raw, int c, int p, i
 // others (k, q and the gate are read in key order, the row map in parallel) and the
 // permutation to storage order goes through LDS (tmp: 3 * D floats), so the staging costs one
 // memory round trip rather than a row-map load followed by dependent k / q loads.
-template <int D, int PER_KEY, int BF16, bool Q>
+template <int D, int NT, int PER_KEY, int BF16, bool Q>
 __device__ __forceinline__ void stage_rows(const StepArgs& a, int64_t unit, int bh, int head, int r,
                                            int tid, float4* srow, float* sv, float* tmp) {
   const int64_t vec = int64_t(bh) * D;
-  constexpr int PER = (D + Geo<D>::NT - 1) / Geo<D>::NT;
+  constexpr int PER = (D + NT - 1) / NT;
   int src[PER];
   float sc[PER];
 #pragma unroll
   for (int n = 0; n < PER; ++n) {
-    const int i = tid + n * Geo<D>::NT;
+    const int i = tid + n * NT;
     if (i < D) {
       src[n] = a.st.rowmap ? a.st.rowmap[head * D + i] : i;
       sc[n] = 1.0f;
@@ -481,7 +508,7 @@ __device__ __forceinline__ void stage_rows(const StepArgs& a, int64_t unit, int 
   __syncthreads();
 #pragma unroll
   for (int n = 0; n < PER; ++n) {
-    const int i = tid + n * Geo<D>::NT;
+    const int i = tid + n * NT;
     if (i < D) {
       const float g = PER_KEY ? tmp[2 * D + src[n]] : g0;
       srow[i] = make_float4(sc[n] * g, tmp[src[n]], tmp[D + src[n]], 0.0f);
@@ -494,12 +521,11 @@ __device__ __forceinline__ void stage_rows(const StepArgs& a, int64_t unit, int 
 // sums of u = S'^T k and p = S'^T q (over its RPL rows) to LDS; thread j then adds the 4*NW
 // partials of column j in a fixed order, forms delta_j = beta (v_j - u_j) (left in sv[j]) and
 // the readout y_j = p_j + (q.k) delta_j. (q.k is summed over row slots with lane swaps.)
-template <int D>
+template <int D, typename G>
 __device__ __forceinline__ void finish_columns(float (*redu)[D], float (*redp)[D], float* redqk,
                                                float* sv, float* pu, float* pp, float pqk,
                                                float beta, float* out_row, int tid, int w, int rs,
                                                int lane, int cg) {
-  using G = Geo<D>;
   constexpr int CPL = G::CPL, NW = G::NW;
   store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(&redu[w * 4 + rs][cg * CPL]),
                        reinterpret_cast<const uint32_t*>(pu));
@@ -526,10 +552,10 @@ __device__ __forceinline__ void finish_columns(float (*redu)[D], float (*redp)[D
 }
 
 // Write the INT8 row scales gathered in sc_lds[r .. D) with consecutive lanes (coalesced).
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void flush_scales(const UnitPtr& u, const float* sc_lds, int r, int tid) {
   __syncthreads();
-  for (int i = r + tid; i < D; i += Geo<D>::NT) {
+  for (int i = r + tid; i < D; i += NT) {
     const uint32_t sb = __float_as_uint(sc_lds[i]);
     buf_store<4>(u.s, static_cast<uint32_t>(i - r) * 4u, u.soff, &sb);
   }
@@ -553,7 +579,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
   const int b = bh / a.H;
   const int head = bh - b * a.H;
   const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
-  const UnitPtr up = unit_ptr<D, FMT_F32>(a.st, unit);
+  const UnitPtr up = unit_ptr<D, FMT_F32>(a.st, unit, 0);
 
   // (1) issue every state load of this lane first, so the whole block is in flight
   float S[RPL][CPL];
@@ -563,7 +589,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
                         reinterpret_cast<uint32_t*>(S[t]));
 
   // (2) per-row scalars and v
-  stage_rows<D, PER_KEY, BF16, false>(a, unit, bh, head, 0, tid, srow, sv, &redu[0][0]);
+  stage_rows<D, G::NT, PER_KEY, BF16, false>(a, unit, bh, head, 0, tid, srow, sv, &redu[0][0]);
 
   // (3) decay, partial u = S'^T k, p = S'^T q over this lane's rows
   float pu[CPL], pp[CPL], pqk = 0.0f;
@@ -582,8 +608,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
   }
 
   // (4) column reductions, delta and the readout y = p + (q.k) delta (one thread per column)
-  finish_columns<D>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + int64_t(bh) * D, tid,
-                    w, rs, lane, cg);
+  finish_columns<D, G>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + int64_t(bh) * D,
+                       tid, w, rs, lane, cg);
   float dl[CPL];
   load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));
 
@@ -599,15 +625,16 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
 }
 
 // ---- the decode step, quantized state (DAMP, uniform INT8): two passes over the codes ------
-// The state stays in VGPRs in its stored, compressed form (~20 registers per lane at d = 128
-// with PLAN_SMALL) rather than as 64 fp32 registers: pass 1 decodes it into the column sums
+// The state stays in VGPRs in its stored, compressed form (~40 registers per lane at d = 128
+// with two waves per unit) rather than as fp32 values: pass 1 decodes it into the column sums
 // u = S'^T k and p = S'^T q (the row multiplier folded into k and q per row), pass 2 decodes it
 // again row step by row step to form X = S' + k delta^T, requantize and store. The second
-// decode costs about one VALU instruction per element; the registers it frees let 7 workgroups
-// share a CU instead of 4, which is what keeps enough bytes in flight to HBM.
-template <int D, int PER_KEY, int BF16, int PLAN>
-__global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q(const StepArgs a) {
-  using G = Geo<D>;
+// decode costs about one VALU instruction per element; the registers it frees let twice as
+// many units share a CU, which is what keeps enough bytes in flight to HBM.
+template <int D, int PER_KEY, int BF16, int PLAN, int WAVES, int NF = 0>
+__global__ __launch_bounds__(64 * WAVES) void step_kernel_q(const StepArgs a) {
+  using G = Geo<D, WAVES>;
+  constexpr int T16 = PLAN == PLAN_FIXED ? NF : G::T16;
   constexpr int CPL = G::CPL, RPL = G::RPL, NW = G::NW, RW = Words<CPL * 2>::W;
   __shared__ float4 srow[D];
   __shared__ float sv[D];     // v, then delta
@@ -621,34 +648,36 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q(const StepArgs a) {
   const int b = bh / a.H;
   const int head = bh - b * a.H;
   const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
-  const int r = a.st.r;
+  const int r = PLAN == PLAN_FIXED ? NF * G::RPS : a.st.r;
   // one buffer resource over a contiguous block unless a row step mixes kinds
-  const UnitPtr up = (PLAN != PLAN_ANY && a.st.contiguous) ? unit_ptr<D, FMT_Q, true>(a.st, unit)
-                                                           : unit_ptr<D, FMT_Q>(a.st, unit);
+  const UnitPtr up = (PLAN != PLAN_ANY && a.st.contiguous) ? unit_ptr<D, FMT_Q, true>(a.st, unit, r)
+                                                           : unit_ptr<D, FMT_Q>(a.st, unit, r);
 
   // (1) issue every state load of this lane first, so the whole block is in flight
   uint32_t raw[RPL][RW];
 #pragma unroll
   for (int t = 0; t < RPL; ++t) {
     const int p0 = t * G::RPS + w * 4;
-    by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
+    by_plan<PLAN, T16>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
       load_row_step<D, K>(up, p0, rs, cg, raw[t]);
     });
   }
 
   // (2) per-row scalars and v
-  stage_rows<D, PER_KEY, BF16, true>(a, unit, bh, head, r, tid, srow, sv, &redu[0][0]);
+  stage_rows<D, G::NT, PER_KEY, BF16, true>(a, unit, bh, head, r, tid, srow, sv, &redu[0][0]);
 
-  // (3) pass 1: u_j += (k_i m_i) c_ij, p_j += (q_i m_i) c_ij over the lane's rows
+  // (3) pass 1: u_j += (k_i m_i) c_ij, p_j += (q_i m_i) c_ij over the lane's rows. The lane's
+  // rows are my_rows[t * RPS]: one LDS base address with immediate offsets per row step.
+  const float4* my_rows = srow + (w * 4 + rs);
   float pu[CPL], pp[CPL], pqk = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) pu[c] = pp[c] = 0.0f;
 #pragma unroll
   for (int t = 0; t < RPL; ++t) {
     const int p0 = t * G::RPS + w * 4, p = p0 + rs;
-    const float4 rw = srow[p];
+    const float4 rw = my_rows[t * G::RPS];
     const float kk = rw.y * rw.x, qq = rw.z * rw.x;
-    by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
+    by_plan<PLAN, T16>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const float x = decode_row<D, K>(raw[t], c, p, r);
@@ -660,8 +689,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q(const StepArgs a) {
   }
 
   // (4) column reductions, delta and the readout y = p + (q.k) delta (one thread per column)
-  finish_columns<D>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + int64_t(bh) * D, tid,
-                    w, rs, lane, cg);
+  finish_columns<D, G>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + int64_t(bh) * D,
+                       tid, w, rs, lane, cg);
   float dl[CPL];
   load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));
 
@@ -676,17 +705,17 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_q(const StepArgs a) {
 #pragma unroll
   for (int t = 0; t < RPL; ++t) {
     const int p0 = t * G::RPS + w * 4, p = p0 + rs;
-    const float4 rw = srow[p];
-    by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
+    const float4 rw = my_rows[t * G::RPS];
+    by_plan<PLAN, T16>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
       float X[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) X[c] = fmaf(rw.y, dl[c], decode_row<D, K>(raw[t], c, p, r) * rw.x);
       each_kind<K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
-        Row<D, K2>::template store<false, MIX>(up, p0, rs, cg, X, ssc);
+        Row<D, K2>::template store<false, MIX, true>(up, p0, rs, cg, X, ssc);
       });
     });
   }
-  flush_scales<D>(up, ssc, r, tid);
+  flush_scales<D, G::NT>(up, ssc, r, tid);
 }
 
 // ---- pack: fp32 states (original key order) -> quantized format (exact rule) -------------
@@ -702,7 +731,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void quantize_kernel(const PackArgs a) 
   const int head = ih - i * a.H;
   const int64_t unit = int64_t(a.slot_idx[i]) * a.H + head;
   const int r = a.st.r;
-  const UnitPtr up = unit_ptr<D, FMT_Q>(a.st, unit);
+  const UnitPtr up = unit_ptr<D, FMT_Q>(a.st, unit, r);
 #pragma unroll
   for (int t = 0; t < G::RPL; ++t) {
     const int p0 = t * G::RPS + w * 4, p = p0 + rs;
@@ -731,7 +760,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequantize_kernel(const PackArgs a
   const int head = ih - i * a.H;
   const int64_t unit = int64_t(a.slot_idx[i]) * a.H + head;
   const int r = a.st.r;
-  const UnitPtr up = unit_ptr<D, FMT_Q>(a.st, unit);
+  const UnitPtr up = unit_ptr<D, FMT_Q>(a.st, unit, r);
 #pragma unroll
   for (int t = 0; t < G::RPL; ++t) {
     const int p0 = t * G::RPS + w * 4, p = p0 + rs;
@@ -750,16 +779,44 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequantize_kernel(const PackArgs a
 }
 
 // ---- launchers -------------------------------------------------------------------------------
+// Waves per workgroup of the quantized step with the row kinds fixed at compile time: two at
+// d = 128 (80 VGPRs with 24 FP16 rows: 6 waves per SIMD, 12 units per CU), which measured a
+// few percent faster than four waves per unit on the short batches and equal on the long one;
+// one wave per unit (115 VGPRs, 16 units per CU) measured slower everywhere.
+constexpr int kStepWaves = 2;
+template <int D>
+constexpr int kWaves = kStepWaves < Geo<D>::NW ? kStepWaves : Geo<D>::NW;
+
+// r = NF * RPS FP16 rows, NF <= T16: the instance for that NF.
+template <int D, int PER_KEY, int BF16, int NF>
+bool launch_step_fixed(int nf, const StepArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (NF < 0) {
+    return false;
+  } else {
+    if (nf == NF) {
+      hipLaunchKernelGGL((step_kernel_q<D, PER_KEY, BF16, PLAN_FIXED, kWaves<D>, NF>), grid,
+                         dim3(64 * kWaves<D>), 0, s, a);
+      return true;
+    }
+    return launch_step_fixed<D, PER_KEY, BF16, NF - 1>(nf, a, grid, s);
+  }
+}
+
+// Instance choice by r: the row kinds fixed at compile time when r is a multiple of the row
+// step (the usual layouts: r in {0, 8, 16, 24, 32} at d = 128); else PLAN_SMALL (r % 4 == 0,
+// r <= 32 at d = 128) with the default workgroup shape; else the general instance.
 template <int D, int PER_KEY, int BF16>
 void launch_step_q(const StepArgs& a, dim3 grid, hipStream_t s) {
-  const dim3 block(Geo<D>::NT);
-  // PLAN_SMALL covers the usual layouts (r <= 32 FP16 rows at d = 128); any other r takes the
-  // general instance (an r % 4 == 0 instance of the step kept its raw words in scratch).
+  using GS = Geo<D, kWaves<D>>;
+  using G = Geo<D>;
   const int r = a.st.r;
-  if (r % 4 == 0 && r <= 2 * Geo<D>::RPS)
-    hipLaunchKernelGGL((step_kernel_q<D, PER_KEY, BF16, PLAN_SMALL>), grid, block, 0, s, a);
+  if (r % GS::RPS == 0 && r <= GS::T16 * GS::RPS &&
+      launch_step_fixed<D, PER_KEY, BF16, GS::T16>(r / GS::RPS, a, grid, s))
+    return;
+  if (r % 4 == 0 && r <= G::T16 * G::RPS)
+    hipLaunchKernelGGL((step_kernel_q<D, PER_KEY, BF16, PLAN_SMALL, G::NW>), grid, dim3(G::NT), 0, s, a);
   else
-    hipLaunchKernelGGL((step_kernel_q<D, PER_KEY, BF16, PLAN_ANY>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((step_kernel_q<D, PER_KEY, BF16, PLAN_ANY, G::NW>), grid, dim3(G::NT), 0, s, a);
 }
 
 template <int D, int PER_KEY, int BF16>

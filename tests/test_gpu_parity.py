@@ -57,6 +57,15 @@ def _damp_ref_and_gpu(rows, S, inp, slots, num_slots):
     (128, 27, 9, 3, synth.KDA, "bf16"),
     (128, 1, 2, 2, synth.GDN, "fp32"),
     (128, 128, 2, 2, synth.KDA, "bf16"),
+    # every launch shape: row kinds fixed at compile time (r a multiple of the row step),
+    # the r % 4 == 0 plan, and the general one
+    (128, 32, 41, 3, synth.KDA, "bf16"),
+    (128, 8, 23, 2, synth.GDN, "fp32"),
+    (128, 12, 19, 2, synth.GDN, "bf16"),
+    (64, 4, 9, 3, synth.GDN, "bf16"),
+    (64, 16, 6, 2, synth.KDA, "fp32"),
+    (32, 8, 7, 2, synth.KDA, "bf16"),
+    (16, 4, 5, 2, synth.GDN, "fp32"),
 ])
 def test_damp_step_sizes_and_edges(D, r, B, H, decay, dtype):
     _log(f"damp step D={D} r={r} B={B} H={H} decay={decay} dtype={dtype}")
