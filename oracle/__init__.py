@@ -57,6 +57,14 @@ def lib() -> ctypes.CDLL:
         L.oracle_step.restype = I
         L.oracle_select_rows.argtypes = [I, I, Lg, P, P, I, P, P]
         L.oracle_select_rows.restype = I
+        L.oracle_int8_row_error.argtypes = [I, P]
+        L.oracle_int8_row_error.restype = ctypes.c_double
+        L.oracle_risk_scores.argtypes = [I, I, Lg, P, P, P]
+        L.oracle_risk_scores.restype = I
+        L.oracle_budget_rows.argtypes = [I, I, ctypes.c_double, I, I]
+        L.oracle_budget_rows.restype = Lg
+        L.oracle_allocate_rows.argtypes = [I, I, P, Lg, I, I, P, P]
+        L.oracle_allocate_rows.restype = I
         _lib = L
     return _lib
 
@@ -175,3 +183,38 @@ def select_rows(S, abar, r: int):
     rc = lib().oracle_select_rows(D, H, n_slots, _p(S), _p(abar), r, _p(rows), _p(score))
     assert rc == 0
     return rows, score
+
+
+def int8_row_error(x) -> float:
+    """Squared error of storing row ``x`` with the INT8 rule (binary64)."""
+    x = _c(x, np.float32)
+    return float(lib().oracle_int8_row_error(x.size, _p(x)))
+
+
+def risk_scores(S, abar) -> np.ndarray:
+    """Per (head, key row) risk score for calibration states ``S[n_slots, H, D, D]`` and mean
+    gates ``abar[H, D]`` (float32); returns float64 [H, D]."""
+    S = _c(S, np.float32)
+    n_slots, H, D, _ = S.shape
+    abar = _c(np.broadcast_to(abar, (H, D)), np.float32)
+    score = np.empty((H, D), np.float64)
+    rc = lib().oracle_risk_scores(D, H, n_slots, _p(S), _p(abar), _p(score))
+    assert rc == 0
+    return score
+
+
+def budget_rows(D: int, H: int, bits_per_value: float, g: int = 1, r_max: int | None = None) -> int:
+    return int(lib().oracle_budget_rows(D, H, float(bits_per_value), g, D if r_max is None else r_max))
+
+
+def allocate_rows(score, R: int, g: int = 1, r_max: int | None = None):
+    """Allocation of ``R`` FP16 rows over the heads of ``score[H, D]`` in groups of ``g``.
+    Returns ``(r int32 [H], map int32 [H, D])``: map[h, :r[h]] are head h's FP16 rows ascending,
+    the rest its INT8 rows ascending."""
+    score = _c(score, np.float64)
+    H, D = score.shape
+    r = np.empty(H, np.int32)
+    m = np.empty((H, D), np.int32)
+    rc = lib().oracle_allocate_rows(D, H, _p(score), R, g, D if r_max is None else r_max, _p(r), _p(m))
+    assert rc == 0
+    return r, m

@@ -272,3 +272,138 @@ int oracle_select_rows(int D, int H, long n_slots, const float* S, const double*
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Budgeted selection with a per-head FP16 row count. The DAMP abstracts: high-risk key
+ * channels are chosen offline from quantization-error energy and decay-based error retention,
+ * and kept in FP16 under a fixed total storage budget (9.9 bits per state value on the
+ * pages); the remaining rows are INT8. Readings taken here:
+ *   - quantization-error energy of a key row = the squared error of storing that row with the
+ *     INT8 rule above, sum_j (x_j - s * c_j)^2, averaged over the calibration states;
+ *   - retention = 1 / (1 - abar) for a channel whose mean gate is abar (each step multiplies
+ *     what the state holds by abar, so an error survives for a geometric series of steps);
+ *   - the budget counts data bytes (FP16 rows, INT8 rows, fp32 INT8 scales), and its FP16
+ *     rows go to the rows with the largest scores over all heads, handed out in groups of g
+ *     rows per head (g = 1 gives a per-row choice), at most r_max per head.
+ * ---------------------------------------------------------------------------------------- */
+
+/* Squared INT8 error of one row, in binary64. s * c is exact in binary64 (24-bit significand
+ * times a 7-bit integer); the difference x - s*c is exact too (when c != 0 both lie within a
+ * factor 256 of s), so only the square and the sum round. */
+double oracle_int8_row_error(int D, const float* x) {
+  int8_t* c = (int8_t*)malloc((size_t)D);
+  if (!c) return -1.0;
+  float s = 0.0f;
+  oracle_quant_row(D, x, c, &s);
+  double e = 0.0;
+  for (int j = 0; j < D; ++j) {
+    const double d = (double)x[j] - (double)s * (double)c[j];
+    e += d * d;
+  }
+  free(c);
+  return e;
+}
+
+/* score[h][i] = (sum over slots, ascending, of the row error) / n_slots / (1 - abar[h][i]). */
+int oracle_risk_scores(int D, int H, long n_slots, const float* S, const float* abar,
+                       double* score) {
+  if (D <= 0 || H <= 0 || n_slots <= 0 || !S || !abar || !score) return -1;
+  const long DD = (long)D * D;
+  for (int hh = 0; hh < H; ++hh) {
+    for (int i = 0; i < D; ++i) {
+      double e = 0.0;
+      for (long sl = 0; sl < n_slots; ++sl)
+        e += oracle_int8_row_error(D, S + (sl * H + hh) * DD + (long)i * D);
+      e /= (double)n_slots;
+      score[(long)hh * D + i] = e / (1.0 - (double)abar[(long)hh * D + i]);
+    }
+  }
+  return 0;
+}
+
+/* Data bytes of one head's block with r FP16 rows: 2rD + (D - r)D + 4(D - r). */
+static double block_data_bytes(int D, long r) {
+  return 2.0 * r * D + (double)(D - r) * D + 4.0 * (D - r);
+}
+
+/* The number of FP16 rows, summed over the H heads of a slot, that fits in bits_per_value bits
+ * per state value: the largest R, a multiple of g and at most H * r_max, with
+ * H * (D^2 + 4D) + (D - 4) * R <= bits_per_value * H * D^2 / 8. -1 if not even R = 0 fits. */
+long oracle_budget_rows(int D, int H, double bits_per_value, int g, int r_max) {
+  if (D <= 4 || H <= 0 || g <= 0 || r_max < 0 || r_max > D) return -1;
+  const double budget = bits_per_value * H * (double)D * D / 8.0;
+  long R = -1;
+  for (long t = 0; t <= (long)H * r_max; t += g) {
+    if ((double)H * block_data_bytes(D, 0) + (double)(D - 4) * t <= budget) R = t;
+  }
+  return R;
+}
+
+/* Allocation of R FP16 rows (R a multiple of g). Per head, the rows are ranked by score, larger
+ * first, ties to the lower row index; group j of head h is that ranking's rows j*g .. j*g+g-1
+ * and its gain is the sum of their scores, added in ranking order. Groups past r_max / g are
+ * never taken. The R / g groups with the largest gains are taken, ties to the lower head and
+ * then the lower group index; since a head's gains do not increase along its ranking, each head
+ * ends up with a prefix of its ranking, r_h = g * (groups taken). This greedy choice maximises
+ * the total score kept in FP16 for the given R (every group costs the same bytes).
+ * Outputs r_out[H] and map_out[H][D]: the head's r_h FP16 rows ascending, then its INT8 rows
+ * ascending. Returns 0, or -1 on an invalid argument. */
+int oracle_allocate_rows(int D, int H, const double* score, long R, int g, int r_max,
+                         int32_t* r_out, int32_t* map_out) {
+  if (D <= 0 || H <= 0 || g <= 0 || r_max < 0 || r_max > D || R < 0 || R % g != 0 || !score ||
+      !r_out || !map_out)
+    return -1;
+  const int G = r_max / g; /* groups per head that may be taken */
+  int32_t* rank = (int32_t*)malloc(sizeof(int32_t) * (size_t)H * D); /* [h][t] -> row */
+  double* gain = (double*)malloc(sizeof(double) * (size_t)H * (G > 0 ? G : 1));
+  char* taken = (char*)calloc((size_t)H * (G > 0 ? G : 1), 1);
+  if (!rank || !gain || !taken) {
+    free(rank); free(gain); free(taken);
+    return -1;
+  }
+  for (int hh = 0; hh < H; ++hh) {
+    const double* sc = score + (long)hh * D;
+    /* selection sort by (score desc, index asc) */
+    char* used = (char*)calloc((size_t)D, 1);
+    for (int t = 0; t < D; ++t) {
+      int best = -1;
+      for (int i = 0; i < D; ++i) {
+        if (used[i]) continue;
+        if (best < 0 || sc[i] > sc[best]) best = i;
+      }
+      used[best] = 1;
+      rank[(long)hh * D + t] = best;
+    }
+    free(used);
+    for (int j = 0; j < G; ++j) {
+      double gsum = 0.0;
+      for (int t = j * g; t < j * g + g; ++t) gsum += sc[rank[(long)hh * D + t]];
+      gain[(long)hh * G + j] = gsum;
+    }
+  }
+  long want = R / g;
+  if (want > (long)H * G) want = (long)H * G;
+  for (long t = 0; t < want; ++t) {
+    long best = -1;
+    for (long x = 0; x < (long)H * G; ++x) {
+      if (taken[x]) continue;
+      if (best < 0 || gain[x] > gain[best]) best = x; /* x ascends in (head, group) order */
+    }
+    taken[best] = 1;
+  }
+  for (int hh = 0; hh < H; ++hh) {
+    int r = 0;
+    for (int j = 0; j < G; ++j) r += taken[(long)hh * G + j] ? g : 0;
+    r_out[hh] = r;
+    char* fp16 = (char*)calloc((size_t)D, 1);
+    for (int t = 0; t < r; ++t) fp16[rank[(long)hh * D + t]] = 1;
+    int n = 0;
+    for (int i = 0; i < D; ++i)
+      if (fp16[i]) map_out[(long)hh * D + n++] = i;
+    for (int i = 0; i < D; ++i)
+      if (!fp16[i]) map_out[(long)hh * D + n++] = i;
+    free(fp16);
+  }
+  free(rank); free(gain); free(taken);
+  return 0;
+}

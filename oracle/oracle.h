@@ -71,6 +71,21 @@ int oracle_step(int D, long n_units, int fmt, const uint8_t* mask, float* S32, u
 int oracle_select_rows(int D, int H, long n_slots, const float* S, const double* abar, int r,
                        int32_t* rows, double* score);
 
+/* Budgeted selection with a per-head FP16 row count (offline calibration, not the decode step).
+ *   oracle_int8_row_error: sum_j (x_j - s c_j)^2 in binary64 for the INT8 rule's (c, s) of x.
+ *   oracle_risk_scores:    score[h][i] = mean over slots of that error for row i of head h,
+ *                          divided by (1 - abar[h][i]); S [n_slots][H][D][D], abar [H][D].
+ *   oracle_budget_rows:    FP16 rows per slot (all heads) that fit bits_per_value data bits per
+ *                          state value, a multiple of g, at most H * r_max; -1 if none fits.
+ *   oracle_allocate_rows:  R rows handed out in groups of g by score; r_out [H], map_out [H][D]
+ *                          (each head's FP16 rows ascending, then its INT8 rows ascending). */
+double oracle_int8_row_error(int D, const float* x);
+int oracle_risk_scores(int D, int H, long n_slots, const float* S, const float* abar,
+                       double* score);
+long oracle_budget_rows(int D, int H, double bits_per_value, int g, int r_max);
+int oracle_allocate_rows(int D, int H, const double* score, long R, int g, int r_max,
+                         int32_t* r_out, int32_t* map_out);
+
 #ifdef __cplusplus
 }
 #endif
