@@ -184,6 +184,89 @@ damp_status uniform_int8_quantize(int8_t* codes, float* scales, int32_t num_slot
                                   int32_t num_heads, int32_t d_k, int32_t d_v, const float* S,
                                   const int32_t* slot_idx, int32_t n, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Per-head DAMP layout. The DAMP abstracts keep the high-risk key channels in FP16 under a
+ * fixed total storage budget; spent where the calibration scores are highest (see
+ * damp_allocate_rows), that budget gives each head its own FP16 row count r_h. Head h's block
+ * has the block format above with r = r_h; within a slot the heads' blocks follow each other,
+ * head h at byte offset off_h = sum over h' < h of round_up(data_bytes(r_h'), 256), and slot
+ * s starts at s * slot_bytes, slot_bytes = sum over h of round_up(data_bytes(r_h), 256).
+ * layout->num_fp16_rows is not used by these calls; damp_state_layout reports -1 for it.
+ * Every other entry point accepts a per-head handle like a uniform one.
+ * ------------------------------------------------------------------------------------- */
+
+/* Device bytes a per-head pool needs (num_slots * slot_bytes), or 0 if the layout or an r_h
+ * (host int32 [num_heads], each in [0, d_k]) is invalid. */
+size_t damp_state_bytes_per_head(const damp_layout* layout, const int32_t* r_per_head);
+
+/* Bind a caller-owned pool to a per-head layout.
+ *   r_per_head host int32 [num_heads], each in [0, d_k]
+ *   row_map    host int32 [num_heads][d_k]: row h lists head h's r_h FP16 key rows strictly
+ *              ascending, then its other key rows strictly ascending (a permutation of
+ *              0 .. d_k-1; the format damp_allocate_rows writes)
+ *   pool       dev, >= damp_state_bytes_per_head bytes, 256-byte aligned, not touched
+ * Allocates a small device table (num_heads * (d_k + 8) bytes), copied synchronously.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (d_k), OUT_OF_MEMORY, HIP. */
+damp_status damp_state_alloc_per_head(const damp_layout* layout, const int32_t* r_per_head,
+                                      const int32_t* row_map, void* pool, size_t pool_bytes,
+                                      damp_state** out);
+
+/* Per-head facts of any handle (uniform handles report r = num_fp16_rows for every head):
+ *   r_out       host int32 [num_heads] or NULL: r_h
+ *   offset_out  host int64 [num_heads] or NULL: off_h, the byte offset of head h's block in
+ *               a slot
+ *   slot_bytes  host int64 or NULL: the bytes of one slot (num_heads * block bytes when
+ *               uniform) */
+damp_status damp_state_head_info(const damp_state* state, int32_t* r_out, int64_t* offset_out,
+                                 int64_t* slot_bytes);
+
+/* ---------------------------------------------------------------------------------------
+ * Offline calibration on the device: the DAMP abstracts choose the high-risk key channels
+ * from quantization-error energy together with decay-based error retention, once, from
+ * calibration data. The library reads the error energy of key row i of head h as the squared
+ * error of storing that row with the INT8 rule above, and the retention as 1 / (1 - abar) for
+ * a channel of mean gate abar (a gate that scales the state by abar per step keeps an error
+ * for a geometric series of steps).
+ * ------------------------------------------------------------------------------------- */
+
+/* Risk scores from n calibration states:
+ *   S          dev fp32 [n][num_heads][d][d], key rows in their original order
+ *   abar       dev fp32 [num_heads][d]: mean gate of each key channel, in [0, 1) (GDN: the
+ *              head's mean gate in every entry)
+ *   row_error  dev fp64 [n][num_heads][d] (output, also a workspace): sum over j of
+ *              (S[s][h][i][j] - scale * code_j)^2 for the INT8 rule's (code, scale) of that
+ *              row, in binary64 with j ascending
+ *   score      dev fp64 [num_heads][d] (output): (sum over s ascending of row_error[s][h][i])
+ *              / n / (1 - abar[h][i]), each operation one binary64 rounding
+ * Deterministic (no atomics). n >= 1. Errors: INVALID_ARGUMENT, UNSUPPORTED (d), HIP. */
+damp_status damp_risk_scores(const float* S, int32_t n, int32_t num_heads, int32_t d,
+                             const float* abar, double* row_error, double* score, void* stream);
+
+/* FP16 rows, summed over the num_heads heads of one slot, that fit bits_per_value data bits
+ * per state value (FP16 rows, INT8 rows and their fp32 scales; padding not counted): the
+ * largest R, a multiple of g and at most num_heads * r_max, with
+ * num_heads * (d^2 + 4 d) + (d - 4) * R <= bits_per_value * num_heads * d^2 / 8.
+ * Returns -1 if not even R = 0 fits or an argument is invalid (d <= 4, g < 1, r_max outside
+ * [0, d]). Host only. At d = 128 with 32 heads, 9.9 bits gives R = 872 (27.25 rows per head). */
+int64_t damp_budget_rows(int32_t d, int32_t num_heads, double bits_per_value, int32_t g,
+                         int32_t r_max);
+
+/* Hand R FP16 rows (R % g == 0) to the heads in groups of g rows by score:
+ *   score   dev fp64 [num_heads][d]
+ *   r_out   dev int32 [num_heads] (output): r_h, a multiple of g, at most r_max
+ *   map_out dev int32 [num_heads][d] (output): head h's r_h FP16 rows ascending, then its other
+ *           rows ascending (the row_map of damp_state_alloc_per_head)
+ * Per head the rows are ranked by score, larger first, ties to the lower row index; group j of
+ * head h is ranks j*g .. j*g+g-1 and its gain the sum of their scores in rank order; groups
+ * past r_max / g are never taken; the R / g largest gains are taken (ties to the lower head,
+ * then the lower group), so each head keeps a prefix of its ranking and the total score kept in
+ * FP16 is the largest any allocation of R rows in groups of g can keep. One workgroup of the
+ * device does it. Limits: num_heads * d <= 8192 and num_heads * (r_max / g) <= 4096 groups
+ * (else UNSUPPORTED). Errors: INVALID_ARGUMENT, UNSUPPORTED, HIP. */
+damp_status damp_allocate_rows(const double* score, int32_t num_heads, int32_t d, int64_t R,
+                               int32_t g, int32_t r_max, int32_t* r_out, int32_t* map_out,
+                               void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). The string
  * is owned by the library and valid until the thread's next call. */
 const char* damp_last_error(void);

@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdamp.so")
-SOURCES = [os.path.join(CSRC, "damp_api.hip"), os.path.join(CSRC, "step_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "damp_api.hip"), os.path.join(CSRC, "step_kernels.hip"),
+           os.path.join(CSRC, "calib_kernels.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

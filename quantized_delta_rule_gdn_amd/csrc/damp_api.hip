@@ -4,6 +4,7 @@
 // validation paths work (and are tested) on a machine without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -15,10 +16,16 @@
 #include "launch.h"
 
 struct damp_state {
-  damp_layout layout;
+  damp_layout layout;    // num_fp16_rows = -1 for a per-head layout
   uint8_t* pool;
-  size_t block_bytes;
-  uint8_t* rowmap_dev;  // [num_heads][d]: storage row -> key row
+  size_t block_bytes;    // uniform layout: the block stride
+  uint8_t* rowmap_dev;   // [num_heads][d]: storage row -> key row; per-head layout: followed by
+                         // the int2 table {block offset in the slot, r} per head
+  bool per_head;
+  std::vector<int32_t> head_r;    // per head: r
+  std::vector<int64_t> head_off;  // per head: byte offset of its block inside a slot
+  size_t slot_bytes;
+  int32_t r_or, r_max;            // bitwise OR and maximum of head_r
 };
 
 namespace {
@@ -78,6 +85,58 @@ size_t data_bytes(const damp_layout* L) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+size_t data_bytes_r(int32_t d_, int32_t r_) {
+  const size_t d = static_cast<size_t>(d_), r = static_cast<size_t>(r_);
+  return 2 * r * d + (d - r) * d + 4 * (d - r);
+}
+
+// Layout checks of the per-head calls (num_fp16_rows not used); *L2 = the layout with
+// num_fp16_rows = -1.
+damp_status check_layout_per_head(const damp_layout* L, const int32_t* r_per_head, damp_layout* L2) {
+  if (!L) return fail(DAMP_ERR_INVALID_ARGUMENT, "layout is NULL");
+  damp_layout T = *L;
+  T.num_fp16_rows = 0;
+  damp_status st = check_layout(&T);
+  if (st != DAMP_OK) return st;
+  if (!r_per_head) return fail(DAMP_ERR_INVALID_ARGUMENT, "r_per_head is NULL");
+  for (int32_t h = 0; h < L->num_heads; ++h)
+    if (r_per_head[h] < 0 || r_per_head[h] > L->d_k)
+      return fail(DAMP_ERR_INVALID_ARGUMENT, "r_per_head[%d] = %d outside [0, d_k = %d]", h,
+                  r_per_head[h], L->d_k);
+  T.num_fp16_rows = -1;
+  if (L2) *L2 = T;
+  return DAMP_OK;
+}
+
+// Device copy of the row map ([H][d] bytes), followed for a per-head layout by the int2 table
+// {block offset in the slot, r} per head (8-byte aligned).
+damp_status upload_table(damp_state* s, const std::vector<uint8_t>& map) {
+  std::vector<uint8_t> blob(map);
+  if (s->per_head) {
+    const size_t H = s->head_r.size();
+    blob.resize(round_up(blob.size(), 8) + 8 * H);
+    int32_t* tab = reinterpret_cast<int32_t*>(blob.data() + round_up(map.size(), 8));
+    for (size_t h = 0; h < H; ++h) {
+      tab[2 * h] = static_cast<int32_t>(s->head_off[h]);
+      tab[2 * h + 1] = s->head_r[h];
+    }
+  }
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->rowmap_dev), blob.size());
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    s->rowmap_dev = nullptr;
+    return fail(e == hipErrorOutOfMemory ? DAMP_ERR_OUT_OF_MEMORY : DAMP_ERR_HIP,
+                "hipMalloc of the row map: %s", hipGetErrorString(e));
+  }
+  e = hipMemcpy(s->rowmap_dev, blob.data(), blob.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(s->rowmap_dev);
+    s->rowmap_dev = nullptr;
+    return fail(DAMP_ERR_HIP, "copying the row map: %s", hipGetErrorString(e));
+  }
+  return DAMP_OK;
+}
+
 // Common checks of a step call's vector arguments.
 damp_status check_step_args(int32_t B, int32_t H, int32_t d, const int32_t* slot_idx,
                             const void* q, const void* k, const void* v, damp_dtype dt,
@@ -133,8 +192,18 @@ damp_status launched(hipError_t e, const char* what) {
 
 damp::StateRef damp_ref(const damp_state* s) {
   const damp_layout& L = s->layout;
-  const int64_t d = L.d_k, r = L.num_fp16_rows;
   damp::StateRef ref{};
+  if (s->per_head) {
+    ref.hbase = s->pool;
+    ref.rowmap = s->rowmap_dev;
+    ref.contiguous = 1;
+    ref.heads = reinterpret_cast<const int2*>(s->rowmap_dev + static_cast<size_t>(L.num_heads) * L.d_k);
+    ref.slot_stride = static_cast<int64_t>(s->slot_bytes);
+    ref.heads_r_or = s->r_or;
+    ref.heads_r_max = s->r_max;
+    return ref;
+  }
+  const int64_t d = L.d_k, r = L.num_fp16_rows;
   ref.hbase = s->pool;
   ref.cbase = s->pool + 2 * r * d;
   ref.sbase = s->pool + 2 * r * d + (d - r) * d;
@@ -207,6 +276,15 @@ size_t damp_state_bytes(const damp_layout* L) {
   return units * blk;
 }
 
+size_t damp_state_bytes_per_head(const damp_layout* L, const int32_t* r_per_head) {
+  if (check_layout_per_head(L, r_per_head, nullptr) != DAMP_OK) return 0;
+  size_t slot = 0;
+  for (int32_t h = 0; h < L->num_heads; ++h) slot += round_up(data_bytes_r(L->d_k, r_per_head[h]), kBlockAlign);
+  const size_t n = static_cast<size_t>(L->num_slots);
+  if (slot != 0 && n > SIZE_MAX / slot) return 0;
+  return n * slot;
+}
+
 damp_status damp_state_alloc(const damp_layout* L, const int32_t* fp16_rows, void* pool,
                              size_t pool_bytes, damp_state** out) {
   if (!out) return fail(DAMP_ERR_INVALID_ARGUMENT, "out is NULL");
@@ -244,20 +322,90 @@ damp_status damp_state_alloc(const damp_layout* L, const int32_t* fp16_rows, voi
   s->layout = *L;
   s->pool = static_cast<uint8_t*>(pool);
   s->block_bytes = round_up(data_bytes(L), kBlockAlign);
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->rowmap_dev), map.size());
-  if (e != hipSuccess) {
+  s->per_head = false;
+  s->head_r.assign(static_cast<size_t>(H), r);
+  s->head_off.resize(static_cast<size_t>(H));
+  for (int32_t h = 0; h < H; ++h) s->head_off[static_cast<size_t>(h)] = static_cast<int64_t>(h) * s->block_bytes;
+  s->slot_bytes = static_cast<size_t>(H) * s->block_bytes;
+  s->r_or = s->r_max = r;
+  st = upload_table(s, map);
+  if (st != DAMP_OK) {
     delete s;
-    (void)hipGetLastError();
-    return fail(e == hipErrorOutOfMemory ? DAMP_ERR_OUT_OF_MEMORY : DAMP_ERR_HIP,
-                "hipMalloc of the row map: %s", hipGetErrorString(e));
-  }
-  e = hipMemcpy(s->rowmap_dev, map.data(), map.size(), hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(s->rowmap_dev);
-    delete s;
-    return fail(DAMP_ERR_HIP, "copying the row map: %s", hipGetErrorString(e));
+    return st;
   }
   *out = s;
+  return ok();
+}
+
+damp_status damp_state_alloc_per_head(const damp_layout* L, const int32_t* r_per_head,
+                                      const int32_t* row_map, void* pool, size_t pool_bytes,
+                                      damp_state** out) {
+  if (!out) return fail(DAMP_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  damp_layout L2{};
+  damp_status st = check_layout_per_head(L, r_per_head, &L2);
+  if (st != DAMP_OK) return st;
+  const int32_t H = L->num_heads, d = L->d_k;
+  if (!row_map) return fail(DAMP_ERR_INVALID_ARGUMENT, "row_map is NULL");
+  if (!pool) return fail(DAMP_ERR_INVALID_ARGUMENT, "pool is NULL");
+  if (!aligned(pool, kBlockAlign)) return fail(DAMP_ERR_INVALID_ARGUMENT, "pool must be 256-byte aligned");
+  const size_t need = damp_state_bytes_per_head(L, r_per_head);
+  if (need == 0) return fail(DAMP_ERR_INVALID_ARGUMENT, "pool size overflows size_t");
+  if (pool_bytes < need)
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "pool_bytes %zu < %zu needed", pool_bytes, need);
+  std::vector<uint8_t> map(static_cast<size_t>(H) * d);
+  std::vector<unsigned char> seen(static_cast<size_t>(d));
+  for (int32_t h = 0; h < H; ++h) {
+    const int32_t r = r_per_head[h];
+    const int32_t* row = row_map + static_cast<size_t>(h) * d;
+    std::fill(seen.begin(), seen.end(), 0);
+    for (int32_t p = 0; p < d; ++p) {
+      if (row[p] < 0 || row[p] >= d)
+        return fail(DAMP_ERR_INVALID_ARGUMENT, "row_map[%d][%d] = %d outside [0, %d)", h, p, row[p], d);
+      if (seen[static_cast<size_t>(row[p])])
+        return fail(DAMP_ERR_INVALID_ARGUMENT, "row_map[%d] repeats row %d", h, row[p]);
+      seen[static_cast<size_t>(row[p])] = 1;
+      if (p > 0 && p != r && row[p] <= row[p - 1])
+        return fail(DAMP_ERR_INVALID_ARGUMENT, "row_map[%d]: the FP16 rows and the other rows must each "
+                    "be strictly ascending", h);
+      map[static_cast<size_t>(h) * d + p] = static_cast<uint8_t>(row[p]);
+    }
+  }
+  damp_state* s = new (std::nothrow) damp_state{};
+  if (!s) return fail(DAMP_ERR_OUT_OF_MEMORY, "host allocation of the handle failed");
+  s->layout = L2;
+  s->pool = static_cast<uint8_t*>(pool);
+  s->block_bytes = 0;
+  s->per_head = true;
+  s->head_r.assign(r_per_head, r_per_head + H);
+  s->head_off.resize(static_cast<size_t>(H));
+  size_t off = 0;
+  s->r_or = 0;
+  s->r_max = 0;
+  for (int32_t h = 0; h < H; ++h) {
+    s->head_off[static_cast<size_t>(h)] = static_cast<int64_t>(off);
+    off += round_up(data_bytes_r(d, r_per_head[h]), kBlockAlign);
+    s->r_or |= r_per_head[h];
+    s->r_max = std::max(s->r_max, r_per_head[h]);
+  }
+  s->slot_bytes = off;
+  st = upload_table(s, map);
+  if (st != DAMP_OK) {
+    delete s;
+    return st;
+  }
+  *out = s;
+  return ok();
+}
+
+damp_status damp_state_head_info(const damp_state* s, int32_t* r_out, int64_t* offset_out,
+                                 int64_t* slot_bytes) {
+  if (!s) return fail(DAMP_ERR_INVALID_ARGUMENT, "state is NULL");
+  for (size_t h = 0; h < s->head_r.size(); ++h) {
+    if (r_out) r_out[h] = s->head_r[h];
+    if (offset_out) offset_out[h] = s->head_off[h];
+  }
+  if (slot_bytes) *slot_bytes = static_cast<int64_t>(s->slot_bytes);
   return ok();
 }
 
@@ -395,6 +543,56 @@ damp_status uniform_int8_quantize(int8_t* codes, float* scales, int32_t num_slot
   a.H = H;
   a.S = const_cast<float*>(S);
   return launched(damp::launch_quantize(d_k, a, st), "quantize");
+}
+
+damp_status damp_risk_scores(const float* S, int32_t n, int32_t H, int32_t d, const float* abar,
+                             double* row_error, double* score, void* stream) {
+  if (n <= 0 || H <= 0)
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "n (%d) and num_heads (%d) must be positive", n, H);
+  if (!supported_d(d))
+    return fail(DAMP_ERR_UNSUPPORTED, "d = %d: supported sizes are {16, 32, 64, 128}", d);
+  if (!S || !abar || !row_error || !score)
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "NULL S, abar, row_error or score");
+  if (!aligned(S, 16) || !aligned(abar, 4) || !aligned(row_error, 8) || !aligned(score, 8))
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "misaligned pointer (S 16 bytes, abar 4, outputs 8)");
+  if (static_cast<int64_t>(n) * H * d > (static_cast<int64_t>(1) << 40))
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "n * num_heads * d is too large");
+  return launched(damp::launch_risk_scores(d, S, n, H, abar, row_error, score,
+                                           static_cast<hipStream_t>(stream)),
+                  "risk scores");
+}
+
+int64_t damp_budget_rows(int32_t d, int32_t H, double bits_per_value, int32_t g, int32_t r_max) {
+  if (d <= 4 || H <= 0 || g < 1 || r_max < 0 || r_max > d) return -1;
+  const double budget = bits_per_value * H * static_cast<double>(d) * d / 8.0;
+  const double base = static_cast<double>(H) * (static_cast<double>(d) * d + 4.0 * d);
+  int64_t R = -1;
+  for (int64_t t = 0; t <= static_cast<int64_t>(H) * r_max; t += g)
+    if (base + static_cast<double>(d - 4) * t <= budget) R = t;
+  return R;
+}
+
+damp_status damp_allocate_rows(const double* score, int32_t H, int32_t d, int64_t R, int32_t g,
+                               int32_t r_max, int32_t* r_out, int32_t* map_out, void* stream) {
+  if (H <= 0 || d <= 0) return fail(DAMP_ERR_INVALID_ARGUMENT, "num_heads (%d) and d (%d) must be positive", H, d);
+  if (d > 128) return fail(DAMP_ERR_UNSUPPORTED, "d = %d: at most 128 key rows per head", d);
+  if (g < 1 || r_max < 0 || r_max > d)
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "g (%d) must be >= 1 and r_max (%d) in [0, d]", g, r_max);
+  if (R < 0 || R % g != 0)
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "R (%lld) must be >= 0 and a multiple of g (%d)",
+                static_cast<long long>(R), g);
+  if (static_cast<int64_t>(H) * d > damp::alloc_max_rows())
+    return fail(DAMP_ERR_UNSUPPORTED, "num_heads * d = %lld exceeds %d",
+                static_cast<long long>(H) * d, damp::alloc_max_rows());
+  if (static_cast<int64_t>(H) * (r_max / g) > damp::alloc_max_groups())
+    return fail(DAMP_ERR_UNSUPPORTED, "num_heads * (r_max / g) = %lld groups exceeds %d",
+                static_cast<long long>(H) * (r_max / g), damp::alloc_max_groups());
+  if (!score || !r_out || !map_out) return fail(DAMP_ERR_INVALID_ARGUMENT, "NULL score, r_out or map_out");
+  if (!aligned(score, 8) || !aligned(r_out, 4) || !aligned(map_out, 4))
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  return launched(damp::launch_allocate_rows(score, H, d, R, g, r_max, r_out, map_out,
+                                             static_cast<hipStream_t>(stream)),
+                  "allocate rows");
 }
 
 }  // extern "C"

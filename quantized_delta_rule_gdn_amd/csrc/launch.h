@@ -16,6 +16,11 @@ enum Fmt : int { FMT_F32 = 0, FMT_Q = 1 };  // fp32 state / FP16 + INT8 rows (DA
 //            with its fp32 scale at sbase + u * sstride + 4 (p - r);
 //            rowmap[head * d + p] = the key row held in storage row p (nullptr = identity).
 //   contiguous: the three regions of a unit are adjacent (DAMP pool blocks).
+//   heads (per-head DAMP layout; nullptr otherwise): heads[h] = {byte offset of head h's block
+//     inside a slot, r of head h}; the block of (slot, h) is at hbase + slot * slot_stride +
+//     heads[h].x and holds that head's FP16 rows, INT8 rows and scales as above (cbase, sbase,
+//     the strides and r are unused). heads_r_or / heads_r_max: bitwise OR and maximum of the
+//     heads' r, for the launcher's choice of kernel instance.
 struct StateRef {
   uint8_t* hbase;
   uint8_t* cbase;
@@ -26,6 +31,10 @@ struct StateRef {
   int32_t r;
   const uint8_t* rowmap;
   int32_t contiguous;
+  const int2* heads;
+  int64_t slot_stride;
+  int32_t heads_r_or;
+  int32_t heads_r_max;
 };
 
 struct StepArgs {
@@ -53,5 +62,14 @@ struct PackArgs {
 hipError_t launch_step(int fmt, int d, int per_key, int bf16, const StepArgs& a, hipStream_t s);
 hipError_t launch_quantize(int d, const PackArgs& a, hipStream_t s);
 hipError_t launch_dequantize(int d, const PackArgs& a, hipStream_t s);
+
+// Calibration (calib_kernels.hip). Sizes are validated by the caller: d in {16, 32, 64, 128},
+// H * d <= alloc_max_rows(), H * (r_max / g) <= alloc_max_groups(), R % g == 0.
+hipError_t launch_risk_scores(int d, const float* S, int32_t n, int32_t H, const float* abar,
+                              double* row_err, double* score, hipStream_t s);
+hipError_t launch_allocate_rows(const double* score, int32_t H, int32_t d, int64_t R, int32_t g,
+                                int32_t r_max, int32_t* r_out, int32_t* map_out, hipStream_t s);
+int alloc_max_rows();
+int alloc_max_groups();
 
 }  // namespace damp

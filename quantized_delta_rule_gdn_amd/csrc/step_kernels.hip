@@ -273,17 +273,37 @@ struct UnitPtr {
   int r;
 };
 
+// Where the unit of (slot, head) lives: its FP16 (or fp32) region, INT8 region, scale region
+// and FP16 row count. Per-head DAMP layouts read the head's block offset and r from a table.
+struct UnitAddr {
+  uint8_t* h;
+  uint8_t* c;
+  uint8_t* s;
+  int r;
+};
+
+template <int D, int FMT>
+__device__ __forceinline__ UnitAddr unit_addr(const StateRef& st, int64_t slot, int head, int H) {
+  if (FMT == FMT_Q && st.heads) {
+    const int2 hi = st.heads[head];
+    uint8_t* blk = st.hbase + slot * st.slot_stride + hi.x;
+    return UnitAddr{blk, blk + 2 * hi.y * D, blk + 2 * hi.y * D + (D - hi.y) * D, hi.y};
+  }
+  const int64_t unit = slot * H + head;
+  return UnitAddr{st.hbase + unit * st.hstride, st.cbase + unit * st.cstride,
+                  st.sbase + unit * st.sstride, FMT == FMT_Q ? st.r : 0};
+}
+
 template <int D, int FMT, bool ONE = false>
-__device__ __forceinline__ UnitPtr unit_ptr(const StateRef& st, int64_t unit, int r_rows) {
+__device__ __forceinline__ UnitPtr unit_ptr(const UnitAddr& ua, int r_rows) {
   const uint32_t r = FMT == FMT_Q ? static_cast<uint32_t>(r_rows) : 0u;
   if constexpr (ONE) {
-    const rsrc_t blk = make_rsrc(st.hbase + unit * st.hstride, 2 * r * D + (D - r) * D + 4 * (D - r));
+    const rsrc_t blk = make_rsrc(ua.h, 2 * r * D + (D - r) * D + 4 * (D - r));
     return UnitPtr{blk, blk, blk, 2 * r * D, 2 * r * D + (D - r) * D, static_cast<int>(r)};
   }
   const uint32_t hbytes = FMT == FMT_F32 ? D * D * 4 : 2 * r * D;
-  return UnitPtr{make_rsrc(st.hbase + unit * st.hstride, hbytes),
-                 make_rsrc(st.cbase + unit * st.cstride, (D - r) * D),
-                 make_rsrc(st.sbase + unit * st.sstride, (D - r) * 4), 0u, 0u, static_cast<int>(r)};
+  return UnitPtr{make_rsrc(ua.h, hbytes), make_rsrc(ua.c, (D - r) * D),
+                 make_rsrc(ua.s, (D - r) * 4), 0u, 0u, static_cast<int>(r)};
 }
 
 // Byte offset of one lane's part of a storage row inside its region, split into a per-lane part
@@ -484,8 +504,8 @@ __device__ __forceinline__ float decode_row(const uint32_t* raw, int c, int p, i
 // permutation to storage order goes through LDS (tmp: 3 * D floats), so the staging costs one
 // memory round trip rather than a row-map load followed by dependent k / q loads.
 template <int D, int NT, int PER_KEY, int BF16, bool Q>
-__device__ __forceinline__ void stage_rows(const StepArgs& a, int64_t unit, int bh, int head, int r,
-                                           int tid, float4* srow, float* sv, float* tmp) {
+__device__ __forceinline__ void stage_rows(const StepArgs& a, const float* sc_old, int bh, int head,
+                                           int r, int tid, float4* srow, float* sv, float* tmp) {
   const int64_t vec = int64_t(bh) * D;
   constexpr int PER = (D + NT - 1) / NT;
   int src[PER];
@@ -497,7 +517,7 @@ __device__ __forceinline__ void stage_rows(const StepArgs& a, int64_t unit, int 
       src[n] = a.st.rowmap ? a.st.rowmap[head * D + i] : i;
       sc[n] = 1.0f;
       if constexpr (Q)
-        if (i >= r) sc[n] = reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[i - r];
+        if (i >= r) sc[n] = sc_old[i - r];
       tmp[i] = load_in<BF16>(a.k, vec + i);
       tmp[D + i] = load_in<BF16>(a.q, vec + i);
       if constexpr (PER_KEY) tmp[2 * D + i] = a.alpha[vec + i];
@@ -578,8 +598,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
   const int bh = __builtin_amdgcn_workgroup_id_x();  // b * H + head
   const int b = bh / a.H;
   const int head = bh - b * a.H;
-  const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
-  const UnitPtr up = unit_ptr<D, FMT_F32>(a.st, unit, 0);
+  const UnitAddr ua = unit_addr<D, FMT_F32>(a.st, a.slot_idx[b], head, a.H);
+  const UnitPtr up = unit_ptr<D, FMT_F32>(ua, 0);
 
   // (1) issue every state load of this lane first, so the whole block is in flight
   float S[RPL][CPL];
@@ -589,7 +609,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
                         reinterpret_cast<uint32_t*>(S[t]));
 
   // (2) per-row scalars and v
-  stage_rows<D, G::NT, PER_KEY, BF16, false>(a, unit, bh, head, 0, tid, srow, sv, &redu[0][0]);
+  stage_rows<D, G::NT, PER_KEY, BF16, false>(a, nullptr, bh, head, 0, tid, srow, sv, &redu[0][0]);
 
   // (3) decay, partial u = S'^T k, p = S'^T q over this lane's rows
   float pu[CPL], pp[CPL], pqk = 0.0f;
@@ -631,27 +651,35 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
 // again row step by row step to form X = S' + k delta^T, requantize and store. The second
 // decode costs about one VALU instruction per element; the registers it frees let twice as
 // many units share a CU, which is what keeps enough bytes in flight to HBM.
-template <int D, int PER_KEY, int BF16, int PLAN, int WAVES, int NF = 0>
-__global__ __launch_bounds__(64 * WAVES) void step_kernel_q(const StepArgs a) {
+// LDS of the quantized step.
+template <int D, int NW>
+struct StepSmem {
+  float4 srow[D];
+  float sv[D];               // v, then delta
+  float redu[4 * NW][D];
+  float redp[4 * NW][D];
+  float redqk[NW];
+  float ssc[D];              // new INT8 row scales, storage order
+};
+
+// The step for one unit (ua) of workgroup bh = b * H + head. PLAN_FIXED: r = NF * RPS.
+template <int D, int PER_KEY, int BF16, int PLAN, int WAVES, int NF>
+__device__ __forceinline__ void step_q_unit(const StepArgs& a, const UnitAddr& ua, int bh, int head,
+                                            StepSmem<D, Geo<D, WAVES>::NW>& sm) {
   using G = Geo<D, WAVES>;
   constexpr int T16 = PLAN == PLAN_FIXED ? NF : G::T16;
-  constexpr int CPL = G::CPL, RPL = G::RPL, NW = G::NW, RW = Words<CPL * 2>::W;
-  __shared__ float4 srow[D];
-  __shared__ float sv[D];     // v, then delta
-  __shared__ float redu[4 * NW][D], redp[4 * NW][D], redqk[NW];
-  __shared__ float ssc[D];    // new INT8 row scales, storage order
+  constexpr int CPL = G::CPL, RPL = G::RPL, RW = Words<CPL * 2>::W;
+  float4* srow = sm.srow;
+  float* sv = sm.sv;
+  float* ssc = sm.ssc;
 
   const int tid = __builtin_amdgcn_workitem_id_x();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, rs = lane >> 4, cg = lane & 15;
-  const int bh = __builtin_amdgcn_workgroup_id_x();  // b * H + head
-  const int b = bh / a.H;
-  const int head = bh - b * a.H;
-  const int64_t unit = int64_t(a.slot_idx[b]) * a.H + head;
-  const int r = PLAN == PLAN_FIXED ? NF * G::RPS : a.st.r;
+  const int r = PLAN == PLAN_FIXED ? NF * G::RPS : ua.r;
   // one buffer resource over a contiguous block unless a row step mixes kinds
-  const UnitPtr up = (PLAN != PLAN_ANY && a.st.contiguous) ? unit_ptr<D, FMT_Q, true>(a.st, unit, r)
-                                                           : unit_ptr<D, FMT_Q>(a.st, unit, r);
+  const UnitPtr up = (PLAN != PLAN_ANY && a.st.contiguous) ? unit_ptr<D, FMT_Q, true>(ua, r)
+                                                           : unit_ptr<D, FMT_Q>(ua, r);
 
   // (1) issue every state load of this lane first, so the whole block is in flight
   uint32_t raw[RPL][RW];
@@ -664,7 +692,8 @@ __global__ __launch_bounds__(64 * WAVES) void step_kernel_q(const StepArgs a) {
   }
 
   // (2) per-row scalars and v
-  stage_rows<D, G::NT, PER_KEY, BF16, true>(a, unit, bh, head, r, tid, srow, sv, &redu[0][0]);
+  stage_rows<D, G::NT, PER_KEY, BF16, true>(a, reinterpret_cast<const float*>(ua.s), bh, head, r, tid,
+                                            srow, sv, &sm.redu[0][0]);
 
   // (3) pass 1: u_j += (k_i m_i) c_ij, p_j += (q_i m_i) c_ij over the lane's rows. The lane's
   // rows are my_rows[t * RPS]: one LDS base address with immediate offsets per row step.
@@ -689,8 +718,8 @@ __global__ __launch_bounds__(64 * WAVES) void step_kernel_q(const StepArgs a) {
   }
 
   // (4) column reductions, delta and the readout y = p + (q.k) delta (one thread per column)
-  finish_columns<D, G>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + int64_t(bh) * D,
-                       tid, w, rs, lane, cg);
+  finish_columns<D, G>(sm.redu, sm.redp, sm.redqk, sv, pu, pp, pqk, a.beta[bh],
+                       a.out + int64_t(bh) * D, tid, w, rs, lane, cg);
   float dl[CPL];
   load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));
 
@@ -718,6 +747,39 @@ __global__ __launch_bounds__(64 * WAVES) void step_kernel_q(const StepArgs a) {
   flush_scales<D, G::NT>(up, ssc, r, tid);
 }
 
+template <int D, int PER_KEY, int BF16, int PLAN, int WAVES, int NF = 0>
+__global__ __launch_bounds__(64 * WAVES) void step_kernel_q(const StepArgs a) {
+  __shared__ StepSmem<D, Geo<D, WAVES>::NW> sm;
+  const int bh = __builtin_amdgcn_workgroup_id_x();  // b * H + head
+  const int b = bh / a.H;
+  const int head = bh - b * a.H;
+  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, a.slot_idx[b], head, a.H);
+  step_q_unit<D, PER_KEY, BF16, PLAN, WAVES, NF>(a, ua, bh, head, sm);
+}
+
+// Per-head DAMP layout whose every r is a multiple of the row step and at most T16 row steps:
+// the row kinds are fixed at compile time per r, chosen by a wave-uniform branch on the head's r.
+template <int D, int PER_KEY, int BF16, int WAVES, int NF>
+__device__ __forceinline__ void step_q_heads_case(const StepArgs& a, const UnitAddr& ua, int bh,
+                                                  int head, StepSmem<D, Geo<D, WAVES>::NW>& sm) {
+  if constexpr (NF >= 0) {
+    if (ua.r == NF * Geo<D, WAVES>::RPS)
+      step_q_unit<D, PER_KEY, BF16, PLAN_FIXED, WAVES, NF>(a, ua, bh, head, sm);
+    else
+      step_q_heads_case<D, PER_KEY, BF16, WAVES, NF - 1>(a, ua, bh, head, sm);
+  }
+}
+
+template <int D, int PER_KEY, int BF16, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void step_kernel_q_heads(const StepArgs a) {
+  __shared__ StepSmem<D, Geo<D, WAVES>::NW> sm;
+  const int bh = __builtin_amdgcn_workgroup_id_x();
+  const int b = bh / a.H;
+  const int head = bh - b * a.H;
+  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, a.slot_idx[b], head, a.H);
+  step_q_heads_case<D, PER_KEY, BF16, WAVES, Geo<D, WAVES>::T16>(a, ua, bh, head, sm);
+}
+
 // ---- pack: fp32 states (original key order) -> quantized format (exact rule) -------------
 template <int D, int PLAN>
 __global__ __launch_bounds__(Geo<D>::NT) void quantize_kernel(const PackArgs a) {
@@ -729,9 +791,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void quantize_kernel(const PackArgs a) 
   const int ih = __builtin_amdgcn_workgroup_id_x();  // i * H + head
   const int i = ih / a.H;
   const int head = ih - i * a.H;
-  const int64_t unit = int64_t(a.slot_idx[i]) * a.H + head;
-  const int r = a.st.r;
-  const UnitPtr up = unit_ptr<D, FMT_Q>(a.st, unit, r);
+  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, a.slot_idx[i], head, a.H);
+  const int r = ua.r;
+  const UnitPtr up = unit_ptr<D, FMT_Q>(ua, r);
 #pragma unroll
   for (int t = 0; t < G::RPL; ++t) {
     const int p0 = t * G::RPS + w * 4, p = p0 + rs;
@@ -758,14 +820,14 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequantize_kernel(const PackArgs a
   const int ih = __builtin_amdgcn_workgroup_id_x();
   const int i = ih / a.H;
   const int head = ih - i * a.H;
-  const int64_t unit = int64_t(a.slot_idx[i]) * a.H + head;
-  const int r = a.st.r;
-  const UnitPtr up = unit_ptr<D, FMT_Q>(a.st, unit, r);
+  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, a.slot_idx[i], head, a.H);
+  const int r = ua.r;
+  const UnitPtr up = unit_ptr<D, FMT_Q>(ua, r);
 #pragma unroll
   for (int t = 0; t < G::RPL; ++t) {
     const int p0 = t * G::RPS + w * 4, p = p0 + rs;
     const int src = a.st.rowmap ? a.st.rowmap[head * D + p] : p;
-    const float sc = p < r ? 1.0f : reinterpret_cast<const float*>(a.st.sbase + unit * a.st.sstride)[p - r];
+    const float sc = p < r ? 1.0f : reinterpret_cast<const float*>(ua.s)[p - r];
     float x[CPL];
     by_plan<PLAN>(t, p0, r, [&]<int K>() __attribute__((always_inline)) {
       uint32_t raw[Words<CPL * 2>::W];
@@ -809,6 +871,15 @@ template <int D, int PER_KEY, int BF16>
 void launch_step_q(const StepArgs& a, dim3 grid, hipStream_t s) {
   using GS = Geo<D, kWaves<D>>;
   using G = Geo<D>;
+  if (a.st.heads) {
+    // per-head r: every r a multiple of the row step and <= T16 row steps -> compile-time row
+    // kinds with a branch on the head's r; otherwise the general instance
+    if (a.st.heads_r_or % GS::RPS == 0 && a.st.heads_r_max <= GS::T16 * GS::RPS)
+      hipLaunchKernelGGL((step_kernel_q_heads<D, PER_KEY, BF16, kWaves<D>>), grid, dim3(GS::NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((step_kernel_q<D, PER_KEY, BF16, PLAN_ANY, G::NW>), grid, dim3(G::NT), 0, s, a);
+    return;
+  }
   const int r = a.st.r;
   if (r % GS::RPS == 0 && r <= GS::T16 * GS::RPS &&
       launch_step_fixed<D, PER_KEY, BF16, GS::T16>(r / GS::RPS, a, grid, s))
@@ -841,7 +912,7 @@ hipError_t step_d(int fmt, int per_key, int bf16, const StepArgs& a, hipStream_t
 template <int D>
 hipError_t quant_d(const PackArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.n) * unsigned(a.H)), block(Geo<D>::NT);
-  if (a.st.r % 4 == 0)
+  if ((a.st.heads ? a.st.heads_r_or : a.st.r) % 4 == 0)
     hipLaunchKernelGGL((quantize_kernel<D, PLAN_R4>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((quantize_kernel<D, PLAN_ANY>), grid, block, 0, s, a);
@@ -851,7 +922,7 @@ hipError_t quant_d(const PackArgs& a, hipStream_t s) {
 template <int D>
 hipError_t dequant_d(const PackArgs& a, hipStream_t s) {
   const dim3 grid(unsigned(a.n) * unsigned(a.H)), block(Geo<D>::NT);
-  if (a.st.r % 4 == 0)
+  if ((a.st.heads ? a.st.heads_r_or : a.st.r) % 4 == 0)
     hipLaunchKernelGGL((dequantize_kernel<D, PLAN_R4>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((dequantize_kernel<D, PLAN_ANY>), grid, block, 0, s, a);

@@ -31,7 +31,9 @@ EXPORTS = (
     "damp_block_bytes", "damp_block_data_bytes", "damp_state_bytes", "damp_state_alloc",
     "damp_state_free", "damp_state_layout", "damp_state_quantize", "damp_state_dequantize",
     "damp_decode_step", "fp32_decode_step", "uniform_int8_decode_step", "uniform_int8_quantize",
-    "damp_last_error", "damp_abi_version",
+    "damp_last_error", "damp_abi_version", "damp_state_bytes_per_head",
+    "damp_state_alloc_per_head", "damp_state_head_info", "damp_risk_scores", "damp_budget_rows",
+    "damp_allocate_rows",
 )
 
 
@@ -79,6 +81,12 @@ def load() -> ctypes.CDLL:
         "uniform_int8_quantize": ([P, P, I32, I32, I32, I32, P, P, I32, P], ctypes.c_int),
         "damp_last_error": ([], ctypes.c_char_p),
         "damp_abi_version": ([], I32),
+        "damp_state_bytes_per_head": ([LP, P], SZ),
+        "damp_state_alloc_per_head": ([LP, P, P, P, SZ, ctypes.POINTER(P)], ctypes.c_int),
+        "damp_state_head_info": ([P, P, P, P], ctypes.c_int),
+        "damp_risk_scores": ([P, I32, I32, I32, P, P, P, P], ctypes.c_int),
+        "damp_budget_rows": ([I32, I32, ctypes.c_double, I32, I32], ctypes.c_int64),
+        "damp_allocate_rows": ([P, I32, I32, ctypes.c_int64, I32, I32, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -177,23 +185,38 @@ def _step_vectors(slot_idx, q, k, v, alpha, beta, out, H, d):
 class DampState:
     """A DAMP state pool bound to its frozen per-head FP16 row map.
 
-    ``pool`` (uint8 device tensor of ``state_bytes`` bytes) is allocated here unless given.
-    ``fp16_rows`` is an int array [num_heads, r] of ascending key rows per head."""
+    ``pool`` (uint8 device tensor of ``nbytes`` bytes) is allocated here unless given.
+    Uniform layout: ``fp16_rows`` is an int array [num_heads, r] of ascending key rows per head.
+    Per-head layout (``r_per_head`` given): ``fp16_rows`` is the int row map [num_heads, d] of
+    ``allocate_rows`` (each head's r_h FP16 rows ascending, then its other rows ascending)."""
 
     def __init__(self, num_slots: int, num_heads: int, d: int, fp16_rows, pool=None,
-                 device=None):
+                 device=None, r_per_head=None):
         torch = _torch()
-        rows = np.ascontiguousarray(np.asarray(fp16_rows, dtype=np.int32).reshape(num_heads, -1))
-        r = rows.shape[1]
-        self.num_slots, self.num_heads, self.d, self.r = num_slots, num_heads, d, r
+        self.num_slots, self.num_heads, self.d = num_slots, num_heads, d
+        self.per_head = r_per_head is not None
+        if self.per_head:
+            rh = np.ascontiguousarray(np.asarray(r_per_head, dtype=np.int32).reshape(num_heads))
+            rows = np.ascontiguousarray(np.asarray(fp16_rows, dtype=np.int32).reshape(num_heads, d))
+            self.r = None
+            self.r_per_head = rh
+            self._layout = layout(num_slots, num_heads, d, 0)
+            nbytes = load().damp_state_bytes_per_head(ctypes.byref(self._layout),
+                                                      rh.ctypes.data_as(ctypes.c_void_p))
+        else:
+            rows = np.ascontiguousarray(np.asarray(fp16_rows, dtype=np.int32).reshape(num_heads, -1))
+            r = rows.shape[1]
+            self.r = r
+            self.r_per_head = np.full(num_heads, r, np.int32)
+            self._layout = layout(num_slots, num_heads, d, r)
+            nbytes = load().damp_state_bytes(ctypes.byref(self._layout))
         self.fp16_rows = rows
-        self._layout = layout(num_slots, num_heads, d, r)
-        nbytes = load().damp_state_bytes(ctypes.byref(self._layout))
         if nbytes == 0:
             raise DampError(DAMP_ERR_INVALID_ARGUMENT, "invalid or unsupported layout")
         self.nbytes = nbytes
-        self.block_bytes = load().damp_block_bytes(ctypes.byref(self._layout))
-        self.block_data_bytes = load().damp_block_data_bytes(ctypes.byref(self._layout))
+        if not self.per_head:
+            self.block_bytes = load().damp_block_bytes(ctypes.byref(self._layout))
+            self.block_data_bytes = load().damp_block_data_bytes(ctypes.byref(self._layout))
         if pool is None:
             pool = torch.empty(nbytes, dtype=torch.uint8,
                                device=device if device is not None else "cuda")
@@ -203,10 +226,22 @@ class DampState:
         self.pool = pool
         h = ctypes.c_void_p()
         with torch.cuda.device(pool.device):
-            _check(load().damp_state_alloc(ctypes.byref(self._layout),
-                                           rows.ctypes.data_as(ctypes.c_void_p) if r else None,
-                                           _ptr(pool), pool.numel(), ctypes.byref(h)))
+            if self.per_head:
+                _check(load().damp_state_alloc_per_head(
+                    ctypes.byref(self._layout), rh.ctypes.data_as(ctypes.c_void_p),
+                    rows.ctypes.data_as(ctypes.c_void_p), _ptr(pool), pool.numel(), ctypes.byref(h)))
+            else:
+                _check(load().damp_state_alloc(ctypes.byref(self._layout),
+                                               rows.ctypes.data_as(ctypes.c_void_p) if r else None,
+                                               _ptr(pool), pool.numel(), ctypes.byref(h)))
         self._h = h
+        r_out = np.empty(num_heads, np.int32)
+        off = np.empty(num_heads, np.int64)
+        sb = ctypes.c_int64()
+        _check(load().damp_state_head_info(h, r_out.ctypes.data_as(ctypes.c_void_p),
+                                           off.ctypes.data_as(ctypes.c_void_p), ctypes.byref(sb)))
+        self.head_offsets = off
+        self.slot_bytes = sb.value
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
@@ -220,8 +255,15 @@ class DampState:
             pass
 
     def blocks(self):
-        """The pool as uint8 [num_slots, num_heads, block_bytes] (a view)."""
+        """The pool as uint8 [num_slots, num_heads, block_bytes] (a view; uniform layout)."""
+        if self.per_head:
+            raise ValueError("a per-head layout has no uniform block; use slots()")
         return self.pool[: self.nbytes].view(self.num_slots, self.num_heads, self.block_bytes)
+
+    def slots(self):
+        """The pool as uint8 [num_slots, slot_bytes] (a view); head h's block of a slot starts
+        at head_offsets[h]."""
+        return self.pool[: self.nbytes].view(self.num_slots, self.slot_bytes)
 
     def quantize(self, S, slot_idx, stream=None) -> None:
         torch = _torch()
@@ -290,3 +332,48 @@ def uniform_int8_quantize(codes, scales, S, slot_idx, stream=None) -> None:
     _need(S, "S", torch.float32, (n, H, d, d2), codes.device)
     _check(load().uniform_int8_quantize(_ptr(codes), _ptr(scales), S_, H, d, d2, _ptr(S),
                                         _ptr(slot_idx), n, _stream(stream)))
+
+
+# ------------------------------------------------------------------------------------------
+# offline calibration
+# ------------------------------------------------------------------------------------------
+def risk_scores(S, abar, row_error=None, score=None, stream=None):
+    """Per (head, key row) risk scores of calibration states ``S`` fp32 [n, H, d, d] with mean
+    gates ``abar`` fp32 [H, d]. Returns ``(score fp64 [H, d], row_error fp64 [n, H, d])``."""
+    torch = _torch()
+    if S.dim() != 4:
+        raise ValueError("S must be [n, H, d, d]")
+    n, H, d, d2 = S.shape
+    dev = S.device
+    _need(S, "S", torch.float32, (n, H, d, d2), dev)
+    _need(abar, "abar", torch.float32, (H, d), dev)
+    if row_error is None:
+        row_error = torch.empty((n, H, d), dtype=torch.float64, device=dev)
+    if score is None:
+        score = torch.empty((H, d), dtype=torch.float64, device=dev)
+    _need(row_error, "row_error", torch.float64, (n, H, d), dev)
+    _need(score, "score", torch.float64, (H, d), dev)
+    if d != d2:
+        raise ValueError("S must be square per head")
+    _check(load().damp_risk_scores(_ptr(S), n, H, d, _ptr(abar), _ptr(row_error), _ptr(score),
+                                   _stream(stream)))
+    return score, row_error
+
+
+def budget_rows(d: int, num_heads: int, bits_per_value: float, g: int = 1, r_max: int | None = None) -> int:
+    """FP16 rows per slot (all heads) that fit ``bits_per_value`` data bits per state value."""
+    return int(load().damp_budget_rows(d, num_heads, float(bits_per_value), g,
+                                       d if r_max is None else r_max))
+
+
+def allocate_rows(score, R: int, g: int = 1, r_max: int | None = None, stream=None):
+    """Allocation of ``R`` FP16 rows over the heads of ``score`` fp64 [H, d] in groups of ``g``.
+    Returns device tensors ``(r int32 [H], row_map int32 [H, d])``."""
+    torch = _torch()
+    H, d = score.shape
+    _need(score, "score", torch.float64, (H, d), score.device)
+    r = torch.empty(H, dtype=torch.int32, device=score.device)
+    m = torch.empty((H, d), dtype=torch.int32, device=score.device)
+    _check(load().damp_allocate_rows(_ptr(score), H, d, R, g, d if r_max is None else r_max,
+                                     _ptr(r), _ptr(m), _stream(stream)))
+    return r, m

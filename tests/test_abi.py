@@ -141,3 +141,97 @@ def test_step_entry_points_reject_bad_arguments_on_host():
     assert L.damp_state_free(None) == lib.DAMP_OK
     assert L.uniform_int8_quantize(fp, fp, 4, 2, 16, 16, ok, ok, -2, None) == \
         lib.DAMP_ERR_INVALID_ARGUMENT
+
+
+# ---- per-head layout and calibration entry points (host logic only) -------------------------
+def _vp(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def test_per_head_bytes():
+    L = lib.load()
+    lay = lib.layout(5, 32, 128, 0)
+    # every head at r = 24 is the uniform layout
+    r = np.full(32, 24, np.int32)
+    assert L.damp_state_bytes_per_head(ctypes.byref(lay), _vp(r)) == lib.state_bytes(5, 32, 128, 24)
+    # mixed r: each head's block rounds up to 256 bytes on its own
+    r = np.array([0, 8, 24, 32, 128] + [16] * 27, np.int32)
+    blk = lambda x: (2 * x * 128 + (128 - x) * 128 + 4 * (128 - x) + 255) // 256 * 256
+    assert L.damp_state_bytes_per_head(ctypes.byref(lay), _vp(r)) == 5 * sum(blk(int(x)) for x in r)
+    # invalid r
+    r[3] = 129
+    assert L.damp_state_bytes_per_head(ctypes.byref(lay), _vp(r)) == 0
+    assert L.damp_state_bytes_per_head(ctypes.byref(lay), None) == 0
+
+
+def test_alloc_per_head_rejects_bad_arguments_on_host():
+    L = lib.load()
+    H, d = 2, 16
+    lay = lib.layout(4, H, d, 0)
+    r = np.array([2, 0], np.int32)
+    good = np.array([[3, 9] + [i for i in range(d) if i not in (3, 9)], list(range(d))], np.int32)
+    need = L.damp_state_bytes_per_head(ctypes.byref(lay), _vp(r))
+    fake_pool = 0x100000
+
+    def alloc(lay_, r_, m_, pool, nbytes):
+        h = ctypes.c_void_p()
+        st = L.damp_state_alloc_per_head(ctypes.byref(lay_) if lay_ is not None else None, _vp(r_),
+                                         _vp(m_), pool, nbytes, ctypes.byref(h))
+        return st, h
+
+    bad_order = good.copy()
+    bad_order[0, :2] = [9, 3]
+    dup = good.copy()
+    dup[1, 5] = 4
+    out_of_range = good.copy()
+    out_of_range[1, 0] = 16
+    cases = [
+        (lay, np.array([2, 17], np.int32), good, fake_pool, need, "r_per_head[1]"),
+        (lay, None, good, fake_pool, need, "r_per_head is NULL"),
+        (lay, r, None, fake_pool, need, "row_map is NULL"),
+        (lay, r, good, None, need, "pool is NULL"),
+        (lay, r, good, fake_pool + 64, need, "aligned"),
+        (lay, r, good, fake_pool, need - 1, "needed"),
+        (lay, r, bad_order, fake_pool, need, "ascending"),
+        (lay, r, dup, fake_pool, need, "repeats"),
+        (lay, r, out_of_range, fake_pool, need, "outside"),
+    ]
+    for lay_, r_, m_, pool, nbytes, msg in cases:
+        st, h = alloc(lay_, r_, m_, pool, nbytes)
+        assert st == lib.DAMP_ERR_INVALID_ARGUMENT, (msg, st, lib.last_error())
+        assert msg in lib.last_error(), (msg, lib.last_error())
+        assert not h.value
+    st, _ = alloc(lib.layout(4, H, 48, 0), np.zeros(H, np.int32), good, fake_pool, need)
+    assert st == lib.DAMP_ERR_UNSUPPORTED
+
+
+def test_budget_rows_matches_the_oracle():
+    import oracle
+    for d in (16, 32, 64, 128):
+        for H in (1, 3, 32):
+            for bits in (8.0, 8.25, 8.3, 9.0, 9.703125, 9.9, 10.5, 12.0, 16.0, 17.0):
+                for g in (1, 4, 8):
+                    for r_max in (0, d // 4, d):
+                        assert lib.budget_rows(d, H, bits, g, r_max) == oracle.budget_rows(d, H, bits, g, r_max)
+    assert lib.budget_rows(128, 32, 9.9) == 872
+    assert lib.budget_rows(4, 32, 9.9) == -1       # d <= 4
+    assert lib.budget_rows(128, 32, 9.9, g=0) == -1
+
+
+def test_calibration_entry_points_reject_bad_arguments_on_host():
+    L = lib.load()
+    p = ctypes.c_void_p(0x100000)
+    E = lib.DAMP_ERR_INVALID_ARGUMENT
+    assert L.damp_risk_scores(p, 0, 2, 16, p, p, p, None) == E
+    assert L.damp_risk_scores(p, 2, 2, 48, p, p, p, None) == lib.DAMP_ERR_UNSUPPORTED
+    assert L.damp_risk_scores(None, 2, 2, 16, p, p, p, None) == E
+    assert L.damp_risk_scores(ctypes.c_void_p(0x100004), 2, 2, 16, p, p, p, None) == E
+    assert L.damp_allocate_rows(p, 2, 16, 6, 4, 16, p, p, None) == E        # R % g
+    assert "multiple" in lib.last_error()
+    assert L.damp_allocate_rows(p, 2, 16, 8, 0, 16, p, p, None) == E        # g
+    assert L.damp_allocate_rows(p, 2, 16, 8, 1, 17, p, p, None) == E        # r_max
+    assert L.damp_allocate_rows(p, 2, 256, 8, 1, 16, p, p, None) == lib.DAMP_ERR_UNSUPPORTED
+    assert L.damp_allocate_rows(p, 128, 128, 8, 1, 128, p, p, None) == lib.DAMP_ERR_UNSUPPORTED
+    assert L.damp_allocate_rows(p, 64, 128, 8, 1, 128, p, p, None) == lib.DAMP_ERR_UNSUPPORTED
+    assert "groups" in lib.last_error()
+    assert L.damp_allocate_rows(None, 2, 16, 8, 1, 16, p, p, None) == E
