@@ -84,6 +84,12 @@ def parse():
                    help="time only this format (for profiling)")
     p.add_argument("--workload", choices=["pool4096", "gdn64", "kda256", "drift"],
                    default="pool4096")
+    p.add_argument("--budget-bits", type=float, default=None, metavar="BITS",
+                   help="DAMP with per-head FP16 rows: calibrate on the device (risk scores and "
+                        "allocation) and spend BITS data bits per state value (the pages: 9.9)")
+    p.add_argument("--budget-group", type=int, default=8,
+                   help="FP16 rows are handed out per head in groups of this many")
+    p.add_argument("--budget-rmax", type=int, default=32, help="at most this many FP16 rows per head")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the step, run a plain device copy of MIB MiB --steps times "
                         "(the reference kernel of known size for HBM byte counters)")
@@ -162,6 +168,29 @@ def cpu_baseline(seconds: float):
                       f"slots of the pool workload) in {el:.1f} s"}
 
 
+def calibrate_budget(torch, lib, synth, dev, H, d, per_key, args):
+    """Per-head FP16 rows for the budget: risk scores of the synthetic calibration states and
+    the allocation, both on the device (each timed over 5 launches after one untimed)."""
+    S_cal, abar = synth.budget_calibration(H, d, per_key=per_key)
+    S_dev = torch.from_numpy(S_cal).to(dev)
+    a_dev = torch.from_numpy(abar).to(dev)
+    score, row_err = lib.risk_scores(S_dev, a_dev)
+    t_score = time_launches(torch, lambda i: lib.risk_scores(S_dev, a_dev, row_err, score), 5, 1)
+    g, r_max = args.budget_group, args.budget_rmax
+    R = lib.budget_rows(d, H, args.budget_bits, g, r_max)
+    if R < 0:
+        raise SystemExit(f"--budget-bits {args.budget_bits}: below the all-INT8 layout")
+    t_alloc = time_launches(torch, lambda i: lib.allocate_rows(score, R, g, r_max), 5, 1)
+    r_dev, m_dev = lib.allocate_rows(score, R, g, r_max)
+    r_h = r_dev.cpu().numpy()
+    data = sum(2 * int(x) * d + (d - int(x)) * d + 4 * (d - int(x)) for x in r_h)
+    return {"kind": "per-head FP16 rows under a storage budget", "bits_per_value": args.budget_bits,
+            "data_bits_per_value": 8.0 * data / (H * d * d), "fp16_rows_total": R, "group": g,
+            "r_max": r_max, "r_per_head": r_h.tolist(), "row_map": m_dev.cpu().numpy(),
+            "calibration_states": int(S_cal.shape[0]), "risk_scores_ms": t_score,
+            "allocate_ms": t_alloc}
+
+
 WORKLOADS = ("pool4096", "gdn64", "kda256", "drift")
 COLD_BYTES = 1 << 30  # rotate copies until this much state lies between two uses of one copy
 
@@ -217,9 +246,23 @@ def main():
     out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
     R = len(slot_sets)
     results = {}
+    budget = None
+    if args.budget_bits is not None:
+        budget = calibrate_budget(torch, lib, synth, dev, H, d, per_key, args)
+        desc = desc.replace(f"{r} FP16 rows/head", f"per-head FP16 rows at {args.budget_bits} bits/value")
+        print(f"# budget {args.budget_bits} bits: R = {budget['fp16_rows_total']}, r per head "
+              f"{budget['r_per_head']}; risk scores {budget['risk_scores_ms']:.3f} ms, allocation "
+              f"{budget['allocate_ms']:.3f} ms", file=sys.stderr, flush=True)
 
     def run(fmt):
-        if fmt == "damp":
+        if fmt == "damp" and budget is not None:
+            st = lib.DampState(pool_slots, H, d, budget["row_map"], device=dev,
+                               r_per_head=budget["r_per_head"])
+            st.pool.zero_()
+            fill_states(torch, st.quantize, all_slots, H, d, dev)
+            launch = lambda i: st.decode_step(slot_sets[i % R], *sets[i % 4], out)
+            keep = st
+        elif fmt == "damp":
             st = lib.DampState(pool_slots, H, d, rows, device=dev)
             st.pool.zero_()
             fill_states(torch, st.quantize, all_slots, H, d, dev)
@@ -241,7 +284,10 @@ def main():
         ms = time_launches(torch, launch, args.steps, args.warmup)
         del keep
         torch.cuda.empty_cache()
-        ab = alg_bytes_per_update(fmt, d, r, per_key) * units
+        if fmt == "damp" and budget is not None:
+            ab = sum(alg_bytes_per_update(fmt, d, int(rh), per_key) for rh in budget["r_per_head"]) * B
+        else:
+            ab = alg_bytes_per_update(fmt, d, r, per_key) * units
         return {"ms_per_step": ms, "updates_per_s": units / (ms * 1e-3),
                 "alg_bytes_per_launch": ab, "gbs": ab / (ms * 1e-3) / 1e9}
 
@@ -268,13 +314,16 @@ def main():
         "data": "synthetic: seeded N(0, 0.1) states, unit-norm bf16 q/k, N(0,1) bf16 v, "
                 "sigmoid gates; no model weights",
         "config": {"workload": desc, "format": main_fmt, "slots_active": B, "heads": H, "d": d,
-                   "fp16_rows": r, "global_batch": B, "seq_len": 1,
+                   "fp16_rows": r if budget is None else "per head", "global_batch": B, "seq_len": 1,
                    "state_cache": "cold (HBM)" if (cold or args.workload == "pool4096") else "warm (Infinity Cache)",
                    "pool_copies": R},
         "roofline": {"bound": "hbm", "achieved": m["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": m["gbs"] / PEAK_HBM_GBS,
-                     "traffic": measured_traffic() if (main_fmt == "damp" and args.workload == "pool4096") else None},
+                     "traffic": measured_traffic() if (main_fmt == "damp" and args.workload == "pool4096"
+                                                       and budget is None) else None},
     }
+    if budget is not None:
+        line["config"]["layout"] = {k: v for k, v in budget.items() if k != "row_map"}
     if "fp32" in results and "damp" in results:
         line["baselines"] = {f: {"ms_per_step": v["ms_per_step"], "updates_per_s": v["updates_per_s"],
                                  "gbs": v["gbs"], "frac": v["gbs"] / PEAK_HBM_GBS}

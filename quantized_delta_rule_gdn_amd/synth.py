@@ -245,3 +245,26 @@ def pool4096_step(which: int = 0) -> StepInputs:
     w = POOL4096
     return step_inputs(np.random.default_rng([w.seed, 3, which]), w.batch, w.heads, w.d,
                        GDN, "bf16")
+
+
+# ---- budgeted selection: calibration data standing in for fp32 warm-up traces ----------------
+BUDGET_SEED = 1005
+BUDGET_CAL_STATES = 64
+
+
+def budget_calibration(H: int = 32, D: int = 128, n: int = BUDGET_CAL_STATES, seed: int = BUDGET_SEED,
+                       per_key: bool = False):
+    """Calibration states and mean gates with the structure the DAMP pages report: a few key
+    rows with large magnitude per head (the quantization-error energy concentrates there) and
+    decay rates that differ between heads (GDN) or key channels (KDA) but not between states.
+    States: N(0, 0.1), 4 random key rows per head times 10**U(0, 1.3). Mean gates:
+    sigmoid(-c) with c ~ N(0, 1) per head (GDN, repeated over the head's rows) or per key
+    channel (KDA). Returns (S float32 [n, H, D, D], abar float32 [H, D])."""
+    rng = np.random.default_rng(seed)
+    S = normal_states(rng, (n, H, D, D), 0.1)
+    for h in range(H):
+        rows = rng.choice(D, 4, replace=False)
+        S[:, h, rows, :] *= (10.0 ** rng.uniform(0.0, 1.3, (4, 1))).astype(np.float32)
+    c = rng.standard_normal((H, D) if per_key else (H, 1))
+    abar = np.broadcast_to(_sigmoid_f32(-c), (H, D)).astype(np.float32)
+    return S, np.ascontiguousarray(abar)

@@ -165,3 +165,27 @@ def test_per_head_pack_unpack_bit_exact(r_per_head):
     assert np.array_equal(got[2], s.reshape(n, H, D))
     ref_back = oracle.dequantize(maskn, h, c, s).reshape(n, H, D, D)
     assert np.array_equal(back.cpu().numpy(), ref_back)
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_budget_workload_full_heads(per_key):
+    """The benchmark's calibration data (32 heads x 128 rows, 64 states) at 9.9 bits, groups of
+    8, at most 32 rows per head; then the step on 64 slots of that layout against the oracle."""
+    H, D, B = 32, 128, 64
+    Sc, abar = synth.budget_calibration(H, D, per_key=per_key)
+    score, _ = lib.risk_scores(to_dev(Sc), to_dev(abar))
+    R = lib.budget_rows(D, H, 9.9, 8, 32)
+    assert R == 872 // 8 * 8
+    r_dev, m_dev = lib.allocate_rows(score, R, 8, 32)
+    r_per_head, row_map = r_dev.cpu().numpy(), m_dev.cpu().numpy()
+    ref_score = oracle.risk_scores(Sc, abar)
+    assert np.array_equal(score.cpu().numpy(), ref_score)
+    rr, mr = oracle.allocate_rows(ref_score, R, 8, 32)
+    assert np.array_equal(r_per_head, rr) and np.array_equal(row_map, mr)
+    assert int(r_per_head.sum()) == R and len(set(r_per_head.tolist())) > 1
+    _log(f"budget workload per_key={per_key}: r per head {r_per_head.tolist()}")
+    decay = synth.KDA if per_key else synth.GDN
+    S, inp, mask, maskn, h, c, s = _per_head_case(11 + per_key, B, H, D, r_per_head, row_map, decay, "bf16")
+    _, stats = _run_per_head(r_per_head, row_map, S, inp, mask, maskn, h, c, s, B + 5,
+                             np.random.default_rng(3).choice(B + 5, B, replace=False))
+    _log(str(stats))
