@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_budget_rows.restype = Lg
         L.oracle_allocate_rows.argtypes = [I, I, P, Lg, I, I, P, P]
         L.oracle_allocate_rows.restype = I
+        L.oracle_prestep.argtypes = [I, Lg, P, P, P, I, P, P, P, P, P]
+        L.oracle_prestep.restype = I
         _lib = L
     return _lib
 
@@ -218,3 +220,21 @@ def allocate_rows(score, R: int, g: int = 1, r_max: int | None = None):
     rc = lib().oracle_allocate_rows(D, H, _p(score), R, g, D if r_max is None else r_max, _p(r), _p(m))
     assert rc == 0
     return r, m
+
+
+def prestep(q, k, g, b):
+    """Pre-step of the layer inputs: ``q, k [n, D]`` (any float), gate logits ``g`` [n] or
+    [n, D], beta logits ``b`` [n]. Returns fp32 ``(q_hat, k_hat, alpha, beta)``."""
+    q = _c(q, np.float32)
+    n, D = q.shape
+    k = _c(k, np.float32).reshape(n, D)
+    g = _c(g, np.float32)
+    per_key = 1 if g.size == n * D and D != 1 else 0
+    g = g.reshape(n, D) if per_key else g.reshape(n)
+    b = _c(b, np.float32).reshape(n)
+    qo, ko = np.empty((n, D), np.float32), np.empty((n, D), np.float32)
+    ao = np.empty(g.shape, np.float32)
+    bo = np.empty(n, np.float32)
+    rc = lib().oracle_prestep(D, n, _p(q), _p(k), _p(g), per_key, _p(b), _p(qo), _p(ko), _p(ao), _p(bo))
+    assert rc == 0
+    return qo, ko, ao, bo

@@ -407,3 +407,34 @@ int oracle_allocate_rows(int D, int H, const double* score, long R, int g, int r
   free(rank); free(gain); free(taken);
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Pre-step (the inputs of the decode step as a GDN / KDA layer produces them). The step's q and
+ * k are unit vectors and its gates come from logits: q_hat = q / ||q||_2, k_hat = k / ||k||_2,
+ * alpha = exp(-softplus(g)) = 1 / (1 + e^g), beta = 1 / (1 + e^-b). A zero vector stays zero
+ * (no division by zero). Each value is computed in binary64 and rounded once to binary32, the
+ * precision the step takes its inputs in.
+ *   q, k [n][D]; g [n] (per_key = 0) or [n][D] (per_key = 1); b [n]; outputs of the same shapes.
+ * ---------------------------------------------------------------------------------------- */
+static double logistic(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+int oracle_prestep(int D, long n, const float* q, const float* k, const float* g, int per_key,
+                   const float* b, float* q_out, float* k_out, float* alpha_out,
+                   float* beta_out) {
+  if (D <= 0 || n < 0 || !q || !k || !g || !b || !q_out || !k_out || !alpha_out || !beta_out)
+    return -1;
+  for (long u = 0; u < n; ++u) {
+    const float* vin[2] = {q + u * D, k + u * D};
+    float* vout[2] = {q_out + u * D, k_out + u * D};
+    for (int t = 0; t < 2; ++t) {
+      double ss = 0.0;
+      for (int i = 0; i < D; ++i) ss += (double)vin[t][i] * (double)vin[t][i];
+      const double nrm = sqrt(ss);
+      for (int i = 0; i < D; ++i) vout[t][i] = nrm > 0.0 ? (float)((double)vin[t][i] / nrm) : 0.0f;
+    }
+    const long ng = per_key ? D : 1;
+    for (long i = 0; i < ng; ++i) alpha_out[u * ng + i] = (float)logistic(-(double)g[u * ng + i]);
+    beta_out[u] = (float)logistic((double)b[u]);
+  }
+  return 0;
+}

@@ -86,6 +86,13 @@ long oracle_budget_rows(int D, int H, double bits_per_value, int g, int r_max);
 int oracle_allocate_rows(int D, int H, const double* score, long R, int g, int r_max,
                          int32_t* r_out, int32_t* map_out);
 
+/* Pre-step: q_hat = q/||q||, k_hat = k/||k|| (zero stays zero), alpha = exp(-softplus(g)),
+ * beta = sigmoid(b); binary64, rounded once to binary32. q, k [n][D]; g [n] or [n][D]
+ * (per_key); b [n]. Returns 0 or -1. */
+int oracle_prestep(int D, long n, const float* q, const float* k, const float* g, int per_key,
+                   const float* b, float* q_out, float* k_out, float* alpha_out,
+                   float* beta_out);
+
 #ifdef __cplusplus
 }
 #endif
