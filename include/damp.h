@@ -159,6 +159,22 @@ damp_status damp_decode_step(damp_state* state, const int32_t* slot_idx, int32_t
                              const float* alpha, damp_decay decay, const float* beta,
                              float* out, void* stream);
 
+/* damp_decode_step with the pre-step fused into it: the arguments are what a GDN / KDA layer's
+ * projections give, and the kernel forms the step's inputs while it stages them:
+ *   q, k        unnormalised; the step uses q / ||q||_2 and k / ||k||_2 over the d_k entries of
+ *               each (b, head) (a zero vector stays zero), the norms summed in fp32
+ *   gate_logit  g, same shapes as alpha; the step uses alpha = exp(-softplus(g)) = 1 / (1 + e^g)
+ *   beta_logit  b, [B][num_heads]; the step uses beta = 1 / (1 + e^-b)
+ * Everything else as damp_decode_step. It saves the separate launches (and HBM round trips of
+ * q, k and the gates) that would form these inputs before the step. The [C2] step takes unit
+ * q_t, k_t and gates in (0, 1); how a layer makes them is the library's reading: L2
+ * normalisation and the gate activations named here, no 1/sqrt(d) query scale. */
+damp_status damp_decode_step_fused(damp_state* state, const int32_t* slot_idx, int32_t B,
+                                   const void* q, const void* k, const void* v,
+                                   damp_dtype qkv_dtype, const float* gate_logit,
+                                   damp_decay decay, const float* beta_logit, float* out,
+                                   void* stream);
+
 /* The same step on an FP32 state pool (the reference format of the DAMP speedups):
  *   pool dev fp32 [num_slots][num_heads][d_k][d_v], 16-byte aligned. Other arguments as in
  *   damp_decode_step. No requantization: X is stored as fp32. */

@@ -231,7 +231,7 @@ damp::StateRef int8_ref(int8_t* codes, float* scales, int32_t d) {
 damp_status run_step(int fmt, const damp::StateRef& ref, int32_t d, int32_t H, int32_t num_slots,
                      const int32_t* slot_idx, int32_t B, const void* q, const void* k,
                      const void* v, damp_dtype dt, const float* alpha, damp_decay decay,
-                     const float* beta, float* out, void* stream) {
+                     const float* beta, float* out, void* stream, int prestep = 0) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   damp_status st = debug_check_slots(slot_idx, B, num_slots, s);
   if (st != DAMP_OK) return st;
@@ -246,6 +246,7 @@ damp_status run_step(int fmt, const damp::StateRef& ref, int32_t d, int32_t H, i
   a.alpha = alpha;
   a.beta = beta;
   a.out = out;
+  a.prestep = prestep;
   return launched(damp::launch_step(fmt, d, decay == DAMP_DECAY_PER_KEY, dt == DAMP_BF16, a, s),
                   "decode step");
 }
@@ -473,6 +474,20 @@ damp_status damp_decode_step(damp_state* s, const int32_t* slot_idx, int32_t B, 
   if (B == 0) return ok();
   return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, B, q, k, v,
                   dt, alpha, decay, beta, out, stream);
+}
+
+damp_status damp_decode_step_fused(damp_state* s, const int32_t* slot_idx, int32_t B, const void* q,
+                                   const void* k, const void* v, damp_dtype dt,
+                                   const float* gate_logit, damp_decay decay,
+                                   const float* beta_logit, float* out, void* stream) {
+  if (!s) return fail(DAMP_ERR_INVALID_ARGUMENT, "state is NULL");
+  const damp_layout& L = s->layout;
+  damp_status st = check_step_args(B, L.num_heads, L.d_k, slot_idx, q, k, v, dt, gate_logit, decay,
+                                   beta_logit, out);
+  if (st != DAMP_OK) return st;
+  if (B == 0) return ok();
+  return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, B, q, k, v,
+                  dt, gate_logit, decay, beta_logit, out, stream, 1);
 }
 
 damp_status fp32_decode_step(float* pool, int32_t num_slots, int32_t H, int32_t d_k, int32_t d_v,

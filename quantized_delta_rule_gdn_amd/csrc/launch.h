@@ -48,6 +48,7 @@ struct StepArgs {
   const float* alpha;       // [B][H] or [B][H][d]
   const float* beta;        // [B][H]
   float* out;               // [B][H][d]
+  int32_t prestep;          // 1: q, k are normalised here and alpha, beta are logits
 };
 
 struct PackArgs {

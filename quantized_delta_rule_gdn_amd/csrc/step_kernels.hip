@@ -503,13 +503,30 @@ __device__ __forceinline__ float decode_row(const uint32_t* raw, int c, int p, i
 // others (k, q and the gate are read in key order, the row map in parallel) and the
 // permutation to storage order goes through LDS (tmp: 3 * D floats), so the staging costs one
 // memory round trip rather than a row-map load followed by dependent k / q loads.
+//
+// Fused pre-step (a.prestep != 0): q and k arrive as the layer's projections and alpha / beta as
+// logits; the step uses q / ||q||, k / ||k|| (a zero vector stays zero), alpha = exp(-softplus(g))
+// = 1 / (1 + e^g) and beta = 1 / (1 + e^-b). The squared norms are summed in fp32 (each thread's
+// elements, then a wave butterfly, then the waves in order, in tmp[3 D ..]) and applied as
+// rsqrt(||x||^2) while permuting into storage order. Returns beta (after the activation).
+__device__ __forceinline__ float gate_from_logit(float g) { return 1.0f / (1.0f + expf(g)); }
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 template <int D, int NT, int PER_KEY, int BF16, bool Q>
-__device__ __forceinline__ void stage_rows(const StepArgs& a, const float* sc_old, int bh, int head,
-                                           int r, int tid, float4* srow, float* sv, float* tmp) {
+__device__ __forceinline__ float stage_rows(const StepArgs& a, const float* sc_old, int bh, int head,
+                                            int r, int tid, float4* srow, float* sv, float* tmp) {
   const int64_t vec = int64_t(bh) * D;
   constexpr int PER = (D + NT - 1) / NT;
+  constexpr int NWS = NT / 64;
+  const bool pre = a.prestep != 0;
   int src[PER];
   float sc[PER];
+  float ssq = 0.0f, ssk = 0.0f;
 #pragma unroll
   for (int n = 0; n < PER; ++n) {
     const int i = tid + n * NT;
@@ -518,23 +535,50 @@ __device__ __forceinline__ void stage_rows(const StepArgs& a, const float* sc_ol
       sc[n] = 1.0f;
       if constexpr (Q)
         if (i >= r) sc[n] = sc_old[i - r];
-      tmp[i] = load_in<BF16>(a.k, vec + i);
-      tmp[D + i] = load_in<BF16>(a.q, vec + i);
-      if constexpr (PER_KEY) tmp[2 * D + i] = a.alpha[vec + i];
+      const float kv = load_in<BF16>(a.k, vec + i), qv = load_in<BF16>(a.q, vec + i);
+      tmp[i] = kv;
+      tmp[D + i] = qv;
+      ssk = fmaf(kv, kv, ssk);
+      ssq = fmaf(qv, qv, ssq);
+      if constexpr (PER_KEY) tmp[2 * D + i] = pre ? gate_from_logit(a.alpha[vec + i]) : a.alpha[vec + i];
       sv[i] = load_in<BF16>(a.v, vec + i);
     }
   }
-  const float g0 = PER_KEY ? 0.0f : a.alpha[bh];
+  float g0 = PER_KEY ? 0.0f : a.alpha[bh];
+  float beta = a.beta[bh];
+  if (pre) {
+    if constexpr (!PER_KEY) g0 = gate_from_logit(g0);
+    beta = 1.0f / (1.0f + expf(-beta));
+    ssq = wave_sum(ssq);
+    ssk = wave_sum(ssk);
+    if ((tid & 63) == 0) {
+      tmp[3 * D + 2 * (tid >> 6)] = ssq;
+      tmp[3 * D + 2 * (tid >> 6) + 1] = ssk;
+    }
+  }
   __syncthreads();
+  float invq = 1.0f, invk = 1.0f;
+  if (pre) {
+    float nq = tmp[3 * D], nk = tmp[3 * D + 1];
+#pragma unroll
+    for (int w2 = 1; w2 < NWS; ++w2) {
+      nq += tmp[3 * D + 2 * w2];
+      nk += tmp[3 * D + 2 * w2 + 1];
+    }
+    invq = nq > 0.0f ? rsqrtf(nq) : 0.0f;
+    invk = nk > 0.0f ? rsqrtf(nk) : 0.0f;
+  }
 #pragma unroll
   for (int n = 0; n < PER; ++n) {
     const int i = tid + n * NT;
     if (i < D) {
       const float g = PER_KEY ? tmp[2 * D + src[n]] : g0;
-      srow[i] = make_float4(sc[n] * g, tmp[src[n]], tmp[D + src[n]], 0.0f);
+      srow[i] = make_float4(sc[n] * g, tmp[src[n]] * invk, tmp[D + src[n]] * invq, 0.0f);
     }
   }
   __syncthreads();
+  // beta (uniform over the workgroup) for the column pass, in a scalar register
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(beta)));
 }
 
 // Column sums over the key rows, shared by the step kernels. Every lane writes its CPL partial
@@ -609,7 +653,8 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
                         reinterpret_cast<uint32_t*>(S[t]));
 
   // (2) per-row scalars and v
-  stage_rows<D, G::NT, PER_KEY, BF16, false>(a, nullptr, bh, head, 0, tid, srow, sv, &redu[0][0]);
+  const float beta = stage_rows<D, G::NT, PER_KEY, BF16, false>(a, nullptr, bh, head, 0, tid, srow, sv,
+                                                                 &redu[0][0]);
 
   // (3) decay, partial u = S'^T k, p = S'^T q over this lane's rows
   float pu[CPL], pp[CPL], pqk = 0.0f;
@@ -628,7 +673,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
   }
 
   // (4) column reductions, delta and the readout y = p + (q.k) delta (one thread per column)
-  finish_columns<D, G>(redu, redp, redqk, sv, pu, pp, pqk, a.beta[bh], a.out + int64_t(bh) * D,
+  finish_columns<D, G>(redu, redp, redqk, sv, pu, pp, pqk, beta, a.out + int64_t(bh) * D,
                        tid, w, rs, lane, cg);
   float dl[CPL];
   load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));
@@ -692,8 +737,8 @@ __device__ __forceinline__ void step_q_unit(const StepArgs& a, const UnitAddr& u
   }
 
   // (2) per-row scalars and v
-  stage_rows<D, G::NT, PER_KEY, BF16, true>(a, reinterpret_cast<const float*>(ua.s), bh, head, r, tid,
-                                            srow, sv, &sm.redu[0][0]);
+  const float beta = stage_rows<D, G::NT, PER_KEY, BF16, true>(a, reinterpret_cast<const float*>(ua.s),
+                                                                bh, head, r, tid, srow, sv, &sm.redu[0][0]);
 
   // (3) pass 1: u_j += (k_i m_i) c_ij, p_j += (q_i m_i) c_ij over the lane's rows. The lane's
   // rows are my_rows[t * RPS]: one LDS base address with immediate offsets per row step.
@@ -718,7 +763,7 @@ __device__ __forceinline__ void step_q_unit(const StepArgs& a, const UnitAddr& u
   }
 
   // (4) column reductions, delta and the readout y = p + (q.k) delta (one thread per column)
-  finish_columns<D, G>(sm.redu, sm.redp, sm.redqk, sv, pu, pp, pqk, a.beta[bh],
+  finish_columns<D, G>(sm.redu, sm.redp, sm.redqk, sv, pu, pp, pqk, beta,
                        a.out + int64_t(bh) * D, tid, w, rs, lane, cg);
   float dl[CPL];
   load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));

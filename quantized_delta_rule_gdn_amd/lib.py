@@ -33,7 +33,7 @@ EXPORTS = (
     "damp_decode_step", "fp32_decode_step", "uniform_int8_decode_step", "uniform_int8_quantize",
     "damp_last_error", "damp_abi_version", "damp_state_bytes_per_head",
     "damp_state_alloc_per_head", "damp_state_head_info", "damp_risk_scores", "damp_budget_rows",
-    "damp_allocate_rows",
+    "damp_allocate_rows", "damp_decode_step_fused",
 )
 
 
@@ -87,6 +87,8 @@ def load() -> ctypes.CDLL:
         "damp_risk_scores": ([P, I32, I32, I32, P, P, P, P], ctypes.c_int),
         "damp_budget_rows": ([I32, I32, ctypes.c_double, I32, I32], ctypes.c_int64),
         "damp_allocate_rows": ([P, I32, I32, ctypes.c_int64, I32, I32, P, P, P], ctypes.c_int),
+        "damp_decode_step_fused": ([P, P, I32, P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, P],
+                                   ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -290,6 +292,17 @@ class DampState:
         _check(load().damp_decode_step(self._h, _ptr(slot_idx), B, _ptr(q), _ptr(k), _ptr(v),
                                        dt, _ptr(alpha), decay, _ptr(beta), _ptr(out),
                                        _stream(stream)))
+
+
+    def decode_step_fused(self, slot_idx, q, k, v, gate_logit, beta_logit, out, stream=None) -> None:
+        """The step with the pre-step fused: q, k unnormalised, gate and beta as logits."""
+        B, dt, decay = _step_vectors(slot_idx, q, k, v, gate_logit, beta_logit, out,
+                                     self.num_heads, self.d)
+        if slot_idx.device != self.pool.device:
+            raise ValueError("slot_idx and the pool are on different devices")
+        _check(load().damp_decode_step_fused(self._h, _ptr(slot_idx), B, _ptr(q), _ptr(k), _ptr(v),
+                                             dt, _ptr(gate_logit), decay, _ptr(beta_logit),
+                                             _ptr(out), _stream(stream)))
 
 
 def fp32_decode_step(pool, slot_idx, q, k, v, alpha, beta, out, stream=None) -> None:

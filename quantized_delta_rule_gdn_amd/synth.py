@@ -268,3 +268,25 @@ def budget_calibration(H: int = 32, D: int = 128, n: int = BUDGET_CAL_STATES, se
     c = rng.standard_normal((H, D) if per_key else (H, 1))
     abar = np.broadcast_to(_sigmoid_f32(-c), (H, D)).astype(np.float32)
     return S, np.ascontiguousarray(abar)
+
+
+def raw_step_inputs(rng: np.random.Generator, B: int, H: int, D: int, decay: int = GDN,
+                    dtype: str = "bf16") -> StepInputs:
+    """Inputs of the fused pre-step, as a layer's projections give them: q, k ~ N(0, 1) times a
+    per-(slot, head) magnitude 10**U(-1, 1) (not normalised), v ~ N(0, 1); ``alpha`` holds gate
+    logits g ~ N(0, 1) (per (slot, head) or per key channel) and ``beta`` logits b ~ N(0, 1).
+    Draw order: q, k, magnitudes, v, g, b."""
+    q = rng.standard_normal((B, H, D), dtype=np.float32)
+    k = rng.standard_normal((B, H, D), dtype=np.float32)
+    mag = (10.0 ** rng.uniform(-1.0, 1.0, (2, B, H, 1))).astype(np.float32)
+    q = (q * mag[0]).astype(np.float32)
+    k = (k * mag[1]).astype(np.float32)
+    v = rng.standard_normal((B, H, D), dtype=np.float32)
+    g = rng.standard_normal((B, H, D) if decay == KDA else (B, H)).astype(np.float32)
+    b = rng.standard_normal((B, H)).astype(np.float32)
+    if dtype == "fp32":
+        return StepInputs(q, k, v, g, b, "fp32")
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    qb, kb, vb = bf16_bits(q), bf16_bits(k), bf16_bits(v)
+    return StepInputs(bf16_widen(qb), bf16_widen(kb), bf16_widen(vb), g, b, "bf16", qb, kb, vb)
