@@ -90,6 +90,9 @@ def parse():
     p.add_argument("--budget-group", type=int, default=8,
                    help="FP16 rows are handed out per head in groups of this many")
     p.add_argument("--budget-rmax", type=int, default=32, help="at most this many FP16 rows per head")
+    p.add_argument("--fused-prestep", action="store_true",
+                   help="DAMP step with the pre-step fused (raw q/k projections, gate and beta "
+                        "logits); also times the same pre-step as separate torch kernels + step")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the step, run a plain device copy of MIB MiB --steps times "
                         "(the reference kernel of known size for HBM byte counters)")
@@ -247,6 +250,14 @@ def main():
     R = len(slot_sets)
     results = {}
     budget = None
+    prestep_info = {}
+    raw_sets = None
+    if args.fused_prestep:
+        rng = np.random.default_rng([w.seed, 11])
+        raw = [synth.raw_step_inputs(rng, B, H, d, w.decay, "bf16") for _ in range(4)]
+        raw_sets = [(bf(i.q_bits), bf(i.k_bits), bf(i.v_bits), torch.from_numpy(i.alpha).to(dev),
+                     torch.from_numpy(i.beta).to(dev)) for i in raw]
+        desc += "; pre-step fused (raw q/k, gate and beta logits)"
     if args.budget_bits is not None:
         budget = calibrate_budget(torch, lib, synth, dev, H, d, per_key, args)
         desc = desc.replace(f"{r} FP16 rows/head", f"per-head FP16 rows at {args.budget_bits} bits/value")
@@ -255,7 +266,21 @@ def main():
               f"{budget['allocate_ms']:.3f} ms", file=sys.stderr, flush=True)
 
     def run(fmt):
-        if fmt == "damp" and budget is not None:
+        if fmt == "damp" and args.fused_prestep:
+            st = lib.DampState(pool_slots, H, d, rows, device=dev)
+            st.pool.zero_()
+            fill_states(torch, st.quantize, all_slots, H, d, dev)
+            launch = lambda i: st.decode_step_fused(slot_sets[i % R], *raw_sets[i % 4], out)
+            keep = st
+            F = torch.nn.functional
+
+            def unfused(i):
+                q, k, v, g, b = raw_sets[i % 4]
+                qn = F.normalize(q.float(), dim=-1)
+                kn = F.normalize(k.float(), dim=-1)
+                st.decode_step(slot_sets[i % R], qn, kn, v.float(), torch.sigmoid(-g), torch.sigmoid(b), out)
+            prestep_info["unfused_ms"] = time_launches(torch, unfused, args.steps, args.warmup)
+        elif fmt == "damp" and budget is not None:
             st = lib.DampState(pool_slots, H, d, budget["row_map"], device=dev,
                                r_per_head=budget["r_per_head"])
             st.pool.zero_()
@@ -324,6 +349,11 @@ def main():
     }
     if budget is not None:
         line["config"]["layout"] = {k: v for k, v in budget.items() if k != "row_map"}
+    if prestep_info:
+        prestep_info["fused_ms"] = results["damp"]["ms_per_step"]
+        prestep_info["unfused"] = ("torch normalize(q), normalize(k), sigmoid(-g), sigmoid(b) in fp32, "
+                                   "then damp_decode_step")
+        line["prestep"] = prestep_info
     if "fp32" in results and "damp" in results:
         line["baselines"] = {f: {"ms_per_step": v["ms_per_step"], "updates_per_s": v["updates_per_s"],
                                  "gbs": v["gbs"], "frac": v["gbs"] / PEAK_HBM_GBS}
