@@ -67,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_allocate_rows.restype = I
         L.oracle_prestep.argtypes = [I, Lg, P, P, P, I, P, P, P, P, P]
         L.oracle_prestep.restype = I
+        L.oracle_window_step.argtypes = [I, Lg, P, P, P, P, P, P, I, P, P, P, P, I, P, P, I]
+        L.oracle_window_step.restype = I
+        L.oracle_window_flush.argtypes = [I, Lg, P, P, P, P, P, P]
+        L.oracle_window_flush.restype = I
         _lib = L
     return _lib
 
@@ -238,3 +242,35 @@ def prestep(q, k, g, b):
     rc = lib().oracle_prestep(D, n, _p(q), _p(k), _p(g), per_key, _p(b), _p(qo), _p(ko), _p(ao), _p(bo))
     assert rc == 0
     return qo, ko, ao, bo
+
+
+class Window:
+    """Per-window requantization state of ``n`` units in the oracle: the quantized arrays
+    ``(h, c, s)`` (updated in place at window ends), each unit's exact binary64 state within its
+    window, and the number of tokens already applied in the current window."""
+
+    def __init__(self, mask, h, c, s, W: int):
+        for a, t in ((h, np.uint16), (c, np.int8), (s, np.float32)):
+            assert a.dtype == t and a.flags.c_contiguous
+        n, D, _ = c.shape
+        self.mask = _c(np.broadcast_to(mask, (n, D)), np.uint8)
+        self.h, self.c, self.s, self.W = h, c, s, W
+        self.Sx = np.zeros((n, D, D), np.float64)
+        self.t = np.zeros(n, np.int32)
+
+    def step(self, q, k, v, alpha, beta, nthreads: int | None = None) -> np.ndarray:
+        n, D, _ = self.c.shape
+        q, k, v, alpha, per_key, beta = _vecs(q, k, v, alpha, beta, n, D)
+        out = np.empty((n, D), np.float32)
+        rc = lib().oracle_window_step(D, n, _p(self.mask), _p(self.h), _p(self.c), _p(self.s),
+                                      _p(self.Sx), _p(self.t), self.W, _p(q), _p(k), _p(v),
+                                      _p(alpha), per_key, _p(beta), _p(out),
+                                      nthreads or default_threads())
+        assert rc == 0
+        return out
+
+    def flush(self) -> None:
+        n, D, _ = self.c.shape
+        rc = lib().oracle_window_flush(D, n, _p(self.mask), _p(self.h), _p(self.c), _p(self.s),
+                                       _p(self.Sx), _p(self.t))
+        assert rc == 0

@@ -438,3 +438,107 @@ int oracle_prestep(int D, long n, const float* q, const float* k, const float* g
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Per-window requantization (the LeapQuant page, abstract: the low-bit state stays fixed for a
+ * window of tokens, the window's updates are held in high precision, outputs come from the
+ * fixed state together with those updates, and the state is quantized once, at the window's
+ * end). Read here as: within a window a unit's state is the exact (binary64) recurrence started
+ * from the reconstruction of its low-bit state, each readout is taken from that state, and after
+ * the window's W-th token the state is rounded once to binary32 and stored with the unit's rule
+ * (FP16 rows RNE, INT8 rows absmax / 127). W = 1 is the per-token step.
+ *   Sx  binary64 [n][D][D]: each unit's state within its window (held by the caller)
+ *   t   [n]: tokens of the current window already applied (0: the window starts with this one)
+ * ---------------------------------------------------------------------------------------- */
+static void store_unit(int D, const uint8_t* mask, uint16_t* h, int8_t* c, float* s,
+                       const double* Sx, float* rowbuf) {
+  for (int i = 0; i < D; ++i) {
+    for (int j = 0; j < D; ++j) rowbuf[j] = (float)Sx[(long)i * D + j];
+    if (mask[i]) {
+      for (int j = 0; j < D; ++j) h[(long)i * D + j] = oracle_f16_from_f32(rowbuf[j]);
+      memset(c + (long)i * D, 0, (size_t)D);
+      s[i] = 0.0f;
+    } else {
+      for (int j = 0; j < D; ++j) h[(long)i * D + j] = 0;
+      oracle_quant_row(D, rowbuf, c + (long)i * D, s + i);
+    }
+  }
+}
+
+int oracle_window_step(int D, long n_units, const uint8_t* mask, uint16_t* h, int8_t* c,
+                       float* s, double* Sx, int32_t* t, int W, const float* q, const float* k,
+                       const float* v, const float* alpha, int per_key, const float* beta,
+                       float* out, int nthreads) {
+  if (D <= 0 || n_units < 0 || W < 1 || !mask || !h || !c || !s || !Sx || !t || !q || !k ||
+      !v || !alpha || !beta || !out)
+    return -1;
+  const long DD = (long)D * D;
+  int bad = 0;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+  {
+    double* u = (double*)malloc(sizeof(double) * (size_t)D);
+    float* rowbuf = (float*)malloc(sizeof(float) * (size_t)D);
+    if (!u || !rowbuf) {
+#pragma omp atomic write
+      bad = 1;
+    }
+#pragma omp for schedule(static)
+    for (long un = 0; un < n_units; ++un) {
+      if (!u || !rowbuf) continue;
+      const uint8_t* mk = mask + un * D;
+      double* X = Sx + un * DD;
+      if (t[un] < 0 || t[un] >= W) continue;
+      if (t[un] == 0) /* a window starts: the exact state is the reconstruction */
+        for (int i = 0; i < D; ++i)
+          for (int j = 0; j < D; ++j)
+            X[(long)i * D + j] = recon(D, mk, h + un * DD, c + un * DD, s + un * D, i, j);
+      const float* qu = q + un * D;
+      const float* ku = k + un * D;
+      const float* vu = v + un * D;
+      const float* au = per_key ? alpha + un * D : alpha + un;
+      /* the decode step on the exact state: S' = D_t S, u = S'^T k, X = S' + k beta (v - u) */
+      for (int i = 0; i < D; ++i) {
+        const double a = (double)(per_key ? au[i] : au[0]);
+        for (int j = 0; j < D; ++j) X[(long)i * D + j] *= a;
+      }
+      for (int j = 0; j < D; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < D; ++i) acc += (double)ku[i] * X[(long)i * D + j];
+        u[j] = acc;
+      }
+      for (int i = 0; i < D; ++i)
+        for (int j = 0; j < D; ++j)
+          X[(long)i * D + j] += (double)ku[i] * ((double)beta[un] * ((double)vu[j] - u[j]));
+      for (int j = 0; j < D; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < D; ++i) acc += (double)qu[i] * X[(long)i * D + j];
+        out[un * D + j] = (float)acc;
+      }
+      t[un] += 1;
+      if (t[un] == W) {
+        store_unit(D, mk, h + un * DD, c + un * DD, s + un * D, X, rowbuf);
+        t[un] = 0;
+      }
+    }
+    free(u);
+    free(rowbuf);
+  }
+  for (long un = 0; un < n_units; ++un)
+    if (t[un] < 0 || t[un] >= W) bad = 1;
+  return bad ? -1 : 0;
+}
+
+/* Store every unit with pending tokens (t > 0) from its exact state and start a new window. */
+int oracle_window_flush(int D, long n_units, const uint8_t* mask, uint16_t* h, int8_t* c,
+                        float* s, const double* Sx, int32_t* t) {
+  if (D <= 0 || n_units < 0 || !mask || !h || !c || !s || !Sx || !t) return -1;
+  const long DD = (long)D * D;
+  float* rowbuf = (float*)malloc(sizeof(float) * (size_t)D);
+  if (!rowbuf) return -1;
+  for (long un = 0; un < n_units; ++un) {
+    if (t[un] > 0) store_unit(D, mask + un * D, h + un * DD, c + un * DD, s + un * D, Sx + un * DD, rowbuf);
+    t[un] = 0;
+  }
+  free(rowbuf);
+  return 0;
+}

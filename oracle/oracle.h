@@ -93,6 +93,20 @@ int oracle_prestep(int D, long n, const float* q, const float* k, const float* g
                    const float* b, float* q_out, float* k_out, float* alpha_out,
                    float* beta_out);
 
+/* Per-window requantization: within a window of W tokens a unit's state is the exact binary64
+ * recurrence started from the reconstruction of (h, c, s), its readouts come from that state,
+ * and after the W-th token it is rounded to binary32 and stored with the unit's rule.
+ *   Sx double [n][D][D] (the units' exact states, caller-held), t int32 [n] (tokens applied in
+ *   the current window; 0 = the window starts with this call's token). Other arguments as in
+ *   oracle_step (fmt 1). oracle_window_flush stores every unit with t > 0 and sets t = 0.
+ * Return 0 or -1. */
+int oracle_window_step(int D, long n_units, const uint8_t* mask, uint16_t* h, int8_t* c,
+                       float* s, double* Sx, int32_t* t, int W, const float* q, const float* k,
+                       const float* v, const float* alpha, int per_key, const float* beta,
+                       float* out, int nthreads);
+int oracle_window_flush(int D, long n_units, const uint8_t* mask, uint16_t* h, int8_t* c,
+                        float* s, const double* Sx, int32_t* t);
+
 #ifdef __cplusplus
 }
 #endif
