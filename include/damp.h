@@ -175,6 +175,41 @@ damp_status damp_decode_step_fused(damp_state* state, const int32_t* slot_idx, i
                                    damp_decay decay, const float* beta_logit, float* out,
                                    void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Per-window requantization (the LeapQuant page, abstract: the low-bit state stays fixed for a
+ * window of tokens, the window's updates are held in high precision, outputs are computed from
+ * both, and the state is quantized once at the window's end). Within a window the state of a
+ * unit is diag(a) S_hat + sum over the window's tokens of K_tau E_tau^T: S_hat the stored DAMP
+ * state (not written until the window ends), a its cumulative row decay, K_tau the token's key
+ * decayed by the later gates and E_tau its delta, all fp32 in a window buffer. Each unit has its
+ * own window position, so the requests of one batch may be at different points of their windows.
+ * ------------------------------------------------------------------------------------- */
+
+/* Bytes of the window buffers of a whole pool (num_slots * num_heads units) for windows of
+ * `window` tokens, 1 <= window <= 8; 0 if invalid. Per unit: round_up(4 (4 + d + 2 window d), 256).
+ * The caller allocates them (256-byte aligned) and fills them with zero bytes once: a zero buffer
+ * is a unit at the start of a window. */
+size_t damp_window_bytes(const damp_layout* layout, int32_t window);
+
+/* One token of a window for B requests, same arguments as damp_decode_step plus the window
+ * buffers and the window length. For each unit: u and the readout come from the stored state and
+ * the buffered tokens (the readout from X before any requantization, as in the step); the token
+ * is appended to the buffer; if it is the window's window-th token, X is stored in the unit's
+ * rule (FP16 rows RNE, INT8 rows absmax / 127) and the buffer emptied. Otherwise the pool is only
+ * read. window = 1 is the per-token step (the same arithmetic as damp_decode_step up to fp32
+ * rounding order). A given buffer must always be used with the same window length.
+ * Errors: INVALID_ARGUMENT, SLOT_INDEX (debug), HIP. */
+damp_status damp_window_step(damp_state* state, void* window_buf, int32_t window,
+                             const int32_t* slot_idx, int32_t B, const void* q, const void* k,
+                             const void* v, damp_dtype qkv_dtype, const float* alpha,
+                             damp_decay decay, const float* beta, float* out, void* stream);
+
+/* End the windows of n slots now: every listed unit with buffered tokens stores its state in the
+ * unit's rule and empties its buffer (units with none are left as they are). Use before reading
+ * the pool with damp_state_dequantize, or when a request ends. */
+damp_status damp_window_flush(damp_state* state, void* window_buf, int32_t window,
+                              const int32_t* slot_idx, int32_t n, void* stream);
+
 /* The same step on an FP32 state pool (the reference format of the DAMP speedups):
  *   pool dev fp32 [num_slots][num_heads][d_k][d_v], 16-byte aligned. Other arguments as in
  *   damp_decode_step. No requantization: X is stored as fp32. */

@@ -228,10 +228,23 @@ damp::StateRef int8_ref(int8_t* codes, float* scales, int32_t d) {
   return ref;
 }
 
+size_t window_unit_bytes(int32_t d, int32_t window) {
+  return round_up(4 * (4 + static_cast<size_t>(d) + 2 * static_cast<size_t>(window) * d), kBlockAlign);
+}
+
+damp_status check_window(const void* win, int32_t window) {
+  if (window < 1 || window > damp::window_max())
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "window %d outside [1, %d]", window, damp::window_max());
+  if (!win) return fail(DAMP_ERR_INVALID_ARGUMENT, "window_buf is NULL");
+  if (!aligned(win, kBlockAlign)) return fail(DAMP_ERR_INVALID_ARGUMENT, "window_buf must be 256-byte aligned");
+  return DAMP_OK;
+}
+
 damp_status run_step(int fmt, const damp::StateRef& ref, int32_t d, int32_t H, int32_t num_slots,
                      const int32_t* slot_idx, int32_t B, const void* q, const void* k,
                      const void* v, damp_dtype dt, const float* alpha, damp_decay decay,
-                     const float* beta, float* out, void* stream, int prestep = 0) {
+                     const float* beta, float* out, void* stream, int prestep = 0,
+                     void* win = nullptr, int32_t window = 0, bool flush_only = false) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   damp_status st = debug_check_slots(slot_idx, B, num_slots, s);
   if (st != DAMP_OK) return st;
@@ -247,6 +260,13 @@ damp_status run_step(int fmt, const damp::StateRef& ref, int32_t d, int32_t H, i
   a.beta = beta;
   a.out = out;
   a.prestep = prestep;
+  if (win) {
+    a.win = static_cast<uint8_t*>(win);
+    a.win_stride = static_cast<int64_t>(window_unit_bytes(d, window));
+    a.window = window;
+    return launched(damp::launch_window(d, decay == DAMP_DECAY_PER_KEY, dt == DAMP_BF16, flush_only, a, s),
+                    flush_only ? "window flush" : "window step");
+  }
   return launched(damp::launch_step(fmt, d, decay == DAMP_DECAY_PER_KEY, dt == DAMP_BF16, a, s),
                   "decode step");
 }
@@ -488,6 +508,48 @@ damp_status damp_decode_step_fused(damp_state* s, const int32_t* slot_idx, int32
   if (B == 0) return ok();
   return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, B, q, k, v,
                   dt, gate_logit, decay, beta_logit, out, stream, 1);
+}
+
+size_t damp_window_bytes(const damp_layout* L, int32_t window) {
+  if (!L || window < 1 || window > damp::window_max()) return 0;
+  damp_layout T = *L;
+  T.num_fp16_rows = 0;
+  if (check_layout(&T) != DAMP_OK) return 0;
+  const size_t units = static_cast<size_t>(L->num_slots) * static_cast<size_t>(L->num_heads);
+  const size_t per = window_unit_bytes(L->d_k, window);
+  if (units != 0 && per > SIZE_MAX / units) return 0;
+  return units * per;
+}
+
+damp_status damp_window_step(damp_state* s, void* window_buf, int32_t window, const int32_t* slot_idx,
+                             int32_t B, const void* q, const void* k, const void* v, damp_dtype dt,
+                             const float* alpha, damp_decay decay, const float* beta, float* out,
+                             void* stream) {
+  if (!s) return fail(DAMP_ERR_INVALID_ARGUMENT, "state is NULL");
+  const damp_layout& L = s->layout;
+  damp_status st = check_step_args(B, L.num_heads, L.d_k, slot_idx, q, k, v, dt, alpha, decay, beta, out);
+  if (st != DAMP_OK) return st;
+  st = check_window(window_buf, window);
+  if (st != DAMP_OK) return st;
+  if (B == 0) return ok();
+  return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, B, q, k, v,
+                  dt, alpha, decay, beta, out, stream, 0, window_buf, window, false);
+}
+
+damp_status damp_window_flush(damp_state* s, void* window_buf, int32_t window, const int32_t* slot_idx,
+                              int32_t n, void* stream) {
+  if (!s) return fail(DAMP_ERR_INVALID_ARGUMENT, "state is NULL");
+  if (n < 0) return fail(DAMP_ERR_INVALID_ARGUMENT, "n (%d) must be >= 0", n);
+  damp_status st = check_window(window_buf, window);
+  if (st != DAMP_OK) return st;
+  if (n == 0) return ok();
+  if (!slot_idx || !aligned(slot_idx, 4)) return fail(DAMP_ERR_INVALID_ARGUMENT, "slot_idx NULL or misaligned");
+  const damp_layout& L = s->layout;
+  if (static_cast<int64_t>(n) * L.num_heads > 0x7fffffffLL)
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "n * num_heads exceeds the grid limit");
+  return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, n, nullptr,
+                  nullptr, nullptr, DAMP_F32, nullptr, DAMP_DECAY_SCALAR, nullptr, nullptr, stream, 0,
+                  window_buf, window, true);
 }
 
 damp_status fp32_decode_step(float* pool, int32_t num_slots, int32_t H, int32_t d_k, int32_t d_v,

@@ -49,6 +49,9 @@ struct StepArgs {
   const float* beta;        // [B][H]
   float* out;               // [B][H][d]
   int32_t prestep;          // 1: q, k are normalised here and alpha, beta are logits
+  uint8_t* win;             // per-window requantization: the window buffers (else nullptr)
+  int64_t win_stride;       //   bytes per (slot, head) buffer
+  int32_t window;           //   tokens per window, 1 .. 8
 };
 
 struct PackArgs {
@@ -63,6 +66,11 @@ struct PackArgs {
 hipError_t launch_step(int fmt, int d, int per_key, int bf16, const StepArgs& a, hipStream_t s);
 hipError_t launch_quantize(int d, const PackArgs& a, hipStream_t s);
 hipError_t launch_dequantize(int d, const PackArgs& a, hipStream_t s);
+// Per-window requantization: one token of a window (flush_only = false; q..out as the step) or
+// the flush of every listed unit with pending tokens (flush_only = true; B units, no vectors).
+hipError_t launch_window(int d, int per_key, int bf16, bool flush_only, const StepArgs& a,
+                         hipStream_t s);
+int window_max();
 
 // Calibration (calib_kernels.hip). Sizes are validated by the caller: d in {16, 32, 64, 128},
 // H * d <= alloc_max_rows(), H * (r_max / g) <= alloc_max_groups(), R % g == 0.

@@ -33,7 +33,8 @@ EXPORTS = (
     "damp_decode_step", "fp32_decode_step", "uniform_int8_decode_step", "uniform_int8_quantize",
     "damp_last_error", "damp_abi_version", "damp_state_bytes_per_head",
     "damp_state_alloc_per_head", "damp_state_head_info", "damp_risk_scores", "damp_budget_rows",
-    "damp_allocate_rows", "damp_decode_step_fused",
+    "damp_allocate_rows", "damp_decode_step_fused", "damp_window_bytes", "damp_window_step",
+    "damp_window_flush",
 )
 
 
@@ -89,6 +90,10 @@ def load() -> ctypes.CDLL:
         "damp_allocate_rows": ([P, I32, I32, ctypes.c_int64, I32, I32, P, P, P], ctypes.c_int),
         "damp_decode_step_fused": ([P, P, I32, P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, P],
                                    ctypes.c_int),
+        "damp_window_bytes": ([LP, I32], SZ),
+        "damp_window_step": ([P, P, I32, P, I32, P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, P],
+                             ctypes.c_int),
+        "damp_window_flush": ([P, P, I32, P, I32, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -303,6 +308,39 @@ class DampState:
         _check(load().damp_decode_step_fused(self._h, _ptr(slot_idx), B, _ptr(q), _ptr(k), _ptr(v),
                                              dt, _ptr(gate_logit), decay, _ptr(beta_logit),
                                              _ptr(out), _stream(stream)))
+
+
+    # ---- per-window requantization ----
+    def window_buffer(self, window: int):
+        """A zero-filled window buffer of the pool for windows of ``window`` tokens."""
+        torch = _torch()
+        lay = layout(self.num_slots, self.num_heads, self.d, 0)
+        n = load().damp_window_bytes(ctypes.byref(lay), window)
+        if n == 0:
+            raise DampError(DAMP_ERR_INVALID_ARGUMENT, f"invalid window length {window}")
+        return torch.zeros(n, dtype=torch.uint8, device=self.pool.device)
+
+    def window_step(self, wbuf, window: int, slot_idx, q, k, v, alpha, beta, out, stream=None) -> None:
+        B, dt, decay = _step_vectors(slot_idx, q, k, v, alpha, beta, out, self.num_heads, self.d)
+        self._check_wbuf(wbuf, window)
+        _check(load().damp_window_step(self._h, _ptr(wbuf), window, _ptr(slot_idx), B, _ptr(q), _ptr(k),
+                                       _ptr(v), dt, _ptr(alpha), decay, _ptr(beta), _ptr(out),
+                                       _stream(stream)))
+
+    def window_flush(self, wbuf, window: int, slot_idx, stream=None) -> None:
+        torch = _torch()
+        n = slot_idx.shape[0]
+        _need(slot_idx, "slot_idx", torch.int32, (n,), self.pool.device)
+        self._check_wbuf(wbuf, window)
+        _check(load().damp_window_flush(self._h, _ptr(wbuf), window, _ptr(slot_idx), n, _stream(stream)))
+
+    def _check_wbuf(self, wbuf, window):
+        torch = _torch()
+        lay = layout(self.num_slots, self.num_heads, self.d, 0)
+        need = load().damp_window_bytes(ctypes.byref(lay), window)
+        _need(wbuf, "window buffer", torch.uint8, (wbuf.numel(),), self.pool.device)
+        if wbuf.numel() < need:
+            raise ValueError(f"window buffer has {wbuf.numel()} bytes, {need} needed")
 
 
 def fp32_decode_step(pool, slot_idx, q, k, v, alpha, beta, out, stream=None) -> None:

@@ -1,0 +1,196 @@
+"""GPU parity of per-window requantization (damp_window_step / damp_window_flush) against the
+oracle's windowed step: readouts every token, the pool untouched inside a window, and the stored
+state at every window end and after a flush. Tolerances as in gpu_common. Covers the
+compile-time row-kind instances, the general instance, a per-head layout, smaller d, a window of
+one token, and requests at different positions of their windows."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+import oracle  # noqa: E402
+import layout_ref  # noqa: E402
+from gpu_common import DampPool, check_quant, check_readout, ref_vectors, step_tensors, to_dev  # noqa: E402
+from quantized_delta_rule_gdn_amd import lib, synth  # noqa: E402
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _setup(seed, B, H, D, r, decay):
+    rng = np.random.default_rng(seed)
+    S = synth.normal_states(rng, (B, H, D, D), 0.1)
+    for hh in range(H):
+        S[:, hh, rng.choice(D, max(1, D // 32), replace=False), :] *= 8
+    rows = synth.random_rows(rng, H, D, r)
+    mask = synth.rows_to_mask(rows, D)
+    maskn = np.broadcast_to(mask, (B, H, D)).reshape(B * H, D)
+    h, c, s = oracle.quantize(maskn, S.reshape(B * H, D, D))
+    return rng, rows, mask, maskn, h, c, s
+
+
+def _resync(win, got):
+    """Parity is judged from identical input states: after a window end has been compared, the
+    oracle continues from the GPU's stored state (the two may differ by the few codes the
+    tolerance allows, which would otherwise carry into the next window's readouts)."""
+    h, c, s = got
+    win.h[...] = h.reshape(win.h.shape)
+    win.c[...] = c.reshape(win.c.shape)
+    win.s[...] = s.reshape(win.s.shape)
+
+
+def _gpu_step(pool, wbuf, W, slots_dev, inp):
+    B = slots_dev.shape[0]
+    q, k, v, a, b = step_tensors(inp)
+    out = torch.empty((B, pool.H, pool.D), dtype=torch.float32, device="cuda")
+    pool.state.window_step(wbuf, W, slots_dev, q, k, v, a, b, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("D,r,B,H,W,decay,dtype,tokens", [
+    (128, 24, 9, 4, 4, synth.GDN, "bf16", 10),    # compile-time row kinds
+    (128, 27, 5, 3, 8, synth.KDA, "bf16", 11),    # general instance
+    (128, 16, 6, 2, 3, synth.KDA, "fp32", 7),
+    (64, 8, 7, 3, 5, synth.GDN, "fp32", 7),
+    (16, 2, 4, 2, 2, synth.KDA, "bf16", 5),
+    (128, 24, 5, 2, 1, synth.GDN, "bf16", 3),     # one token per window: the per-token step
+])
+def test_window_steps_and_flush(D, r, B, H, W, decay, dtype, tokens):
+    rng, rows, mask, maskn, h, c, s = _setup(D + r + W, B, H, D, r, decay)
+    win = oracle.Window(maskn, h.copy(), c.copy(), s.copy(), W)
+    slots = np.random.default_rng(B + W).choice(2 * B, B, replace=False)
+    pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), slots, 2 * B)
+    wbuf = pool.state.window_buffer(W)
+    start = pool.state.blocks().clone()
+    for tok in range(tokens):
+        inp = synth.step_inputs(rng, B, H, D, decay, dtype)
+        out = _gpu_step(pool, wbuf, W, pool.slot_dev, inp)
+        ref = win.step(*ref_vectors(inp, B, H, D))
+        check_readout(out, ref.reshape(B, H, D))
+        if (tok + 1) % W == 0:
+            got = pool.logical()
+            stats = check_quant(mask, got, (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D),
+                                            win.s.reshape(B, H, D)))
+            _resync(win, got)
+            start = pool.state.blocks().clone()
+            _log(f"window end after token {tok + 1}: {stats}")
+        else:
+            assert torch.equal(pool.state.blocks(), start), "pool written inside a window"
+    # flush what is pending and compare
+    pool.state.window_flush(wbuf, W, pool.slot_dev)
+    win.flush()
+    torch.cuda.synchronize()
+    check_quant(mask, pool.logical(), (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D),
+                                       win.s.reshape(B, H, D)))
+    # a second flush finds nothing pending and leaves the pool as it is
+    before = pool.state.blocks().clone()
+    pool.state.window_flush(wbuf, W, pool.slot_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(pool.state.blocks(), before)
+
+
+def test_requests_at_different_window_positions():
+    D, r, H, W = 128, 24, 3, 4
+    B = 8
+    rng, rows, mask, maskn, h, c, s = _setup(77, B, H, D, r, synth.GDN)
+    first = np.arange(3)            # these slots run two tokens on their own first
+    pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D),
+                    np.arange(B), B)
+    wbuf = pool.state.window_buffer(W)
+    nf = len(first) * H
+    wa = oracle.Window(maskn[:nf], h[:nf].copy(), c[:nf].copy(), s[:nf].copy(), W)
+    wb = oracle.Window(maskn[nf:], h[nf:].copy(), c[nf:].copy(), s[nf:].copy(), W)
+    sub = torch.from_numpy(first.astype(np.int32)).cuda()
+    for _ in range(2):
+        inp = synth.step_inputs(rng, len(first), H, D, synth.GDN, "bf16")
+        out = _gpu_step(pool, wbuf, W, sub, inp)
+        check_readout(out, wa.step(*ref_vectors(inp, len(first), H, D)).reshape(len(first), H, D))
+    na = len(first)
+    for j in range(5):
+        inp = synth.step_inputs(rng, B, H, D, synth.GDN, "bf16")
+        out = _gpu_step(pool, wbuf, W, pool.slot_dev, inp)
+        v = ref_vectors(inp, B, H, D)
+        ra = wa.step(*(x[:nf] for x in v))
+        rb = wb.step(*(x[nf:] for x in v))
+        check_readout(out, np.concatenate([ra, rb]).reshape(B, H, D))
+        # the first group's windows end after its 4th token (joint token 2), the others' after
+        # joint token 4: compare there and continue from the GPU's stored state
+        got = pool.logical()
+        for wo, sl, ends in ((wa, slice(0, na), j == 1), (wb, slice(na, B), j == 3)):
+            if ends:
+                part = tuple(x[sl] for x in got)
+                n_ = part[2].shape[0]
+                check_quant(mask, part, (wo.h.reshape(n_, H, D, D), wo.c.reshape(n_, H, D, D),
+                                         wo.s.reshape(n_, H, D)))
+                _resync(wo, part)
+    pool.state.window_flush(wbuf, W, pool.slot_dev)
+    wa.flush()
+    wb.flush()
+    torch.cuda.synchronize()
+    ref = tuple(np.concatenate([x, y]) for x, y in ((wa.h, wb.h), (wa.c, wb.c), (wa.s, wb.s)))
+    check_quant(mask, pool.logical(), (ref[0].reshape(B, H, D, D), ref[1].reshape(B, H, D, D),
+                                       ref[2].reshape(B, H, D)))
+
+
+def test_window_on_per_head_layout():
+    B, H, D, W = 6, 6, 128, 4
+    r_per_head = np.array([0, 8, 16, 24, 32, 24], np.int32)
+    rng = np.random.default_rng(21)
+    row_map = np.empty((H, D), np.int32)
+    for hh in range(H):
+        f = np.sort(rng.choice(D, r_per_head[hh], replace=False))
+        row_map[hh] = np.concatenate([f, np.setdiff1d(np.arange(D), f)])
+    S = synth.normal_states(rng, (B, H, D, D), 0.1)
+    mask = layout_ref.mask_per_head(r_per_head, row_map, D)
+    maskn = np.broadcast_to(mask, (B, H, D)).reshape(B * H, D)
+    h, c, s = oracle.quantize(maskn, S.reshape(B * H, D, D))
+    st = lib.DampState(B, H, D, row_map, r_per_head=r_per_head)
+    st.slots()[:] = to_dev(layout_ref.pack_per_head(r_per_head, row_map, h.reshape(B, H, D, D),
+                                                    c.reshape(B, H, D, D), s.reshape(B, H, D)))
+    wbuf = st.window_buffer(W)
+    win = oracle.Window(maskn, h.copy(), c.copy(), s.copy(), W)
+    slots = torch.arange(B, dtype=torch.int32, device="cuda")
+    for tok in range(6):
+        inp = synth.step_inputs(rng, B, H, D, synth.KDA, "bf16")
+        q, k, v, a, b = step_tensors(inp)
+        out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+        st.window_step(wbuf, W, slots, q, k, v, a, b, out)
+        torch.cuda.synchronize()
+        check_readout(out.cpu().numpy(), win.step(*ref_vectors(inp, B, H, D)).reshape(B, H, D))
+        if tok + 1 == W:
+            got = layout_ref.unpack_per_head(r_per_head, row_map, st.slots().cpu().numpy(), D)
+            check_quant(mask, got, (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D),
+                                    win.s.reshape(B, H, D)))
+            _resync(win, got)
+    st.window_flush(wbuf, W, slots)
+    win.flush()
+    torch.cuda.synchronize()
+    got = layout_ref.unpack_per_head(r_per_head, row_map, st.slots().cpu().numpy(), D)
+    check_quant(mask, got, (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D), win.s.reshape(B, H, D)))
+
+
+def test_window_full_heads_gdn64_shape():
+    """64 slots x 32 heads x 128, 24 FP16 rows, windows of 8 tokens: 12 tokens and a flush."""
+    B, H, D, r, W = 64, 32, 128, 24, 8
+    rng, rows, mask, maskn, h, c, s = _setup(64, B, H, D, r, synth.GDN)
+    win = oracle.Window(maskn, h.copy(), c.copy(), s.copy(), W)
+    pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), np.arange(B), B)
+    wbuf = pool.state.window_buffer(W)
+    for tok in range(12):
+        inp = synth.step_inputs(rng, B, H, D, synth.GDN, "bf16")
+        out = _gpu_step(pool, wbuf, W, pool.slot_dev, inp)
+        check_readout(out, win.step(*ref_vectors(inp, B, H, D)).reshape(B, H, D))
+        if (tok + 1) % W == 0:
+            got = pool.logical()
+            check_quant(mask, got, (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D), win.s.reshape(B, H, D)))
+            _resync(win, got)
+    pool.state.window_flush(wbuf, W, pool.slot_dev)
+    win.flush()
+    torch.cuda.synchronize()
+    _log(str(check_quant(mask, pool.logical(), (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D),
+                                                win.s.reshape(B, H, D)))))
