@@ -56,6 +56,21 @@ def measured_traffic():
     return int(kv["traffic_bytes_per_launch"])
 
 
+def alg_bytes_window(W: int, d: int = 128, r: int = 24, per_key: bool = False, qkv_bytes: int = 2) -> float:
+    """Bytes per (slot, head) update of the windowed step, averaged over the W tokens of a
+    window: every token reads the stored block and its buffered terms; a token that does not end
+    the window writes the decayed row gains and keys back and appends its key and delta (4 d
+    bytes each); the last one writes the block instead."""
+    block = 2 * r * d + (d - r) * d + 4 * (d - r)
+    vecs = 3 * qkv_bytes * d + (4 * d if per_key else 4) + 4 + 4 * d + 4
+    total = 0
+    for t in range(W):
+        rd = block + 4 + (4 * d if t else 0) + t * 2 * 4 * d
+        wr = block if t == W - 1 else 4 + 4 * d + t * 4 * d + 2 * 4 * d
+        total += rd + wr + vecs
+    return total / W
+
+
 def alg_bytes_per_update(fmt: str, d: int = 128, r: int = 24, per_key: bool = False,
                          qkv_bytes: int = 2) -> int:
     """Bytes one (slot, head) update must move: the state block in and out, q/k/v, the gate
@@ -93,6 +108,9 @@ def parse():
     p.add_argument("--fused-prestep", action="store_true",
                    help="DAMP step with the pre-step fused (raw q/k projections, gate and beta "
                         "logits); also times the same pre-step as separate torch kernels + step")
+    p.add_argument("--window", type=int, default=0, metavar="W",
+                   help="DAMP with per-window requantization: windows of W tokens (1..8); the "
+                        "timed launches run whole windows, so the figures average over a window")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the step, run a plain device copy of MIB MiB --steps times "
                         "(the reference kernel of known size for HBM byte counters)")
@@ -252,6 +270,13 @@ def main():
     budget = None
     prestep_info = {}
     raw_sets = None
+    if args.window:
+        if not 1 <= args.window <= 8:
+            raise SystemExit("--window must be in 1..8")
+        # whole windows per timed run, and every pool copy at the same window position
+        args.steps = -(-args.steps // (args.window * R)) * args.window * R
+        args.warmup = -(-args.warmup // (args.window * R)) * args.window * R
+        desc += f"; per-window requantization, windows of {args.window} tokens"
     if args.fused_prestep:
         rng = np.random.default_rng([w.seed, 11])
         raw = [synth.raw_step_inputs(rng, B, H, d, w.decay, "bf16") for _ in range(4)]
@@ -266,7 +291,14 @@ def main():
               f"{budget['allocate_ms']:.3f} ms", file=sys.stderr, flush=True)
 
     def run(fmt):
-        if fmt == "damp" and args.fused_prestep:
+        if fmt == "damp" and args.window:
+            st = lib.DampState(pool_slots, H, d, rows, device=dev)
+            st.pool.zero_()
+            fill_states(torch, st.quantize, all_slots, H, d, dev)
+            wbuf = st.window_buffer(args.window)
+            launch = lambda i: st.window_step(wbuf, args.window, slot_sets[i % R], *sets[i % 4], out)
+            keep = (st, wbuf)
+        elif fmt == "damp" and args.fused_prestep:
             st = lib.DampState(pool_slots, H, d, rows, device=dev)
             st.pool.zero_()
             fill_states(torch, st.quantize, all_slots, H, d, dev)
@@ -287,7 +319,7 @@ def main():
             fill_states(torch, st.quantize, all_slots, H, d, dev)
             launch = lambda i: st.decode_step(slot_sets[i % R], *sets[i % 4], out)
             keep = st
-        elif fmt == "damp":
+        elif fmt in ("damp", "damp_token"):
             st = lib.DampState(pool_slots, H, d, rows, device=dev)
             st.pool.zero_()
             fill_states(torch, st.quantize, all_slots, H, d, dev)
@@ -309,7 +341,11 @@ def main():
         ms = time_launches(torch, launch, args.steps, args.warmup)
         del keep
         torch.cuda.empty_cache()
-        if fmt == "damp" and budget is not None:
+        if fmt == "damp" and args.window:
+            ab = alg_bytes_window(args.window, d, r, per_key) * units
+        elif fmt == "damp_token":
+            ab = alg_bytes_per_update("damp", d, r, per_key) * units
+        elif fmt == "damp" and budget is not None:
             ab = sum(alg_bytes_per_update(fmt, d, int(rh), per_key) for rh in budget["r_per_head"]) * B
         else:
             ab = alg_bytes_per_update(fmt, d, r, per_key) * units
@@ -317,6 +353,8 @@ def main():
                 "alg_bytes_per_launch": ab, "gbs": ab / (ms * 1e-3) / 1e9}
 
     fmts = [args.only] if args.only else (["damp"] if args.no_baselines else ["damp", "fp32", "int8"])
+    if args.window and not args.only:
+        fmts.insert(1, "damp_token")   # the per-token step on the same pool, for comparison
     for f in fmts:
         results[f] = run(f)
         print(f"# {args.workload} {f}: {results[f]['ms_per_step'] * 1e3:.1f} us/step, "
@@ -345,7 +383,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": m["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": m["gbs"] / PEAK_HBM_GBS,
                      "traffic": measured_traffic() if (main_fmt == "damp" and args.workload == "pool4096"
-                                                       and budget is None) else None},
+                                                       and budget is None and not args.window
+                                                       and not args.fused_prestep) else None},
     }
     if budget is not None:
         line["config"]["layout"] = {k: v for k, v in budget.items() if k != "row_map"}
