@@ -71,6 +71,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_window_step.restype = I
         L.oracle_window_flush.argtypes = [I, Lg, P, P, P, P, P, P]
         L.oracle_window_flush.restype = I
+        L.oracle_stq_quantize.argtypes = [I, Lg, P, P, P, P, P, P, P]
+        L.oracle_stq_quantize.restype = I
+        L.oracle_stq_dequantize.argtypes = [I, Lg, P, P, P, P, P, P]
+        L.oracle_stq_dequantize.restype = I
+        L.oracle_stq_step.argtypes = [I, Lg, P, P, P, P, P, P, P, P, P, P, P, P, P, P, I, P, P, I]
+        L.oracle_stq_step.restype = I
         _lib = L
     return _lib
 
@@ -274,3 +280,48 @@ class Window:
         rc = lib().oracle_window_flush(D, n, _p(self.mask), _p(self.h), _p(self.c), _p(self.s),
                                        _p(self.Sx), _p(self.t))
         assert rc == 0
+
+
+# ---- STEPQuant-style state -------------------------------------------------------------------
+def stq_quantize(bits, w, S):
+    """fp32 states ``S[n, D, D]`` -> ``(h, c, rf, cs)`` for per-row code widths ``bits[n, D]``
+    (16 = pivot, 8, 6, 4) and row-impact scores ``w[n, D]``."""
+    S = _c(S, np.float32)
+    n, D, _ = S.shape
+    bits = _c(np.broadcast_to(bits, (n, D)), np.uint8)
+    w = _c(np.broadcast_to(w, (n, D)), np.float32)
+    h = np.empty((n, D, D), np.uint16)
+    c = np.empty((n, D, D), np.int8)
+    rf = np.empty((n, D), np.uint16)
+    cs = np.empty((n, D), np.uint16)
+    rc = lib().oracle_stq_quantize(D, n, _p(bits), _p(w), _p(S), _p(h), _p(c), _p(rf), _p(cs))
+    assert rc == 0
+    return h, c, rf, cs
+
+
+def stq_dequantize(bits, h, c, rf, cs):
+    h, c = _c(h, np.uint16), _c(c, np.int8)
+    rf, cs = _c(rf, np.uint16), _c(cs, np.uint16)
+    n, D, _ = c.shape
+    bits = _c(np.broadcast_to(bits, (n, D)), np.uint8)
+    S = np.empty((n, D, D), np.float32)
+    rc = lib().oracle_stq_dequantize(D, n, _p(bits), _p(h), _p(c), _p(rf), _p(cs), _p(S))
+    assert rc == 0
+    return S
+
+
+def stq_step(bits, w, h, c, rf, cs, q, k, v, alpha, beta, nthreads: int | None = None):
+    """One step; returns ``(out [n, D], (h2, c2, rf2, cs2))`` (the inputs are not modified)."""
+    h, c = _c(h, np.uint16), _c(c, np.int8)
+    rf, cs = _c(rf, np.uint16), _c(cs, np.uint16)
+    n, D, _ = c.shape
+    bits = _c(np.broadcast_to(bits, (n, D)), np.uint8)
+    w = _c(np.broadcast_to(w, (n, D)), np.float32)
+    q, k, v, alpha, per_key, beta = _vecs(q, k, v, alpha, beta, n, D)
+    h2, c2, rf2, cs2 = np.empty_like(h), np.empty_like(c), np.empty_like(rf), np.empty_like(cs)
+    out = np.empty((n, D), np.float32)
+    rc = lib().oracle_stq_step(D, n, _p(bits), _p(w), _p(h), _p(c), _p(rf), _p(cs), _p(h2), _p(c2),
+                               _p(rf2), _p(cs2), _p(q), _p(k), _p(v), _p(alpha), per_key, _p(beta),
+                               _p(out), nthreads or default_threads())
+    assert rc == 0
+    return out, (h2, c2, rf2, cs2)

@@ -542,3 +542,176 @@ int oracle_window_flush(int D, long n_units, const uint8_t* mask, uint16_t* h, i
   free(rowbuf);
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * STEPQuant-style state (the STEPQuant page: Table C2 steps 1-6, Table C1 for KDA, Table D3).
+ * Each key row of a head is a pivot (kept in FP16) or an integer row with its own code width
+ * b in {4, 6, 8} (a frozen precision map); the integer rows share one column-scale vector per
+ * head and carry one row factor each, both stored in FP16; entry (i, j) of an integer row is
+ * code_ij * rf_i * cs_j. The page names the fit (key-row-aware dual-axis fitting; for KDA one
+ * shared column-scale vector fitted with squared row-impact factors over all non-pivot integer
+ * rows) but not its formulas; the reading taken here, for the non-pivot rows N of a unit:
+ *   cs_j = fp16( sqrt( sum_{i in N} w_i^2 X_ij^2 / sum_{i in N} w_i^2 ) )   (binary64, then
+ *          binary16 RNE; all w_i = 0 is read as all w_i = 1)
+ *   rf_i = fp16( fl32( max_{j: cs_j > 0} fl32(|X_ij| / cs_j) / qmax_i ) ),  qmax = 2^(b-1) - 1
+ *   code = clamp(rint(fl32(X_ij / fl32(rf_i cs_j))), -qmax, qmax) when rf_i cs_j > 0, else 0
+ * with w_i the row-impact score (an input, as on the page). rf_i cs_j is exact in binary32 (two
+ * 11-bit significands), so the decisions are taken in binary32 on that product.
+ * Logical arrays per unit: bits [D] (16 = pivot, or 8, 6, 4), w [D], h [D][D] (binary16 bits of
+ * the pivot rows, 0 elsewhere), c [D][D] (codes, 0 on pivot rows), rf [D] (binary16 bits, 0 on
+ * pivot rows), cs [D] (binary16 bits).
+ * ---------------------------------------------------------------------------------------- */
+static int stq_qmax(int b) { return (1 << (b - 1)) - 1; }
+
+static void stq_store_unit(int D, const uint8_t* bits, const float* w, const float* X,
+                           uint16_t* h, int8_t* c, uint16_t* rf, uint16_t* cs) {
+  double sw = 0.0;
+  for (int i = 0; i < D; ++i)
+    if (bits[i] != 16) sw += (double)w[i] * (double)w[i];
+  const int unweighted = !(sw > 0.0);
+  if (unweighted) {
+    sw = 0.0;
+    for (int i = 0; i < D; ++i)
+      if (bits[i] != 16) sw += 1.0;
+  }
+  for (int j = 0; j < D; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < D; ++i) {
+      if (bits[i] == 16) continue;
+      const double wi = unweighted ? 1.0 : (double)w[i];
+      acc += wi * wi * (double)X[(long)i * D + j] * (double)X[(long)i * D + j];
+    }
+    cs[j] = sw > 0.0 ? oracle_f16_from_f32((float)sqrt(acc / sw)) : 0;
+  }
+  for (int i = 0; i < D; ++i) {
+    const float* x = X + (long)i * D;
+    if (bits[i] == 16) {
+      for (int j = 0; j < D; ++j) {
+        h[(long)i * D + j] = oracle_f16_from_f32(x[j]);
+        c[(long)i * D + j] = 0;
+      }
+      rf[i] = 0;
+      continue;
+    }
+    const int qm = stq_qmax(bits[i]);
+    float m = 0.0f;
+    for (int j = 0; j < D; ++j) {
+      const float csj = oracle_f32_from_f16(cs[j]);
+      if (csj > 0.0f) {
+        const float a = fabsf(x[j]) / csj;
+        if (a > m) m = a;
+      }
+    }
+    rf[i] = oracle_f16_from_f32(m / (float)qm);
+    const float rfi = oracle_f32_from_f16(rf[i]);
+    for (int j = 0; j < D; ++j) {
+      h[(long)i * D + j] = 0;
+      const float sc = rfi * oracle_f32_from_f16(cs[j]); /* exact */
+      float code = 0.0f;
+      if (sc > 0.0f) {
+        code = nearbyintf(x[j] / sc);
+        if (code > (float)qm) code = (float)qm;
+        if (code < (float)-qm) code = (float)-qm;
+      }
+      c[(long)i * D + j] = (int8_t)code;
+    }
+  }
+}
+
+static double stq_recon(int D, const uint8_t* bits, const uint16_t* h, const int8_t* c,
+                        const uint16_t* rf, const uint16_t* cs, int i, int j) {
+  if (bits[i] == 16) return (double)oracle_f32_from_f16(h[(long)i * D + j]);
+  return (double)c[(long)i * D + j] * (double)oracle_f32_from_f16(rf[i]) *
+         (double)oracle_f32_from_f16(cs[j]);
+}
+
+static int stq_bits_ok(int D, const uint8_t* bits) {
+  for (int i = 0; i < D; ++i)
+    if (bits[i] != 16 && bits[i] != 8 && bits[i] != 6 && bits[i] != 4) return 0;
+  return 1;
+}
+
+int oracle_stq_quantize(int D, long n, const uint8_t* bits, const float* w, const float* S,
+                        uint16_t* h, int8_t* c, uint16_t* rf, uint16_t* cs) {
+  if (D <= 0 || n < 0 || !bits || !w || !S || !h || !c || !rf || !cs) return -1;
+  const long DD = (long)D * D;
+  for (long u = 0; u < n; ++u) {
+    if (!stq_bits_ok(D, bits + u * D)) return -1;
+    stq_store_unit(D, bits + u * D, w + u * D, S + u * DD, h + u * DD, c + u * DD, rf + u * D,
+                   cs + u * D);
+  }
+  return 0;
+}
+
+int oracle_stq_dequantize(int D, long n, const uint8_t* bits, const uint16_t* h,
+                          const int8_t* c, const uint16_t* rf, const uint16_t* cs, float* S) {
+  if (D <= 0 || n < 0 || !bits || !h || !c || !rf || !cs || !S) return -1;
+  const long DD = (long)D * D;
+  for (long u = 0; u < n; ++u)
+    for (int i = 0; i < D; ++i)
+      for (int j = 0; j < D; ++j)
+        S[u * DD + (long)i * D + j] = (float)stq_recon(D, bits + u * D, h + u * DD, c + u * DD,
+                                                       rf + u * D, cs + u * D, i, j);
+  return 0;
+}
+
+/* One decode step on STEPQuant-style states: Table C2 steps 1-3 as in oracle_step (binary64,
+ * X rounded once to binary32), then steps 4-6 with the fit above. The new state goes to
+ * (h2, c2, rf2, cs2), which may be the input arrays (in place) or others (the old
+ * representation kept for its readers, Table C2 step 6). */
+int oracle_stq_step(int D, long n, const uint8_t* bits, const float* w, const uint16_t* h,
+                    const int8_t* c, const uint16_t* rf, const uint16_t* cs, uint16_t* h2,
+                    int8_t* c2, uint16_t* rf2, uint16_t* cs2, const float* q, const float* k,
+                    const float* v, const float* alpha, int per_key, const float* beta,
+                    float* out, int nthreads) {
+  if (D <= 0 || n < 0 || !bits || !w || !h || !c || !rf || !cs || !h2 || !c2 || !rf2 || !cs2 ||
+      !q || !k || !v || !alpha || !beta || !out)
+    return -1;
+  const long DD = (long)D * D;
+  for (long u = 0; u < n; ++u)
+    if (!stq_bits_ok(D, bits + u * D)) return -1;
+  int bad = 0;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+  {
+    double* X = (double*)malloc(sizeof(double) * (size_t)(DD + D));
+    float* Xf = (float*)malloc(sizeof(float) * (size_t)DD);
+    if (!X || !Xf) {
+#pragma omp atomic write
+      bad = 1;
+    }
+#pragma omp for schedule(static)
+    for (long un = 0; un < n; ++un) {
+      if (!X || !Xf) continue;
+      double* uu = X + DD;
+      const uint8_t* bt = bits + un * D;
+      const float* ku = k + un * D;
+      const float* qu = q + un * D;
+      const float* vu = v + un * D;
+      const float* au = per_key ? alpha + un * D : alpha + un;
+      for (int i = 0; i < D; ++i) {
+        const double a = (double)(per_key ? au[i] : au[0]);
+        for (int j = 0; j < D; ++j)
+          X[(long)i * D + j] = a * stq_recon(D, bt, h + un * DD, c + un * DD, rf + un * D,
+                                             cs + un * D, i, j);
+      }
+      for (int j = 0; j < D; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < D; ++i) acc += (double)ku[i] * X[(long)i * D + j];
+        uu[j] = acc;
+      }
+      for (int i = 0; i < D; ++i)
+        for (int j = 0; j < D; ++j)
+          X[(long)i * D + j] += (double)ku[i] * ((double)beta[un] * ((double)vu[j] - uu[j]));
+      for (int j = 0; j < D; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < D; ++i) acc += (double)qu[i] * X[(long)i * D + j];
+        out[un * D + j] = (float)acc;
+      }
+      for (long e = 0; e < DD; ++e) Xf[e] = (float)X[e];
+      stq_store_unit(D, bt, w + un * D, Xf, h2 + un * DD, c2 + un * DD, rf2 + un * D, cs2 + un * D);
+    }
+    free(X);
+    free(Xf);
+  }
+  return bad ? -1 : 0;
+}

@@ -107,6 +107,22 @@ int oracle_window_step(int D, long n_units, const uint8_t* mask, uint16_t* h, in
 int oracle_window_flush(int D, long n_units, const uint8_t* mask, uint16_t* h, int8_t* c,
                         float* s, const double* Sx, int32_t* t);
 
+/* STEPQuant-style state: pivot rows in FP16, integer rows with per-row code widths {4, 6, 8},
+ * one FP16 row factor per integer row and one FP16 column-scale vector per unit, fitted from X
+ * with squared row-impact weights (the fit is written out in oracle.c).
+ *   bits [n][D] (16 = pivot, 8, 6, 4), w [n][D] row-impact scores, h [n][D][D] binary16 pivot
+ *   values, c [n][D][D] codes, rf [n][D] and cs [n][D] binary16 bits.
+ * oracle_stq_step writes the new state to (h2, c2, rf2, cs2), which may alias the inputs. */
+int oracle_stq_quantize(int D, long n, const uint8_t* bits, const float* w, const float* S,
+                        uint16_t* h, int8_t* c, uint16_t* rf, uint16_t* cs);
+int oracle_stq_dequantize(int D, long n, const uint8_t* bits, const uint16_t* h,
+                          const int8_t* c, const uint16_t* rf, const uint16_t* cs, float* S);
+int oracle_stq_step(int D, long n, const uint8_t* bits, const float* w, const uint16_t* h,
+                    const int8_t* c, const uint16_t* rf, const uint16_t* cs, uint16_t* h2,
+                    int8_t* c2, uint16_t* rf2, uint16_t* cs2, const float* q, const float* k,
+                    const float* v, const float* alpha, int per_key, const float* beta,
+                    float* out, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
