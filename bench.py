@@ -33,7 +33,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "damp_step_pool4096_hbm_traffic.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "quantized_delta_rule_gdn_amd", "csrc", "step_kernels.hip")
+# the DAMP step's kernel source: its building blocks and its kernels
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_delta_rule_gdn_amd", "csrc", f)
+                  for f in ("step_common.h", "step_kernels.hip")]
 
 
 def measured_traffic():
@@ -48,7 +50,7 @@ def measured_traffic():
             if line and not line.startswith("#") and "=" in line:
                 key, val = (x.strip() for x in line.split("=", 1))
                 kv[key] = val
-        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()
     except OSError:
         return None
     if kv.get("kernel_source_sha256") != sha:

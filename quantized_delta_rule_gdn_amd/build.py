@@ -15,8 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdamp.so")
-SOURCES = [os.path.join(CSRC, "damp_api.hip"), os.path.join(CSRC, "step_kernels.hip"),
-           os.path.join(CSRC, "calib_kernels.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("damp_api.hip", "step_kernels.hip", "window_kernels.hip", "calib_kernels.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -37,19 +37,38 @@ FLAGS = [
 ]
 
 
+def _compile(src: str, obj: str, extra: list[str]) -> tuple[int, str]:
+    flags = [f for f in FLAGS if f != "-shared"]
+    res = subprocess.run([HIPCC, *flags, *extra, "-c", src, "-o", obj], capture_output=True, text=True)
+    return res.returncode, res.stdout + res.stderr
+
+
 def build(resource_usage: bool = False, verbose: bool = False) -> str:
+    """Compile every source to an object in parallel (one hipcc per file), then link."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if msgs and (verbose or resource_usage):
-        print("\n".join(msgs))
+    with tempfile.TemporaryDirectory(prefix="damp_build_") as tmpd:
+        objs = [os.path.join(tmpd, os.path.basename(s) + ".o") for s in SOURCES]
+        if verbose:
+            print(f"{HIPCC} {' '.join(FLAGS)} -c <each of {len(SOURCES)} sources>", flush=True)
+        jobs = min(len(SOURCES), os.cpu_count() or 1, 16)
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            results = list(ex.map(lambda so: _compile(so[0], so[1], extra), zip(SOURCES, objs)))
+        msgs = []
+        for (rc, out), src in zip(results, SOURCES):
+            lines = [ln for ln in out.splitlines() if noise not in ln]
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n" + "\n".join(lines))
+            msgs.extend(lines)
+        if msgs and (verbose or resource_usage):
+            print("\n".join(msgs))
+        tmp = LIB + ".tmp"
+        res = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+                             capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
     os.replace(tmp, LIB)
     return LIB
 
