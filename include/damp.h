@@ -318,6 +318,65 @@ damp_status damp_allocate_rows(const double* score, int32_t num_heads, int32_t d
                                int32_t g, int32_t r_max, int32_t* r_out, int32_t* map_out,
                                void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * STEPQuant-style state ([C2] Table C2 steps 1-6; Table C1: for KDA the allocation unit is the
+ * key row and the integer widths at a 6-bit budget are {4, 6, 8}; Table D3: FP16 scales and
+ * pivots). Each key row of a head is a pivot kept in FP16 or an integer row of 8, 6 or 4 bits,
+ * fixed per head by a frozen precision map; the integer rows carry one FP16 row factor each and
+ * share one FP16 column-scale vector per (slot, head); entry (i, j) of an integer row is
+ * code * rf_i * cs_j. Each step refits the scales to the new state X, for the integer rows N:
+ *   cs_j = fp16( sqrt( sum_{i in N} w_i^2 X_ij^2 / sum_{i in N} w_i^2 ) )
+ *   rf_i = fp16( max_{j: cs_j > 0} (|X_ij| / cs_j) / qmax_i ),   qmax = 2^(b - 1) - 1
+ *   code = clamp(rint(X_ij / (rf_i cs_j)), -qmax, qmax), 0 where rf_i cs_j = 0
+ * with w_i the frozen row-impact score (all w_i = 0 in a head means equal weights), binary32
+ * divisions and binary16 round-to-nearest-even. The page names this fit (key-row-aware
+ * dual-axis fitting, one shared column-scale vector fitted with squared row-impact factors) but
+ * prints no formula: the formulas are the library's reading.
+ * Block of (slot, head): storage rows ordered pivots, 8-bit, 6-bit, 4-bit (each by ascending key
+ * index): FP16 pivot rows (2 d bytes each) | 8-bit rows (d bytes) | 6-bit rows (3 d / 4 bytes: d / 2
+ * bytes of low nibbles, then d / 4 bytes of the top two bits: column c at bits 4 (c mod 2) of byte
+ * c / 2 and 2 (c mod 4) of byte c / 4) | 4-bit rows (d / 2 bytes, nibbles as in the 6-bit rows' low
+ * plane) | FP16 row factors of the
+ * integer rows (storage order) | FP16 column scales (d) | zero padding to 256 bytes; codes are two's
+ * complement. A slot is its heads' blocks in order. Supported: d_k = d_v = d in {64, 128}.
+ * ------------------------------------------------------------------------------------- */
+typedef struct stq_state stq_state;
+
+/* Device bytes of a pool of num_slots slots for the precision map row_bits (host uint8
+ * [num_heads][d], each 16 (pivot), 8, 6 or 4), or 0 if invalid. */
+size_t stq_state_bytes(int32_t num_slots, int32_t num_heads, int32_t d, const uint8_t* row_bits);
+
+/* Bind a caller-owned pool (256-byte aligned, >= stq_state_bytes) to a precision map and the
+ * row-impact scores impact (host fp32 [num_heads][d], finite, >= 0). Allocates a device table of
+ * num_heads * (5 d + 16) bytes, copied synchronously. Errors: INVALID_ARGUMENT, UNSUPPORTED (d),
+ * OUT_OF_MEMORY, HIP. */
+damp_status stq_state_alloc(int32_t num_slots, int32_t num_heads, int32_t d,
+                            const uint8_t* row_bits, const float* impact, void* pool,
+                            size_t pool_bytes, stq_state** out);
+
+damp_status stq_state_free(stq_state* state);
+
+/* Byte offset of each head's block inside a slot (host int64 [num_heads] or NULL) and the bytes
+ * of a slot (or NULL). */
+damp_status stq_state_head_info(const stq_state* state, int64_t* offset_out, int64_t* slot_bytes);
+
+/* Pack fp32 states S[n][num_heads][d][d] (key rows in original order) with the fit above, into
+ * the slots slot_idx[n]; and the reverse (code * rf * cs in binary32, FP16 pivots widened). */
+damp_status stq_state_quantize(stq_state* state, const float* S, const int32_t* slot_idx,
+                               int32_t n, void* stream);
+damp_status stq_state_dequantize(const stq_state* state, float* S, const int32_t* slot_idx,
+                                 int32_t n, void* stream);
+
+/* One decode step on the STEPQuant-style state ([C2] Table C2 steps 1-6): reconstruct, decay,
+ * update, readout y = X^T q before requantization, refit and pack. dst_pool: NULL writes the new
+ * state in place; otherwise a second pool of the same layout receives it and the state bound to
+ * the handle is only read (step 6: the old representation stays valid until its readers finish;
+ * the caller then binds the other pool or copies). Other arguments as in damp_decode_step. */
+damp_status stq_decode_step(stq_state* state, void* dst_pool, const int32_t* slot_idx, int32_t B,
+                            const void* q, const void* k, const void* v, damp_dtype qkv_dtype,
+                            const float* alpha, damp_decay decay, const float* beta, float* out,
+                            void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). The string
  * is owned by the library and valid until the thread's next call. */
 const char* damp_last_error(void);

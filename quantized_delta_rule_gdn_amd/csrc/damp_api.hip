@@ -28,6 +28,14 @@ struct damp_state {
   int32_t r_or, r_max;            // bitwise OR and maximum of head_r
 };
 
+struct stq_state {
+  int32_t num_slots, num_heads, d;
+  uint8_t* pool;
+  size_t slot_bytes;
+  std::vector<int64_t> head_off;
+  uint8_t* table_dev;   // rowmap [H][d] (uint8) | w2 [H][d] (fp32) | heads [H] (int4)
+};
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -188,6 +196,51 @@ damp_status debug_check_slots(const int32_t* slot_idx, int32_t n, int32_t num_sl
 damp_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(DAMP_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+// ---- STEPQuant-style layout (stq_*) ----------------------------------------------------------
+bool stq_supported_d(int32_t d) { return d == 64 || d == 128; }
+
+size_t stq_block_bytes(int32_t d_, int n16, int n8, int n6, int n4) {
+  const size_t d = static_cast<size_t>(d_);
+  return 2 * d * n16 + d * n8 + (3 * d / 4) * n6 + (d / 2) * n4 + 2 * (d - n16) + 2 * d;
+}
+
+// Per-head counts of each code width; row_bits must hold 16, 8, 6 or 4.
+damp_status stq_counts(int32_t H, int32_t d, const uint8_t* row_bits, std::vector<int>* counts) {
+  if (!row_bits) return fail(DAMP_ERR_INVALID_ARGUMENT, "row_bits is NULL");
+  counts->assign(static_cast<size_t>(H) * 4, 0);
+  for (int32_t h = 0; h < H; ++h)
+    for (int32_t i = 0; i < d; ++i) {
+      const int b = row_bits[static_cast<size_t>(h) * d + i];
+      const int k = b == 16 ? 0 : b == 8 ? 1 : b == 6 ? 2 : b == 4 ? 3 : -1;
+      if (k < 0)
+        return fail(DAMP_ERR_INVALID_ARGUMENT, "row_bits[%d][%d] = %d is not 16, 8, 6 or 4", h, i, b);
+      (*counts)[static_cast<size_t>(h) * 4 + k] += 1;
+    }
+  return DAMP_OK;
+}
+
+damp_status stq_check_dims(int32_t num_slots, int32_t H, int32_t d) {
+  if (num_slots <= 0 || H <= 0)
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "num_slots (%d) and num_heads (%d) must be positive", num_slots, H);
+  if (!stq_supported_d(d))
+    return fail(DAMP_ERR_UNSUPPORTED, "d = %d: the STEPQuant-style state supports d in {64, 128}", d);
+  return DAMP_OK;
+}
+
+damp::StqArgs stq_args(const stq_state* s) {
+  damp::StqArgs a{};
+  const size_t H = static_cast<size_t>(s->num_heads), d = static_cast<size_t>(s->d);
+  a.pool = s->pool;
+  a.slot_stride = static_cast<int64_t>(s->slot_bytes);
+  a.rowmap = s->table_dev;
+  a.w2 = reinterpret_cast<const float*>(s->table_dev + H * d);
+  a.heads = reinterpret_cast<const int4*>(s->table_dev + H * d + 4 * H * d);
+  a.H = s->num_heads;
+  a.step.st.rowmap = s->table_dev;
+  a.step.H = s->num_heads;
+  return a;
 }
 
 damp::StateRef damp_ref(const damp_state* s) {
@@ -670,6 +723,164 @@ damp_status damp_allocate_rows(const double* score, int32_t H, int32_t d, int64_
   return launched(damp::launch_allocate_rows(score, H, d, R, g, r_max, r_out, map_out,
                                              static_cast<hipStream_t>(stream)),
                   "allocate rows");
+}
+
+size_t stq_state_bytes(int32_t num_slots, int32_t H, int32_t d, const uint8_t* row_bits) {
+  if (stq_check_dims(num_slots, H, d) != DAMP_OK) return 0;
+  std::vector<int> cnt;
+  if (stq_counts(H, d, row_bits, &cnt) != DAMP_OK) return 0;
+  size_t slot = 0;
+  for (int32_t h = 0; h < H; ++h)
+    slot += round_up(stq_block_bytes(d, cnt[4 * h], cnt[4 * h + 1], cnt[4 * h + 2], cnt[4 * h + 3]), kBlockAlign);
+  if (slot != 0 && static_cast<size_t>(num_slots) > SIZE_MAX / slot) return 0;
+  return static_cast<size_t>(num_slots) * slot;
+}
+
+damp_status stq_state_alloc(int32_t num_slots, int32_t H, int32_t d, const uint8_t* row_bits,
+                            const float* impact, void* pool, size_t pool_bytes, stq_state** out) {
+  if (!out) return fail(DAMP_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  damp_status st = stq_check_dims(num_slots, H, d);
+  if (st != DAMP_OK) return st;
+  std::vector<int> cnt;
+  st = stq_counts(H, d, row_bits, &cnt);
+  if (st != DAMP_OK) return st;
+  if (!impact) return fail(DAMP_ERR_INVALID_ARGUMENT, "impact is NULL");
+  for (size_t e = 0; e < static_cast<size_t>(H) * d; ++e)
+    if (!(impact[e] >= 0.0f) || impact[e] > 1e18f)
+      return fail(DAMP_ERR_INVALID_ARGUMENT, "impact[%zu] must be finite and >= 0", e);
+  if (!pool) return fail(DAMP_ERR_INVALID_ARGUMENT, "pool is NULL");
+  if (!aligned(pool, kBlockAlign)) return fail(DAMP_ERR_INVALID_ARGUMENT, "pool must be 256-byte aligned");
+  const size_t need = stq_state_bytes(num_slots, H, d, row_bits);
+  if (need == 0) return fail(DAMP_ERR_INVALID_ARGUMENT, "pool size overflows size_t");
+  if (pool_bytes < need) return fail(DAMP_ERR_INVALID_ARGUMENT, "pool_bytes %zu < %zu needed", pool_bytes, need);
+  const size_t Hs = static_cast<size_t>(H), ds = static_cast<size_t>(d);
+  // device table: rowmap (storage order: pivots, 8-bit, 6-bit, 4-bit, each ascending) | w2 | heads
+  std::vector<uint8_t> blob(Hs * ds + 4 * Hs * ds + 16 * Hs, 0);
+  float* w2 = reinterpret_cast<float*>(blob.data() + Hs * ds);
+  int32_t* heads = reinterpret_cast<int32_t*>(blob.data() + Hs * ds + 4 * Hs * ds);
+  stq_state* s = new (std::nothrow) stq_state{};
+  if (!s) return fail(DAMP_ERR_OUT_OF_MEMORY, "host allocation of the handle failed");
+  s->num_slots = num_slots;
+  s->num_heads = H;
+  s->d = d;
+  s->pool = static_cast<uint8_t*>(pool);
+  s->head_off.resize(Hs);
+  size_t off = 0;
+  static const int kWidths[4] = {16, 8, 6, 4};
+  for (int32_t h = 0; h < H; ++h) {
+    const uint8_t* bits = row_bits + static_cast<size_t>(h) * d;
+    const float* w = impact + static_cast<size_t>(h) * d;
+    double sw = 0.0;
+    for (int32_t i = 0; i < d; ++i)
+      if (bits[i] != 16) sw += static_cast<double>(w[i]) * w[i];
+    const bool unweighted = !(sw > 0.0);
+    int p = 0;
+    double swf = 0.0;
+    for (int k = 0; k < 4; ++k)
+      for (int32_t i = 0; i < d; ++i) {
+        if (bits[i] != kWidths[k]) continue;
+        blob[static_cast<size_t>(h) * d + p] = static_cast<uint8_t>(i);
+        const float wi = k == 0 ? 0.0f : (unweighted ? 1.0f : w[i]);
+        w2[static_cast<size_t>(h) * d + p] = wi * wi;
+        swf += static_cast<double>(wi) * wi;
+        ++p;
+      }
+    s->head_off[static_cast<size_t>(h)] = static_cast<int64_t>(off);
+    heads[4 * h] = static_cast<int32_t>(off);
+    heads[4 * h + 1] = cnt[4 * h] | (cnt[4 * h + 1] << 8) | (cnt[4 * h + 2] << 16) | (cnt[4 * h + 3] << 24);
+    const float swv = static_cast<float>(swf);
+    std::memcpy(&heads[4 * h + 2], &swv, 4);
+    off += round_up(stq_block_bytes(d, cnt[4 * h], cnt[4 * h + 1], cnt[4 * h + 2], cnt[4 * h + 3]), kBlockAlign);
+  }
+  s->slot_bytes = off;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&s->table_dev), blob.size());
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    delete s;
+    return fail(e == hipErrorOutOfMemory ? DAMP_ERR_OUT_OF_MEMORY : DAMP_ERR_HIP, "hipMalloc of the table: %s",
+                hipGetErrorString(e));
+  }
+  e = hipMemcpy(s->table_dev, blob.data(), blob.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(s->table_dev);
+    delete s;
+    return fail(DAMP_ERR_HIP, "copying the table: %s", hipGetErrorString(e));
+  }
+  *out = s;
+  return ok();
+}
+
+damp_status stq_state_free(stq_state* s) {
+  if (!s) return ok();
+  const hipError_t e = s->table_dev ? hipFree(s->table_dev) : hipSuccess;
+  delete s;
+  if (e != hipSuccess) return fail(DAMP_ERR_HIP, "hipFree of the table: %s", hipGetErrorString(e));
+  return ok();
+}
+
+damp_status stq_state_head_info(const stq_state* s, int64_t* offset_out, int64_t* slot_bytes) {
+  if (!s) return fail(DAMP_ERR_INVALID_ARGUMENT, "state is NULL");
+  for (size_t h = 0; h < s->head_off.size(); ++h)
+    if (offset_out) offset_out[h] = s->head_off[h];
+  if (slot_bytes) *slot_bytes = static_cast<int64_t>(s->slot_bytes);
+  return ok();
+}
+
+namespace {
+damp_status stq_pack(const stq_state* s, float* S, const int32_t* slot_idx, int32_t n, void* stream, int mode) {
+  if (!s) return fail(DAMP_ERR_INVALID_ARGUMENT, "state is NULL");
+  if (n < 0) return fail(DAMP_ERR_INVALID_ARGUMENT, "n (%d) must be >= 0", n);
+  if (n == 0) return ok();
+  if (!S || !slot_idx) return fail(DAMP_ERR_INVALID_ARGUMENT, "NULL S or slot_idx");
+  if (!aligned(S, 16) || !aligned(slot_idx, 4))
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "S must be 16-byte and slot_idx 4-byte aligned");
+  if (static_cast<int64_t>(n) * s->num_heads > 0x7fffffffLL)
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "n * num_heads exceeds the grid limit");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  damp_status r = debug_check_slots(slot_idx, n, s->num_slots, st);
+  if (r != DAMP_OK) return r;
+  damp::StqArgs a = stq_args(s);
+  a.slot_idx = slot_idx;
+  a.B = n;
+  a.S = S;
+  return launched(damp::launch_stq(mode, s->d, 0, 0, a, st), mode == 1 ? "stq quantize" : "stq dequantize");
+}
+}  // namespace
+
+damp_status stq_state_quantize(stq_state* s, const float* S, const int32_t* slot_idx, int32_t n, void* stream) {
+  return stq_pack(s, const_cast<float*>(S), slot_idx, n, stream, 1);
+}
+
+damp_status stq_state_dequantize(const stq_state* s, float* S, const int32_t* slot_idx, int32_t n, void* stream) {
+  return stq_pack(s, S, slot_idx, n, stream, 2);
+}
+
+damp_status stq_decode_step(stq_state* s, void* dst_pool, const int32_t* slot_idx, int32_t B, const void* q,
+                            const void* k, const void* v, damp_dtype dt, const float* alpha, damp_decay decay,
+                            const float* beta, float* out, void* stream) {
+  if (!s) return fail(DAMP_ERR_INVALID_ARGUMENT, "state is NULL");
+  damp_status st = check_step_args(B, s->num_heads, s->d, slot_idx, q, k, v, dt, alpha, decay, beta, out);
+  if (st != DAMP_OK) return st;
+  if (dst_pool && !aligned(dst_pool, kBlockAlign))
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "dst_pool must be 256-byte aligned");
+  if (B == 0) return ok();
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = debug_check_slots(slot_idx, B, s->num_slots, hs);
+  if (st != DAMP_OK) return st;
+  damp::StqArgs a = stq_args(s);
+  a.dst = static_cast<uint8_t*>(dst_pool);
+  a.slot_idx = slot_idx;
+  a.B = B;
+  a.step.slot_idx = slot_idx;
+  a.step.B = B;
+  a.step.q = q;
+  a.step.k = k;
+  a.step.v = v;
+  a.step.alpha = alpha;
+  a.step.beta = beta;
+  a.step.out = out;
+  return launched(damp::launch_stq(0, s->d, decay == DAMP_DECAY_PER_KEY, dt == DAMP_BF16, a, hs), "stq step");
 }
 
 }  // extern "C"

@@ -72,6 +72,26 @@ hipError_t launch_window(int d, int per_key, int bf16, bool flush_only, const St
                          hipStream_t s);
 int window_max();
 
+// STEPQuant-style state (stq_kernels.hip). The block of (slot, head) is at pool + slot *
+// slot_stride + heads[head].x; heads[head] = {offset, n16 | n8 << 8 | n6 << 16 | n4 << 24,
+// bits of the fp32 sum of w2 over the head's integer rows, 0}; rowmap [H][d] storage row ->
+// key row; w2 [H][d] squared row-impact weights in storage order (0 on pivot rows).
+struct StqArgs {
+  StepArgs step;            // q, k, v, alpha, beta, out and st.rowmap for the step's staging
+  uint8_t* pool;            // source state
+  uint8_t* dst;             // destination state (nullptr = in place)
+  int64_t slot_stride;
+  const int4* heads;
+  const float* w2;
+  const uint8_t* rowmap;
+  const int32_t* slot_idx;
+  int32_t B;                // units = B * H
+  int32_t H;
+  float* S;                 // pack / unpack: fp32 [B][H][d][d], key rows in original order
+};
+// mode 0 = decode step, 1 = pack, 2 = unpack; d is 64 or 128.
+hipError_t launch_stq(int mode, int d, int per_key, int bf16, const StqArgs& a, hipStream_t s);
+
 // Calibration (calib_kernels.hip). Sizes are validated by the caller: d in {16, 32, 64, 128},
 // H * d <= alloc_max_rows(), H * (r_max / g) <= alloc_max_groups(), R % g == 0.
 hipError_t launch_risk_scores(int d, const float* S, int32_t n, int32_t H, const float* abar,

@@ -34,7 +34,8 @@ EXPORTS = (
     "damp_last_error", "damp_abi_version", "damp_state_bytes_per_head",
     "damp_state_alloc_per_head", "damp_state_head_info", "damp_risk_scores", "damp_budget_rows",
     "damp_allocate_rows", "damp_decode_step_fused", "damp_window_bytes", "damp_window_step",
-    "damp_window_flush",
+    "damp_window_flush", "stq_state_bytes", "stq_state_alloc", "stq_state_free",
+    "stq_state_head_info", "stq_state_quantize", "stq_state_dequantize", "stq_decode_step",
 )
 
 
@@ -94,6 +95,14 @@ def load() -> ctypes.CDLL:
         "damp_window_step": ([P, P, I32, P, I32, P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, P],
                              ctypes.c_int),
         "damp_window_flush": ([P, P, I32, P, I32, P], ctypes.c_int),
+        "stq_state_bytes": ([I32, I32, I32, P], SZ),
+        "stq_state_alloc": ([I32, I32, I32, P, P, P, SZ, ctypes.POINTER(P)], ctypes.c_int),
+        "stq_state_free": ([P], ctypes.c_int),
+        "stq_state_head_info": ([P, P, P], ctypes.c_int),
+        "stq_state_quantize": ([P, P, P, I32, P], ctypes.c_int),
+        "stq_state_dequantize": ([P, P, P, I32, P], ctypes.c_int),
+        "stq_decode_step": ([P, P, P, I32, P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, P],
+                            ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -428,3 +437,86 @@ def allocate_rows(score, R: int, g: int = 1, r_max: int | None = None, stream=No
     _check(load().damp_allocate_rows(_ptr(score), H, d, R, g, d if r_max is None else r_max,
                                      _ptr(r), _ptr(m), _stream(stream)))
     return r, m
+
+
+# ------------------------------------------------------------------------------------------
+# STEPQuant-style state
+# ------------------------------------------------------------------------------------------
+class StqState:
+    """A pool in the STEPQuant-style layout bound to its frozen precision map ``row_bits``
+    (uint8 [num_heads, d]: 16 = FP16 pivot, or 8, 6, 4) and row-impact scores ``impact`` (fp32
+    [num_heads, d])."""
+
+    def __init__(self, num_slots: int, num_heads: int, d: int, row_bits, impact, pool=None,
+                 device=None):
+        torch = _torch()
+        self.num_slots, self.num_heads, self.d = num_slots, num_heads, d
+        self.row_bits = np.ascontiguousarray(np.asarray(row_bits, np.uint8).reshape(num_heads, d))
+        self.impact = np.ascontiguousarray(np.asarray(impact, np.float32).reshape(num_heads, d))
+        nbytes = load().stq_state_bytes(num_slots, num_heads, d,
+                                        self.row_bits.ctypes.data_as(ctypes.c_void_p))
+        if nbytes == 0:
+            raise DampError(DAMP_ERR_INVALID_ARGUMENT, "invalid or unsupported layout")
+        self.nbytes = nbytes
+        if pool is None:
+            pool = torch.zeros(nbytes, dtype=torch.uint8, device=device if device is not None else "cuda")
+        _need(pool, "pool", torch.uint8, (pool.numel(),))
+        if pool.numel() < nbytes:
+            raise ValueError(f"pool has {pool.numel()} bytes, {nbytes} needed")
+        self.pool = pool
+        h = ctypes.c_void_p()
+        with torch.cuda.device(pool.device):
+            _check(load().stq_state_alloc(num_slots, num_heads, d,
+                                          self.row_bits.ctypes.data_as(ctypes.c_void_p),
+                                          self.impact.ctypes.data_as(ctypes.c_void_p), _ptr(pool),
+                                          pool.numel(), ctypes.byref(h)))
+        self._h = h
+        off = np.empty(num_heads, np.int64)
+        sb = ctypes.c_int64()
+        _check(load().stq_state_head_info(h, off.ctypes.data_as(ctypes.c_void_p), ctypes.byref(sb)))
+        self.head_offsets, self.slot_bytes = off, sb.value
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _check(load().stq_state_free(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def slots(self, pool=None):
+        """A pool as uint8 [num_slots, slot_bytes] (a view)."""
+        p = self.pool if pool is None else pool
+        return p[: self.nbytes].view(self.num_slots, self.slot_bytes)
+
+    def quantize(self, S, slot_idx, stream=None) -> None:
+        torch = _torch()
+        n = slot_idx.shape[0]
+        _need(slot_idx, "slot_idx", torch.int32, (n,), self.pool.device)
+        _need(S, "S", torch.float32, (n, self.num_heads, self.d, self.d), self.pool.device)
+        _check(load().stq_state_quantize(self._h, _ptr(S), _ptr(slot_idx), n, _stream(stream)))
+
+    def dequantize(self, slot_idx, S=None, stream=None):
+        torch = _torch()
+        n = slot_idx.shape[0]
+        _need(slot_idx, "slot_idx", torch.int32, (n,), self.pool.device)
+        if S is None:
+            S = torch.empty((n, self.num_heads, self.d, self.d), dtype=torch.float32, device=self.pool.device)
+        _need(S, "S", torch.float32, (n, self.num_heads, self.d, self.d), self.pool.device)
+        _check(load().stq_state_dequantize(self._h, _ptr(S), _ptr(slot_idx), n, _stream(stream)))
+        return S
+
+    def decode_step(self, slot_idx, q, k, v, alpha, beta, out, dst=None, stream=None) -> None:
+        """One step; ``dst`` (a pool of the same size) receives the new state, else in place."""
+        torch = _torch()
+        B, dt, decay = _step_vectors(slot_idx, q, k, v, alpha, beta, out, self.num_heads, self.d)
+        if dst is not None:
+            _need(dst, "dst", torch.uint8, (dst.numel(),), self.pool.device)
+            if dst.numel() < self.nbytes:
+                raise ValueError(f"dst has {dst.numel()} bytes, {self.nbytes} needed")
+        _check(load().stq_decode_step(self._h, _ptr(dst) if dst is not None else None, _ptr(slot_idx),
+                                      B, _ptr(q), _ptr(k), _ptr(v), dt, _ptr(alpha), decay,
+                                      _ptr(beta), _ptr(out), _stream(stream)))

@@ -290,3 +290,26 @@ def raw_step_inputs(rng: np.random.Generator, B: int, H: int, D: int, decay: int
         raise ValueError(dtype)
     qb, kb, vb = bf16_bits(q), bf16_bits(k), bf16_bits(v)
     return StepInputs(bf16_widen(qb), bf16_widen(kb), bf16_widen(vb), g, b, "bf16", qb, kb, vb)
+
+
+# ---- STEPQuant-style precision maps ----------------------------------------------------------
+STQ_SEED = 1006
+
+
+def stq_map(rng: np.random.Generator, H: int, D: int, pivots: int = 2):
+    """A frozen precision map at a nominal 6-bit budget with row-impact scores: impact
+    lognormal(0, 1) per key row; per head the `pivots` rows of largest impact are FP16 pivots,
+    then the next quarter of the rows by impact 8-bit, the next half 6-bit and the rest 4-bit
+    (integer widths from {4, 6, 8}, mean 6 bits). Returns (row_bits uint8 [H, D], impact float32
+    [H, D])."""
+    impact = np.exp(rng.standard_normal((H, D))).astype(np.float32)
+    bits = np.empty((H, D), np.uint8)
+    for h in range(H):
+        order = np.argsort(-impact[h], kind="stable")
+        rest = D - pivots
+        n8, n6 = rest // 4, rest // 2
+        bits[h, order[:pivots]] = 16
+        bits[h, order[pivots:pivots + n8]] = 8
+        bits[h, order[pivots + n8:pivots + n8 + n6]] = 6
+        bits[h, order[pivots + n8 + n6:]] = 4
+    return bits, impact

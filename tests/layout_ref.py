@@ -117,3 +117,119 @@ def mask_per_head(r_per_head, row_map, D: int) -> np.ndarray:
     for hh in range(H):
         m[hh, row_map[hh, :int(r_per_head[hh])]] = 1
     return m
+
+
+# ---- STEPQuant-style layout (written from include/damp.h) ------------------------------------
+STQ_WIDTHS = (16, 8, 6, 4)
+
+
+def stq_storage(row_bits_h: np.ndarray) -> np.ndarray:
+    """One head's storage order: pivots, 8-bit, 6-bit, 4-bit rows, each ascending."""
+    return np.concatenate([np.flatnonzero(row_bits_h == b) for b in STQ_WIDTHS])
+
+
+def stq_block_bytes(D: int, row_bits_h: np.ndarray) -> int:
+    n = {b: int((row_bits_h == b).sum()) for b in STQ_WIDTHS}
+    raw = 2 * D * n[16] + D * n[8] + 3 * D // 4 * n[6] + D // 2 * n[4] + 2 * (D - n[16]) + 2 * D
+    return (raw + 255) // 256 * 256
+
+
+def _nibbles(codes: np.ndarray) -> np.ndarray:
+    """[rows, D] signed codes -> [rows, D/2] bytes of their low nibbles (column c at bits 4(c%2))."""
+    u = codes.astype(np.int64) & 0xF
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _tops(codes: np.ndarray) -> np.ndarray:
+    u = (codes.astype(np.int64) >> 4) & 0x3
+    return (u[:, 0::4] | (u[:, 1::4] << 2) | (u[:, 2::4] << 4) | (u[:, 3::4] << 6)).astype(np.uint8)
+
+
+def stq_pack(row_bits, h, c, rf, cs) -> np.ndarray:
+    """Logical (n, H, ...) -> uint8 slots [n, slot_bytes]."""
+    n, H, D, _ = c.shape
+    sizes = [stq_block_bytes(D, row_bits[hh]) for hh in range(H)]
+    out = np.zeros((n, sum(sizes)), np.uint8)
+    off = 0
+    for hh in range(H):
+        rb = row_bits[hh]
+        order = stq_storage(rb)
+        parts = []
+        for u in range(n):
+            seg = []
+            for b in STQ_WIDTHS:
+                rows = order[rb[order] == b]
+                if b == 16:
+                    seg.append(np.ascontiguousarray(h[u, hh][rows]).view(np.uint8).ravel())
+                elif b == 8:
+                    seg.append(c[u, hh][rows].view(np.uint8).ravel())
+                elif b == 6:
+                    cc = c[u, hh][rows]
+                    seg.append(np.concatenate([_nibbles(cc), _tops(cc)], axis=1).ravel())
+                else:
+                    seg.append(_nibbles(c[u, hh][rows]).ravel())
+            ints = order[rb[order] != 16]
+            seg.append(np.ascontiguousarray(rf[u, hh][ints]).view(np.uint8).ravel())
+            seg.append(np.ascontiguousarray(cs[u, hh]).view(np.uint8).ravel())
+            parts.append(np.concatenate(seg))
+        blk = np.stack(parts)
+        out[:, off:off + blk.shape[1]] = blk
+        off += sizes[hh]
+    return out
+
+
+def _from_nibbles(b: np.ndarray) -> np.ndarray:
+    lo = (b & 0xF).astype(np.int64)
+    hi = (b >> 4).astype(np.int64)
+    out = np.empty((b.shape[0], 2 * b.shape[1]), np.int64)
+    out[:, 0::2], out[:, 1::2] = lo, hi
+    return out
+
+
+def _from_tops(b: np.ndarray) -> np.ndarray:
+    out = np.empty((b.shape[0], 4 * b.shape[1]), np.int64)
+    for k in range(4):
+        out[:, k::4] = (b >> (2 * k)) & 0x3
+    return out
+
+
+def stq_unpack(row_bits, slots: np.ndarray, D: int):
+    """uint8 slots [n, slot_bytes] -> logical (h, c, rf, cs) in key order."""
+    n = slots.shape[0]
+    H = row_bits.shape[0]
+    h = np.zeros((n, H, D, D), np.uint16)
+    c = np.zeros((n, H, D, D), np.int8)
+    rf = np.zeros((n, H, D), np.uint16)
+    cs = np.zeros((n, H, D), np.uint16)
+    off = 0
+    for hh in range(H):
+        rb = row_bits[hh]
+        order = stq_storage(rb)
+        o = off
+        for b in STQ_WIDTHS:
+            rows = order[rb[order] == b]
+            m = len(rows)
+            if b == 16:
+                nb = 2 * D * m
+                h[:, hh][:, rows, :] = slots[:, o:o + nb].copy().view(np.uint16).reshape(n, m, D)
+            elif b == 8:
+                nb = D * m
+                c[:, hh][:, rows, :] = slots[:, o:o + nb].copy().view(np.int8).reshape(n, m, D)
+            elif b == 6:
+                nb = 3 * D // 4 * m
+                blk = slots[:, o:o + nb].reshape(n * m, 3 * D // 4)
+                v = _from_nibbles(blk[:, :D // 2]) | (_from_tops(blk[:, D // 2:]) << 4)
+                v = np.where(v >= 32, v - 64, v)
+                c[:, hh][:, rows, :] = v.reshape(n, m, D).astype(np.int8)
+            else:
+                nb = D // 2 * m
+                v = _from_nibbles(slots[:, o:o + nb].reshape(n * m, D // 2))
+                v = np.where(v >= 8, v - 16, v)
+                c[:, hh][:, rows, :] = v.reshape(n, m, D).astype(np.int8)
+            o += nb
+        ints = order[rb[order] != 16]
+        rf[:, hh][:, ints] = slots[:, o:o + 2 * len(ints)].copy().view(np.uint16).reshape(n, len(ints))
+        o += 2 * len(ints)
+        cs[:, hh] = slots[:, o:o + 2 * D].copy().view(np.uint16).reshape(n, D)
+        off += stq_block_bytes(D, rb)
+    return h, c, rf, cs

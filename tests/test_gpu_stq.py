@@ -1,0 +1,128 @@
+"""GPU parity of the STEPQuant-style state (stq_state_*, stq_decode_step) against the oracle.
+
+The device fits the column scales from fp32 column sums, the oracle from binary64 ones, so a
+column scale (and with it the row factors and codes of that column) can land one binary16 step
+apart where the sum sits at a rounding tie. Tolerances, from identical input states:
+  FP16 pivots <= 1 ulp; column scales <= 1 binary16 ulp and >= 99% equal; row factors <= 2
+  binary16 ulps (a column scale one ulp off moves the row's largest quotient by up to 2^-10
+  relative, up to two ulps of the row factor) and >= 99% equal;
+  codes |delta| <= 2 everywhere and, where the row factor and column scale agree, >= 99.9% equal
+  with |delta| <= 1; readout as in gpu_common; reconstruction (unpack) bit-exact.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+import oracle  # noqa: E402
+import layout_ref  # noqa: E402
+from gpu_common import _f16_ord, check_readout, ref_vectors, step_tensors, to_dev  # noqa: E402
+from quantized_delta_rule_gdn_amd import lib, synth  # noqa: E402
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def check_stq(bits, got, ref):
+    """bits [H, D]; got / ref = logical (h, c, rf, cs) [n, H, ...]."""
+    hg, cg, rg, sg = got
+    hr, cr, rr, sr = ref
+    n, H, D, _ = cg.shape
+    piv = np.broadcast_to(bits == 16, (n, H, D))
+    ulp = np.abs(_f16_ord(hg[piv]) - _f16_ord(hr[piv])) if piv.any() else np.zeros(1)
+    assert ulp.max() <= 1, f"pivots: {ulp.max()} ulp"
+    dcs = np.abs(_f16_ord(sg) - _f16_ord(sr))
+    assert dcs.max() <= 1 and (dcs == 0).mean() >= 0.99, f"column scales: max {dcs.max()}, eq {(dcs == 0).mean()}"
+    ints = ~piv
+    drf = np.abs(_f16_ord(rg[ints]) - _f16_ord(rr[ints]))
+    assert drf.max() <= 2 and (drf == 0).mean() >= 0.99, f"row factors: max {drf.max()}, eq {(drf == 0).mean()}"
+    dc = np.abs(cg.astype(np.int32) - cr.astype(np.int32))
+    m = np.broadcast_to(ints[..., None], dc.shape)
+    assert dc[m].max() <= 2
+    same = m & (rg == rr)[..., None] & (sg == sr)[:, :, None, :]
+    eq = float((dc[same] == 0).mean())
+    assert dc[same].max() <= 1 and eq >= 0.999, f"codes: eq {eq}, max {dc[same].max()}"
+    return {"cs_eq": float((dcs == 0).mean()), "rf_eq": float((drf == 0).mean()), "code_eq": eq}
+
+
+def _state(seed, n, H, D, pivots=2):
+    rng = np.random.default_rng(seed)
+    bits, impact = synth.stq_map(rng, H, D, pivots)
+    S = synth.normal_states(rng, (n, H, D, D), 0.1)
+    for h in range(H):
+        S[:, h, rng.choice(D, 3, replace=False), :] *= 8
+        S[:, h, :, rng.choice(D, 3, replace=False)] *= 5
+    return rng, bits, impact, S
+
+
+def _oracle_logical(bits, impact, S):
+    n, H, D, _ = S.shape
+    b = np.broadcast_to(bits, (n, H, D)).reshape(n * H, D)
+    w = np.broadcast_to(impact, (n, H, D)).reshape(n * H, D)
+    out = oracle.stq_quantize(b, w, S.reshape(n * H, D, D))
+    return tuple(x.reshape((n, H) + x.shape[1:]) for x in out)
+
+
+@pytest.mark.parametrize("D,H,n,pivots", [(128, 4, 3, 2), (64, 3, 5, 0), (128, 2, 2, 5)])
+def test_pack_and_unpack(D, H, n, pivots):
+    rng, bits, impact, S = _state(D + n + pivots, n, H, D, pivots)
+    st = lib.StqState(2 * n, H, D, bits, impact)
+    assert st.slot_bytes == sum(layout_ref.stq_block_bytes(D, bits[h]) for h in range(H))
+    slots = torch.tensor(np.random.default_rng(n).choice(2 * n, n, replace=False), dtype=torch.int32, device="cuda")
+    st.quantize(to_dev(S), slots)
+    back = st.dequantize(slots)
+    torch.cuda.synchronize()
+    got = layout_ref.stq_unpack(bits, st.slots()[slots.long()].cpu().numpy(), D)
+    _log(str(check_stq(bits, got, _oracle_logical(bits, impact, S))))
+    # unpack reconstructs the stored bytes exactly
+    b = np.broadcast_to(bits, (n, H, D)).reshape(n * H, D)
+    ref = oracle.stq_dequantize(b, *(x.reshape((n * H,) + x.shape[2:]) for x in got))
+    assert np.array_equal(back.cpu().numpy(), ref.reshape(n, H, D, D))
+
+
+def _step_case(D, H, B, decay, dtype, pivots, seed, inplace):
+    rng, bits, impact, S = _state(seed, B, H, D, pivots)
+    num = 2 * B + 1
+    st = lib.StqState(num, H, D, bits, impact)
+    slots = np.random.default_rng(seed).choice(num, B, replace=False)
+    sl = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    st.quantize(to_dev(S), sl)
+    torch.cuda.synchronize()
+    start = layout_ref.stq_unpack(bits, st.slots()[sl.long()].cpu().numpy(), D)   # identical input state
+    inp = synth.step_inputs(rng, B, H, D, decay, dtype)
+    q, k, v, a, be = step_tensors(inp)
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    before = st.pool.clone()
+    dst = None if inplace else torch.zeros_like(st.pool)
+    st.decode_step(sl, q, k, v, a, be, out, dst=dst)
+    torch.cuda.synchronize()
+    if not inplace:
+        assert torch.equal(st.pool, before), "the old representation was modified"
+    newp = st.pool if inplace else dst
+    got = layout_ref.stq_unpack(bits, st.slots(newp)[sl.long()].cpu().numpy(), D)
+    n = B * H
+    bb = np.broadcast_to(bits, (B, H, D)).reshape(n, D)
+    ww = np.broadcast_to(impact, (B, H, D)).reshape(n, D)
+    ref_out, ref_state = oracle.stq_step(bb, ww, *(x.reshape((n,) + x.shape[2:]) for x in start),
+                                         *ref_vectors(inp, B, H, D))
+    check_readout(out.cpu().numpy(), ref_out.reshape(B, H, D))
+    return check_stq(bits, got, tuple(x.reshape((B, H) + x.shape[1:]) for x in ref_state))
+
+
+@pytest.mark.parametrize("D,H,B,decay,dtype,pivots,inplace", [
+    (128, 4, 9, synth.KDA, "bf16", 2, True),
+    (128, 3, 5, synth.KDA, "bf16", 1, False),   # the new state to a second pool
+    (128, 2, 4, synth.GDN, "fp32", 0, True),
+    (64, 4, 7, synth.KDA, "fp32", 3, False),
+])
+def test_step(D, H, B, decay, dtype, pivots, inplace):
+    _log(str(_step_case(D, H, B, decay, dtype, pivots, D * 10 + B, inplace)))
+
+
+def test_step_full_heads_kda():
+    """64 slots x 32 KDA heads x 128 at the nominal 6-bit map (2 pivots per head)."""
+    _log(str(_step_case(128, 32, 64, synth.KDA, "bf16", 2, 4242, True)))
