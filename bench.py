@@ -113,6 +113,9 @@ def parse():
     p.add_argument("--window", type=int, default=0, metavar="W",
                    help="DAMP with per-window requantization: windows of W tokens (1..8); the "
                         "timed launches run whole windows, so the figures average over a window")
+    p.add_argument("--stq", action="store_true",
+                   help="the STEPQuant-style state instead of DAMP (FP16 pivots, 8/6/4-bit rows at "
+                        "a nominal 6-bit map, FP16 row factors and column scales refitted each step)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the step, run a plain device copy of MIB MiB --steps times "
                         "(the reference kernel of known size for HBM byte counters)")
@@ -272,6 +275,17 @@ def main():
     budget = None
     prestep_info = {}
     raw_sets = None
+    stq_bits = stq_impact = None
+    stq_data = 0
+    if args.stq:
+        stq_bits, stq_impact = synth.stq_map(np.random.default_rng(synth.STQ_SEED), H, d)
+        for hh in range(H):
+            n = {b: int((stq_bits[hh] == b).sum()) for b in (16, 8, 6, 4)}
+            stq_data += (2 * d * n[16] + d * n[8] + 3 * d // 4 * n[6] + d // 2 * n[4]
+                         + 2 * (d - n[16]) + 2 * d)
+        stq_data /= H
+        desc = desc.replace(f"{r} FP16 rows/head", "STEPQuant-style state, 2 FP16 pivots/head, "
+                            f"8/6/4-bit rows at a nominal 6-bit map ({8 * stq_data / (d * d):.3f} bits/value)")
     if args.window:
         if not 1 <= args.window <= 8:
             raise SystemExit("--window must be in 1..8")
@@ -293,7 +307,12 @@ def main():
               f"{budget['allocate_ms']:.3f} ms", file=sys.stderr, flush=True)
 
     def run(fmt):
-        if fmt == "damp" and args.window:
+        if fmt == "damp" and args.stq:
+            st = lib.StqState(pool_slots, H, d, stq_bits, stq_impact, device=dev)
+            fill_states(torch, st.quantize, all_slots, H, d, dev)
+            launch = lambda i: st.decode_step(slot_sets[i % R], *sets[i % 4], out)
+            keep = st
+        elif fmt == "damp" and args.window:
             st = lib.DampState(pool_slots, H, d, rows, device=dev)
             st.pool.zero_()
             fill_states(torch, st.quantize, all_slots, H, d, dev)
@@ -343,7 +362,9 @@ def main():
         ms = time_launches(torch, launch, args.steps, args.warmup)
         del keep
         torch.cuda.empty_cache()
-        if fmt == "damp" and args.window:
+        if fmt == "damp" and args.stq:
+            ab = (2 * stq_data + alg_bytes_per_update("damp", d, r, per_key) - 2 * (2 * r * d + (d - r) * d + 4 * (d - r))) * units
+        elif fmt == "damp" and args.window:
             ab = alg_bytes_window(args.window, d, r, per_key) * units
         elif fmt == "damp_token":
             ab = alg_bytes_per_update("damp", d, r, per_key) * units
@@ -359,7 +380,8 @@ def main():
         fmts.insert(1, "damp_token")   # the per-token step on the same pool, for comparison
     for f in fmts:
         results[f] = run(f)
-        print(f"# {args.workload} {f}: {results[f]['ms_per_step'] * 1e3:.1f} us/step, "
+        label = "stq" if (f == "damp" and args.stq) else f
+        print(f"# {args.workload} {label}: {results[f]['ms_per_step'] * 1e3:.1f} us/step, "
               f"{results[f]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
     main_fmt = args.only or "damp"
@@ -378,7 +400,7 @@ def main():
         "dtype": "f32+fp16+int8" if main_fmt == "damp" else ("f32" if main_fmt == "fp32" else "f32+int8"),
         "data": "synthetic: seeded N(0, 0.1) states, unit-norm bf16 q/k, N(0,1) bf16 v, "
                 "sigmoid gates; no model weights",
-        "config": {"workload": desc, "format": main_fmt, "slots_active": B, "heads": H, "d": d,
+        "config": {"workload": desc, "format": "stq" if args.stq else main_fmt, "slots_active": B, "heads": H, "d": d,
                    "fp16_rows": r if budget is None else "per head", "global_batch": B, "seq_len": 1,
                    "state_cache": "cold (HBM)" if (cold or args.workload == "pool4096") else "warm (Infinity Cache)",
                    "pool_copies": R},
@@ -386,7 +408,7 @@ def main():
                      "frac": m["gbs"] / PEAK_HBM_GBS,
                      "traffic": measured_traffic() if (main_fmt == "damp" and args.workload == "pool4096"
                                                        and budget is None and not args.window
-                                                       and not args.fused_prestep) else None},
+                                                       and not args.fused_prestep and not args.stq) else None},
     }
     if budget is not None:
         line["config"]["layout"] = {k: v for k, v in budget.items() if k != "row_map"}
