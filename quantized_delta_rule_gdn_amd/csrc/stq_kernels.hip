@@ -8,9 +8,8 @@
 //   cs_j = fp16( sqrt( sum_{i in N} w_i^2 X_ij^2 / sum_{i in N} w_i^2 ) )
 //   rf_i = fp16( max_{j: cs_j > 0} (|X_ij| / cs_j) / qmax_i ),   qmax = 2^(b-1) - 1
 //   code = clamp(rint(X_ij / (rf_i cs_j)), -qmax, qmax)   (0 where rf_i cs_j = 0)
-// with IEEE binary32 divisions for every decision (rf_i cs_j is exact in binary32). The page
-// gives the structure (shared column scales fitted with squared row-impact factors, row factors,
-// FP16 scales and pivots) but not these formulas; they are the library's reading.
+// The page gives the structure (shared column scales fitted with squared row-impact factors, row
+// factors, FP16 scales and pivots) but not these formulas; they are the library's reading.
 //
 // Block of one (slot, head), storage rows ordered pivots, 8-bit, 6-bit, 4-bit (each ascending
 // key index): FP16 pivot rows (2 d bytes each) | 8-bit rows (d) | 6-bit rows (3 d / 4: a plane of
@@ -20,9 +19,26 @@
 // codes of a row are CPL bytes (8-bit), CPL / 2 + CPL / 4 bytes (6-bit) or CPL / 2 bytes (4-bit):
 // d is 64 or 128.
 //
-// The state is held as fp32 X in VGPRs (64 per lane at d = 128), which the fit needs three times
-// (column sums, row maxima, codes). The step may write its new state to another pool than it
-// read (Table C2 step 6: the old representation stays valid until its readers finish).
+// Mapping. One workgroup per unit; 16 lanes own a row, a wave's 4 row slots take 4 consecutive
+// storage rows. The precision map is a runtime table, but the rows are stored by kind, so a
+// wave's 4 rows almost always share one kind: every per-kind step (load, decode, pack + store)
+// is chosen by a wave-uniform test of the kinds of the wave's first and last row, and only the
+// few row groups that straddle two kinds run two kinds under an exec mask. The state is held as
+// fp32 X in VGPRs (the fit needs it three times: column sums, row maxima, codes); state bytes go
+// through raw buffer instructions with the non-temporal policy, like the DAMP step.
+//
+// Arithmetic of the fit. Column scales: fp32 partial sums per lane, added per column in a fixed
+// order, one IEEE division and square root per column; the column thread also forms
+// rcs_j = RN(1 / cs_j). Row factor: the row maximum of |X_ij| rcs_j (pack: the quotient corrected
+// to the IEEE one by one residual step, exact because cs_j has an 11-bit significand), divided by
+// qmax with one multiply and one residual correction (correctly rounded for 7, 31 and 127 at every
+// binary32 significand). Codes: pack decides every code as the IEEE quotient does (an estimate,
+// with the IEEE division where the estimate lies within 2^-13 of a half-integer); the step rounds
+// the estimate X rcp(rf) rcs_j with one fma against 1.5 * 2^23, like the DAMP step's codes.
+// The step may write its new state to another pool than it read (Table C2 step 6: the old
+// representation stays valid until its readers finish).
+#include <type_traits>
+
 #include "step_common.h"
 
 namespace damp {
@@ -32,7 +48,7 @@ enum StqKind : int { SK_F16 = 0, SK_I8 = 1, SK_I6 = 2, SK_I4 = 3 };
 enum StqMode : int { SM_STEP = 0, SM_PACK = 1, SM_UNPACK = 2 };
 
 struct StqBlock {
-  uint32_t o8, o6, o4, orf, ocs;
+  uint32_t o8, o6, o4, orf, ocs, bytes;
   int n16, n8, n6, n4;
   float sw;
 };
@@ -50,6 +66,7 @@ __device__ __forceinline__ StqBlock stq_block(const StqArgs& a, int head) {
   b.o4 = b.o6 + (3 * D / 4) * b.n6;
   b.orf = b.o4 + (D / 2) * b.n4;
   b.ocs = b.orf + 2 * (D - b.n16);
+  b.bytes = b.ocs + 2 * D;
   b.sw = __int_as_float(hi.z);
   return b;
 }
@@ -58,96 +75,218 @@ __device__ __forceinline__ int stq_kind(const StqBlock& b, int p) {
   return p < b.n16 ? SK_F16 : (p < b.n16 + b.n8 ? SK_I8 : (p < b.n16 + b.n8 + b.n6 ? SK_I6 : SK_I4));
 }
 
-__device__ __forceinline__ int stq_qmax(int kind) {
-  return kind == SK_I8 ? 127 : (kind == SK_I6 ? 31 : 7);
+// The lane's row slot, made opaque to the compiler once per row group and phase: without it the
+// compiler computes the per-kind addresses and lane masks of every row group once, early, and
+// holds them (some 40 VGPRs and many scalar pairs) from the loads to the stores.
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
-// The lane's codes of row p, as raw words: F16 CPL halves, I8 CPL bytes, I6 / I4 the nibbles in
-// w[0..] and (I6) the top bits in hw.
-template <int D>
-__device__ __forceinline__ void stq_load(const uint8_t* blk, const StqBlock& b, int kind, int p,
-                                         int cg, uint32_t* w, uint32_t& hw) {
-  constexpr int CPL = D / 16;
-  if (kind == SK_F16) {
-    load_bytes<CPL * 2>(blk + (p * D + cg * CPL) * 2, w);
-  } else if (kind == SK_I8) {
-    load_bytes<CPL>(blk + b.o8 + (p - b.n16) * D + cg * CPL, w);
-  } else if (kind == SK_I6) {
-    const uint8_t* row = blk + b.o6 + (p - b.n16 - b.n8) * (3 * D / 4);
-    load_bytes<CPL / 2>(row + cg * (CPL / 2), w);
-    uint32_t t[1];
-    load_bytes<CPL / 4>(row + D / 2 + cg * (CPL / 4), t);
-    hw = t[0];
-  } else {
-    load_bytes<CPL / 2>(blk + b.o4 + (p - b.n16 - b.n8 - b.n6) * (D / 2) + cg * (CPL / 2), w);
+// The same for a wave-uniform value (the group's first row, from which the kind tests follow).
+__device__ __forceinline__ int fresh_s(int x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+// Run f(kind) for the lanes whose row has that kind; k0 / k3 (wave-uniform) are the kinds of the
+// wave's first and last row of the group, so kinds outside [k0, k3] cost one scalar compare.
+template <int K, typename F>
+__device__ __forceinline__ void on_kind(int k0, int k3, int mine, F& f) {
+  if (K >= k0 && K <= k3) {
+    if (mine == K) f(std::integral_constant<int, K>{});
   }
 }
 
-// Code (or FP16 value) c of a loaded row.
-__device__ __forceinline__ float stq_decode(int kind, const uint32_t* w, uint32_t hw, int c) {
-  if (kind == SK_F16) return half_bits_to_float(w[c >> 1] >> (16 * (c & 1)));
-  if (kind == SK_I8) return static_cast<float>(static_cast<int8_t>(w[c >> 2] >> (8 * (c & 3))));
-  const uint32_t nib = (w[c >> 3] >> (4 * (c & 7))) & 0xFu;
-  if (kind == SK_I4) return static_cast<float>(static_cast<int32_t>(nib << 28) >> 28);
-  const uint32_t top = (hw >> (2 * c)) & 0x3u;
-  return static_cast<float>(static_cast<int32_t>((nib | (top << 4)) << 26) >> 26);
+template <typename F>
+__device__ __forceinline__ void by_kind(int k0, int k3, int mine, F&& f) {
+  on_kind<SK_F16>(k0, k3, mine, f);
+  on_kind<SK_I8>(k0, k3, mine, f);
+  on_kind<SK_I6>(k0, k3, mine, f);
+  on_kind<SK_I4>(k0, k3, mine, f);
 }
 
-// Store the lane's part of row p: FP16 values, or codes of the row's width.
-template <int D>
-__device__ __forceinline__ void stq_store(uint8_t* blk, const StqBlock& b, int kind, int p, int cg,
-                                          const float* x, const int32_t* code) {
+// Byte offset of the lane's part of storage row p (kind K) in the block; I6: of its nibbles (its
+// top bits: stq_top_off).
+template <int D, int K>
+__device__ __forceinline__ uint32_t stq_off(const StqBlock& b, int p, int cg) {
   constexpr int CPL = D / 16;
-  if (kind == SK_F16) {
+  if constexpr (K == SK_F16) return static_cast<uint32_t>(p * 2 * D + cg * 2 * CPL);
+  if constexpr (K == SK_I8) return b.o8 + static_cast<uint32_t>((p - b.n16) * D + cg * CPL);
+  if constexpr (K == SK_I6)
+    return b.o6 + static_cast<uint32_t>((p - b.n16 - b.n8) * (3 * D / 4) + cg * (CPL / 2));
+  return b.o4 + static_cast<uint32_t>((p - b.n16 - b.n8 - b.n6) * (D / 2) + cg * (CPL / 2));
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t stq_top_off(const StqBlock& b, int p, int cg) {
+  constexpr int CPL = D / 16;
+  return b.o6 + static_cast<uint32_t>((p - b.n16 - b.n8) * (3 * D / 4) + D / 2 + cg * (CPL / 4));
+}
+
+// The lane's stored words of row p (kind K): F16 CPL halves, I8 CPL bytes, I6 / I4 CPL nibbles
+// in w, and (I6) the CPL top-bit pairs in top.
+template <int D, int K>
+__device__ __forceinline__ void stq_load(rsrc_t rs, const StqBlock& b, int p, int cg, uint32_t* w,
+                                         uint32_t& top) {
+  constexpr int CPL = D / 16;
+  constexpr int N = K == SK_F16 ? 2 * CPL : (K == SK_I8 ? CPL : CPL / 2);
+  buf_load<N>(rs, stq_off<D, K>(b, p, cg), 0u, w);
+  if constexpr (K == SK_I6) {
+    uint32_t t[1];
+    buf_load<CPL / 4>(rs, stq_top_off<D>(b, p, cg), 0u, t);
+    top = t[0];
+  }
+}
+
+// Value c of a loaded row: the binary16 value (F16) or the integer code, as fp32.
+template <int K>
+__device__ __forceinline__ float stq_decode(const uint32_t* w, uint32_t top, int c) {
+  if constexpr (K == SK_F16) return half_bits_to_float(w[c >> 1] >> (16 * (c & 1)));
+  if constexpr (K == SK_I8) return static_cast<float>(static_cast<int8_t>(w[c >> 2] >> (8 * (c & 3))));
+  if constexpr (K == SK_I4) return static_cast<float>(static_cast<int32_t>(w[c >> 3] << (28 - 4 * (c & 7))) >> 28);
+  const uint32_t nib = (w[c >> 3] >> (4 * (c & 7))) & 0xFu;
+  const int32_t hi = static_cast<int32_t>(top << (30 - 2 * c)) >> 30;   // signed top two bits
+  return static_cast<float>(static_cast<int32_t>((static_cast<uint32_t>(hi) << 4) | nib));
+}
+
+// Store the lane's part of row p: F16 from x, else the codes in the low bits of tb (two's
+// complement: tb holds 1.5 * 2^23 + code as binary32 bits).
+template <int D, int K>
+__device__ __forceinline__ void stq_store(rsrc_t rs, const StqBlock& b, int p, int cg, const float* x,
+                                          const uint32_t* tb) {
+  constexpr int CPL = D / 16;
+  const uint32_t off = stq_off<D, K>(b, p, cg);
+  if constexpr (K == SK_F16) {
     uint32_t wd[CPL / 2];
 #pragma unroll
-    for (int i = 0; i < CPL / 2; ++i) wd[i] = 0;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) wd[c >> 1] |= float_to_half_bits(x[c]) << (16 * (c & 1));
-    store_bytes<CPL * 2>(blk + (p * D + cg * CPL) * 2, wd);
-  } else if (kind == SK_I8) {
+    for (int i = 0; i < CPL / 2; ++i)
+      wd[i] = float_to_half_bits(x[2 * i]) | (float_to_half_bits(x[2 * i + 1]) << 16);
+    buf_store<2 * CPL>(rs, off, 0u, wd);
+  } else if constexpr (K == SK_I8) {
     uint32_t wd[CPL / 4];
 #pragma unroll
-    for (int i = 0; i < CPL / 4; ++i) wd[i] = 0;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) wd[c >> 2] |= (static_cast<uint32_t>(code[c]) & 0xFFu) << (8 * (c & 3));
-    store_bytes<CPL>(blk + b.o8 + (p - b.n16) * D + cg * CPL, wd);
+    for (int i = 0; i < CPL / 4; ++i) wd[i] = pack4_low_bytes(tb[4 * i], tb[4 * i + 1], tb[4 * i + 2], tb[4 * i + 3]);
+    buf_store<CPL>(rs, off, 0u, wd);
   } else {
-    uint32_t lo[(CPL + 7) / 8], hi = 0;
-#pragma unroll
-    for (int i = 0; i < (CPL + 7) / 8; ++i) lo[i] = 0;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const uint32_t u = static_cast<uint32_t>(code[c]);
-      lo[c >> 3] |= (u & 0xFu) << (4 * (c & 7));
-      hi |= ((u >> 4) & 0x3u) << (2 * c);
-    }
-    if (kind == SK_I6) {
-      uint8_t* row = blk + b.o6 + (p - b.n16 - b.n8) * (3 * D / 4);
-      store_bytes<CPL / 2>(row + cg * (CPL / 2), lo);
-      store_bytes<CPL / 4>(row + D / 2 + cg * (CPL / 4), &hi);
+    uint32_t lo, hi = 0;
+    if constexpr (CPL == 8) {
+      // even codes in the bytes of e, odd codes in the bytes of o
+      const uint32_t e = pack4_low_bytes(tb[0], tb[2], tb[4], tb[6]);
+      const uint32_t o = pack4_low_bytes(tb[1], tb[3], tb[5], tb[7]);
+      lo = (e & 0x0F0F0F0Fu) | ((o & 0x0F0F0F0Fu) << 4);
+      if constexpr (K == SK_I6) {
+        // byte k of n: top bits of codes 2k (bits 0-1) and 2k+1 (bits 2-3); then two nibbles a byte
+        const uint32_t n = ((e >> 4) & 0x03030303u) | (((o >> 4) & 0x03030303u) << 2);
+        hi = __builtin_amdgcn_perm(0u, n | (n >> 4), 0x0c0c0200u);
+      }
     } else {
-      store_bytes<CPL / 2>(blk + b.o4 + (p - b.n16 - b.n8 - b.n6) * (D / 2) + cg * (CPL / 2), lo);
+      lo = 0;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        lo |= (tb[c] & 0xFu) << (4 * c);
+        hi |= ((tb[c] >> 4) & 0x3u) << (2 * c);
+      }
     }
+    buf_store<CPL / 2>(rs, off, 0u, &lo);
+    if constexpr (K == SK_I6) buf_store<CPL / 4>(rs, stq_top_off<D>(b, p, cg), 0u, &hi);
   }
+}
+
+// m / qmax correctly rounded: one multiply by RN(1 / qmax) and one residual correction (checked
+// against IEEE division for every binary32 significand at exponents 2^-120 .. 2^127 for qmax in
+// {7, 31, 127}).
+__device__ __forceinline__ float div_qmax(float m, float qm, float inv) {
+  const float q = m * inv;
+  const float r = fmaf(-q, qm, m);
+  return fmaf(r, inv, q);
 }
 
 template <int D, int NW>
 struct StqSmem {
-  float4 srow[D];        // {gate_p, k_p, q_p, w_p^2}, storage order
-  float sv[D];           // v, then delta
-  float redu[4 * NW][D];
-  float redp[4 * NW][D];
+  float4 srow[D];            // {gate_p, k_p, q_p, rf_p (1 for pivots)}, storage order
+  float sw2[D];              // w_p^2 (0 for pivots), storage order
+  float sv[D];               // v, then delta
+  float red[2][4 * NW][D];   // partial sums: u and p; then the column-scale sums in red[0]
   float redqk[NW];
-  float scs[D];          // column scales (binary16 values as fp32)
+  float scs[D];              // column scales (binary16 values as fp32)
+  float srcs[D];             // RN(1 / cs_j), 0 where cs_j = 0
 };
+
+// The step's per-row scalars in two halves, so that their loads overlap the state loads while
+// the state is decoded in between: stq_stage_load issues the loads (k, q, the gate, v, the row
+// map, the fit's row weights and the stored row factors, one element per thread),
+// stq_stage_store writes them to LDS in storage order (srow = {gate_p, k_p, q_p, rf_p} with
+// rf = 1 for pivots, sv = v, sw2) and returns beta.
+template <int D, int NT>
+struct StqStage {
+  static constexpr int PER = (D + NT - 1) / NT;
+  int src[PER];
+  float kv[PER], qv[PER], gv[PER], vv[PER], w2[PER];
+  uint32_t rf[PER];
+  float g0, beta;
+};
+
+template <int D, int NT, int PER_KEY, int BF16>
+__device__ __forceinline__ StqStage<D, NT> stq_stage_load(const StqArgs& a, rsrc_t blk_rs, const StqBlock& blk,
+                                                          int bh, int head, int tid) {
+  StqStage<D, NT> st;
+  const int64_t vec = int64_t(bh) * D;
+#pragma unroll
+  for (int n = 0; n < StqStage<D, NT>::PER; ++n) {
+    const int i = tid + n * NT;
+    if (i < D) {
+      st.src[n] = a.rowmap[head * D + i];
+      st.kv[n] = load_in<BF16>(a.step.k, vec + i);
+      st.qv[n] = load_in<BF16>(a.step.q, vec + i);
+      st.gv[n] = PER_KEY ? a.step.alpha[vec + i] : 0.0f;
+      st.vv[n] = load_in<BF16>(a.step.v, vec + i);
+      st.w2[n] = a.w2[head * D + i];
+      const int ri = i - blk.n16;
+      st.rf[n] = 0x3C00u;   // 1.0 for pivots
+      if (ri >= 0) buf_load<2>(blk_rs, blk.orf + 2u * static_cast<uint32_t>(ri), 0u, &st.rf[n]);
+    }
+  }
+  st.g0 = PER_KEY ? 0.0f : a.step.alpha[bh];
+  st.beta = a.step.beta[bh];
+  return st;
+}
+
+template <int D, int NT, int PER_KEY>
+__device__ __forceinline__ float stq_stage_store(const StqStage<D, NT>& st, int tid, float4* srow, float* sv,
+                                                 float* sw2, float* tmp) {
+#pragma unroll
+  for (int n = 0; n < StqStage<D, NT>::PER; ++n) {
+    const int i = tid + n * NT;
+    if (i < D) {
+      tmp[i] = st.kv[n];
+      tmp[D + i] = st.qv[n];
+      if constexpr (PER_KEY) tmp[2 * D + i] = st.gv[n];
+      sv[i] = st.vv[n];
+      sw2[i] = st.w2[n];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < StqStage<D, NT>::PER; ++n) {
+    const int i = tid + n * NT;
+    if (i < D) {
+      const int j = st.src[n];
+      srow[i] = make_float4(PER_KEY ? tmp[2 * D + j] : st.g0, tmp[j], tmp[D + j], half_bits_to_float(st.rf[n]));
+    }
+  }
+  __syncthreads();
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(st.beta)));
+}
 
 // MODE = SM_STEP: one decode step (reads src, writes dst). SM_PACK: fp32 states (key order) ->
 // format. SM_UNPACK: format -> fp32 states (key order).
-template <int D, int PER_KEY, int BF16, int MODE>
-__global__ __launch_bounds__(Geo<D>::NT) void stq_kernel(const StqArgs a) {
-  using G = Geo<D>;
-  constexpr int CPL = G::CPL, RPL = G::RPL, NW = G::NW;
+template <int D, int NW, int PER_KEY, int BF16, int MODE>
+__global__ __launch_bounds__(NW * 64) void stq_kernel(const StqArgs a) {
+  using G = Geo<D, NW>;
+  constexpr int CPL = G::CPL, RPL = G::RPL, RPS = G::RPS, NT = G::NT;
+  constexpr bool EXACT = MODE == SM_PACK;
+  constexpr float kMagic = 0x1.8p23f;
   __shared__ StqSmem<D, NW> sm;
   const int tid = __builtin_amdgcn_workitem_id_x();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,161 +297,209 @@ __global__ __launch_bounds__(Geo<D>::NT) void stq_kernel(const StqArgs a) {
   const int64_t slot = a.slot_idx[b];
   const StqBlock blk = stq_block<D>(a, head);
   const int64_t boff = slot * a.slot_stride + a.heads[head].x;
-  const uint8_t* src = a.pool + boff;
-  uint8_t* dst = (a.dst ? a.dst : a.pool) + boff;
+  const rsrc_t src = make_rsrc(a.pool + boff, blk.bytes);
+  const rsrc_t dst = make_rsrc((a.dst ? a.dst : a.pool) + boff, blk.bytes);
   const uint8_t* rowmap = a.rowmap + head * D;
 
   float X[RPL][CPL];
   if constexpr (MODE == SM_PACK) {
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
-      const int p = t * G::RPS + w * 4 + rs;
+      const int p = t * RPS + w * 4 + rs;
       load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(a.S + (int64_t(bh) * D + rowmap[p]) * D + cg * CPL),
                           reinterpret_cast<uint32_t*>(X[t]));
     }
+    for (int i = tid; i < D; i += NT) sm.sw2[i] = a.w2[head * D + i];
+    __syncthreads();
   } else {
-    // (1) the stored state: codes, row factors, column scales; reconstructed into X
-    float csv[CPL];
-    {
-      uint32_t cw[CPL / 2];
-      load_bytes<CPL * 2>(src + blk.ocs + cg * CPL * 2, cw);
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) csv[c] = half_bits_to_float(cw[c >> 1] >> (16 * (c & 1)));
-    }
+    // (1) the stored state: the lane's words of each row, its row factor, its column scales
     uint32_t raw[RPL][CPL / 2];
-    uint32_t hw[RPL];
+    uint32_t top[RPL];
     float rfv[RPL];
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
-      const int p = t * G::RPS + w * 4 + rs;
-      const int kind = stq_kind(blk, p);
-      hw[t] = 0;
-      stq_load<D>(src, blk, kind, p, cg, raw[t], hw[t]);
-      rfv[t] = 1.0f;
-      if (kind != SK_F16) rfv[t] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(src + blk.orf + 2 * (p - blk.n16)));
+      const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
+      const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3), mine = stq_kind(blk, p);
+      top[t] = 0;
+      by_kind(k0, k3, mine, [&](auto KC) { stq_load<D, decltype(KC)::value>(src, blk, p, cg, raw[t], top[t]); });
+      if constexpr (MODE == SM_UNPACK) {
+        const int ri = p - blk.n16;
+        uint32_t rb[1];
+        buf_load<2>(src, blk.orf + 2u * static_cast<uint32_t>(ri < 0 ? 0 : ri), 0u, rb);
+        rfv[t] = ri < 0 ? 1.0f : half_bits_to_float(rb[0]);
+      }
+    }
+    float csv[CPL];
+    {
+      uint32_t cw[CPL / 2];
+      buf_load<2 * CPL>(src, blk.ocs + 2u * cg * CPL, 0u, cw);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) csv[c] = half_bits_to_float(cw[c >> 1] >> (16 * (c & 1)));
     }
     if constexpr (MODE == SM_UNPACK) {
+      // code * (rf * cs): rf * cs is exact in binary32, so one rounding, as the definition
 #pragma unroll
       for (int t = 0; t < RPL; ++t) {
-        const int p = t * G::RPS + w * 4 + rs;
-        const int kind = stq_kind(blk, p);
+        const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
+        const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3), mine = stq_kind(blk, p);
+        by_kind(k0, k3, mine, [&](auto KC) {
+          constexpr int K = decltype(KC)::value;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const float v = stq_decode(kind, raw[t], hw[t], c);
-          X[t][c] = kind == SK_F16 ? v : v * (rfv[t] * csv[c]);
-        }
+          for (int c = 0; c < CPL; ++c) {
+            const float v = stq_decode<K>(raw[t], top[t], c);
+            X[t][c] = K == SK_F16 ? v : v * (rfv[t] * csv[c]);
+          }
+        });
         store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(a.S + (int64_t(bh) * D + rowmap[p]) * D + cg * CPL),
                              reinterpret_cast<const uint32_t*>(X[t]));
       }
       return;
     } else {
-      // (2) per-row scalars: gate, k, q (storage order) and v
-      const float beta = stage_rows<D, G::NT, PER_KEY, BF16, false>(a.step, nullptr, bh, head, 0, tid,
-                                                                     sm.srow, sm.sv, &sm.redu[0][0]);
-      // (3) S' = gate * S_hat in X, and the column sums u, p
+      // (2) the per-row scalars' loads go out; meanwhile the state is decoded as it arrives:
+      // X = code * cs_j (integer rows) or the FP16 value, and the stored words are dropped
+      const StqStage<D, NT> stage = stq_stage_load<D, NT, PER_KEY, BF16>(a, src, blk, bh, head, tid);
+#pragma unroll
+      for (int t = 0; t < RPL; ++t) {
+        const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
+        const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3), mine = stq_kind(blk, p);
+        by_kind(k0, k3, mine, [&](auto KC) {
+          constexpr int K = decltype(KC)::value;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const float v = stq_decode<K>(raw[t], top[t], c);
+            X[t][c] = K == SK_F16 ? v : v * csv[c];
+          }
+        });
+      }
+      const float beta = stq_stage_store<D, NT, PER_KEY>(stage, tid, sm.srow, sm.sv, sm.sw2, &sm.red[0][0][0]);
+      // (3) S' = diag(gate) S_hat (row multiplier gate_p * rf_p), and the partial column sums of
+      // u = S'^T k and p = S'^T q
       float pu[CPL], pp[CPL], pqk = 0.0f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) pu[c] = pp[c] = 0.0f;
 #pragma unroll
       for (int t = 0; t < RPL; ++t) {
-        const int p = t * G::RPS + w * 4 + rs;
-        const int kind = stq_kind(blk, p);
-        const float4 rw = sm.srow[p];
+        const float4 rw = sm.srow[t * RPS + w * 4 + rs];
+        const float m = rw.x * rw.w;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-          const float v = stq_decode(kind, raw[t], hw[t], c);
-          X[t][c] = rw.x * (kind == SK_F16 ? v : v * (rfv[t] * csv[c]));
+          X[t][c] *= m;
           pu[c] = fmaf(rw.y, X[t][c], pu[c]);
           pp[c] = fmaf(rw.z, X[t][c], pp[c]);
         }
         pqk = fmaf(rw.z, rw.y, pqk);
       }
-      finish_columns<D, G>(sm.redu, sm.redp, sm.redqk, sm.sv, pu, pp, pqk, beta,
+      finish_columns<D, G>(sm.red[0], sm.red[1], sm.redqk, sm.sv, pu, pp, pqk, beta,
                            a.step.out + int64_t(bh) * D, tid, w, rs, lane, cg);
+      // (4) X = S' + k delta^T
       float dl[CPL];
       load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sm.sv + cg * CPL), reinterpret_cast<uint32_t*>(dl));
-      // (4) X = S' + k delta^T
 #pragma unroll
       for (int t = 0; t < RPL; ++t) {
-        const float kp = sm.srow[t * G::RPS + w * 4 + rs].y;
+        const float kp = sm.srow[t * RPS + w * 4 + rs].y;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) X[t][c] = fmaf(kp, dl[c], X[t][c]);
       }
     }
   }
 
-  // (5) the fit. Row weights w_p^2 of the integer rows (0 for pivots), in storage order.
-  float cs_part[CPL];
+  // (5) the fit: column scales from the weighted column sums of squares
+  {
+    float acc[CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) cs_part[c] = 0.0f;
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
 #pragma unroll
-  for (int t = 0; t < RPL; ++t) {
-    const int p = t * G::RPS + w * 4 + rs;
-    const float w2 = a.w2[head * D + p];
+    for (int t = 0; t < RPL; ++t) {
+      const float w2 = sm.sw2[t * RPS + w * 4 + rs];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) cs_part[c] = fmaf(w2 * X[t][c], X[t][c], cs_part[c]);
+      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w2 * X[t][c], X[t][c], acc[c]);
+    }
+    store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(&sm.red[0][w * 4 + rs][cg * CPL]),
+                         reinterpret_cast<const uint32_t*>(acc));
   }
-  store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(&sm.redu[w * 4 + rs][cg * CPL]),
-                       reinterpret_cast<const uint32_t*>(cs_part));
   __syncthreads();
-  for (int j = tid; j < D; j += G::NT) {
-    float s = sm.redu[0][j];
+  for (int j = tid; j < D; j += NT) {
+    float s = sm.red[0][0][j];
 #pragma unroll
-    for (int k = 1; k < 4 * NW; ++k) s += sm.redu[k][j];
+    for (int k = 1; k < 4 * NW; ++k) s += sm.red[0][k][j];
     const uint32_t hb = blk.sw > 0.0f ? float_to_half_bits(sqrtf(__fdiv_rn(s, blk.sw))) : 0u;
-    sm.scs[j] = half_bits_to_float(hb);
-    reinterpret_cast<uint16_t*>(dst + blk.ocs)[j] = static_cast<uint16_t>(hb);
+    const float cs = half_bits_to_float(hb);
+    sm.scs[j] = cs;
+    sm.srcs[j] = cs > 0.0f ? __fdiv_rn(1.0f, cs) : 0.0f;
+    buf_store<2>(dst, blk.ocs + 2u * j, 0u, &hb);
   }
   __syncthreads();
-  float csv2[CPL];
-  load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sm.scs + cg * CPL), reinterpret_cast<uint32_t*>(csv2));
+  float rcs[CPL], csx[CPL];
+  load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sm.srcs + cg * CPL), reinterpret_cast<uint32_t*>(rcs));
+  if constexpr (EXACT)
+    load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sm.scs + cg * CPL), reinterpret_cast<uint32_t*>(csx));
+
+  // (6) per row: row factor, codes, store
 #pragma unroll
   for (int t = 0; t < RPL; ++t) {
-    const int p = t * G::RPS + w * 4 + rs;
-    const int kind = stq_kind(blk, p);
-    int32_t code[CPL];
-    if (kind != SK_F16) {
-      float m = 0.0f;
+    const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
+    const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3), mine = stq_kind(blk, p);
+    float mq = 0.0f;
 #pragma unroll
-      for (int c = 0; c < CPL; ++c)
-        if (csv2[c] > 0.0f) m = fmaxf(m, __fdiv_rn(fabsf(X[t][c]), csv2[c]));
-      m = max_row16(m);
-      const int qm = stq_qmax(kind);
-      const uint32_t rb = float_to_half_bits(__fdiv_rn(m, static_cast<float>(qm)));
-      const float rf = half_bits_to_float(rb);
-      if (cg == 0) reinterpret_cast<uint16_t*>(dst + blk.orf)[p - blk.n16] = static_cast<uint16_t>(rb);
+    for (int c = 0; c < CPL; ++c) {
+      const float ax = fabsf(X[t][c]);
+      float q = ax * rcs[c];
+      if constexpr (EXACT) q = fmaf(fmaf(-q, csx[c], ax), rcs[c], q);   // = fl(|x| / cs) (0 if cs = 0)
+      mq = fmaxf(mq, q);
+    }
+    const float m = max_row16(mq);
+    const float qm = mine == SK_I8 ? 127.0f : (mine == SK_I6 ? 31.0f : 7.0f);
+    const float inv = mine == SK_I8 ? 1.0f / 127.0f : (mine == SK_I6 ? 1.0f / 31.0f : 1.0f / 7.0f);
+    const uint32_t rb = float_to_half_bits(div_qmax(m, qm, inv));
+    const float rf = half_bits_to_float(rb);
+    if (mine != SK_F16 && cg == 0) buf_store<2>(dst, blk.orf + 2u * static_cast<uint32_t>(p - blk.n16), 0u, &rb);
+    float rrf = 0.0f;
+    if (rf > 0.0f) rrf = EXACT ? __fdiv_rn(1.0f, rf) : __builtin_amdgcn_rcpf(rf);
+    uint32_t tb[CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const float sc = rf * csv2[c];   // exact: two binary16 significands
-        float q = sc > 0.0f ? rintf(__fdiv_rn(X[t][c], sc)) : 0.0f;
-        q = fminf(fmaxf(q, static_cast<float>(-qm)), static_cast<float>(qm));
-        code[c] = static_cast<int32_t>(q);
+    for (int c = 0; c < CPL; ++c) {
+      if constexpr (EXACT) {
+        const float y = (X[t][c] * rrf) * rcs[c];
+        float n = rintf(y);
+        if (fabsf(y - n) > 0.5f - 0x1p-13f) {
+          const float sc = rf * csx[c];   // exact: two binary16 significands
+          n = sc > 0.0f ? rintf(__fdiv_rn(X[t][c], sc)) : 0.0f;
+        }
+        n = fminf(fmaxf(n, -qm), qm);
+        tb[c] = __float_as_uint(n + kMagic);
+      } else {
+        tb[c] = __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(X[t][c] * rrf, rcs[c], kMagic), kMagic - qm, kMagic + qm));
       }
     }
-    stq_store<D>(dst, blk, kind, p, cg, X[t], code);
+    by_kind(k0, k3, mine, [&](auto KC) { stq_store<D, decltype(KC)::value>(dst, blk, p, cg, X[t], tb); });
   }
 }
 
-template <int D, int MODE>
+template <int D, int NW, int MODE>
 hipError_t stq_launch_mode(int per_key, int bf16, const StqArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H)), block(Geo<D>::NT);
+  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H)), block(NW * 64);
   if constexpr (MODE != SM_STEP) {
-    hipLaunchKernelGGL((stq_kernel<D, 0, 0, MODE>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((stq_kernel<D, NW, 0, 0, MODE>), grid, block, 0, s, a);
   } else if (per_key) {
-    if (bf16) hipLaunchKernelGGL((stq_kernel<D, 1, 1, MODE>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stq_kernel<D, 1, 0, MODE>), grid, block, 0, s, a);
+    if (bf16) hipLaunchKernelGGL((stq_kernel<D, NW, 1, 1, MODE>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stq_kernel<D, NW, 1, 0, MODE>), grid, block, 0, s, a);
   } else {
-    if (bf16) hipLaunchKernelGGL((stq_kernel<D, 0, 1, MODE>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stq_kernel<D, 0, 0, MODE>), grid, block, 0, s, a);
+    if (bf16) hipLaunchKernelGGL((stq_kernel<D, NW, 0, 1, MODE>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stq_kernel<D, NW, 0, 0, MODE>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
 
+// Waves per unit: four at d = 128 (each lane holds 8 rows x 8 columns of X), two at d = 64.
+template <int D>
+constexpr int kStqWaves = D >= 128 ? 4 : 2;
+
 template <int D>
 hipError_t stq_d(int mode, int per_key, int bf16, const StqArgs& a, hipStream_t s) {
-  if (mode == SM_STEP) return stq_launch_mode<D, SM_STEP>(per_key, bf16, a, s);
-  if (mode == SM_PACK) return stq_launch_mode<D, SM_PACK>(per_key, bf16, a, s);
-  return stq_launch_mode<D, SM_UNPACK>(per_key, bf16, a, s);
+  constexpr int NW = kStqWaves<D>;
+  if (mode == SM_STEP) return stq_launch_mode<D, NW, SM_STEP>(per_key, bf16, a, s);
+  if (mode == SM_PACK) return stq_launch_mode<D, NW, SM_PACK>(per_key, bf16, a, s);
+  return stq_launch_mode<D, NW, SM_UNPACK>(per_key, bf16, a, s);
 }
 
 }  // namespace
