@@ -607,6 +607,10 @@ __device__ __forceinline__ void finish_columns(float (*redu)[D], float (*redp)[D
     for (int k = 1; k < 4 * NW; ++k) {
       uu += redu[k][j];
       pv += redp[k][j];
+      // with many waves, keep the LDS reads to eight in flight: read all at once, the 2 * 4 * NW
+      // partials would take as many VGPRs while the caller's state is live
+      if constexpr (4 * NW > 8)
+        if ((k & 7) == 7) asm volatile("" ::: "memory");
     }
     float qk = redqk[0];
 #pragma unroll

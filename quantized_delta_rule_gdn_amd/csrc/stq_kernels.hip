@@ -27,14 +27,20 @@
 // fp32 X in VGPRs (the fit needs it three times: column sums, row maxima, codes); state bytes go
 // through raw buffer instructions with the non-temporal policy, like the DAMP step.
 //
+// Decoding. 6-bit codes are rebuilt as signed bytes holding 4 * code and 4-bit codes as 16 * code
+// (the sign bit moved to bit 7), so every integer row converts with one signed-byte instruction
+// per value; the staged row multiplier carries the exact power-of-two inverse.
+//
 // Arithmetic of the fit. Column scales: fp32 partial sums per lane, added per column in a fixed
 // order, one IEEE division and square root per column; the column thread also forms
-// rcs_j = RN(1 / cs_j). Row factor: the row maximum of |X_ij| rcs_j (pack: the quotient corrected
-// to the IEEE one by one residual step, exact because cs_j has an 11-bit significand), divided by
-// qmax with one multiply and one residual correction (correctly rounded for 7, 31 and 127 at every
-// binary32 significand). Codes: pack decides every code as the IEEE quotient does (an estimate,
-// with the IEEE division where the estimate lies within 2^-13 of a half-integer); the step rounds
-// the estimate X rcp(rf) rcs_j with one fma against 1.5 * 2^23, like the DAMP step's codes.
+// rcs_j = RN(1 / cs_j). Row factor: the row maximum m of |X_ij| rcs_j (pack: the quotient
+// corrected to the IEEE one by one residual step, exact because cs_j has an 11-bit significand),
+// divided by qmax with one multiply and one residual correction (correctly rounded for 7, 31 and
+// 127 at every binary32 significand). Codes: pack takes the IEEE quotient X / (rf cs) for each
+// (rf cs is exact in binary32); the step rounds a_j rcp(rf), with a_j = X_ij rcs_j the same
+// product its row maximum used, by one fma against 1.5 * 2^23, like the DAMP step's codes. Since
+// |a_j| <= m and rf >= (m / qmax)(1 - 2^-11) for a normal binary16 rf, no such code rounds past
+// qmax; only a row group holding a subnormal or zero row factor clamps.
 // The step may write its new state to another pool than it read (Table C2 step 6: the old
 // representation stays valid until its readers finish).
 #include <type_traits>
@@ -139,15 +145,40 @@ __device__ __forceinline__ void stq_load(rsrc_t rs, const StqBlock& b, int p, in
   }
 }
 
-// Value c of a loaded row: the binary16 value (F16) or the integer code, as fp32.
+// Power of two each row kind's decoded values carry (the row multiplier divides it out
+// exactly): 6-bit codes decode as 4 * code and 4-bit codes as 16 * code, the code's sign bit
+// moved to bit 7 of a byte so that one signed-byte conversion reads it.
 template <int K>
-__device__ __forceinline__ float stq_decode(const uint32_t* w, uint32_t top, int c) {
-  if constexpr (K == SK_F16) return half_bits_to_float(w[c >> 1] >> (16 * (c & 1)));
-  if constexpr (K == SK_I8) return static_cast<float>(static_cast<int8_t>(w[c >> 2] >> (8 * (c & 3))));
-  if constexpr (K == SK_I4) return static_cast<float>(static_cast<int32_t>(w[c >> 3] << (28 - 4 * (c & 7))) >> 28);
-  const uint32_t nib = (w[c >> 3] >> (4 * (c & 7))) & 0xFu;
-  const int32_t hi = static_cast<int32_t>(top << (30 - 2 * c)) >> 30;   // signed top two bits
-  return static_cast<float>(static_cast<int32_t>((static_cast<uint32_t>(hi) << 4) | nib));
+constexpr float kDecodeScale = K == SK_I6 ? 4.0f : (K == SK_I4 ? 16.0f : 1.0f);
+
+// The lane's CPL values of a loaded row, times kDecodeScale<K>: FP16 values widened, codes
+// converted from signed bytes.
+template <int D, int K>
+__device__ __forceinline__ void stq_decode_row(const uint32_t* w, uint32_t top, float* out) {
+  constexpr int CPL = D / 16;
+  auto sbyte = [](uint32_t x, int k) { return static_cast<float>(static_cast<int8_t>(x >> (8 * k))); };
+  if constexpr (K == SK_F16) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) out[c] = half_bits_to_float(w[c >> 1] >> (16 * (c & 1)));
+  } else if constexpr (K == SK_I8) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) out[c] = sbyte(w[c >> 2], c & 3);
+  } else {
+    // codes 2k in the bytes of e, codes 2k + 1 in the bytes of o, each at bits 4..7 (I4) or 2..7
+    // (I6, the top bits from t: byte k of t = the top-bit pairs of codes 2k and 2k + 1)
+    uint32_t e, o;
+    if constexpr (K == SK_I4) {
+      e = (w[0] << 4) & 0xF0F0F0F0u;
+      o = w[0] & 0xF0F0F0F0u;
+    } else {
+      const uint32_t y = __builtin_amdgcn_perm(0u, top, 0x01010000u);   // bytes t0 t0 t1 t1
+      const uint32_t t = (y & 0x000F000Fu) | ((y >> 4) & 0x0F000F00u);
+      e = ((w[0] << 2) & 0x3C3C3C3Cu) | ((t << 6) & 0xC0C0C0C0u);
+      o = ((w[0] >> 2) & 0x3C3C3C3Cu) | ((t << 4) & 0xC0C0C0C0u);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) out[c] = sbyte((c & 1) ? o : e, c >> 1);
+  }
 }
 
 // Store the lane's part of row p: F16 from x, else the codes in the low bits of tb (two's
@@ -216,8 +247,8 @@ struct StqSmem {
 // The step's per-row scalars in two halves, so that their loads overlap the state loads while
 // the state is decoded in between: stq_stage_load issues the loads (k, q, the gate, v, the row
 // map, the fit's row weights and the stored row factors, one element per thread),
-// stq_stage_store writes them to LDS in storage order (srow = {gate_p, k_p, q_p, rf_p} with
-// rf = 1 for pivots, sv = v, sw2) and returns beta.
+// stq_stage_store writes them to LDS in storage order (srow = {gate_p, k_p, q_p, rf_p / scale_p}
+// with rf = 1 for pivots and scale_p the row kind's decode scale, sv = v, sw2) and returns beta.
 template <int D, int NT>
 struct StqStage {
   static constexpr int PER = (D + NT - 1) / NT;
@@ -253,7 +284,8 @@ __device__ __forceinline__ StqStage<D, NT> stq_stage_load(const StqArgs& a, rsrc
 }
 
 template <int D, int NT, int PER_KEY>
-__device__ __forceinline__ float stq_stage_store(const StqStage<D, NT>& st, int tid, float4* srow, float* sv,
+__device__ __forceinline__ float stq_stage_store(const StqStage<D, NT>& st, const StqBlock& blk, int tid,
+                                                 float4* srow, float* sv,
                                                  float* sw2, float* tmp) {
 #pragma unroll
   for (int n = 0; n < StqStage<D, NT>::PER; ++n) {
@@ -272,7 +304,10 @@ __device__ __forceinline__ float stq_stage_store(const StqStage<D, NT>& st, int 
     const int i = tid + n * NT;
     if (i < D) {
       const int j = st.src[n];
-      srow[i] = make_float4(PER_KEY ? tmp[2 * D + j] : st.g0, tmp[j], tmp[D + j], half_bits_to_float(st.rf[n]));
+      const int kind = stq_kind(blk, i);   // exact: a power-of-two division of a binary16 value
+      const float rfs = half_bits_to_float(st.rf[n]) *
+                        (kind == SK_I6 ? 1.0f / kDecodeScale<SK_I6> : (kind == SK_I4 ? 1.0f / kDecodeScale<SK_I4> : 1.0f));
+      srow[i] = make_float4(PER_KEY ? tmp[2 * D + j] : st.g0, tmp[j], tmp[D + j], rfs);
     }
   }
   __syncthreads();
@@ -281,8 +316,10 @@ __device__ __forceinline__ float stq_stage_store(const StqStage<D, NT>& st, int 
 
 // MODE = SM_STEP: one decode step (reads src, writes dst). SM_PACK: fp32 states (key order) ->
 // format. SM_UNPACK: format -> fp32 states (key order).
+// At least four waves per SIMD (<= 128 VGPRs): the step holds X (64 VGPRs at d = 128) and
+// is bound by how many units are in flight per CU; the allocator meets this without spilling.
 template <int D, int NW, int PER_KEY, int BF16, int MODE>
-__global__ __launch_bounds__(NW * 64) void stq_kernel(const StqArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) void stq_kernel(const StqArgs a) {
   using G = Geo<D, NW>;
   constexpr int CPL = G::CPL, RPL = G::RPL, RPS = G::RPS, NT = G::NT;
   constexpr bool EXACT = MODE == SM_PACK;
@@ -344,10 +381,11 @@ __global__ __launch_bounds__(NW * 64) void stq_kernel(const StqArgs a) {
         const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3), mine = stq_kind(blk, p);
         by_kind(k0, k3, mine, [&](auto KC) {
           constexpr int K = decltype(KC)::value;
+          stq_decode_row<D, K>(raw[t], top[t], X[t]);
+          if constexpr (K != SK_F16) {
+            const float rs_ = rfv[t] * (1.0f / kDecodeScale<K>);   // exact
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            const float v = stq_decode<K>(raw[t], top[t], c);
-            X[t][c] = K == SK_F16 ? v : v * (rfv[t] * csv[c]);
+            for (int c = 0; c < CPL; ++c) X[t][c] *= rs_ * csv[c];
           }
         });
         store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(a.S + (int64_t(bh) * D + rowmap[p]) * D + cg * CPL),
@@ -364,14 +402,14 @@ __global__ __launch_bounds__(NW * 64) void stq_kernel(const StqArgs a) {
         const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3), mine = stq_kind(blk, p);
         by_kind(k0, k3, mine, [&](auto KC) {
           constexpr int K = decltype(KC)::value;
+          stq_decode_row<D, K>(raw[t], top[t], X[t]);
+          if constexpr (K != SK_F16) {
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            const float v = stq_decode<K>(raw[t], top[t], c);
-            X[t][c] = K == SK_F16 ? v : v * csv[c];
+            for (int c = 0; c < CPL; ++c) X[t][c] *= csv[c];
           }
         });
       }
-      const float beta = stq_stage_store<D, NT, PER_KEY>(stage, tid, sm.srow, sm.sv, sm.sw2, &sm.red[0][0][0]);
+      const float beta = stq_stage_store<D, NT, PER_KEY>(stage, blk, tid, sm.srow, sm.sv, sm.sw2, &sm.red[0][0][0]);
       // (3) S' = diag(gate) S_hat (row multiplier gate_p * rf_p), and the partial column sums of
       // u = S'^T k and p = S'^T q
       float pu[CPL], pp[CPL], pqk = 0.0f;
@@ -439,13 +477,18 @@ __global__ __launch_bounds__(NW * 64) void stq_kernel(const StqArgs a) {
   for (int t = 0; t < RPL; ++t) {
     const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
     const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3), mine = stq_kind(blk, p);
+    float av[CPL];
     float mq = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const float ax = fabsf(X[t][c]);
-      float q = ax * rcs[c];
-      if constexpr (EXACT) q = fmaf(fmaf(-q, csx[c], ax), rcs[c], q);   // = fl(|x| / cs) (0 if cs = 0)
-      mq = fmaxf(mq, q);
+      if constexpr (EXACT) {
+        const float ax = fabsf(X[t][c]);
+        const float q = ax * rcs[c];
+        mq = fmaxf(mq, fmaf(fmaf(-q, csx[c], ax), rcs[c], q));   // = fl(|x| / cs) (0 if cs = 0)
+      } else {
+        av[c] = X[t][c] * rcs[c];
+        mq = fmaxf(mq, fabsf(av[c]));
+      }
     }
     const float m = max_row16(mq);
     const float qm = mine == SK_I8 ? 127.0f : (mine == SK_I6 ? 31.0f : 7.0f);
@@ -454,21 +497,23 @@ __global__ __launch_bounds__(NW * 64) void stq_kernel(const StqArgs a) {
     const float rf = half_bits_to_float(rb);
     if (mine != SK_F16 && cg == 0) buf_store<2>(dst, blk.orf + 2u * static_cast<uint32_t>(p - blk.n16), 0u, &rb);
     float rrf = 0.0f;
-    if (rf > 0.0f) rrf = EXACT ? __fdiv_rn(1.0f, rf) : __builtin_amdgcn_rcpf(rf);
+    if (rf > 0.0f) rrf = __builtin_amdgcn_rcpf(rf);
     uint32_t tb[CPL];
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      if constexpr (EXACT) {
-        const float y = (X[t][c] * rrf) * rcs[c];
-        float n = rintf(y);
-        if (fabsf(y - n) > 0.5f - 0x1p-13f) {
-          const float sc = rf * csx[c];   // exact: two binary16 significands
-          n = sc > 0.0f ? rintf(__fdiv_rn(X[t][c], sc)) : 0.0f;
-        }
+      for (int c = 0; c < CPL; ++c) {
+        const float sc = rf * csx[c];   // exact: two binary16 significands
+        float n = sc > 0.0f ? rintf(__fdiv_rn(X[t][c], sc)) : 0.0f;
         n = fminf(fmaxf(n, -qm), qm);
         tb[c] = __float_as_uint(n + kMagic);
-      } else {
-        tb[c] = __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(X[t][c] * rrf, rcs[c], kMagic), kMagic - qm, kMagic + qm));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) tb[c] = __float_as_uint(fmaf(av[c], rrf, kMagic));
+      if (__any(mine != SK_F16 && rf < 0x1p-14f)) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          tb[c] = __float_as_uint(__builtin_amdgcn_fmed3f(__uint_as_float(tb[c]), kMagic - qm, kMagic + qm));
       }
     }
     by_kind(k0, k3, mine, [&](auto KC) { stq_store<D, decltype(KC)::value>(dst, blk, p, cg, X[t], tb); });
