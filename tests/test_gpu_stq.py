@@ -38,6 +38,9 @@ def check_stq(bits, got, ref):
     dcs = np.abs(_f16_ord(sg) - _f16_ord(sr))
     assert dcs.max() <= 1 and (dcs == 0).mean() >= 0.99, f"column scales: max {dcs.max()}, eq {(dcs == 0).mean()}"
     ints = ~piv
+    if not ints.any():   # every row a pivot: no codes, no row factors, the column scales are 0
+        assert not sg.any() and not cg.any() and not rg.any()
+        return {"cs_eq": 1.0, "rf_eq": 1.0, "code_eq": 1.0}
     drf = np.abs(_f16_ord(rg[ints]) - _f16_ord(rr[ints]))
     assert drf.max() <= 2 and (drf == 0).mean() >= 0.99, f"row factors: max {drf.max()}, eq {(drf == 0).mean()}"
     dc = np.abs(cg.astype(np.int32) - cr.astype(np.int32))
@@ -84,8 +87,10 @@ def test_pack_and_unpack(D, H, n, pivots):
     assert np.array_equal(back.cpu().numpy(), ref.reshape(n, H, D, D))
 
 
-def _step_case(D, H, B, decay, dtype, pivots, seed, inplace):
-    rng, bits, impact, S = _state(seed, B, H, D, pivots)
+def _step_case(D, H, B, decay, dtype, pivots, seed, inplace, bits=None, impact=None):
+    rng, bits0, impact0, S = _state(seed, B, H, D, pivots)
+    bits = bits0 if bits is None else bits
+    impact = impact0 if impact is None else impact
     num = 2 * B + 1
     st = lib.StqState(num, H, D, bits, impact)
     slots = np.random.default_rng(seed).choice(num, B, replace=False)
@@ -126,3 +131,62 @@ def test_step(D, H, B, decay, dtype, pivots, inplace):
 def test_step_full_heads_kda():
     """64 slots x 32 KDA heads x 128 at the nominal 6-bit map (2 pivots per head)."""
     _log(str(_step_case(128, 32, 64, synth.KDA, "bf16", 2, 4242, True)))
+
+
+def _edge_map(name, H, D, rng):
+    """Precision maps at the edges of the layout: every kind in one row group, a single kind,
+    per-head ragged counts, zero row weights."""
+    impact = np.exp(rng.standard_normal((H, D))).astype(np.float32)
+    bits = np.empty((H, D), np.uint8)
+    for h in range(H):
+        perm = rng.permutation(D)
+        if name == "one_of_each":        # 1 pivot, one 8-bit and one 6-bit row, the rest 4-bit
+            counts = (1, 1, 1, D - 3)
+        elif name == "all16":
+            counts = (D, 0, 0, 0)
+        elif name == "all4":
+            counts = (0, 0, 0, D)
+        elif name == "ragged":           # different counts in every head, none a multiple of 4
+            n16 = (3 + 2 * h) % 11
+            n8 = ((5 + 7 * h) % 37 + 1) * D // 128
+            n6 = ((13 * h + 9) % 41 + 1) * D // 128
+            counts = (n16, n8, n6, D - n16 - n8 - n6)
+        else:
+            raise ValueError(name)
+        start = 0
+        for width, c in zip((16, 8, 6, 4), counts):
+            bits[h, perm[start:start + c]] = width
+            start += c
+    assert np.isin(bits, (16, 8, 6, 4)).all()
+    if name == "ragged":
+        impact[1] = 0.0                  # one head with all-zero weights: the unweighted fit
+    return bits, impact
+
+
+@pytest.mark.parametrize("name,D,decay,inplace", [
+    ("one_of_each", 128, synth.KDA, True),
+    ("all16", 64, synth.GDN, True),
+    ("all4", 128, synth.GDN, False),
+    ("ragged", 128, synth.KDA, True),
+    ("ragged", 64, synth.GDN, False),
+])
+def test_step_edge_maps(name, D, decay, inplace):
+    H, B = 5, 6
+    bits, impact = _edge_map(name, H, D, np.random.default_rng(len(name) + D))
+    _log(f"{name} D={D}: " + str(_step_case(D, H, B, decay, "bf16", 0, 7 * D + len(name), inplace, bits, impact)))
+
+
+def test_empty_batch_is_a_no_op():
+    D, H = 128, 2
+    rng, bits, impact, S = _state(3, 2, H, D)
+    st = lib.StqState(2, H, D, bits, impact)
+    sl = torch.arange(2, dtype=torch.int32, device="cuda")
+    st.quantize(to_dev(S), sl)
+    before = st.pool.clone()
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    z = torch.empty((0, H, D), dtype=torch.bfloat16, device="cuda")
+    st.decode_step(e, z, z, z, torch.empty((0, H), device="cuda"), torch.empty((0, H), device="cuda"),
+                   torch.empty((0, H, D), device="cuda"))
+    st.quantize(torch.empty((0, H, D, D), device="cuda"), e)
+    torch.cuda.synchronize()
+    assert torch.equal(st.pool, before)
