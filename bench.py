@@ -179,19 +179,32 @@ def cpu_baseline(seconds: float):
     vec = (inp.q[:n_slots].reshape(n, w.d), inp.k[:n_slots].reshape(n, w.d),
            inp.v[:n_slots].reshape(n, w.d), inp.alpha[:n_slots].reshape(n),
            inp.beta[:n_slots].reshape(n))
+    def timed(nthreads, budget):
+        calls = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.step_quant(mask, h, c, s, *vec, nthreads=nthreads)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return calls, el
+
     threads = oracle.default_threads()
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.step_quant(mask, h, c, s, *vec, nthreads=threads)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    calls, el = timed(threads, seconds)
+    calls1, el1 = timed(1, max(1.0, seconds / 4))
+    model = ""
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    alg = alg_bytes_per_update("damp", w.d, w.fp16_rows, False)
     return {"value": calls * n / el, "unit": "state-updates/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{calls} oracle steps of 2,048 (slot, head) DAMP updates (first 64 active "
-                      f"slots of the pool workload) in {el:.1f} s"}
+                      f"slots of the pool workload) in {el:.1f} s",
+            "gbs": calls * n * alg / el / 1e9,
+            "one_core": {"value": calls1 * n / el1, "sample": f"{calls1} steps in {el1:.1f} s"},
+            "cpu_model": model}
 
 
 def calibrate_budget(torch, lib, synth, dev, H, d, per_key, args):

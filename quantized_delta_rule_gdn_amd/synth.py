@@ -68,17 +68,20 @@ def _sigmoid_f32(g: np.ndarray) -> np.ndarray:
 
 
 def step_inputs(rng: np.random.Generator, B: int, H: int, D: int, decay: int = GDN,
-                dtype: str = "bf16", col_mult: np.ndarray | None = None) -> StepInputs:
+                dtype: str = "bf16", col_mult: np.ndarray | None = None,
+                gate_mean: float = 0.0) -> StepInputs:
     """q, k ~ N(0, 1) then L2-normalised in fp32; v ~ N(0, 1) (times the per-head column
     multipliers ``col_mult[H, D]`` if given); alpha = exp(-softplus(g)) = sigmoid(-g) with
-    g ~ N(0, 1), one per (slot, head) for GDN or per key channel for KDA; beta = sigmoid(N(0,1)).
-    Draw order: q, k, v, g, beta."""
+    g ~ N(gate_mean, 1), one per (slot, head) for GDN or per key channel for KDA;
+    beta = sigmoid(N(0,1)). Draw order: q, k, v, g, beta."""
     q = _unit_norm(rng.standard_normal((B, H, D), dtype=np.float32))
     k = _unit_norm(rng.standard_normal((B, H, D), dtype=np.float32))
     v = rng.standard_normal((B, H, D), dtype=np.float32)
     if col_mult is not None:
         v = (v * col_mult[None, :, :]).astype(np.float32)
     g = rng.standard_normal((B, H, D) if decay == KDA else (B, H))
+    if gate_mean:
+        g = g + gate_mean
     alpha = _sigmoid_f32(-g)
     beta = _sigmoid_f32(rng.standard_normal((B, H)))
     if dtype == "fp32":
@@ -169,10 +172,12 @@ def gdn64_step() -> StepInputs:
     return step_inputs(np.random.default_rng([w.seed, 2]), w.batch, w.heads, w.d, GDN, "bf16")
 
 
-def drift_step(t: int) -> StepInputs:
-    """Step t (0..2047) of the drift run, continuing from the warmed 64-slot GDN state."""
+def drift_step(t: int, gate_mean: float = 0.0) -> StepInputs:
+    """Step t (0..2047) of the drift run, continuing from the warmed 64-slot GDN state.
+    ``gate_mean`` < 0 gives the slow-decay variant (alpha near 1: errors are retained longer)."""
     w = DRIFT
-    return step_inputs(np.random.default_rng([w.seed, 1, t]), w.batch, w.heads, w.d, GDN, "bf16")
+    return step_inputs(np.random.default_rng([w.seed, 1, t]), w.batch, w.heads, w.d, GDN, "bf16",
+                       gate_mean=gate_mean)
 
 
 def kda256(slots: int | None = None):
