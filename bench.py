@@ -163,27 +163,64 @@ def time_launches(torch, launch, steps, warmup):
     return e0.elapsed_time(e1) / steps  # ms per launch
 
 
-def cpu_baseline(seconds: float):
-    """The oracle timed on this host's cores on a bounded sample of the same workload: the
-    first 64 active slots (x 32 heads = 2,048 updates per call) of the pool, DAMP format."""
+def cpu_baseline(seconds: float, mode: dict):
+    """The oracle timed on this host's cores on a bounded sample of the workload being measured:
+    its first 64 active slots (x heads units per call), in the format and mode the GPU runs.
+    ``mode``: workload (synth.Workload), inputs (its first StepInputs), rows (FP16 rows [H, r]),
+    and at most one of stq=(bits, impact), window=W, raw=(raw StepInputs for the fused pre-step),
+    budget=(r_per_head, row_map)."""
     import oracle
     from quantized_delta_rule_gdn_amd import synth
-    w = synth.POOL4096
-    n_slots = 64
-    S = synth.pool4096_states(0, n_slots).reshape(n_slots * w.heads, w.d, w.d)
-    rows = synth.pool4096_rows()
-    mask = np.broadcast_to(synth.rows_to_mask(rows, w.d), (n_slots, w.heads, w.d)).reshape(-1, w.d)
-    h, c, s = oracle.quantize(mask, S)
-    inp = synth.pool4096_step(0)
-    n = n_slots * w.heads
-    vec = (inp.q[:n_slots].reshape(n, w.d), inp.k[:n_slots].reshape(n, w.d),
-           inp.v[:n_slots].reshape(n, w.d), inp.alpha[:n_slots].reshape(n),
+    w, inp = mode["workload"], mode["inputs"]
+    n_slots = min(64, w.batch)
+    H, D = w.heads, w.d
+    n = n_slots * H
+    per_key = w.decay == synth.KDA
+    S = synth.normal_states(np.random.default_rng([w.seed, 99]), (n, D, D), 0.1)
+    vec = (inp.q[:n_slots].reshape(n, D), inp.k[:n_slots].reshape(n, D), inp.v[:n_slots].reshape(n, D),
+           inp.alpha[:n_slots].reshape(n, D) if per_key else inp.alpha[:n_slots].reshape(n),
            inp.beta[:n_slots].reshape(n))
+    if mode.get("budget") is not None:
+        r_h, row_map = mode["budget"]
+        mh = np.zeros((H, D), np.uint8)
+        for hh in range(H):
+            mh[hh, row_map[hh][:r_h[hh]]] = 1
+    else:
+        mh = synth.rows_to_mask(mode["rows"], D)
+    mask = np.ascontiguousarray(np.broadcast_to(mh, (n_slots, H, D)).reshape(n, D))
+    what = "DAMP"
+    if mode.get("stq") is not None:
+        bits, impact = mode["stq"]
+        bb = np.ascontiguousarray(np.broadcast_to(bits, (n_slots, H, D)).reshape(n, D))
+        ww = np.ascontiguousarray(np.broadcast_to(impact, (n_slots, H, D)).reshape(n, D))
+        st = oracle.stq_quantize(bb, ww, S)
+        call = lambda nt: oracle.stq_step(bb, ww, *st, *vec, nthreads=nt)
+        what = "STEPQuant-style"
+    elif mode.get("window"):
+        h, c, s = oracle.quantize(mask, S)
+        win = oracle.Window(mask, h, c, s, mode["window"])
+        call = lambda nt: win.step(*vec, nthreads=nt)
+        what = f"per-window (W = {mode['window']}) DAMP"
+    elif mode.get("raw") is not None:
+        raw = mode["raw"]
+        h, c, s = oracle.quantize(mask, S)
+        rv = (raw.q[:n_slots].reshape(n, D), raw.k[:n_slots].reshape(n, D),
+              raw.alpha[:n_slots].reshape(n, D) if per_key else raw.alpha[:n_slots].reshape(n),
+              raw.beta[:n_slots].reshape(n))
+
+        def call(nt):
+            qh, kh, a, bt = oracle.prestep(*rv)
+            oracle.step_quant(mask, h, c, s, qh, kh, vec[2], a, bt, nthreads=nt)
+        what = "pre-step + DAMP"
+    else:
+        h, c, s = oracle.quantize(mask, S)
+        call = lambda nt: oracle.step_quant(mask, h, c, s, *vec, nthreads=nt)
+
     def timed(nthreads, budget):
         calls = 0
         t0 = time.perf_counter()
         while True:
-            oracle.step_quant(mask, h, c, s, *vec, nthreads=nthreads)
+            call(nthreads)
             calls += 1
             el = time.perf_counter() - t0
             if el >= budget:
@@ -197,13 +234,12 @@ def cpu_baseline(seconds: float):
         model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
     except (OSError, StopIteration):
         pass
-    alg = alg_bytes_per_update("damp", w.d, w.fp16_rows, False)
     return {"value": calls * n / el, "unit": "state-updates/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{calls} oracle steps of 2,048 (slot, head) DAMP updates (first 64 active "
-                      f"slots of the pool workload) in {el:.1f} s",
-            "gbs": calls * n * alg / el / 1e9,
-            "one_core": {"value": calls1 * n / el1, "sample": f"{calls1} steps in {el1:.1f} s"},
+            "sample": f"{calls} oracle calls of {n:,} (slot, head) {what} updates (the first {n_slots} "
+                      f"active slots of the workload) in {el:.1f} s",
+            "gbs": calls * n * mode["alg_bytes"] / el / 1e9,
+            "one_core": {"value": calls1 * n / el1, "sample": f"{calls1} calls in {el1:.1f} s"},
             "cpu_model": model}
 
 
@@ -436,7 +472,13 @@ def main():
                              for f, v in results.items() if f != "damp"}
         line["speedup_vs_fp32"] = results["fp32"]["ms_per_step"] / results["damp"]["ms_per_step"]
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        mode = {"workload": w, "inputs": inputs[0], "rows": rows,
+                "alg_bytes": results[main_fmt]["alg_bytes_per_launch"] / units,
+                "stq": (stq_bits, stq_impact) if args.stq else None,
+                "window": args.window,
+                "raw": raw[0] if args.fused_prestep else None,
+                "budget": (budget["r_per_head"], budget["row_map"]) if budget is not None else None}
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds, mode)
     print(json.dumps(line), flush=True)
 
 
