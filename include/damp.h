@@ -331,14 +331,18 @@ damp_status damp_allocate_rows(const double* score, int32_t num_heads, int32_t d
  * with w_i the frozen row-impact score (all w_i = 0 in a head means equal weights), binary32
  * divisions and binary16 round-to-nearest-even. The page names this fit (key-row-aware
  * dual-axis fitting, one shared column-scale vector fitted with squared row-impact factors) but
- * prints no formula: the formulas are the library's reading.
+ * prints no formula: the formulas are the library's reading. The device sums the column sums
+ * of squares in fp32 (a column scale can land one binary16 step from the binary64 fit where the
+ * sum sits at a rounding tie). stq_state_quantize takes every other decision as written; inside
+ * stq_decode_step the row maximum and the codes use products with rounded reciprocals, so a
+ * code can differ by one where its quotient lies within a few ulps of a half-integer.
  * Block of (slot, head): storage rows ordered pivots, 8-bit, 6-bit, 4-bit (each by ascending key
  * index): FP16 pivot rows (2 d bytes each) | 8-bit rows (d bytes) | 6-bit rows (3 d / 4 bytes: d / 2
  * bytes of low nibbles, then d / 4 bytes of the top two bits: column c at bits 4 (c mod 2) of byte
  * c / 2 and 2 (c mod 4) of byte c / 4) | 4-bit rows (d / 2 bytes, nibbles as in the 6-bit rows' low
- * plane) | FP16 row factors of the
- * integer rows (storage order) | FP16 column scales (d) | zero padding to 256 bytes; codes are two's
- * complement. A slot is its heads' blocks in order. Supported: d_k = d_v = d in {64, 128}.
+ * plane) | FP16 row factors of the integer rows (storage order) | FP16 column scales (d) | zero
+ * padding to 256 bytes; codes are two's complement. A slot is its heads' blocks in order.
+ * Supported: d_k = d_v = d in {64, 128}.
  * ------------------------------------------------------------------------------------- */
 typedef struct stq_state stq_state;
 
