@@ -1,0 +1,44 @@
+"""CPU checks of bench.py's host logic: the algorithmic bytes it divides by, the window average,
+the traffic file's source hash, and the one-GPU guard."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_bytes_per_update():
+    # block 2 x 19,872 + q, k, v bf16 (768) + alpha (4) + beta (4) + readout (512) + slot index (4)
+    assert bench.alg_bytes_per_update("damp", 128, 24, False) == 2 * 19872 + 1292 == 41036
+    assert bench.alg_bytes_per_update("damp", 128, 24, True) == 41036 + 508 == 41544   # KDA gate
+    assert bench.alg_bytes_per_update("int8", 128) == 2 * 16896 + 1292 == 35084
+    assert bench.alg_bytes_per_update("fp32", 128) == 2 * 65536 + 1292 == 132364
+    assert bench.alg_bytes_per_update("damp", 128, 24, False, qkv_bytes=4) == 41036 + 768
+
+
+def test_window_bytes_reduce_to_the_per_token_step():
+    # a window of one token reads and writes the block once per token, plus the empty header
+    assert abs(bench.alg_bytes_window(1) - (41036 + 4)) < 1e-9
+    w4, w8 = bench.alg_bytes_window(4), bench.alg_bytes_window(8)
+    assert w4 < 41036 and w8 < 41036          # the block is written once per window
+    assert w8 > w4                            # the buffered terms grow with the window
+
+
+def test_traffic_is_reported_only_for_the_profiled_source():
+    t = bench.measured_traffic()
+    if t is None:
+        pytest.skip("the step's source changed since its HBM counters were taken (traffic: null)")
+    # counter bytes of one pool4096 launch (32,768 updates) within 1% of the algorithmic bytes
+    assert abs(t / (32768 * 41036) - 1) < 0.01
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
