@@ -1,0 +1,65 @@
+"""The steps inside a HIP graph: one damp_decode_step (and one in-place STEPQuant-style step)
+captured with torch.cuda.graph and replayed several times, with eager work and synchronisation
+between the replays; every replay must equal, bit for bit, the same step run eagerly the same
+number of times (the states evolve in place, so replay i is eager step i)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+from gpu_common import step_tensors, to_dev  # noqa: E402
+from quantized_delta_rule_gdn_amd import lib, synth  # noqa: E402
+
+B, H, D, r, REPLAYS = 24, 4, 128, 24, 4
+
+
+def _run(make_state, step):
+    inp = step_tensors(synth.step_inputs(np.random.default_rng(8), B, H, D, synth.GDN, "bf16"))
+    slots = to_dev(np.random.default_rng(9).choice(2 * B, B, replace=False).astype(np.int32))
+    S = torch.randn((B, H, D, D), generator=torch.Generator(device="cuda").manual_seed(10), device="cuda") * 0.1
+    eager, graphed = make_state(), make_state()
+    eager.quantize(S, slots)
+    graphed.pool.copy_(eager.pool)
+    out_e = torch.empty((B, H, D), device="cuda")
+    out_g = torch.empty((B, H, D), device="cuda")
+    # warm-up on a scratch state: first launches load the kernels outside the capture
+    scratch = make_state()
+    scratch.pool.copy_(eager.pool)
+    step(scratch, slots, inp, out_g)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(graphed, slots, inp, out_g)
+    torch.cuda.synchronize()
+    noise = torch.zeros(1 << 20, device="cuda")
+    for i in range(REPLAYS):
+        step(eager, slots, inp, out_e)
+        g.replay()
+        noise.add_(1.0)                      # the program's own eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"readout of replay {i}"
+        assert torch.equal(graphed.pool, eager.pool), f"state after replay {i}"
+
+
+def test_damp_step_in_a_graph():
+    rows = synth.random_rows(np.random.default_rng(7), H, D, r)
+
+    def make():
+        st = lib.DampState(2 * B, H, D, rows)
+        st.pool.zero_()
+        return st
+
+    _run(make, lambda st, sl, x, out: st.decode_step(sl, *x, out))
+
+
+def test_stq_step_in_a_graph():
+    bits, impact = synth.stq_map(np.random.default_rng(6), H, D)
+
+    def make():
+        st = lib.StqState(2 * B, H, D, bits, impact)
+        return st
+
+    _run(make, lambda st, sl, x, out: st.decode_step(sl, *x, out))
