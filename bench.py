@@ -10,13 +10,17 @@ Cache. Other workloads (--workload gdn64 | kda256 | drift) have 64 or 256 contig
 state fits in that cache: gdn64 and kda256 rotate over enough copies of the pool that each launch
 finds its state in HBM (cold), drift reruns the same 64 slots (warm, labelled so).
 
-A step = one damp_decode_step launch over the batch (reconstruct, decay, delta update, readout,
-requantize). Timing: HIP events recorded on the stream the kernels are launched on, around
-exactly --steps launches after --warmup untimed ones, with device synchronisation on both sides.
+A step = one pass of the decode step over the batch (reconstruct, decay, delta update, readout,
+requantize). On pool4096 a step is two launches: damp_batch_order lists the batch by ascending
+slot, then damp_decode_step_ordered takes the units in that order (the results are those of
+damp_decode_step bit for bit; nearby blocks stream faster together). Smaller batches run
+damp_decode_step alone (--order). Timing: HIP events recorded on the stream the kernels are
+launched on, around exactly --steps steps after --warmup untimed ones, with device
+synchronisation on both sides.
 
 Prints ONE JSON line. value = (slot, head) state updates per second. roofline.achieved uses the
 algorithmic bytes of one update (state block read + written, q/k/v, alpha, beta, readout, slot
-index) times the updates per launch, divided by the average launch time.
+index) times the updates per step, divided by the average step time (both launches).
 """
 from __future__ import annotations
 
@@ -32,6 +36,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+# Batches of at least this many (slot, head) units run the step in ascending slot order under
+# --order auto. The step keeps about 3,000 units in flight (12 per CU); a batch that spans many
+# such waves gains from streaming nearby blocks together more than the ordering launch costs
+# (about 2 us), a batch that is resident at once does not.
+ORDER_MIN_UNITS = 16384
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "damp_step_pool4096_hbm_traffic.txt")
 # the DAMP step's kernel source: its building blocks and its kernels
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_delta_rule_gdn_amd", "csrc", f)
@@ -116,6 +125,11 @@ def parse():
     p.add_argument("--stq", action="store_true",
                    help="the STEPQuant-style state instead of DAMP (FP16 pivots, 8/6/4-bit rows at "
                         "a nominal 6-bit map, FP16 row factors and column scales refitted each step)")
+    p.add_argument("--order", choices=["auto", "on", "off"], default="auto",
+                   help="DAMP step (uniform or per-head layout) with the batch taken in ascending "
+                        "slot order: damp_batch_order runs inside every timed step, then "
+                        "damp_decode_step_ordered; auto = on for batches of at least "
+                        f"{ORDER_MIN_UNITS} units")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the step, run a plain device copy of MIB MiB --steps times "
                         "(the reference kernel of known size for HBM byte counters)")
@@ -355,6 +369,18 @@ def main():
               f"{budget['r_per_head']}; risk scores {budget['risk_scores_ms']:.3f} ms, allocation "
               f"{budget['allocate_ms']:.3f} ms", file=sys.stderr, flush=True)
 
+    use_order = args.order == "on" or (args.order == "auto" and units >= ORDER_MIN_UNITS)
+    use_order = use_order and not (args.stq or args.window or args.fused_prestep)
+    order_bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(R)]
+
+    def ordered(fmt, st, launch_plain):
+        """The headline DAMP step lists its batch by slot first, then runs in that order;
+        "damp_batch_order" is the same step in batch order."""
+        def launch(i):
+            o = st.batch_order(slot_sets[i % R], out=order_bufs[i % R])
+            st.decode_step(slot_sets[i % R], *sets[i % 4], out, order=o)
+        return launch if (use_order and fmt == "damp") else launch_plain
+
     def run(fmt):
         if fmt == "damp" and args.stq:
             st = lib.StqState(pool_slots, H, d, stq_bits, stq_impact, device=dev)
@@ -382,18 +408,18 @@ def main():
                 kn = F.normalize(k.float(), dim=-1)
                 st.decode_step(slot_sets[i % R], qn, kn, v.float(), torch.sigmoid(-g), torch.sigmoid(b), out)
             prestep_info["unfused_ms"] = time_launches(torch, unfused, args.steps, args.warmup)
-        elif fmt == "damp" and budget is not None:
+        elif fmt in ("damp", "damp_batch_order") and budget is not None:
             st = lib.DampState(pool_slots, H, d, budget["row_map"], device=dev,
                                r_per_head=budget["r_per_head"])
             st.pool.zero_()
             fill_states(torch, st.quantize, all_slots, H, d, dev)
-            launch = lambda i: st.decode_step(slot_sets[i % R], *sets[i % 4], out)
+            launch = ordered(fmt, st, lambda i: st.decode_step(slot_sets[i % R], *sets[i % 4], out))
             keep = st
-        elif fmt in ("damp", "damp_token"):
+        elif fmt in ("damp", "damp_token", "damp_batch_order"):
             st = lib.DampState(pool_slots, H, d, rows, device=dev)
             st.pool.zero_()
             fill_states(torch, st.quantize, all_slots, H, d, dev)
-            launch = lambda i: st.decode_step(slot_sets[i % R], *sets[i % 4], out)
+            launch = ordered(fmt, st, lambda i: st.decode_step(slot_sets[i % R], *sets[i % 4], out))
             keep = st
         elif fmt == "fp32":
             pool = torch.zeros((pool_slots, H, d, d), dtype=torch.float32, device=dev)
@@ -415,10 +441,10 @@ def main():
             ab = (2 * stq_data + alg_bytes_per_update("damp", d, r, per_key) - 2 * (2 * r * d + (d - r) * d + 4 * (d - r))) * units
         elif fmt == "damp" and args.window:
             ab = alg_bytes_window(args.window, d, r, per_key) * units
-        elif fmt == "damp_token":
+        elif fmt in ("damp", "damp_batch_order") and budget is not None:
+            ab = sum(alg_bytes_per_update("damp", d, int(rh), per_key) for rh in budget["r_per_head"]) * B
+        elif fmt in ("damp_token", "damp_batch_order"):
             ab = alg_bytes_per_update("damp", d, r, per_key) * units
-        elif fmt == "damp" and budget is not None:
-            ab = sum(alg_bytes_per_update(fmt, d, int(rh), per_key) for rh in budget["r_per_head"]) * B
         else:
             ab = alg_bytes_per_update(fmt, d, r, per_key) * units
         return {"ms_per_step": ms, "updates_per_s": units / (ms * 1e-3),
@@ -427,6 +453,8 @@ def main():
     fmts = [args.only] if args.only else (["damp"] if args.no_baselines else ["damp", "fp32", "int8"])
     if args.window and not args.only:
         fmts.insert(1, "damp_token")   # the per-token step on the same pool, for comparison
+    if use_order and "fp32" in fmts:
+        fmts.insert(1, "damp_batch_order")   # like for like with the baselines, which keep batch order
     for f in fmts:
         results[f] = run(f)
         label = "stq" if (f == "damp" and args.stq) else f
@@ -452,7 +480,9 @@ def main():
         "config": {"workload": desc, "format": "stq" if args.stq else main_fmt, "slots_active": B, "heads": H, "d": d,
                    "fp16_rows": r if budget is None else "per head", "global_batch": B, "seq_len": 1,
                    "state_cache": "cold (HBM)" if (cold or args.workload == "pool4096") else "warm (Infinity Cache)",
-                   "pool_copies": R},
+                   "pool_copies": R,
+                   "unit_order": "ascending slot (damp_batch_order + damp_decode_step_ordered, both "
+                                 "timed in every step)" if use_order else "batch order"},
         "roofline": {"bound": "hbm", "achieved": m["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": m["gbs"] / PEAK_HBM_GBS,
                      "traffic": measured_traffic() if (main_fmt == "damp" and args.workload == "pool4096"
@@ -470,7 +500,8 @@ def main():
         line["baselines"] = {f: {"ms_per_step": v["ms_per_step"], "updates_per_s": v["updates_per_s"],
                                  "gbs": v["gbs"], "frac": v["gbs"] / PEAK_HBM_GBS}
                              for f, v in results.items() if f != "damp"}
-        line["speedup_vs_fp32"] = results["fp32"]["ms_per_step"] / results["damp"]["ms_per_step"]
+        same = results.get("damp_batch_order", results["damp"])   # the baselines run in batch order
+        line["speedup_vs_fp32"] = results["fp32"]["ms_per_step"] / same["ms_per_step"]
     if not args.no_cpu_baseline:
         mode = {"workload": w, "inputs": inputs[0], "rows": rows,
                 "alg_bytes": results[main_fmt]["alg_bytes_per_launch"] / units,

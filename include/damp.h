@@ -176,6 +176,41 @@ damp_status damp_decode_step_fused(damp_state* state, const int32_t* slot_idx, i
                                    void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Processing order. The pages keep one state per concurrent request in a pool that grows with
+ * the number of requests ([C2] abstract and Fig. 1a); which slots a batch holds is up to the
+ * caller's scheduler, so they can lie anywhere in the pool. A step reads and writes each listed
+ * block once in any order, but HBM delivers the blocks faster when those a launch has in flight
+ * together lie close in the pool. These two calls let the step take the batch in slot order;
+ * the pages define no order, and no result depends on it.
+ * ------------------------------------------------------------------------------------- */
+
+/* order[0..B) = a permutation of [0, B) listing the batch positions by ascending slot bucket,
+ * bucket = min(max(slot_idx[b], 0), num_slots - 1) >> shift, with the smallest shift that gives
+ * at most 4,096 buckets (shift = 0, an exact sort, for pools of up to 4,096 slots). Positions in
+ * one bucket come in no fixed order. Any slot_idx values give a permutation (repeated or
+ * out-of-range entries included). One single-workgroup kernel on `stream`. A batch that keeps
+ * its slots can reuse the order for every later step and layer.
+ *   slot_idx dev int32 [B]
+ *   order    dev int32 [B], written; caller-owned, must not overlap slot_idx
+ * B == 0 is a no-op. Errors: INVALID_ARGUMENT (B < 0, num_slots <= 0, NULL or misaligned
+ * pointers, overlap), HIP. */
+damp_status damp_batch_order(const int32_t* slot_idx, int32_t B, int32_t num_slots, int32_t* order,
+                             void* stream);
+
+/* damp_decode_step with the batch positions taken in the order `order` lists them (the units of
+ * order[0] first, then those of order[1], ...). For any permutation, the results are exactly
+ * those of damp_decode_step, bit for bit. Uniform and per-head layouts.
+ *   order dev int32 [B]: a permutation of [0, B), e.g. from damp_batch_order. The units of an
+ *         entry outside [0, B) are skipped (no memory is touched for them). A repeated entry
+ *         updates its units twice at once: undefined, like a repeated slot. With DAMP_DEBUG=1 a
+ *         non-permutation returns DAMP_ERR_SLOT_INDEX.
+ * Other arguments and errors as damp_decode_step (order NULL or misaligned: INVALID_ARGUMENT). */
+damp_status damp_decode_step_ordered(damp_state* state, const int32_t* slot_idx, const int32_t* order,
+                                     int32_t B, const void* q, const void* k, const void* v,
+                                     damp_dtype qkv_dtype, const float* alpha, damp_decay decay,
+                                     const float* beta, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Per-window requantization (the LeapQuant page, abstract: the low-bit state stays fixed for a
  * window of tokens, the window's updates are held in high precision, outputs are computed from
  * both, and the state is quantized once at the window's end). Within a window the state of a

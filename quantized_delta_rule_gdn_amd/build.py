@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdamp.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("damp_api.hip", "step_kernels.hip", "window_kernels.hip", "calib_kernels.hip",
-            "stq_kernels.hip")]
+            "stq_kernels.hip", "order_kernels.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -193,6 +193,23 @@ damp_status debug_check_slots(const int32_t* slot_idx, int32_t n, int32_t num_sl
   return DAMP_OK;
 }
 
+// DAMP_DEBUG=1: synchronously check that order is a permutation of [0, B).
+damp_status debug_check_order(const int32_t* order, int32_t B, hipStream_t stream) {
+  if (!debug_mode() || !order || B == 0) return DAMP_OK;
+  std::vector<int32_t> h(static_cast<size_t>(B));
+  hipError_t e = hipMemcpyAsync(h.data(), order, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(DAMP_ERR_HIP, "reading order for DAMP_DEBUG: %s", hipGetErrorString(e));
+  std::vector<unsigned char> seen(static_cast<size_t>(B), 0);
+  for (int32_t i = 0; i < B; ++i) {
+    const int32_t p = h[static_cast<size_t>(i)];
+    if (p < 0 || p >= B || seen[static_cast<size_t>(p)])
+      return fail(DAMP_ERR_SLOT_INDEX, "order is not a permutation of [0, %d): order[%d] = %d", B, i, p);
+    seen[static_cast<size_t>(p)] = 1;
+  }
+  return DAMP_OK;
+}
+
 damp_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(DAMP_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return ok();
@@ -297,11 +314,15 @@ damp_status run_step(int fmt, const damp::StateRef& ref, int32_t d, int32_t H, i
                      const int32_t* slot_idx, int32_t B, const void* q, const void* k,
                      const void* v, damp_dtype dt, const float* alpha, damp_decay decay,
                      const float* beta, float* out, void* stream, int prestep = 0,
-                     void* win = nullptr, int32_t window = 0, bool flush_only = false) {
+                     void* win = nullptr, int32_t window = 0, bool flush_only = false,
+                     const int32_t* order = nullptr) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   damp_status st = debug_check_slots(slot_idx, B, num_slots, s);
   if (st != DAMP_OK) return st;
+  st = debug_check_order(order, B, s);
+  if (st != DAMP_OK) return st;
   damp::StepArgs a{};
+  a.order = order;
   a.st = ref;
   a.slot_idx = slot_idx;
   a.B = B;
@@ -328,7 +349,7 @@ damp_status run_step(int fmt, const damp::StateRef& ref, int32_t d, int32_t H, i
 
 extern "C" {
 
-int32_t damp_abi_version(void) { return (1 << 16) | 0; }
+int32_t damp_abi_version(void) { return (1 << 16) | 1; }
 
 const char* damp_last_error(void) { return g_last_error.c_str(); }
 
@@ -547,6 +568,35 @@ damp_status damp_decode_step(damp_state* s, const int32_t* slot_idx, int32_t B, 
   if (B == 0) return ok();
   return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, B, q, k, v,
                   dt, alpha, decay, beta, out, stream);
+}
+
+damp_status damp_batch_order(const int32_t* slot_idx, int32_t B, int32_t num_slots, int32_t* order,
+                             void* stream) {
+  if (B < 0) return fail(DAMP_ERR_INVALID_ARGUMENT, "B (%d) must be >= 0", B);
+  if (num_slots <= 0) return fail(DAMP_ERR_INVALID_ARGUMENT, "num_slots (%d) must be positive", num_slots);
+  if (B == 0) return ok();
+  if (!slot_idx || !order) return fail(DAMP_ERR_INVALID_ARGUMENT, "NULL slot_idx or order");
+  if (!aligned(slot_idx, 4) || !aligned(order, 4))
+    return fail(DAMP_ERR_INVALID_ARGUMENT, "slot_idx and order must be 4-byte aligned");
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(slot_idx), a1 = reinterpret_cast<uintptr_t>(order);
+  const uintptr_t n = sizeof(int32_t) * static_cast<uintptr_t>(B);
+  if (a0 < a1 + n && a1 < a0 + n) return fail(DAMP_ERR_INVALID_ARGUMENT, "order overlaps slot_idx");
+  return launched(damp::launch_batch_order(slot_idx, B, num_slots, order, static_cast<hipStream_t>(stream)),
+                  "batch order");
+}
+
+damp_status damp_decode_step_ordered(damp_state* s, const int32_t* slot_idx, const int32_t* order,
+                                     int32_t B, const void* q, const void* k, const void* v,
+                                     damp_dtype dt, const float* alpha, damp_decay decay,
+                                     const float* beta, float* out, void* stream) {
+  if (!s) return fail(DAMP_ERR_INVALID_ARGUMENT, "state is NULL");
+  const damp_layout& L = s->layout;
+  damp_status st = check_step_args(B, L.num_heads, L.d_k, slot_idx, q, k, v, dt, alpha, decay, beta, out);
+  if (st != DAMP_OK) return st;
+  if (B == 0) return ok();
+  if (!order || !aligned(order, 4)) return fail(DAMP_ERR_INVALID_ARGUMENT, "order is NULL or misaligned");
+  return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, B, q, k, v,
+                  dt, alpha, decay, beta, out, stream, 0, nullptr, 0, false, order);
 }
 
 damp_status damp_decode_step_fused(damp_state* s, const int32_t* slot_idx, int32_t B, const void* q,

@@ -52,6 +52,7 @@ struct StepArgs {
   uint8_t* win;             // per-window requantization: the window buffers (else nullptr)
   int64_t win_stride;       //   bytes per (slot, head) buffer
   int32_t window;           //   tokens per window, 1 .. 8
+  const int32_t* order;     // [B]: workgroups take batch positions in this order (nullptr: 0 .. B-1)
 };
 
 struct PackArgs {
@@ -71,6 +72,13 @@ hipError_t launch_dequantize(int d, const PackArgs& a, hipStream_t s);
 hipError_t launch_window(int d, int per_key, int bf16, bool flush_only, const StepArgs& a,
                          hipStream_t s);
 int window_max();
+
+// Batch order (order_kernels.hip): order[0..B) = the batch positions by ascending slot bucket,
+// bucket = clamp(slot, 0, num_slots - 1) >> order_shift(num_slots), at most kOrderBuckets buckets.
+constexpr int kOrderBuckets = 4096;
+int order_shift(int32_t num_slots);
+hipError_t launch_batch_order(const int32_t* slot_idx, int32_t B, int32_t num_slots, int32_t* order,
+                              hipStream_t s);
 
 // STEPQuant-style state (stq_kernels.hip). The block of (slot, head) is at pool + slot *
 // slot_stride + heads[head].x; heads[head] = {offset, n16 | n8 << 8 | n6 << 16 | n4 << 24,

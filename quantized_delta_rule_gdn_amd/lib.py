@@ -36,6 +36,7 @@ EXPORTS = (
     "damp_allocate_rows", "damp_decode_step_fused", "damp_window_bytes", "damp_window_step",
     "damp_window_flush", "stq_state_bytes", "stq_state_alloc", "stq_state_free",
     "stq_state_head_info", "stq_state_quantize", "stq_state_dequantize", "stq_decode_step",
+    "damp_batch_order", "damp_decode_step_ordered",
 )
 
 
@@ -103,6 +104,9 @@ def load() -> ctypes.CDLL:
         "stq_state_dequantize": ([P, P, P, I32, P], ctypes.c_int),
         "stq_decode_step": ([P, P, P, I32, P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, P],
                             ctypes.c_int),
+        "damp_batch_order": ([P, I32, I32, P, P], ctypes.c_int),
+        "damp_decode_step_ordered": ([P, P, P, I32, P, P, P, ctypes.c_int, P, ctypes.c_int, P, P,
+                                      P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -299,13 +303,25 @@ class DampState:
         _check(load().damp_state_dequantize(self._h, _ptr(S), _ptr(slot_idx), n, _stream(stream)))
         return S
 
-    def decode_step(self, slot_idx, q, k, v, alpha, beta, out, stream=None) -> None:
+    def decode_step(self, slot_idx, q, k, v, alpha, beta, out, stream=None, order=None) -> None:
+        """One decode step; with ``order`` (int32 [B], a permutation of the batch positions, as
+        ``batch_order`` makes) the units are processed in that order."""
         B, dt, decay = _step_vectors(slot_idx, q, k, v, alpha, beta, out, self.num_heads, self.d)
         if slot_idx.device != self.pool.device:
             raise ValueError("slot_idx and the pool are on different devices")
-        _check(load().damp_decode_step(self._h, _ptr(slot_idx), B, _ptr(q), _ptr(k), _ptr(v),
-                                       dt, _ptr(alpha), decay, _ptr(beta), _ptr(out),
-                                       _stream(stream)))
+        if order is None:
+            _check(load().damp_decode_step(self._h, _ptr(slot_idx), B, _ptr(q), _ptr(k), _ptr(v),
+                                           dt, _ptr(alpha), decay, _ptr(beta), _ptr(out),
+                                           _stream(stream)))
+            return
+        _need(order, "order", _torch().int32, (B,), self.pool.device)
+        _check(load().damp_decode_step_ordered(self._h, _ptr(slot_idx), _ptr(order), B, _ptr(q),
+                                               _ptr(k), _ptr(v), dt, _ptr(alpha), decay,
+                                               _ptr(beta), _ptr(out), _stream(stream)))
+
+    def batch_order(self, slot_idx, out=None, stream=None):
+        """The batch positions by ascending slot of this pool (damp_batch_order)."""
+        return batch_order(slot_idx, self.num_slots, out=out, stream=stream)
 
 
     def decode_step_fused(self, slot_idx, q, k, v, gate_logit, beta_logit, out, stream=None) -> None:
@@ -350,6 +366,19 @@ class DampState:
         _need(wbuf, "window buffer", torch.uint8, (wbuf.numel(),), self.pool.device)
         if wbuf.numel() < need:
             raise ValueError(f"window buffer has {wbuf.numel()} bytes, {need} needed")
+
+
+def batch_order(slot_idx, num_slots: int, out=None, stream=None):
+    """int32 [B] permutation of the batch positions by ascending slot bucket of a pool of
+    ``num_slots`` slots (damp_batch_order), written into ``out`` if given."""
+    torch = _torch()
+    B = slot_idx.shape[0]
+    _need(slot_idx, "slot_idx", torch.int32, (B,))
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=slot_idx.device)
+    _need(out, "order", torch.int32, (B,), slot_idx.device)
+    _check(load().damp_batch_order(_ptr(slot_idx), B, num_slots, _ptr(out), _stream(stream)))
+    return out
 
 
 def fp32_decode_step(pool, slot_idx, q, k, v, alpha, beta, out, stream=None) -> None:

@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.damp_abi_version() == (1 << 16)
+    assert L.damp_abi_version() == (1 << 16) | 1
 
 
 def test_block_accounting_d128():
@@ -235,3 +235,23 @@ def test_calibration_entry_points_reject_bad_arguments_on_host():
     assert L.damp_allocate_rows(p, 64, 128, 8, 1, 128, p, p, None) == lib.DAMP_ERR_UNSUPPORTED
     assert "groups" in lib.last_error()
     assert L.damp_allocate_rows(None, 2, 16, 8, 1, 16, p, p, None) == E
+
+
+def test_order_entry_points_reject_bad_arguments_on_host():
+    L = lib.load()
+    a, o = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    bad = lib.DAMP_ERR_INVALID_ARGUMENT
+    assert L.damp_batch_order(a, -1, 16, o, None) == bad
+    assert L.damp_batch_order(a, 4, 0, o, None) == bad and "num_slots" in lib.last_error()
+    assert L.damp_batch_order(None, 4, 16, o, None) == bad
+    assert L.damp_batch_order(a, 4, 16, None, None) == bad
+    assert L.damp_batch_order(a, 4, 16, ctypes.c_void_p(0x200002), None) == bad
+    assert "aligned" in lib.last_error()
+    # order overlapping slot_idx (both ways), and adjacent buffers that do not overlap
+    assert L.damp_batch_order(a, 4, 16, ctypes.c_void_p(0x10000c), None) == bad
+    assert "overlaps" in lib.last_error()
+    assert L.damp_batch_order(ctypes.c_void_p(0x10000c), 4, 16, a, None) == bad
+    # B == 0 is a no-op that needs no GPU
+    assert L.damp_batch_order(None, 0, 16, None, None) == lib.DAMP_OK
+    assert L.damp_decode_step_ordered(None, a, o, 1, a, a, a, 0, a, 0, a, a, None) == bad
+    assert "state is NULL" in lib.last_error()

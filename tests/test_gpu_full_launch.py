@@ -171,3 +171,27 @@ def test_budget_layout_pool4096_launch():
                                      st.slots()[torch.from_numpy(slots[SAMPLE_B]).long().cuda()].cpu().numpy(), D)
     _log(f"budget pool4096 (r per head {sorted(set(r_per_head.tolist()))}): " +
          str(check_quant(mask, got, (h.reshape(ns, H, D, D), c.reshape(ns, H, D, D), s.reshape(ns, H, D)))))
+
+
+def test_ordered_step_pool4096_launch():
+    """The benchmark's step at its launch configuration: batch_order, then the step in that
+    order, against the step in batch order on a copy of the pool -- every byte of the pool and
+    every readout equal (inactive slots included, which keep their sentinel)."""
+    rows = synth.pool4096_rows()
+    slots = synth.pool4096_slots()
+    ref = _damp_pool(rows, slots, 9)
+    got = lib.DampState(W.pool_slots, H, D, rows)
+    got.pool.copy_(ref.pool)
+    slots_dev = to_dev(slots)
+    order = got.batch_order(slots_dev)
+    assert np.array_equal(slots[order.cpu().numpy()], np.sort(slots))
+    for t in range(2):
+        x = step_tensors(synth.pool4096_step(t))
+        o_ref = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+        o_got = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+        ref.decode_step(slots_dev, *x, o_ref)
+        got.decode_step(slots_dev, *x, o_got, order=order)
+        torch.cuda.synchronize()
+        assert torch.equal(o_got, o_ref), f"readout, step {t}"
+        assert torch.equal(got.pool, ref.pool), f"pool, step {t}"
+    _inactive_untouched(got.blocks(), slots)
