@@ -1,5 +1,5 @@
-"""The steps inside a HIP graph: one damp_decode_step (and one in-place STEPQuant-style step)
-captured with torch.cuda.graph and replayed several times, with eager work and synchronisation
+"""The steps inside a HIP graph: one damp_decode_step (plain, and in slot order after
+damp_batch_order; and one in-place STEPQuant-style step) captured with torch.cuda.graph and replayed several times, with eager work and synchronisation
 between the replays; every replay must equal, bit for bit, the same step run eagerly the same
 number of times (the states evolve in place, so replay i is eager step i)."""
 import numpy as np
@@ -53,6 +53,23 @@ def test_damp_step_in_a_graph():
         return st
 
     _run(make, lambda st, sl, x, out: st.decode_step(sl, *x, out))
+
+
+def test_ordered_damp_step_in_a_graph():
+    """The benchmark's step: damp_batch_order into a fixed buffer, then the step in that order
+    (two launches captured together)."""
+    rows = synth.random_rows(np.random.default_rng(7), H, D, r)
+    order = torch.empty(B, dtype=torch.int32, device="cuda")
+
+    def make():
+        st = lib.DampState(2 * B, H, D, rows)
+        st.pool.zero_()
+        return st
+
+    def step(st, sl, x, out):
+        st.decode_step(sl, *x, out, order=st.batch_order(sl, out=order))
+
+    _run(make, step)
 
 
 def test_stq_step_in_a_graph():

@@ -50,10 +50,13 @@ def test_damp_steps_on_two_streams():
     o2 = [torch.empty((B // 2, H, D), device="cuda") for _ in steps]
     torch.cuda.synchronize()
     for i, (q, k, v, a, b) in enumerate(steps):
+        # stream 1 in batch order, stream 2 in slot order (its own order buffer, made on it)
         with torch.cuda.stream(s1):
             two.decode_step(sa, *(_split(x, True) for x in (q, k, v, a, b)), o1[i], stream=s1)
         with torch.cuda.stream(s2):
-            two.decode_step(sb, *(_split(x, False) for x in (q, k, v, a, b)), o2[i], stream=s2)
+            order = two.batch_order(sb, stream=s2)
+            two.decode_step(sb, *(_split(x, False) for x in (q, k, v, a, b)), o2[i], stream=s2,
+                            order=order)
     torch.cuda.synchronize()
     assert torch.equal(two.pool, ref.pool)
     for i in range(len(steps)):
