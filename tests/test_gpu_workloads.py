@@ -6,7 +6,8 @@
 * kda256:   256 slots x 32 KDA heads with lognormal value-column multipliers, 24 FP16 rows by
             score with per-channel mean gates, 4 INT8 rows per head scaled x20; one step.
 * pool4096: the benchmark's configuration: a 4,096-slot DAMP pool, 1,024 random active slots,
-            one step with the benchmark's first input set; every active unit compared, every
+            one step with the benchmark's first input set, launched as the benchmark launches it
+            (damp_batch_order, then the step in slot order); every active unit compared, every
             inactive block checked bit-identical.
 * drift:    the 64-slot state run for 2,048 steps in all three formats on the GPU; the oracle runs
             the same steps for a sample of units, and at sampled steps the GPU restarts from the
@@ -113,7 +114,8 @@ def test_kda256_damp():
 
 
 def test_pool4096_full_size():
-    """The benchmark's launch: 1,024 of 4,096 slots, 32 heads, d = 128, r = 24, bf16 inputs."""
+    """The benchmark's launch: 1,024 of 4,096 slots, 32 heads, d = 128, r = 24, bf16 inputs,
+    the batch ordered by slot and the step taken in that order."""
     w = synth.POOL4096
     B, H, D, r = w.batch, w.heads, w.d, w.fp16_rows
     slots = synth.pool4096_slots()
@@ -138,7 +140,8 @@ def test_pool4096_full_size():
     _log("pool4096 uploaded")
     q, k, v, a, b = step_tensors(inp)
     out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
-    st.decode_step(to_dev(slots), q, k, v, a, b, out)
+    slots_dev = to_dev(slots)
+    st.decode_step(slots_dev, q, k, v, a, b, out, order=st.batch_order(slots_dev))
     torch.cuda.synchronize()
     out = out.cpu().numpy()
     inactive = torch.ones(w.pool_slots, dtype=torch.bool, device="cuda")
