@@ -104,8 +104,19 @@ __device__ __forceinline__ void on_kind(int k0, int k3, int mine, F& f) {
   }
 }
 
+// The row group of storage rows p0 .. p0 + 3 (p0 wave-uniform, p = the lane's row): f(kind) runs
+// for each kind in the group, on the lanes whose row has it. A group almost always holds one
+// kind; then every lane takes it from the scalar kind of the group, and only a group that
+// straddles two kinds forms each lane's own kind (a branch the compiler may not flatten, so the
+// per-lane compares are not paid by every group).
 template <typename F>
-__device__ __forceinline__ void by_kind(int k0, int k3, int mine, F&& f) {
+__device__ __forceinline__ void by_kind(const StqBlock& blk, int p0, int p, F&& f) {
+  const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3);
+  int mine = k0;
+  if (k0 != k3) {
+    mine = stq_kind(blk, p);
+    asm volatile("" : "+v"(mine));
+  }
   on_kind<SK_F16>(k0, k3, mine, f);
   on_kind<SK_I8>(k0, k3, mine, f);
   on_kind<SK_I6>(k0, k3, mine, f);
@@ -356,9 +367,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
       const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
-      const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3), mine = stq_kind(blk, p);
       top[t] = 0;
-      by_kind(k0, k3, mine, [&](auto KC) { stq_load<D, decltype(KC)::value>(src, blk, p, cg, raw[t], top[t]); });
+      by_kind(blk, p0, p, [&](auto KC) { stq_load<D, decltype(KC)::value>(src, blk, p, cg, raw[t], top[t]); });
       if constexpr (MODE == SM_UNPACK) {
         const int ri = p - blk.n16;
         uint32_t rb[1];
@@ -378,8 +388,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 #pragma unroll
       for (int t = 0; t < RPL; ++t) {
         const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
-        const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3), mine = stq_kind(blk, p);
-        by_kind(k0, k3, mine, [&](auto KC) {
+        by_kind(blk, p0, p, [&](auto KC) {
           constexpr int K = decltype(KC)::value;
           stq_decode_row<D, K>(raw[t], top[t], X[t]);
           if constexpr (K != SK_F16) {
@@ -399,8 +408,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 #pragma unroll
       for (int t = 0; t < RPL; ++t) {
         const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
-        const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3), mine = stq_kind(blk, p);
-        by_kind(k0, k3, mine, [&](auto KC) {
+        by_kind(blk, p0, p, [&](auto KC) {
           constexpr int K = decltype(KC)::value;
           stq_decode_row<D, K>(raw[t], top[t], X[t]);
           if constexpr (K != SK_F16) {
@@ -472,51 +480,54 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   if constexpr (EXACT)
     load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sm.scs + cg * CPL), reinterpret_cast<uint32_t*>(csx));
 
-  // (6) per row: row factor, codes, store
+  // (6) per row: row factor, codes, store, with the row kind (and so qmax) known at compile time
 #pragma unroll
   for (int t = 0; t < RPL; ++t) {
     const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
-    const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3), mine = stq_kind(blk, p);
-    float av[CPL];
-    float mq = 0.0f;
+    by_kind(blk, p0, p, [&](auto KC) {
+      constexpr int K = decltype(KC)::value;
+      uint32_t tb[CPL];
+      if constexpr (K != SK_F16) {
+        constexpr float qm = K == SK_I8 ? 127.0f : (K == SK_I6 ? 31.0f : 7.0f);
+        constexpr float inv = 1.0f / qm;
+        float av[CPL];
+        float mq = 0.0f;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      if constexpr (EXACT) {
-        const float ax = fabsf(X[t][c]);
-        const float q = ax * rcs[c];
-        mq = fmaxf(mq, fmaf(fmaf(-q, csx[c], ax), rcs[c], q));   // = fl(|x| / cs) (0 if cs = 0)
-      } else {
-        av[c] = X[t][c] * rcs[c];
-        mq = fmaxf(mq, fabsf(av[c]));
+        for (int c = 0; c < CPL; ++c) {
+          if constexpr (EXACT) {
+            const float ax = fabsf(X[t][c]);
+            const float q = ax * rcs[c];
+            mq = fmaxf(mq, fmaf(fmaf(-q, csx[c], ax), rcs[c], q));   // = fl(|x| / cs) (0 if cs = 0)
+          } else {
+            av[c] = X[t][c] * rcs[c];
+            mq = fmaxf(mq, fabsf(av[c]));
+          }
+        }
+        const float m = max_row16(mq);
+        const uint32_t rb = float_to_half_bits(div_qmax(m, qm, inv));
+        const float rf = half_bits_to_float(rb);
+        if (cg == 0) buf_store<2>(dst, blk.orf + 2u * static_cast<uint32_t>(p - blk.n16), 0u, &rb);
+        if constexpr (EXACT) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const float sc = rf * csx[c];   // exact: two binary16 significands
+            float n = sc > 0.0f ? rintf(__fdiv_rn(X[t][c], sc)) : 0.0f;
+            n = fminf(fmaxf(n, -qm), qm);
+            tb[c] = __float_as_uint(n + kMagic);
+          }
+        } else {
+          const float rrf = rf > 0.0f ? __builtin_amdgcn_rcpf(rf) : 0.0f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) tb[c] = __float_as_uint(fmaf(av[c], rrf, kMagic));
+          if (__any(rf < 0x1p-14f)) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+              tb[c] = __float_as_uint(__builtin_amdgcn_fmed3f(__uint_as_float(tb[c]), kMagic - qm, kMagic + qm));
+          }
+        }
       }
-    }
-    const float m = max_row16(mq);
-    const float qm = mine == SK_I8 ? 127.0f : (mine == SK_I6 ? 31.0f : 7.0f);
-    const float inv = mine == SK_I8 ? 1.0f / 127.0f : (mine == SK_I6 ? 1.0f / 31.0f : 1.0f / 7.0f);
-    const uint32_t rb = float_to_half_bits(div_qmax(m, qm, inv));
-    const float rf = half_bits_to_float(rb);
-    if (mine != SK_F16 && cg == 0) buf_store<2>(dst, blk.orf + 2u * static_cast<uint32_t>(p - blk.n16), 0u, &rb);
-    float rrf = 0.0f;
-    if (rf > 0.0f) rrf = __builtin_amdgcn_rcpf(rf);
-    uint32_t tb[CPL];
-    if constexpr (EXACT) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const float sc = rf * csx[c];   // exact: two binary16 significands
-        float n = sc > 0.0f ? rintf(__fdiv_rn(X[t][c], sc)) : 0.0f;
-        n = fminf(fmaxf(n, -qm), qm);
-        tb[c] = __float_as_uint(n + kMagic);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) tb[c] = __float_as_uint(fmaf(av[c], rrf, kMagic));
-      if (__any(mine != SK_F16 && rf < 0x1p-14f)) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-          tb[c] = __float_as_uint(__builtin_amdgcn_fmed3f(__uint_as_float(tb[c]), kMagic - qm, kMagic + qm));
-      }
-    }
-    by_kind(k0, k3, mine, [&](auto KC) { stq_store<D, decltype(KC)::value>(dst, blk, p, cg, X[t], tb); });
+      stq_store<D, K>(dst, blk, p, cg, X[t], tb);
+    });
   }
 }
 
