@@ -18,8 +18,9 @@
 // (CPL = d/16 value columns each), the 4 row slots of a wave cover 4 consecutive storage rows,
 // and a row step of the workgroup covers 4 * NW rows, so each load/store instruction of a wave
 // touches 4 whole consecutive rows (512 B INT8 / 1 KiB FP16 / 2 KiB fp32 at d = 128):
-// fully coalesced. Column sums over key rows use the gfx950 cross-row lane swaps
-// (v_permlane16_swap / v_permlane32_swap) inside a wave and LDS across waves; the row absmax for
+// fully coalesced. Column sums over key rows go through LDS: every lane writes its partial sums
+// once and one thread per column adds them in a fixed order (only q.k, one value per lane, uses
+// the gfx950 cross-row lane swaps v_permlane16_swap / v_permlane32_swap); the row absmax for
 // requantization is a DPP butterfly inside the 16 lanes of a row. No MFMA: each unit is a
 // matrix-vector update at ~4 flop/byte, far below the fp32 ridge; the kernel is HBM-bound, and
 // its VALU work per state element is kept to about ten instructions so that it stays so
