@@ -219,7 +219,8 @@ def test_tiny_workload_every_step_from_identical_state():
 
 
 def test_debug_mode_rejects_bad_slots(monkeypatch):
-    """DAMP_DEBUG=1 validates slot indices on the host before launching anything."""
+    """DAMP_DEBUG=1 validates slot indices (and the ordered step's order) on the host before
+    launching anything."""
     import subprocess
     import sys
     import os
@@ -237,6 +238,14 @@ for bad in ([0, 4], [1, 1], [-1, 0]):
     except lib.DampError as e:
         assert e.status == lib.DAMP_ERR_SLOT_INDEX, e
 st.decode_step(torch.tensor([3, 0], dtype=torch.int32, device='cuda'), q, q, q, a, a, out)
+good = torch.tensor([3, 0], dtype=torch.int32, device='cuda')
+for bad in ([0, 0], [0, 2], [-1, 1]):   # the ordered step: order must be a permutation of [0, B)
+    try:
+        st.decode_step(good, q, q, q, a, a, out, order=torch.tensor(bad, dtype=torch.int32, device='cuda'))
+        raise SystemExit('accepted order %r' % (bad,))
+    except lib.DampError as e:
+        assert e.status == lib.DAMP_ERR_SLOT_INDEX, e
+st.decode_step(good, q, q, q, a, a, out, order=torch.tensor([1, 0], dtype=torch.int32, device='cuda'))
 torch.cuda.synchronize()
 print('ok')
 """
