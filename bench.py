@@ -69,15 +69,22 @@ def measured_traffic():
 
 def alg_bytes_window(W: int, d: int = 128, r: int = 24, per_key: bool = False, qkv_bytes: int = 2) -> float:
     """Bytes per (slot, head) update of the windowed step, averaged over the W tokens of a
-    window: every token reads the stored block and its buffered terms; a token that does not end
-    the window writes the decayed row gains and keys back and appends its key and delta (4 d
-    bytes each); the last one writes the block instead."""
+    window: every token reads the stored block and its buffered terms (keys and deltas, 4 d bytes
+    each); a token that does not end the window appends its key and delta, the last one writes
+    the block instead. The decay: with a gate per key row (KDA) the row gains (4 d bytes) and
+    every buffered key are read and written back decayed; with one gate per unit (GDN) the decay
+    is one number for the window and one per buffered key, in the buffer's header words."""
     block = 2 * r * d + (d - r) * d + 4 * (d - r)
     vecs = 3 * qkv_bytes * d + (4 * d if per_key else 4) + 4 + 4 * d + 4
     total = 0
     for t in range(W):
-        rd = block + 4 + (4 * d if t else 0) + t * 2 * 4 * d
-        wr = block if t == W - 1 else 4 + 4 * d + t * 4 * d + 2 * 4 * d
+        last = t == W - 1
+        if per_key:
+            rd = block + 4 + (4 * d if t else 0) + t * 2 * 4 * d
+            wr = block if last else 4 + 4 * d + t * 4 * d + 2 * 4 * d
+        else:
+            rd = block + 4 + (4 + 4 * t if t else 0) + t * 2 * 4 * d
+            wr = block if last else 12 + 4 * (t + 1) + 2 * 4 * d
         total += rd + wr + vecs
     return total / W
 

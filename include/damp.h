@@ -232,7 +232,10 @@ size_t damp_window_bytes(const damp_layout* layout, int32_t window);
  * is appended to the buffer; if it is the window's window-th token, X is stored in the unit's
  * rule (FP16 rows RNE, INT8 rows absmax / 127) and the buffer emptied. Otherwise the pool is only
  * read. window = 1 is the per-token step (the same arithmetic as damp_decode_step up to fp32
- * rounding order). A given buffer must always be used with the same window length.
+ * rounding order). A given buffer must always be used with the same window length and the same
+ * decay mode: with DAMP_DECAY_SCALAR the buffer holds the decay as scalars (one for the window,
+ * one per buffered key) and the keys as appended, with DAMP_DECAY_PER_KEY as row gains and
+ * decayed keys.
  * Errors: INVALID_ARGUMENT, SLOT_INDEX (debug), HIP. */
 damp_status damp_window_step(damp_state* state, void* window_buf, int32_t window,
                              const int32_t* slot_idx, int32_t B, const void* q, const void* k,

@@ -16,11 +16,18 @@ namespace {
 // buffered terms to u and p, and appends (k, delta); the state block is not written. The
 // window's last token also materialises X = diag(a') S_hat + sum K'_tau E_tau^T + k delta^T,
 // requantizes it in place and empties the buffer.
+// With one gate per unit (GDN) every row decays alike, so a is one number and the decay of K_tau
+// is one number c_tau: the keys are stored as appended and only the scalars change per token
+// (with a gate per key row, KDA, a and every K_tau are rewritten decayed).
 //
 // Window buffer of one unit, fp32 words at a.win + (slot * H + head) * a.win_stride bytes:
 //   [0]            t, the tokens applied in the current window (int32; 0 = empty, a = 1)
-//   [4, 4 + D)     a, storage row order
-//   [4 + D, ..)    K[tau][p], tau < W, storage row order
+//   [1]            scalar gate: a, the product of the window's gates so far
+//   [2]            1 for a window with a scalar gate (written by its tokens), 0 for per-row gates
+//   [4, 4 + D)     per-row gates: a, storage row order
+//                  scalar gate: [4, 4 + W) c[tau], the product of the gates after token tau
+//   [4 + D, ..)    K[tau][p], tau < W, storage row order (per-row gates: decayed; scalar gate:
+//                  as appended)
 //   then           E[tau][j], tau < W
 constexpr int kMaxWindow = 8;
 
@@ -38,7 +45,7 @@ struct WinSmem {
 
 struct WinPtr {
   int32_t* hdr;
-  float* A;
+  float* A;   // per-row gates: a; scalar gate: c[tau] (the same words)
   float* K;
   float* E;
 };
@@ -49,16 +56,27 @@ __device__ __forceinline__ WinPtr win_ptr(const StepArgs& a, int64_t slot, int h
   return WinPtr{reinterpret_cast<int32_t*>(wb), wb + 4, wb + 4 + D, wb + 4 + D + a.window * D};
 }
 
+// Whether the unit's window holds the scalar-gate form: a step knows it from its gate; a flush
+// (no token, no gate) reads the flag its tokens left.
+template <int PER_KEY, bool FLUSH_ONLY>
+__device__ __forceinline__ bool win_scalar(const WinPtr& wp, int t) {
+  if constexpr (!FLUSH_ONLY) return !PER_KEY;
+  return t > 0 && __builtin_amdgcn_readfirstlane(wp.hdr[2]) == 1;
+}
+
 // Staging of a window step (FLUSH_ONLY = false) or of a flush with no token (true). As
 // stage_rows, plus: a'_p = gate_p * a_p (a = 1 when the window is empty), srow.x = scale * a'_p,
 // srow.w = gate_p; every buffered key decayed, K'_tau,p = gate_p K_tau,p, and its dot products
 // with k and q summed per wave into sdot. Unless the window ends here, a' and K' go back to the
-// buffer. Returns beta.
+// buffer. Scalar gate (scal): a' = gate a and K'_tau = c'_tau K_tau with c'_tau = gate c_tau,
+// so the dot products are c'_tau (K_tau . k); a', c' and c[t] = 1 go back to the header words.
+// Returns beta.
 template <int D, int NT, int PER_KEY, int BF16, bool FLUSH_ONLY>
 __device__ __forceinline__ float stage_rows_win(const StepArgs& a, const WinPtr& wp, int t,
                                                 bool ends, const float* sc_old, int bh, int head,
                                                 int r, int tid, float4* srow, float* sv,
-                                                float* tmp, float (*sdot)[kMaxWindow][2]) {
+                                                float* tmp, float (*sdot)[kMaxWindow][2],
+                                                bool scal) {
   const int64_t vec = int64_t(bh) * D;
   constexpr int PER = (D + NT - 1) / NT;
   constexpr int NWS = NT / 64;
@@ -110,6 +128,9 @@ __device__ __forceinline__ float stage_rows_win(const StepArgs& a, const WinPtr&
     invq = nq > 0.0f ? rsqrtf(nq) : 0.0f;
     invk = nk > 0.0f ? rsqrtf(nk) : 0.0f;
   }
+  // scalar gate: the gate of this token (1 for a flush) and the window's product before it
+  const float gs = FLUSH_ONLY ? 1.0f : g0;
+  const float as = scal && t > 0 ? __int_as_float(__builtin_amdgcn_readfirstlane(wp.hdr[1])) : 1.0f;
   float kh[PER], qh[PER], gt[PER];
 #pragma unroll
   for (int n = 0; n < PER; ++n) {
@@ -122,9 +143,9 @@ __device__ __forceinline__ float stage_rows_win(const StepArgs& a, const WinPtr&
         kh[n] = tmp[src[n]] * invk;
         qh[n] = tmp[D + src[n]] * invq;
       }
-      const float ap = gt[n] * (t > 0 ? wp.A[i] : 1.0f);
+      const float ap = scal ? gs * as : gt[n] * (t > 0 ? wp.A[i] : 1.0f);
       srow[i] = make_float4(sc[n] * ap, kh[n], qh[n], gt[n]);
-      if (!FLUSH_ONLY && !ends) wp.A[i] = ap;
+      if (!FLUSH_ONLY && !ends && !scal) wp.A[i] = ap;
     }
   }
   if constexpr (!FLUSH_ONLY) {
@@ -134,14 +155,20 @@ __device__ __forceinline__ float stage_rows_win(const StepArgs& a, const WinPtr&
       for (int n = 0; n < PER; ++n) {
         const int i = tid + n * NT;
         if (i < D) {
-          const float kd = gt[n] * wp.K[tau * D + i];
-          if (!ends) wp.K[tau * D + i] = kd;
+          const float kb = wp.K[tau * D + i];
+          const float kd = scal ? kb : gt[n] * kb;
+          if (!scal && !ends) wp.K[tau * D + i] = kd;
           ck = fmaf(kd, kh[n], ck);
           cq = fmaf(kd, qh[n], cq);
         }
       }
       ck = wave_sum(ck);
       cq = wave_sum(cq);
+      if (scal) {
+        const float cf = gs * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wp.A[tau])));
+        ck *= cf;
+        cq *= cf;
+      }
       if ((tid & 63) == 0) {
         sdot[tid >> 6][tau][0] = ck;
         sdot[tid >> 6][tau][1] = cq;
@@ -149,6 +176,13 @@ __device__ __forceinline__ float stage_rows_win(const StepArgs& a, const WinPtr&
     }
   }
   __syncthreads();
+  // scalar gate: every wave has read the old words above; the next token's words go back now
+  if (!FLUSH_ONLY && scal && !ends && tid == 0) {
+    for (int tau = 0; tau < t; ++tau) wp.A[tau] = gs * wp.A[tau];
+    wp.A[t] = 1.0f;
+    wp.hdr[1] = __float_as_int(gs * as);
+    wp.hdr[2] = 1;
+  }
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(beta)));
 }
 
@@ -208,6 +242,7 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
   const int t = __builtin_amdgcn_readfirstlane(*wp.hdr);
   if (FLUSH_ONLY && t == 0) return;   // nothing pending (uniform over the workgroup)
   const bool ends = FLUSH_ONLY || t + 1 >= a.window;
+  const bool scal = win_scalar<PER_KEY, FLUSH_ONLY>(wp, t);
   float4* srow = sm.srow;
   float* sv = sm.sv;
   float* ssc = sm.ssc;
@@ -228,7 +263,7 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
   }
   const float beta = stage_rows_win<D, G::NT, PER_KEY, BF16, FLUSH_ONLY>(
       a, wp, t, ends, reinterpret_cast<const float*>(ua.s), bh, head, r, tid, srow, sv,
-      &sm.redu[0][0], sm.sdot);
+      &sm.redu[0][0], sm.sdot, scal);
   const float4* my_rows = srow + (w * 4 + rs);
 
   int terms = t;   // buffered terms in X at the window's end (the token's own one included)
@@ -271,7 +306,10 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
       sm.redp[tau][i] = srow[i].y;
     } else {
       sm.redu[tau][i] = wp.E[tau * D + i];
-      sm.redp[tau][i] = srow[i].w * wp.K[tau * D + i];
+      // K'_tau,p: per-row gates gate_p K_tau,p (K decayed up to the previous token); scalar
+      // gate (gate c_tau) K_tau,p with the key as appended
+      const float g = scal ? srow[i].w * wp.A[tau] : srow[i].w;
+      sm.redp[tau][i] = g * wp.K[tau * D + i];
     }
   }
   __syncthreads();

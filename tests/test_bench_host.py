@@ -23,9 +23,19 @@ def test_algorithmic_bytes_per_update():
 def test_window_bytes_reduce_to_the_per_token_step():
     # a window of one token reads and writes the block once per token, plus the empty header
     assert abs(bench.alg_bytes_window(1) - (41036 + 4)) < 1e-9
-    w4, w8 = bench.alg_bytes_window(4), bench.alg_bytes_window(8)
-    assert w4 < 41036 and w8 < 41036          # the block is written once per window
-    assert w8 > w4                            # the buffered terms grow with the window
+    assert abs(bench.alg_bytes_window(1, per_key=True) - (41544 + 4)) < 1e-9
+    for pk in (False, True):
+        w4, w8 = bench.alg_bytes_window(4, per_key=pk), bench.alg_bytes_window(8, per_key=pk)
+        assert w4 < 41036 and w8 < 41036      # the block is written once per window
+    # per-row gates: every buffered key is rewritten decayed each token, so the bytes grow with W
+    assert bench.alg_bytes_window(8, per_key=True) > bench.alg_bytes_window(4, per_key=True)
+    # one gate per unit, W = 2, by hand: token 0 reads the block and the count (19,872 + 4) and
+    # writes the header words, c[0], its key and its delta (12 + 4 + 512 + 512); token 1 reads the
+    # block, count, a, c[0], one key and one delta (19,872 + 4 + 4 + 4 + 1,024) and writes the
+    # block; each token also moves its 1,292 vector bytes
+    t0 = 19872 + 4 + 12 + 4 + 512 + 512 + 1292
+    t1 = 19872 + 4 + 4 + 4 + 1024 + 19872 + 1292
+    assert abs(bench.alg_bytes_window(2) - (t0 + t1) / 2) < 1e-9
 
 
 def test_traffic_is_reported_only_for_the_profiled_source():
