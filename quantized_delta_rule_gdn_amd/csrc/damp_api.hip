@@ -86,17 +86,15 @@ damp_status check_layout(const damp_layout* L) {
   return DAMP_OK;
 }
 
-size_t data_bytes(const damp_layout* L) {
-  const size_t d = static_cast<size_t>(L->d_k), r = static_cast<size_t>(L->num_fp16_rows);
-  return 2 * r * d + (d - r) * d + 4 * (d - r);
-}
-
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
+// Data bytes of one DAMP block: r FP16 rows, d - r INT8 rows, d - r fp32 scales.
 size_t data_bytes_r(int32_t d_, int32_t r_) {
   const size_t d = static_cast<size_t>(d_), r = static_cast<size_t>(r_);
   return 2 * r * d + (d - r) * d + 4 * (d - r);
 }
+
+size_t data_bytes(const damp_layout* L) { return data_bytes_r(L->d_k, L->num_fp16_rows); }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Layout checks of the per-head calls (num_fp16_rows not used); *L2 = the layout with
 // num_fp16_rows = -1.
