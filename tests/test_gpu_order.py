@@ -114,3 +114,29 @@ def test_order_entries_outside_the_batch_are_skipped():
     assert bool((o_got[-1] == 7.0).all()), "the skipped position's readout was written"
     assert torch.equal(got.blocks()[int(slots[-1])], before), "the skipped position's state changed"
     assert torch.equal(got.pool, ref.pool)
+
+
+@pytest.mark.parametrize("D,r,Bn,Hn,decay", [(16, 5, 9, 2, synth.KDA), (32, 8, 7, 3, synth.GDN),
+                                             (64, 4, 11, 2, synth.GDN), (128, 12, 5, 2, synth.KDA),
+                                             (128, 27, 6, 3, synth.GDN)])
+def test_ordered_step_every_instance(D, r, Bn, Hn, decay):
+    """Every d and launch plan (general r, r % 4 == 0, compile-time kinds): a random order gives the
+    batch-order step bit for bit."""
+    print(f"ordered step D={D} r={r} B={Bn} H={Hn}", flush=True)
+    rng = np.random.default_rng([D, r, Bn])
+    slots = rng.choice(3 * Bn, Bn, replace=False).astype(np.int32)
+    rows = synth.random_rows(rng, Hn, D, r)
+    g = torch.Generator(device="cuda").manual_seed(D + r)
+    ref, got = lib.DampState(3 * Bn, Hn, D, rows), lib.DampState(3 * Bn, Hn, D, rows)
+    ref.pool.fill_(SENTINEL)
+    ref.quantize(torch.randn((Bn, Hn, D, D), generator=g, device="cuda") * 0.1, to_dev(slots))
+    got.pool.copy_(ref.pool)
+    x = step_tensors(synth.step_inputs(np.random.default_rng([D, 1]), Bn, Hn, D, decay, "bf16"))
+    o_ref = torch.empty((Bn, Hn, D), device="cuda")
+    o_got = torch.empty((Bn, Hn, D), device="cuda")
+    sl = to_dev(slots)
+    ref.decode_step(sl, *x, o_ref)
+    got.decode_step(sl, *x, o_got, order=to_dev(rng.permutation(Bn).astype(np.int32)))
+    torch.cuda.synchronize()
+    assert torch.equal(o_got, o_ref)
+    assert torch.equal(got.pool, ref.pool)
