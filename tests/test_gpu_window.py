@@ -34,7 +34,7 @@ def _setup(seed, B, H, D, r, decay):
 
 
 def _resync(win, got):
-    """Parity is judged from identical input states: after a window end has been compared, the
+    """Parity is checked from identical input states: after a window end has been compared, the
     oracle continues from the GPU's stored state (the two may differ by the few codes the
     tolerance allows, which would otherwise carry into the next window's readouts)."""
     h, c, s = got
