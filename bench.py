@@ -133,10 +133,10 @@ def parse():
                    help="the STEPQuant-style state instead of DAMP (FP16 pivots, 8/6/4-bit rows at "
                         "a nominal 6-bit map, FP16 row factors and column scales refitted each step)")
     p.add_argument("--order", choices=["auto", "on", "off"], default="auto",
-                   help="DAMP step (uniform or per-head layout) with the batch taken in ascending "
-                        "slot order: damp_batch_order runs inside every timed step, then "
-                        "damp_decode_step_ordered; auto = on for batches of at least "
-                        f"{ORDER_MIN_UNITS} units")
+                   help="DAMP steps (plain, per-head layout, fused pre-step, per-window) with the "
+                        "batch taken in ascending slot order: damp_batch_order runs inside every "
+                        "timed step, then the ordered entry point; auto = on for batches of at "
+                        f"least {ORDER_MIN_UNITS} units, except the per-window step")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the step, run a plain device copy of MIB MiB --steps times "
                         "(the reference kernel of known size for HBM byte counters)")
@@ -376,17 +376,19 @@ def main():
               f"{budget['r_per_head']}; risk scores {budget['risk_scores_ms']:.3f} ms, allocation "
               f"{budget['allocate_ms']:.3f} ms", file=sys.stderr, flush=True)
 
-    use_order = args.order == "on" or (args.order == "auto" and units >= ORDER_MIN_UNITS)
-    use_order = use_order and not (args.stq or args.window or args.fused_prestep)
+    # auto leaves the per-window step in batch order: measured on pool4096, the order gains
+    # nothing there (W = 4: 188.5 us ordered against 187.4 us; W = 8: 206.9 against 205.7 us)
+    use_order = args.order == "on" or (args.order == "auto" and units >= ORDER_MIN_UNITS and not args.window)
+    use_order = use_order and not args.stq
     order_bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(R)]
 
-    def ordered(fmt, st, launch_plain):
-        """The headline DAMP step lists its batch by slot first, then runs in that order;
-        "damp_batch_order" is the same step in batch order."""
-        def launch(i):
-            o = st.batch_order(slot_sets[i % R], out=order_bufs[i % R])
-            st.decode_step(slot_sets[i % R], *sets[i % 4], out, order=o)
-        return launch if (use_order and fmt == "damp") else launch_plain
+    def with_order(fmt, st, step):
+        """The timed launch: step(i, order). With the order on, the DAMP steps ("damp", and the
+        per-token step a window run compares with) list their batch by slot first, in every step,
+        then run in that order; "damp_batch_order" is the same step in batch order."""
+        if use_order and fmt in ("damp", "damp_token"):
+            return lambda i: step(i, st.batch_order(slot_sets[i % R], out=order_bufs[i % R]))
+        return lambda i: step(i, None)
 
     def run(fmt):
         if fmt == "damp" and args.stq:
@@ -399,34 +401,38 @@ def main():
             st.pool.zero_()
             fill_states(torch, st.quantize, all_slots, H, d, dev)
             wbuf = st.window_buffer(args.window)
-            launch = lambda i: st.window_step(wbuf, args.window, slot_sets[i % R], *sets[i % 4], out)
+            launch = with_order(fmt, st, lambda i, o: st.window_step(wbuf, args.window, slot_sets[i % R],
+                                                                      *sets[i % 4], out, order=o))
             keep = (st, wbuf)
         elif fmt == "damp" and args.fused_prestep:
             st = lib.DampState(pool_slots, H, d, rows, device=dev)
             st.pool.zero_()
             fill_states(torch, st.quantize, all_slots, H, d, dev)
-            launch = lambda i: st.decode_step_fused(slot_sets[i % R], *raw_sets[i % 4], out)
+            launch = with_order(fmt, st, lambda i, o: st.decode_step_fused(slot_sets[i % R], *raw_sets[i % 4],
+                                                                            out, order=o))
             keep = st
             F = torch.nn.functional
 
-            def unfused(i):
+            def unfused(i, o):
                 q, k, v, g, b = raw_sets[i % 4]
                 qn = F.normalize(q.float(), dim=-1)
                 kn = F.normalize(k.float(), dim=-1)
-                st.decode_step(slot_sets[i % R], qn, kn, v.float(), torch.sigmoid(-g), torch.sigmoid(b), out)
-            prestep_info["unfused_ms"] = time_launches(torch, unfused, args.steps, args.warmup)
+                st.decode_step(slot_sets[i % R], qn, kn, v.float(), torch.sigmoid(-g), torch.sigmoid(b), out,
+                               order=o)
+            prestep_info["unfused_ms"] = time_launches(torch, with_order(fmt, st, unfused), args.steps,
+                                                       args.warmup)
         elif fmt in ("damp", "damp_batch_order") and budget is not None:
             st = lib.DampState(pool_slots, H, d, budget["row_map"], device=dev,
                                r_per_head=budget["r_per_head"])
             st.pool.zero_()
             fill_states(torch, st.quantize, all_slots, H, d, dev)
-            launch = ordered(fmt, st, lambda i: st.decode_step(slot_sets[i % R], *sets[i % 4], out))
+            launch = with_order(fmt, st, lambda i, o: st.decode_step(slot_sets[i % R], *sets[i % 4], out, order=o))
             keep = st
         elif fmt in ("damp", "damp_token", "damp_batch_order"):
             st = lib.DampState(pool_slots, H, d, rows, device=dev)
             st.pool.zero_()
             fill_states(torch, st.quantize, all_slots, H, d, dev)
-            launch = ordered(fmt, st, lambda i: st.decode_step(slot_sets[i % R], *sets[i % 4], out))
+            launch = with_order(fmt, st, lambda i, o: st.decode_step(slot_sets[i % R], *sets[i % 4], out, order=o))
             keep = st
         elif fmt == "fp32":
             pool = torch.zeros((pool_slots, H, d, d), dtype=torch.float32, device=dev)
@@ -501,7 +507,7 @@ def main():
     if prestep_info:
         prestep_info["fused_ms"] = results["damp"]["ms_per_step"]
         prestep_info["unfused"] = ("torch normalize(q), normalize(k), sigmoid(-g), sigmoid(b) in fp32, "
-                                   "then damp_decode_step")
+                                   "then damp_decode_step" + (" in slot order" if use_order else ""))
         line["prestep"] = prestep_info
     if "fp32" in results and "damp" in results:
         line["baselines"] = {f: {"ms_per_step": v["ms_per_step"], "updates_per_s": v["updates_per_s"],

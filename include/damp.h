@@ -210,6 +210,15 @@ damp_status damp_decode_step_ordered(damp_state* state, const int32_t* slot_idx,
                                      damp_dtype qkv_dtype, const float* alpha, damp_decay decay,
                                      const float* beta, float* out, void* stream);
 
+/* damp_decode_step_fused with the batch positions taken in the order `order` lists them, as
+ * damp_decode_step_ordered does for damp_decode_step: bit-identical results for any permutation.
+ * Arguments and errors as damp_decode_step_fused, plus `order` as in damp_decode_step_ordered. */
+damp_status damp_decode_step_fused_ordered(damp_state* state, const int32_t* slot_idx,
+                                           const int32_t* order, int32_t B, const void* q,
+                                           const void* k, const void* v, damp_dtype qkv_dtype,
+                                           const float* gate_logit, damp_decay decay,
+                                           const float* beta_logit, float* out, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * Per-window requantization (the LeapQuant page, abstract: the low-bit state stays fixed for a
  * window of tokens, the window's updates are held in high precision, outputs are computed from
@@ -241,6 +250,16 @@ damp_status damp_window_step(damp_state* state, void* window_buf, int32_t window
                              const int32_t* slot_idx, int32_t B, const void* q, const void* k,
                              const void* v, damp_dtype qkv_dtype, const float* alpha,
                              damp_decay decay, const float* beta, float* out, void* stream);
+
+/* damp_window_step with the batch positions taken in the order `order` lists them, as
+ * damp_decode_step_ordered does for damp_decode_step: bit-identical results (readouts, pool and
+ * window buffers) for any permutation. Arguments and errors as damp_window_step, plus `order` as
+ * in damp_decode_step_ordered. */
+damp_status damp_window_step_ordered(damp_state* state, void* window_buf, int32_t window,
+                                     const int32_t* slot_idx, const int32_t* order, int32_t B,
+                                     const void* q, const void* k, const void* v,
+                                     damp_dtype qkv_dtype, const float* alpha, damp_decay decay,
+                                     const float* beta, float* out, void* stream);
 
 /* End the windows of n slots now: every listed unit with buffered tokens stores its state in the
  * unit's rule and empties its buffer (units with none are left as they are). Use before reading

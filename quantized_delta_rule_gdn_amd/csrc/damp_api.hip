@@ -347,7 +347,7 @@ damp_status run_step(int fmt, const damp::StateRef& ref, int32_t d, int32_t H, i
 
 extern "C" {
 
-int32_t damp_abi_version(void) { return (1 << 16) | 1; }
+int32_t damp_abi_version(void) { return (1 << 16) | 2; }
 
 const char* damp_last_error(void) { return g_last_error.c_str(); }
 
@@ -611,6 +611,21 @@ damp_status damp_decode_step_fused(damp_state* s, const int32_t* slot_idx, int32
                   dt, gate_logit, decay, beta_logit, out, stream, 1);
 }
 
+damp_status damp_decode_step_fused_ordered(damp_state* s, const int32_t* slot_idx, const int32_t* order,
+                                           int32_t B, const void* q, const void* k, const void* v,
+                                           damp_dtype dt, const float* gate_logit, damp_decay decay,
+                                           const float* beta_logit, float* out, void* stream) {
+  if (!s) return fail(DAMP_ERR_INVALID_ARGUMENT, "state is NULL");
+  const damp_layout& L = s->layout;
+  damp_status st = check_step_args(B, L.num_heads, L.d_k, slot_idx, q, k, v, dt, gate_logit, decay,
+                                   beta_logit, out);
+  if (st != DAMP_OK) return st;
+  if (B == 0) return ok();
+  if (!order || !aligned(order, 4)) return fail(DAMP_ERR_INVALID_ARGUMENT, "order is NULL or misaligned");
+  return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, B, q, k, v,
+                  dt, gate_logit, decay, beta_logit, out, stream, 1, nullptr, 0, false, order);
+}
+
 size_t damp_window_bytes(const damp_layout* L, int32_t window) {
   if (!L || window < 1 || window > damp::window_max()) return 0;
   damp_layout T = *L;
@@ -635,6 +650,23 @@ damp_status damp_window_step(damp_state* s, void* window_buf, int32_t window, co
   if (B == 0) return ok();
   return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, B, q, k, v,
                   dt, alpha, decay, beta, out, stream, 0, window_buf, window, false);
+}
+
+damp_status damp_window_step_ordered(damp_state* s, void* window_buf, int32_t window,
+                                    const int32_t* slot_idx, const int32_t* order, int32_t B,
+                                    const void* q, const void* k, const void* v, damp_dtype dt,
+                                    const float* alpha, damp_decay decay, const float* beta,
+                                    float* out, void* stream) {
+  if (!s) return fail(DAMP_ERR_INVALID_ARGUMENT, "state is NULL");
+  const damp_layout& L = s->layout;
+  damp_status st = check_step_args(B, L.num_heads, L.d_k, slot_idx, q, k, v, dt, alpha, decay, beta, out);
+  if (st != DAMP_OK) return st;
+  st = check_window(window_buf, window);
+  if (st != DAMP_OK) return st;
+  if (B == 0) return ok();
+  if (!order || !aligned(order, 4)) return fail(DAMP_ERR_INVALID_ARGUMENT, "order is NULL or misaligned");
+  return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, B, q, k, v,
+                  dt, alpha, decay, beta, out, stream, 0, window_buf, window, false, order);
 }
 
 damp_status damp_window_flush(damp_state* s, void* window_buf, int32_t window, const int32_t* slot_idx,

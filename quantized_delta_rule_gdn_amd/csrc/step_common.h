@@ -521,6 +521,16 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// The unit of this workgroup: head = w mod H of batch position order[w / H] (w / H without an
+// order). False for an order entry outside [0, B): the workgroup then does nothing.
+__device__ __forceinline__ bool unit_of(const StepArgs& a, int& b, int& head) {
+  const int w = __builtin_amdgcn_workgroup_id_x();
+  const int p = w / a.H;
+  head = w - p * a.H;
+  b = a.order ? a.order[p] : p;
+  return static_cast<unsigned>(b) < static_cast<unsigned>(a.B);
+}
+
 template <int D, int NT, int PER_KEY, int BF16, bool Q>
 __device__ __forceinline__ float stage_rows(const StepArgs& a, const float* sc_old, int bh, int head,
                                             int r, int tid, float4* srow, float* sv, float* tmp) {

@@ -174,16 +174,6 @@ __device__ __forceinline__ void step_q_unit(const StepArgs& a, const UnitAddr& u
   flush_scales<D, G::NT>(up, ssc, r, tid);
 }
 
-// The unit of this workgroup: head = w mod H of batch position order[w / H] (w / H without an
-// order). False for an order entry outside [0, B): the workgroup then does nothing.
-__device__ __forceinline__ bool unit_of(const StepArgs& a, int& b, int& head) {
-  const int w = __builtin_amdgcn_workgroup_id_x();
-  const int p = w / a.H;
-  head = w - p * a.H;
-  b = a.order ? a.order[p] : p;
-  return static_cast<unsigned>(b) < static_cast<unsigned>(a.B);
-}
-
 template <int D, int PER_KEY, int BF16, int PLAN, int WAVES, int NF = 0>
 __global__ __launch_bounds__(64 * WAVES) void step_kernel_q(const StepArgs a) {
   __shared__ StepSmem<D, Geo<D, WAVES>::NW> sm;

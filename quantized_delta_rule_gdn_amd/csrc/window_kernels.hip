@@ -358,9 +358,9 @@ __device__ __forceinline__ void window_heads_case(const StepArgs& a, const UnitA
 template <int D, int PER_KEY, int BF16, int PLAN, int WAVES, int NF, bool FLUSH_ONLY, bool HEADS>
 __global__ __launch_bounds__(64 * WAVES) void window_kernel(const StepArgs a) {
   __shared__ WinSmem<D, Geo<D, WAVES>::NW> sm;
-  const int bh = __builtin_amdgcn_workgroup_id_x();
-  const int b = bh / a.H;
-  const int head = bh - b * a.H;
+  int b, head;
+  if (!unit_of(a, b, head)) return;
+  const int bh = b * a.H + head;
   const int64_t slot = a.slot_idx[b];
   const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, slot, head, a.H);
   if constexpr (HEADS)

@@ -36,7 +36,8 @@ EXPORTS = (
     "damp_allocate_rows", "damp_decode_step_fused", "damp_window_bytes", "damp_window_step",
     "damp_window_flush", "stq_state_bytes", "stq_state_alloc", "stq_state_free",
     "stq_state_head_info", "stq_state_quantize", "stq_state_dequantize", "stq_decode_step",
-    "damp_batch_order", "damp_decode_step_ordered",
+    "damp_batch_order", "damp_decode_step_ordered", "damp_decode_step_fused_ordered",
+    "damp_window_step_ordered",
 )
 
 
@@ -107,6 +108,10 @@ def load() -> ctypes.CDLL:
         "damp_batch_order": ([P, I32, I32, P, P], ctypes.c_int),
         "damp_decode_step_ordered": ([P, P, P, I32, P, P, P, ctypes.c_int, P, ctypes.c_int, P, P,
                                       P], ctypes.c_int),
+        "damp_decode_step_fused_ordered": ([P, P, P, I32, P, P, P, ctypes.c_int, P, ctypes.c_int,
+                                            P, P, P], ctypes.c_int),
+        "damp_window_step_ordered": ([P, P, I32, P, P, I32, P, P, P, ctypes.c_int, P,
+                                      ctypes.c_int, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -324,15 +329,24 @@ class DampState:
         return batch_order(slot_idx, self.num_slots, out=out, stream=stream)
 
 
-    def decode_step_fused(self, slot_idx, q, k, v, gate_logit, beta_logit, out, stream=None) -> None:
-        """The step with the pre-step fused: q, k unnormalised, gate and beta as logits."""
+    def decode_step_fused(self, slot_idx, q, k, v, gate_logit, beta_logit, out, stream=None,
+                          order=None) -> None:
+        """The step with the pre-step fused: q, k unnormalised, gate and beta as logits; with
+        ``order`` the units are processed in that order."""
         B, dt, decay = _step_vectors(slot_idx, q, k, v, gate_logit, beta_logit, out,
                                      self.num_heads, self.d)
         if slot_idx.device != self.pool.device:
             raise ValueError("slot_idx and the pool are on different devices")
-        _check(load().damp_decode_step_fused(self._h, _ptr(slot_idx), B, _ptr(q), _ptr(k), _ptr(v),
-                                             dt, _ptr(gate_logit), decay, _ptr(beta_logit),
-                                             _ptr(out), _stream(stream)))
+        if order is None:
+            _check(load().damp_decode_step_fused(self._h, _ptr(slot_idx), B, _ptr(q), _ptr(k),
+                                                 _ptr(v), dt, _ptr(gate_logit), decay,
+                                                 _ptr(beta_logit), _ptr(out), _stream(stream)))
+            return
+        _need(order, "order", _torch().int32, (B,), self.pool.device)
+        _check(load().damp_decode_step_fused_ordered(self._h, _ptr(slot_idx), _ptr(order), B,
+                                                     _ptr(q), _ptr(k), _ptr(v), dt,
+                                                     _ptr(gate_logit), decay, _ptr(beta_logit),
+                                                     _ptr(out), _stream(stream)))
 
 
     # ---- per-window requantization ----
@@ -345,12 +359,20 @@ class DampState:
             raise DampError(DAMP_ERR_INVALID_ARGUMENT, f"invalid window length {window}")
         return torch.zeros(n, dtype=torch.uint8, device=self.pool.device)
 
-    def window_step(self, wbuf, window: int, slot_idx, q, k, v, alpha, beta, out, stream=None) -> None:
+    def window_step(self, wbuf, window: int, slot_idx, q, k, v, alpha, beta, out, stream=None,
+                    order=None) -> None:
+        """One token of a window; with ``order`` the units are processed in that order."""
         B, dt, decay = _step_vectors(slot_idx, q, k, v, alpha, beta, out, self.num_heads, self.d)
         self._check_wbuf(wbuf, window)
-        _check(load().damp_window_step(self._h, _ptr(wbuf), window, _ptr(slot_idx), B, _ptr(q), _ptr(k),
-                                       _ptr(v), dt, _ptr(alpha), decay, _ptr(beta), _ptr(out),
-                                       _stream(stream)))
+        if order is None:
+            _check(load().damp_window_step(self._h, _ptr(wbuf), window, _ptr(slot_idx), B, _ptr(q),
+                                           _ptr(k), _ptr(v), dt, _ptr(alpha), decay, _ptr(beta),
+                                           _ptr(out), _stream(stream)))
+            return
+        _need(order, "order", _torch().int32, (B,), self.pool.device)
+        _check(load().damp_window_step_ordered(self._h, _ptr(wbuf), window, _ptr(slot_idx), _ptr(order),
+                                               B, _ptr(q), _ptr(k), _ptr(v), dt, _ptr(alpha), decay,
+                                               _ptr(beta), _ptr(out), _stream(stream)))
 
     def window_flush(self, wbuf, window: int, slot_idx, stream=None) -> None:
         torch = _torch()

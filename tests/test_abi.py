@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.damp_abi_version() == (1 << 16) | 1
+    assert L.damp_abi_version() == (1 << 16) | 2
 
 
 def test_block_accounting_d128():
@@ -255,3 +255,5 @@ def test_order_entry_points_reject_bad_arguments_on_host():
     assert L.damp_batch_order(None, 0, 16, None, None) == lib.DAMP_OK
     assert L.damp_decode_step_ordered(None, a, o, 1, a, a, a, 0, a, 0, a, a, None) == bad
     assert "state is NULL" in lib.last_error()
+    assert L.damp_decode_step_fused_ordered(None, a, o, 1, a, a, a, 0, a, 0, a, a, None) == bad
+    assert L.damp_window_step_ordered(None, a, 4, a, o, 1, a, a, a, 0, a, 0, a, a, None) == bad

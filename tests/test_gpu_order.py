@@ -140,3 +140,33 @@ def test_ordered_step_every_instance(D, r, Bn, Hn, decay):
     torch.cuda.synchronize()
     assert torch.equal(o_got, o_ref)
     assert torch.equal(got.pool, ref.pool)
+
+
+def test_ordered_fused_and_window_steps_are_bit_exact():
+    """The fused pre-step and the per-window step (windows of 2 over 3 tokens: one end, one
+    pending; both decay modes) in a random order give the batch-order results bit for bit:
+    readouts, pool and window buffers."""
+    rng = np.random.default_rng(21)
+    slots = rng.choice(4 * B, B, replace=False).astype(np.int32)
+    rows = synth.random_rows(rng, H, D, 24)
+    ref, got = _states(lambda: lib.DampState(4 * B, H, D, rows), slots, 13)
+    sl = to_dev(slots)
+    perm = to_dev(rng.permutation(B).astype(np.int32))
+    o_ref = torch.empty((B, H, D), device="cuda")
+    o_got = torch.empty((B, H, D), device="cuda")
+    for decay in (synth.GDN, synth.KDA):
+        raw = step_tensors(synth.raw_step_inputs(np.random.default_rng([22, decay]), B, H, D, decay, "bf16"))
+        ref.decode_step_fused(sl, *raw, o_ref)
+        got.decode_step_fused(sl, *raw, o_got, order=perm)
+        torch.cuda.synchronize()
+        assert torch.equal(o_got, o_ref), f"fused readout, decay {decay}"
+        assert torch.equal(got.pool, ref.pool), f"fused pool, decay {decay}"
+        w_ref, w_got = ref.window_buffer(2), got.window_buffer(2)
+        for t in range(3):
+            x = step_tensors(synth.step_inputs(np.random.default_rng([23, decay, t]), B, H, D, decay, "bf16"))
+            ref.window_step(w_ref, 2, sl, *x, o_ref)
+            got.window_step(w_got, 2, sl, *x, o_got, order=perm)
+            torch.cuda.synchronize()
+            assert torch.equal(o_got, o_ref), f"window readout, decay {decay}, token {t}"
+            assert torch.equal(got.pool, ref.pool), f"window pool, decay {decay}, token {t}"
+            assert torch.equal(w_got, w_ref), f"window buffer, decay {decay}, token {t}"
