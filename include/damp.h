@@ -64,7 +64,8 @@ typedef enum damp_status {
   DAMP_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, misaligned pointer, bad enum */
   DAMP_ERR_UNSUPPORTED = -2,      /* a size the kernels are not built for */
   DAMP_ERR_OUT_OF_MEMORY = -3,    /* the library's small device allocation failed */
-  DAMP_ERR_SLOT_INDEX = -4,       /* DAMP_DEBUG=1 only: slot index out of range or repeated */
+  DAMP_ERR_SLOT_INDEX = -4,       /* DAMP_DEBUG=1 only: slot index out of range or repeated, or
+                                     an order that is not a permutation of the batch */
   DAMP_ERR_HIP = -5               /* a HIP runtime call or kernel launch failed */
 } damp_status;
 
@@ -180,8 +181,8 @@ damp_status damp_decode_step_fused(damp_state* state, const int32_t* slot_idx, i
  * the number of requests ([C2] abstract and Fig. 1a); which slots a batch holds is up to the
  * caller's scheduler, so they can lie anywhere in the pool. A step reads and writes each listed
  * block once in any order, but HBM delivers the blocks faster when those a launch has in flight
- * together lie close in the pool. These two calls let the step take the batch in slot order;
- * the pages define no order, and no result depends on it.
+ * together lie close in the pool. damp_batch_order makes that order and the *_ordered steps
+ * take the batch in it; the pages define no order, and no result depends on it.
  * ------------------------------------------------------------------------------------- */
 
 /* order[0..B) = a permutation of [0, B) listing the batch positions by ascending slot bucket,
