@@ -159,7 +159,7 @@ def _edge_map(name, H, D, rng):
             start += c
     assert np.isin(bits, (16, 8, 6, 4)).all()
     if name == "ragged":
-        impact[1] = 0.0                  # one head with all-zero weights: the unweighted fit
+        impact[min(1, H - 1)] = 0.0      # one head with all-zero weights: the unweighted fit
     return bits, impact
 
 
