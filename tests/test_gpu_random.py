@@ -2,7 +2,10 @@
 state outliers and unit orders for the DAMP step, and random shapes, pivot counts, edge precision
 maps and in-place / second-pool writes for the STEPQuant-style step, each against the oracle
 from identical input states with the tolerances of gpu_common / test_gpu_stq. (The same sweep was
-run offline at 5,000 DAMP and 400 STEPQuant-style cases with no failure.)"""
+run offline at 5,000 DAMP and 400 STEPQuant-style cases with no failure.) DAMP_SWEEP_SCALE=n runs
+n times as many cases of each sweep (the first ones are the same)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -17,11 +20,13 @@ from quantized_delta_rule_gdn_amd import synth  # noqa: E402
 from test_gpu_parity import _random_case  # noqa: E402
 from test_gpu_stq import _edge_map, _step_case  # noqa: E402
 
+SCALE = int(os.environ.get("DAMP_SWEEP_SCALE", "1"))
+
 
 def test_random_damp_steps():
     master = np.random.default_rng(20261203)
     worst = 1.0
-    for i in range(300):
+    for i in range(300 * SCALE):
         D = int(master.choice([16, 32, 64, 128, 128, 128]))
         if master.random() < 0.3:
             r = int(master.integers(0, D + 1))
@@ -53,12 +58,12 @@ def test_random_damp_steps():
         except AssertionError as e:
             raise AssertionError(f"{case}: {e}") from None
         worst = min(worst, st.get("code_eq_frac", 1.0))
-    print(f"300 random DAMP steps, worst code agreement {worst:.6f}", flush=True)
+    print(f"{300 * SCALE} random DAMP steps, worst code agreement {worst:.6f}", flush=True)
 
 
 def test_random_stq_steps():
     master = np.random.default_rng(7070)
-    for i in range(150):
+    for i in range(150 * SCALE):
         D = int(master.choice([64, 128, 128]))
         H, B = int(master.integers(1, 5)), int(master.integers(1, 12))
         decay, dtype = int(master.integers(0, 2)), ("bf16" if master.random() < 0.7 else "fp32")
@@ -74,3 +79,74 @@ def test_random_stq_steps():
         except AssertionError as e:
             raise AssertionError(f"case {i}: D={D} H={H} B={B} decay={decay} {dtype} pivots={pivots} "
                                  f"seed={seed} inplace={inplace} map={name}: {e}") from None
+
+
+def test_random_window_runs():
+    """Random window lengths, token counts (ending mid-window, then a flush), shapes and gate
+    forms, against the oracle's windowed step token by token."""
+    from test_gpu_window import _resync, _setup
+    master = np.random.default_rng(4242)
+    for i in range(40 * SCALE):
+        D = int(master.choice([16, 64, 128, 128]))
+        r = min(int(master.choice([0, 8, 24, 27])), D)
+        B, H = int(master.integers(1, 12)), int(master.integers(1, 4))
+        W, tokens = int(master.integers(1, 9)), int(master.integers(1, 12))
+        decay, dtype = int(master.integers(0, 2)), ("bf16" if master.random() < 0.7 else "fp32")
+        seed, ordered = int(master.integers(0, 2**31)), bool(master.random() < 0.5)
+        case = f"case {i}: D={D} r={r} B={B} H={H} W={W} tokens={tokens} decay={decay} {dtype} ordered={ordered}"
+        rng, rows, mask, maskn, h, c, s = _setup(seed, B, H, D, r, decay)
+        win = oracle.Window(maskn, h.copy(), c.copy(), s.copy(), W)
+        slots = np.random.default_rng(seed + 1).choice(2 * B, B, replace=False)
+        pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), slots, 2 * B)
+        wbuf = pool.state.window_buffer(W)
+        order = pool.state.batch_order(pool.slot_dev) if ordered else None
+        want = lambda: (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D), win.s.reshape(B, H, D))
+        try:
+            for tok in range(tokens):
+                inp = synth.step_inputs(rng, B, H, D, decay, dtype)
+                q, k, v, a, b = step_tensors(inp)
+                out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+                pool.state.window_step(wbuf, W, pool.slot_dev, q, k, v, a, b, out, order=order)
+                torch.cuda.synchronize()
+                check_readout(out.cpu().numpy(), win.step(*ref_vectors(inp, B, H, D)).reshape(B, H, D))
+                if (tok + 1) % W == 0:
+                    got = pool.logical()
+                    check_quant(mask, got, want())
+                    _resync(win, got)
+            pool.state.window_flush(wbuf, W, pool.slot_dev)
+            win.flush()
+            torch.cuda.synchronize()
+            check_quant(mask, pool.logical(), want())
+        except AssertionError as e:
+            raise AssertionError(f"{case}: {e}") from None
+
+
+def test_random_fused_steps():
+    """Random shapes, gate forms and unit orders of the step with the pre-step fused (raw q, k
+    with magnitudes over two decades, gate and beta logits), against the oracle's pre-step and
+    step."""
+    from test_gpu_prestep import _case, _oracle_fused
+    master = np.random.default_rng(5151)
+    for i in range(100 * SCALE):
+        D = int(master.choice([16, 64, 128, 128]))
+        r = min(int(master.choice([0, 8, 12, 24, 27])), D)
+        B, H = int(master.integers(1, 30)), int(master.integers(1, 5))
+        decay, dtype = int(master.integers(0, 2)), ("bf16" if master.random() < 0.7 else "fp32")
+        seed, ordered = int(master.integers(0, 2**31)), bool(master.random() < 0.5)
+        case = f"case {i}: D={D} r={r} B={B} H={H} decay={decay} {dtype} seed={seed} ordered={ordered}"
+        rows, S, inp = _case(seed, B, H, D, r, decay, dtype)
+        mask = synth.rows_to_mask(rows, D)
+        maskn = np.broadcast_to(mask, (B, H, D)).reshape(B * H, D)
+        h, c, s = oracle.quantize(maskn, S.reshape(B * H, D, D))
+        slots = np.random.default_rng(seed + 1).choice(2 * B, B, replace=False)
+        pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), slots, 2 * B)
+        q, k, v, g, b = step_tensors(inp)
+        out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+        order = pool.state.batch_order(pool.slot_dev) if ordered else None
+        pool.state.decode_step_fused(pool.slot_dev, q, k, v, g, b, out, order=order)
+        torch.cuda.synchronize()
+        try:
+            check_readout(out.cpu().numpy(), _oracle_fused(maskn, h, c, s, inp, B, H, D).reshape(B, H, D))
+            check_quant(mask, pool.logical(), (h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D)))
+        except AssertionError as e:
+            raise AssertionError(f"{case}: {e}") from None

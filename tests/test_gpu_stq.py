@@ -41,15 +41,25 @@ def check_stq(bits, got, ref):
     if not ints.any():   # every row a pivot: no codes, no row factors, the column scales are 0
         assert not sg.any() and not cg.any() and not rg.any()
         return {"cs_eq": 1.0, "rf_eq": 1.0, "code_eq": 1.0}
-    drf = np.abs(_f16_ord(rg[ints]) - _f16_ord(rr[ints]))
-    assert drf.max() <= 2 and (drf == 0).mean() >= 0.99, f"row factors: max {drf.max()}, eq {(drf == 0).mean()}"
+    drf_all = np.abs(_f16_ord(rg) - _f16_ord(rr))
+    drf = drf_all[ints]
+    assert drf.max() <= 2, f"row factors: max {drf.max()} ulp"
+    # rf_i depends on every column scale of its unit: where a column scale is one ulp off (allowed
+    # above), |X_ij| / cs_j moves by 2^-10 for each row whose maximum lies in that column, so the
+    # equal fraction is taken over the units whose column scales all agree
+    cs_same = (sg == sr).all(axis=-1)                                   # [n, H]
+    sel = ints & cs_same[..., None]
+    if sel.any():
+        rf_eq = float((drf_all[sel] == 0).mean())
+        assert rf_eq >= 0.99, f"row factors: eq {rf_eq} where the column scales agree"
     dc = np.abs(cg.astype(np.int32) - cr.astype(np.int32))
     m = np.broadcast_to(ints[..., None], dc.shape)
     assert dc[m].max() <= 2
     same = m & (rg == rr)[..., None] & (sg == sr)[:, :, None, :]
     eq = float((dc[same] == 0).mean())
     assert dc[same].max() <= 1 and eq >= 0.999, f"codes: eq {eq}, max {dc[same].max()}"
-    return {"cs_eq": float((dcs == 0).mean()), "rf_eq": float((drf == 0).mean()), "code_eq": eq}
+    return {"cs_eq": float((dcs == 0).mean()), "rf_eq": float((drf == 0).mean()), "code_eq": eq,
+            "units_cs_equal": float(cs_same.mean())}
 
 
 def _state(seed, n, H, D, pivots=2):
