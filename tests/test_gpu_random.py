@@ -150,3 +150,49 @@ def test_random_fused_steps():
             check_quant(mask, pool.logical(), (h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D)))
         except AssertionError as e:
             raise AssertionError(f"{case}: {e}") from None
+
+
+def test_random_per_head_layouts():
+    """Random per-head layouts (each head its own r and FP16 rows; all r multiples of the row
+    step up to 32, which takes the compile-time row-kind instance, or any r), random gate forms
+    and unit orders, the step against the oracle."""
+    import layout_ref
+    from gpu_common import SENTINEL, to_dev
+    from quantized_delta_rule_gdn_amd import lib
+    master = np.random.default_rng(6161)
+    for i in range(30 * SCALE):
+        D = int(master.choice([64, 128, 128]))
+        H, B = int(master.integers(1, 6)), int(master.integers(1, 20))
+        if D == 128 and master.random() < 0.5:
+            r_per_head = (8 * master.integers(0, 5, H)).astype(np.int32)
+        else:
+            r_per_head = master.integers(0, D + 1, H).astype(np.int32)
+        row_map = np.empty((H, D), np.int32)
+        for h in range(H):
+            p = master.permutation(D)
+            row_map[h] = np.concatenate([np.sort(p[:r_per_head[h]]), np.sort(p[r_per_head[h]:])])
+        decay, dtype = int(master.integers(0, 2)), ("bf16" if master.random() < 0.7 else "fp32")
+        seed, ordered = int(master.integers(0, 2**31)), bool(master.random() < 0.5)
+        case = f"case {i}: D={D} H={H} B={B} r={r_per_head.tolist()} decay={decay} {dtype} ordered={ordered}"
+        rng = np.random.default_rng(seed)
+        S = synth.normal_states(rng, (B, H, D, D), 0.1)
+        mask = layout_ref.mask_per_head(r_per_head, row_map, D)
+        maskn = np.broadcast_to(mask, (B, H, D)).reshape(B * H, D)
+        h_, c_, s_ = oracle.quantize(maskn, S.reshape(B * H, D, D))
+        logical = (h_.reshape(B, H, D, D), c_.reshape(B, H, D, D), s_.reshape(B, H, D))
+        num = 2 * B + 1
+        st = lib.DampState(num, H, D, row_map, r_per_head=r_per_head)
+        st.pool.fill_(SENTINEL)
+        slots = np.random.default_rng(seed + 1).choice(num, B, replace=False).astype(np.int32)
+        sl = to_dev(slots)
+        st.slots()[sl.long()] = to_dev(layout_ref.pack_per_head(r_per_head, row_map, *logical))
+        inp = synth.step_inputs(rng, B, H, D, decay, dtype)
+        out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+        st.decode_step(sl, *step_tensors(inp), out, order=st.batch_order(sl) if ordered else None)
+        torch.cuda.synchronize()
+        got = layout_ref.unpack_per_head(r_per_head, row_map, st.slots()[sl.long()].cpu().numpy(), D)
+        try:
+            check_readout(out.cpu().numpy(), oracle.step_quant(maskn, h_, c_, s_, *ref_vectors(inp, B, H, D)).reshape(B, H, D))
+            check_quant(mask, got, logical)
+        except AssertionError as e:
+            raise AssertionError(f"{case}: {e}") from None
