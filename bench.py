@@ -494,8 +494,8 @@ def main():
                    "fp16_rows": r if budget is None else "per head", "global_batch": B, "seq_len": 1,
                    "state_cache": "cold (HBM)" if (cold or args.workload == "pool4096") else "warm (Infinity Cache)",
                    "pool_copies": R,
-                   "unit_order": "ascending slot (damp_batch_order + damp_decode_step_ordered, both "
-                                 "timed in every step)" if use_order else "batch order"},
+                   "unit_order": "ascending slot (damp_batch_order, then the ordered step, both timed "
+                                 "in every step)" if use_order else "batch order"},
         "roofline": {"bound": "hbm", "achieved": m["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": m["gbs"] / PEAK_HBM_GBS,
                      "traffic": measured_traffic() if (main_fmt == "damp" and args.workload == "pool4096"
