@@ -67,6 +67,19 @@ def measured_traffic():
     return int(kv["traffic_bytes_per_launch"])
 
 
+def order_enabled(order: str, units: int, window: int = 0, stq: bool = False) -> bool:
+    """Whether the timed DAMP steps list their batch by slot first (damp_batch_order, then the
+    ordered step). "on" / "off" force it; "auto" orders batches of at least ORDER_MIN_UNITS units
+    and leaves the per-window step in batch order: measured on pool4096, the order gains nothing
+    there (W = 4: 188.5 us ordered against 187.4 us; W = 8: 206.9 against 205.7 us). The
+    STEPQuant-style step has no ordered entry point."""
+    if stq:
+        return False
+    if order == "on":
+        return True
+    return order == "auto" and units >= ORDER_MIN_UNITS and not window
+
+
 def alg_bytes_window(W: int, d: int = 128, r: int = 24, per_key: bool = False, qkv_bytes: int = 2) -> float:
     """Bytes per (slot, head) update of the windowed step, averaged over the W tokens of a
     window: every token reads the stored block and its buffered terms (keys and deltas, 4 d bytes
@@ -376,10 +389,7 @@ def main():
               f"{budget['r_per_head']}; risk scores {budget['risk_scores_ms']:.3f} ms, allocation "
               f"{budget['allocate_ms']:.3f} ms", file=sys.stderr, flush=True)
 
-    # auto leaves the per-window step in batch order: measured on pool4096, the order gains
-    # nothing there (W = 4: 188.5 us ordered against 187.4 us; W = 8: 206.9 against 205.7 us)
-    use_order = args.order == "on" or (args.order == "auto" and units >= ORDER_MIN_UNITS and not args.window)
-    use_order = use_order and not args.stq
+    use_order = order_enabled(args.order, units, args.window, args.stq)
     order_bufs = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(R)]
 
     def with_order(fmt, st, step):

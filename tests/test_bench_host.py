@@ -52,3 +52,16 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_order_policy():
+    # auto: the 32,768-unit pool4096 batch is ordered, the 8,192-unit kda256 and 2,048-unit gdn64
+    # batches are not; the per-window step stays in batch order; on / off force it; never for
+    # the STEPQuant-style step
+    assert bench.order_enabled("auto", 1024 * 32)
+    assert not bench.order_enabled("auto", 256 * 32)
+    assert not bench.order_enabled("auto", 64 * 32)
+    assert not bench.order_enabled("auto", 1024 * 32, window=4)
+    assert bench.order_enabled("on", 64 * 32) and bench.order_enabled("on", 1024 * 32, window=4)
+    assert not bench.order_enabled("off", 1024 * 32)
+    assert not bench.order_enabled("on", 1024 * 32, stq=True)
