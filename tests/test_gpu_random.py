@@ -23,6 +23,41 @@ from test_gpu_stq import _edge_map, _step_case  # noqa: E402
 SCALE = int(os.environ.get("DAMP_SWEEP_SCALE", "1"))
 
 
+def _random_per_head(master, H, D):
+    """A random per-head layout: each head's r (all multiples of the row step up to 32, half the
+    time at d = 128, else any r) and a row map listing its FP16 rows, then its other rows, each
+    ascending."""
+    if D == 128 and master.random() < 0.5:
+        r_per_head = (8 * master.integers(0, 5, H)).astype(np.int32)
+    else:
+        r_per_head = master.integers(0, D + 1, H).astype(np.int32)
+    row_map = np.empty((H, D), np.int32)
+    for h in range(H):
+        p = master.permutation(D)
+        row_map[h] = np.concatenate([np.sort(p[:r_per_head[h]]), np.sort(p[r_per_head[h]:])])
+    return r_per_head, row_map
+
+
+class _PerHeadPool:
+    """The per-head counterpart of gpu_common.DampPool: logical states packed at ``slots``."""
+
+    def __init__(self, r_per_head, row_map, logical, slots, num_slots):
+        import layout_ref
+        from gpu_common import SENTINEL, to_dev
+        from quantized_delta_rule_gdn_amd import lib
+        H, D = row_map.shape
+        self.r_per_head, self.row_map, self.D, self.H = r_per_head, row_map, D, H
+        self.state = lib.DampState(num_slots, H, D, row_map, r_per_head=r_per_head)
+        self.state.pool.fill_(SENTINEL)
+        self.slot_dev = to_dev(np.asarray(slots, np.int32))
+        self.state.slots()[self.slot_dev.long()] = to_dev(layout_ref.pack_per_head(r_per_head, row_map, *logical))
+
+    def logical(self):
+        import layout_ref
+        return layout_ref.unpack_per_head(self.r_per_head, self.row_map,
+                                          self.state.slots()[self.slot_dev.long()].cpu().numpy(), self.D)
+
+
 def test_random_damp_steps():
     master = np.random.default_rng(20261203)
     worst = 1.0
@@ -82,8 +117,9 @@ def test_random_stq_steps():
 
 
 def test_random_window_runs():
-    """Random window lengths, token counts (ending mid-window, then a flush), shapes and gate
-    forms, against the oracle's windowed step token by token."""
+    """Random window lengths, token counts (ending mid-window, then a flush), shapes, gate forms,
+    unit orders and (a third of the runs) per-head layouts, against the oracle's windowed step
+    token by token."""
     from test_gpu_window import _resync, _setup
     master = np.random.default_rng(4242)
     for i in range(40 * SCALE):
@@ -93,11 +129,25 @@ def test_random_window_runs():
         W, tokens = int(master.integers(1, 9)), int(master.integers(1, 12))
         decay, dtype = int(master.integers(0, 2)), ("bf16" if master.random() < 0.7 else "fp32")
         seed, ordered = int(master.integers(0, 2**31)), bool(master.random() < 0.5)
-        case = f"case {i}: D={D} r={r} B={B} H={H} W={W} tokens={tokens} decay={decay} {dtype} ordered={ordered}"
-        rng, rows, mask, maskn, h, c, s = _setup(seed, B, H, D, r, decay)
-        win = oracle.Window(maskn, h.copy(), c.copy(), s.copy(), W)
+        per_head = D >= 64 and master.random() < 0.34
+        case = (f"case {i}: D={D} r={r} B={B} H={H} W={W} tokens={tokens} decay={decay} {dtype} "
+                f"ordered={ordered} per_head={per_head}")
         slots = np.random.default_rng(seed + 1).choice(2 * B, B, replace=False)
-        pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), slots, 2 * B)
+        if per_head:
+            import layout_ref
+            r_per_head, row_map = _random_per_head(master, H, D)
+            rng = np.random.default_rng(seed)
+            S = synth.normal_states(rng, (B, H, D, D), 0.1)
+            mask = layout_ref.mask_per_head(r_per_head, row_map, D)
+            maskn = np.broadcast_to(mask, (B, H, D)).reshape(B * H, D)
+            h, c, s = oracle.quantize(maskn, S.reshape(B * H, D, D))
+            pool = _PerHeadPool(r_per_head, row_map, (h.reshape(B, H, D, D), c.reshape(B, H, D, D),
+                                                      s.reshape(B, H, D)), slots, 2 * B)
+            case += f" r_per_head={r_per_head.tolist()}"
+        else:
+            rng, rows, mask, maskn, h, c, s = _setup(seed, B, H, D, r, decay)
+            pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), slots, 2 * B)
+        win = oracle.Window(maskn, h.copy(), c.copy(), s.copy(), W)
         wbuf = pool.state.window_buffer(W)
         order = pool.state.batch_order(pool.slot_dev) if ordered else None
         want = lambda: (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D), win.s.reshape(B, H, D))
@@ -163,14 +213,7 @@ def test_random_per_head_layouts():
     for i in range(30 * SCALE):
         D = int(master.choice([64, 128, 128]))
         H, B = int(master.integers(1, 6)), int(master.integers(1, 20))
-        if D == 128 and master.random() < 0.5:
-            r_per_head = (8 * master.integers(0, 5, H)).astype(np.int32)
-        else:
-            r_per_head = master.integers(0, D + 1, H).astype(np.int32)
-        row_map = np.empty((H, D), np.int32)
-        for h in range(H):
-            p = master.permutation(D)
-            row_map[h] = np.concatenate([np.sort(p[:r_per_head[h]]), np.sort(p[r_per_head[h]:])])
+        r_per_head, row_map = _random_per_head(master, H, D)
         decay, dtype = int(master.integers(0, 2)), ("bf16" if master.random() < 0.7 else "fp32")
         seed, ordered = int(master.integers(0, 2**31)), bool(master.random() < 0.5)
         case = f"case {i}: D={D} H={H} B={B} r={r_per_head.tolist()} decay={decay} {dtype} ordered={ordered}"
