@@ -205,10 +205,11 @@ def test_random_fused_steps():
 def test_random_per_head_layouts():
     """Random per-head layouts (each head its own r and FP16 rows; all r multiples of the row
     step up to 32, which takes the compile-time row-kind instance, or any r), random gate forms
-    and unit orders, the step against the oracle."""
+    and unit orders, the step (a third of the cases with the pre-step fused) against the oracle."""
     import layout_ref
     from gpu_common import SENTINEL, to_dev
     from quantized_delta_rule_gdn_amd import lib
+    from test_gpu_prestep import _oracle_fused
     master = np.random.default_rng(6161)
     for i in range(30 * SCALE):
         D = int(master.choice([64, 128, 128]))
@@ -216,7 +217,9 @@ def test_random_per_head_layouts():
         r_per_head, row_map = _random_per_head(master, H, D)
         decay, dtype = int(master.integers(0, 2)), ("bf16" if master.random() < 0.7 else "fp32")
         seed, ordered = int(master.integers(0, 2**31)), bool(master.random() < 0.5)
-        case = f"case {i}: D={D} H={H} B={B} r={r_per_head.tolist()} decay={decay} {dtype} ordered={ordered}"
+        fused = bool(master.random() < 0.34)
+        case = (f"case {i}: D={D} H={H} B={B} r={r_per_head.tolist()} decay={decay} {dtype} "
+                f"ordered={ordered} fused={fused}")
         rng = np.random.default_rng(seed)
         S = synth.normal_states(rng, (B, H, D, D), 0.1)
         mask = layout_ref.mask_per_head(r_per_head, row_map, D)
@@ -229,13 +232,20 @@ def test_random_per_head_layouts():
         slots = np.random.default_rng(seed + 1).choice(num, B, replace=False).astype(np.int32)
         sl = to_dev(slots)
         st.slots()[sl.long()] = to_dev(layout_ref.pack_per_head(r_per_head, row_map, *logical))
-        inp = synth.step_inputs(rng, B, H, D, decay, dtype)
         out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
-        st.decode_step(sl, *step_tensors(inp), out, order=st.batch_order(sl) if ordered else None)
+        order = st.batch_order(sl) if ordered else None
+        if fused:
+            inp = synth.raw_step_inputs(rng, B, H, D, decay, dtype)
+            st.decode_step_fused(sl, *step_tensors(inp), out, order=order)
+            ref = _oracle_fused(maskn, h_, c_, s_, inp, B, H, D)
+        else:
+            inp = synth.step_inputs(rng, B, H, D, decay, dtype)
+            st.decode_step(sl, *step_tensors(inp), out, order=order)
+            ref = oracle.step_quant(maskn, h_, c_, s_, *ref_vectors(inp, B, H, D))
         torch.cuda.synchronize()
         got = layout_ref.unpack_per_head(r_per_head, row_map, st.slots()[sl.long()].cpu().numpy(), D)
         try:
-            check_readout(out.cpu().numpy(), oracle.step_quant(maskn, h_, c_, s_, *ref_vectors(inp, B, H, D)).reshape(B, H, D))
+            check_readout(out.cpu().numpy(), ref.reshape(B, H, D))
             check_quant(mask, got, logical)
         except AssertionError as e:
             raise AssertionError(f"{case}: {e}") from None
