@@ -531,68 +531,126 @@ __device__ __forceinline__ bool unit_of(const StepArgs& a, int& b, int& head) {
   return static_cast<unsigned>(b) < static_cast<unsigned>(a.B);
 }
 
+// The staging in two phases. load() issues every global load the staging needs (row map, old
+// INT8 scales, k, q, the gate, v, beta) into registers and touches no LDS; store() writes them to
+// LDS, applies the fused pre-step and permutes to storage order. A step kernel calls load()
+// BEFORE it issues the state loads: the memory counter is in order, so store()'s wait then
+// covers only these few older loads and the staging and its barriers run while the unit's state
+// is still arriving, instead of after the last state byte (the state loads are the bulk of the
+// unit's bytes; the first row steps can be reduced as soon as they land).
+template <int D, int NT, int PER_KEY, int BF16, bool Q>
+struct Stage {
+  static constexpr int PER = (D + NT - 1) / NT;
+  static constexpr int NWS = NT / 64;
+  // Loaded values as raw words: bf16 inputs are widened only in store(), so no instruction that
+  // uses a loaded value (and waits for it) sits before the caller's state loads.
+  uint32_t src[PER], sc[PER], kv[PER], qv[PER], gv[PER], vv[PER];
+  float g0, beta;
+
+  template <int B16>
+  __device__ static __forceinline__ uint32_t raw_in(const void* base, int64_t i) {
+    if constexpr (B16)
+      return reinterpret_cast<const uint16_t*>(base)[i];
+    else
+      return reinterpret_cast<const uint32_t*>(base)[i];
+  }
+  __device__ static __forceinline__ float widen(uint32_t w) {
+    return BF16 ? __uint_as_float(w << 16) : __uint_as_float(w);  // bf16 -> fp32 is exact
+  }
+
+  __device__ __forceinline__ void load(const StepArgs& a, const float* sc_old, int bh, int head, int r,
+                                       int tid) {
+    const int64_t vec = int64_t(bh) * D;
+#pragma unroll
+    for (int n = 0; n < PER; ++n) {
+      const int i = tid + n * NT;
+      src[n] = static_cast<uint32_t>(i);
+      sc[n] = __float_as_uint(1.0f);
+      kv[n] = qv[n] = gv[n] = vv[n] = 0u;
+      if (PER * NT == D || i < D) {
+        if (a.st.rowmap) src[n] = a.st.rowmap[head * D + i];
+        if constexpr (Q)
+          if (i >= r) sc[n] = reinterpret_cast<const uint32_t*>(sc_old)[i - r];
+        kv[n] = raw_in<BF16>(a.k, vec + i);
+        qv[n] = raw_in<BF16>(a.q, vec + i);
+        if constexpr (PER_KEY) gv[n] = reinterpret_cast<const uint32_t*>(a.alpha)[vec + i];
+        vv[n] = raw_in<BF16>(a.v, vec + i);
+      }
+    }
+    g0 = PER_KEY ? 0.0f : a.alpha[bh];
+    beta = a.beta[bh];
+  }
+
+  // An empty asm statement that takes the staged values: the compiler keeps memory accesses on
+  // their side of it, so a caller that issues its state loads between load() and store() gets
+  // them issued before the first use of the staged values (and before the wait for them).
+  __device__ __forceinline__ void fence() {
+#pragma unroll
+    for (int n = 0; n < PER; ++n)
+      asm volatile("" : "+v"(src[n]), "+v"(sc[n]), "+v"(kv[n]), "+v"(qv[n]), "+v"(gv[n]), "+v"(vv[n]));
+  }
+
+  // Returns beta (after the activation with the fused pre-step) in a scalar register.
+  __device__ __forceinline__ float store(const StepArgs& a, int tid, float4* srow, float* sv, float* tmp) {
+    fence();
+    const bool pre = a.prestep != 0;
+    float ssq = 0.0f, ssk = 0.0f;
+#pragma unroll
+    for (int n = 0; n < PER; ++n) {
+      const int i = tid + n * NT;
+      if (PER * NT == D || i < D) {
+        const float kf = widen(kv[n]), qf = widen(qv[n]), gf = __uint_as_float(gv[n]);
+        tmp[i] = kf;
+        tmp[D + i] = qf;
+        ssk = fmaf(kf, kf, ssk);
+        ssq = fmaf(qf, qf, ssq);
+        if constexpr (PER_KEY) tmp[2 * D + i] = pre ? gate_from_logit(gf) : gf;
+        sv[i] = widen(vv[n]);
+      }
+    }
+    float g = g0, bt = beta;
+    if (pre) {
+      if constexpr (!PER_KEY) g = gate_from_logit(g);
+      bt = 1.0f / (1.0f + expf(-bt));
+      ssq = wave_sum(ssq);
+      ssk = wave_sum(ssk);
+      if ((tid & 63) == 0) {
+        tmp[3 * D + 2 * (tid >> 6)] = ssq;
+        tmp[3 * D + 2 * (tid >> 6) + 1] = ssk;
+      }
+    }
+    __syncthreads();
+    float invq = 1.0f, invk = 1.0f;
+    if (pre) {
+      float nq = tmp[3 * D], nk = tmp[3 * D + 1];
+#pragma unroll
+      for (int w2 = 1; w2 < NWS; ++w2) {
+        nq += tmp[3 * D + 2 * w2];
+        nk += tmp[3 * D + 2 * w2 + 1];
+      }
+      invq = nq > 0.0f ? rsqrtf(nq) : 0.0f;
+      invk = nk > 0.0f ? rsqrtf(nk) : 0.0f;
+    }
+#pragma unroll
+    for (int n = 0; n < PER; ++n) {
+      const int i = tid + n * NT;
+      if (PER * NT == D || i < D) {
+        const float gi = PER_KEY ? tmp[2 * D + src[n]] : g;
+        srow[i] = make_float4(__uint_as_float(sc[n]) * gi, tmp[src[n]] * invk, tmp[D + src[n]] * invq, 0.0f);
+      }
+    }
+    __syncthreads();
+    // beta (uniform over the workgroup) for the column pass, in a scalar register
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bt)));
+  }
+};
+
 template <int D, int NT, int PER_KEY, int BF16, bool Q>
 __device__ __forceinline__ float stage_rows(const StepArgs& a, const float* sc_old, int bh, int head,
                                             int r, int tid, float4* srow, float* sv, float* tmp) {
-  const int64_t vec = int64_t(bh) * D;
-  constexpr int PER = (D + NT - 1) / NT;
-  constexpr int NWS = NT / 64;
-  const bool pre = a.prestep != 0;
-  int src[PER];
-  float sc[PER];
-  float ssq = 0.0f, ssk = 0.0f;
-#pragma unroll
-  for (int n = 0; n < PER; ++n) {
-    const int i = tid + n * NT;
-    if (i < D) {
-      src[n] = a.st.rowmap ? a.st.rowmap[head * D + i] : i;
-      sc[n] = 1.0f;
-      if constexpr (Q)
-        if (i >= r) sc[n] = sc_old[i - r];
-      const float kv = load_in<BF16>(a.k, vec + i), qv = load_in<BF16>(a.q, vec + i);
-      tmp[i] = kv;
-      tmp[D + i] = qv;
-      ssk = fmaf(kv, kv, ssk);
-      ssq = fmaf(qv, qv, ssq);
-      if constexpr (PER_KEY) tmp[2 * D + i] = pre ? gate_from_logit(a.alpha[vec + i]) : a.alpha[vec + i];
-      sv[i] = load_in<BF16>(a.v, vec + i);
-    }
-  }
-  float g0 = PER_KEY ? 0.0f : a.alpha[bh];
-  float beta = a.beta[bh];
-  if (pre) {
-    if constexpr (!PER_KEY) g0 = gate_from_logit(g0);
-    beta = 1.0f / (1.0f + expf(-beta));
-    ssq = wave_sum(ssq);
-    ssk = wave_sum(ssk);
-    if ((tid & 63) == 0) {
-      tmp[3 * D + 2 * (tid >> 6)] = ssq;
-      tmp[3 * D + 2 * (tid >> 6) + 1] = ssk;
-    }
-  }
-  __syncthreads();
-  float invq = 1.0f, invk = 1.0f;
-  if (pre) {
-    float nq = tmp[3 * D], nk = tmp[3 * D + 1];
-#pragma unroll
-    for (int w2 = 1; w2 < NWS; ++w2) {
-      nq += tmp[3 * D + 2 * w2];
-      nk += tmp[3 * D + 2 * w2 + 1];
-    }
-    invq = nq > 0.0f ? rsqrtf(nq) : 0.0f;
-    invk = nk > 0.0f ? rsqrtf(nk) : 0.0f;
-  }
-#pragma unroll
-  for (int n = 0; n < PER; ++n) {
-    const int i = tid + n * NT;
-    if (i < D) {
-      const float g = PER_KEY ? tmp[2 * D + src[n]] : g0;
-      srow[i] = make_float4(sc[n] * g, tmp[src[n]] * invk, tmp[D + src[n]] * invq, 0.0f);
-    }
-  }
-  __syncthreads();
-  // beta (uniform over the workgroup) for the column pass, in a scalar register
-  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(beta)));
+  Stage<D, NT, PER_KEY, BF16, Q> sg;
+  sg.load(a, sc_old, bh, head, r, tid);
+  return sg.store(a, tid, srow, sv, tmp);
 }
 
 // Column sums over the key rows, shared by the step kernels. Every lane writes its CPL partial

@@ -27,16 +27,18 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
   const UnitAddr ua = unit_addr<D, FMT_F32>(a.st, a.slot_idx[b], head, a.H);
   const UnitPtr up = unit_ptr<D, FMT_F32>(ua, 0);
 
-  // (1) issue every state load of this lane first, so the whole block is in flight
+  // (1) the staging loads (per-row scalars, v), then every state load of this lane, so the
+  // whole block is in flight while the staging completes
+  Stage<D, G::NT, PER_KEY, BF16, false> sg;
+  sg.load(a, nullptr, bh, head, 0, tid);
   float S[RPL][CPL];
 #pragma unroll
   for (int t = 0; t < RPL; ++t)
     Row<D, K_F32>::load(up, Row<D, K_F32>::template loc<false>(up, t * G::RPS + w * 4, rs, cg),
                         reinterpret_cast<uint32_t*>(S[t]));
 
-  // (2) per-row scalars and v
-  const float beta = stage_rows<D, G::NT, PER_KEY, BF16, false>(a, nullptr, bh, head, 0, tid, srow, sv,
-                                                                 &redu[0][0]);
+  // (2) per-row scalars and v into LDS
+  const float beta = sg.store(a, tid, srow, sv, &redu[0][0]);
 
   // (3) decay, partial u = S'^T k, p = S'^T q over this lane's rows
   float pu[CPL], pp[CPL], pqk = 0.0f;
@@ -52,6 +54,7 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
       pp[c] = fmaf(rw.z, S[t][c], pp[c]);
     }
     pqk = fmaf(rw.z, rw.y, pqk);
+    __builtin_amdgcn_sched_barrier(0);  // row steps in load order, as in the quantized step
   }
 
   // (4) column reductions, delta and the readout y = p + (q.k) delta (one thread per column)
@@ -108,7 +111,10 @@ __device__ __forceinline__ void step_q_unit(const StepArgs& a, const UnitAddr& u
   const UnitPtr up = (PLAN != PLAN_ANY && a.st.contiguous) ? unit_ptr<D, FMT_Q, true>(ua, r)
                                                            : unit_ptr<D, FMT_Q>(ua, r);
 
-  // (1) issue every state load of this lane first, so the whole block is in flight
+  // (1) the staging loads (per-row scalars, v), then every state load of this lane, so the
+  // whole block is in flight while the staging completes
+  Stage<D, G::NT, PER_KEY, BF16, true> sg;
+  sg.load(a, reinterpret_cast<const float*>(ua.s), bh, head, r, tid);
   uint32_t raw[RPL][RW];
 #pragma unroll
   for (int t = 0; t < RPL; ++t) {
@@ -118,12 +124,14 @@ __device__ __forceinline__ void step_q_unit(const StepArgs& a, const UnitAddr& u
     });
   }
 
-  // (2) per-row scalars and v
-  const float beta = stage_rows<D, G::NT, PER_KEY, BF16, true>(a, reinterpret_cast<const float*>(ua.s),
-                                                                bh, head, r, tid, srow, sv, &sm.redu[0][0]);
+  // (2) per-row scalars and v into LDS
+  const float beta = sg.store(a, tid, srow, sv, &sm.redu[0][0]);
 
   // (3) pass 1: u_j += (k_i m_i) c_ij, p_j += (q_i m_i) c_ij over the lane's rows. The lane's
-  // rows are my_rows[t * RPS]: one LDS base address with immediate offsets per row step.
+  // rows are my_rows[t * RPS]: one LDS base address with immediate offsets per row step. Each
+  // row step's raw words pass through an empty asm statement first: those keep their order, so
+  // the compiler cannot hoist a later row step's decode (and the wait for its load) ahead of
+  // the earlier ones, and the reduction follows the loads as they land.
   const float4* my_rows = srow + (w * 4 + rs);
   float pu[CPL], pp[CPL], pqk = 0.0f;
 #pragma unroll
@@ -142,6 +150,7 @@ __device__ __forceinline__ void step_q_unit(const StepArgs& a, const UnitAddr& u
       }
     });
     pqk = fmaf(rw.z, rw.y, pqk);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // (4) column reductions, delta and the readout y = p + (q.k) delta (one thread per column)
