@@ -220,6 +220,27 @@ damp_status damp_decode_step_fused_ordered(damp_state* state, const int32_t* slo
                                            const float* gate_logit, damp_decay decay,
                                            const float* beta_logit, float* out, void* stream);
 
+/* Largest batch damp_decode_step_sorted takes: the entries of its library-held order buffer. */
+#define DAMP_SORTED_MAX_B 65536
+
+/* For callers that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. damp_batch_order followed by
+ * damp_decode_step_ordered, with the order kept in a buffer the library holds instead of a
+ * caller-owned one: a file-scope device array of DAMP_SORTED_MAX_B int32 (256 KiB) on each GPU
+ * the library runs on, held until the process ends. The call allocates nothing, issues no memset
+ * and enqueues the two kernels on `stream`; its results (readouts and pool) are those of
+ * damp_decode_step, bit for bit. The first call on a device looks the buffer's address up once
+ * (with that device current), on the device that runs `stream`.
+ * Every call on one device shares that buffer, which keeps the last call's order: calls that
+ * overlap on one device (on other streams, or from other threads) race and must be serialized
+ * by the caller.
+ * Errors: UNSUPPORTED for B > DAMP_SORTED_MAX_B (checked first, before any other argument); the
+ * rest as damp_decode_step. */
+damp_status damp_decode_step_sorted(damp_state* state, const int32_t* slot_idx, int32_t B,
+                                    const void* q, const void* k, const void* v,
+                                    damp_dtype qkv_dtype, const float* alpha, damp_decay decay,
+                                    const float* beta, float* out, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * Per-window requantization (the LeapQuant page, abstract: the low-bit state stays fixed for a
  * window of tokens, the window's updates are held in high precision, outputs are computed from

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -35,6 +36,13 @@ struct stq_state {
   std::vector<int64_t> head_off;
   uint8_t* table_dev;   // rowmap [H][d] (uint8) | w2 [H][d] (fp32) | heads [H] (int4)
 };
+
+// The library-held order buffer of damp_decode_step_sorted: one copy of this file-scope device
+// array on every GPU the library runs on, held until the process ends. In host code its name
+// stands for a host-side symbol, not a device address: the device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and only that address is ever handed
+// to a kernel.
+static __device__ __align__(256) int32_t scratch[DAMP_SORTED_MAX_B];
 
 namespace {
 
@@ -343,11 +351,44 @@ damp_status run_step(int fmt, const damp::StateRef& ref, int32_t d, int32_t H, i
                   "decode step");
 }
 
+// ---- the library-held order buffer of damp_decode_step_sorted (`scratch`, below) ----------
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device that runs `stream`, in *out.
+damp_status scratch_for(hipStream_t stream, int32_t** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DAMP_ERR_HIP, "finding the stream's device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DAMP_ERR_UNSUPPORTED, "device %d is beyond the %d devices this library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return fail(DAMP_ERR_HIP, "looking up the order buffer on device %d: %s", dev,
+                                     hipGetErrorString(e));
+    if (!ptr) return fail(DAMP_ERR_HIP, "the order buffer has no address on device %d", dev);
+    g_scratch_ptr[dev] = static_cast<int32_t*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return DAMP_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t damp_abi_version(void) { return (1 << 16) | 2; }
+int32_t damp_abi_version(void) { return (1 << 16) | 3; }
 
 const char* damp_last_error(void) { return g_last_error.c_str(); }
 
@@ -593,6 +634,29 @@ damp_status damp_decode_step_ordered(damp_state* s, const int32_t* slot_idx, con
   if (st != DAMP_OK) return st;
   if (B == 0) return ok();
   if (!order || !aligned(order, 4)) return fail(DAMP_ERR_INVALID_ARGUMENT, "order is NULL or misaligned");
+  return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, B, q, k, v,
+                  dt, alpha, decay, beta, out, stream, 0, nullptr, 0, false, order);
+}
+
+damp_status damp_decode_step_sorted(damp_state* s, const int32_t* slot_idx, int32_t B, const void* q,
+                                    const void* k, const void* v, damp_dtype dt, const float* alpha,
+                                    damp_decay decay, const float* beta, float* out, void* stream) {
+  if (B > DAMP_SORTED_MAX_B)
+    return fail(DAMP_ERR_UNSUPPORTED, "B = %d exceeds the library-held order buffer (%d entries); "
+                "use damp_batch_order and damp_decode_step_ordered with a caller buffer", B,
+                DAMP_SORTED_MAX_B);
+  if (!s) return fail(DAMP_ERR_INVALID_ARGUMENT, "state is NULL");
+  const damp_layout& L = s->layout;
+  damp_status st = check_step_args(B, L.num_heads, L.d_k, slot_idx, q, k, v, dt, alpha, decay, beta, out);
+  if (st != DAMP_OK) return st;
+  if (B == 0) return ok();
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* order = nullptr;
+  st = scratch_for(hs, &order);
+  if (st != DAMP_OK) return st;
+  // every entry of order[0, B) is written by the ordering kernel before the step reads it
+  st = launched(damp::launch_batch_order(slot_idx, B, L.num_slots, order, hs), "batch order");
+  if (st != DAMP_OK) return st;
   return run_step(damp::FMT_Q, damp_ref(s), L.d_k, L.num_heads, L.num_slots, slot_idx, B, q, k, v,
                   dt, alpha, decay, beta, out, stream, 0, nullptr, 0, false, order);
 }

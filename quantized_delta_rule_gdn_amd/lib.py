@@ -26,6 +26,7 @@ DAMP_DECAY_SCALAR = 0
 DAMP_DECAY_PER_KEY = 1
 DAMP_F32 = 0
 DAMP_BF16 = 1
+SORTED_MAX_B = 65536  # DAMP_SORTED_MAX_B: the library-held order buffer of damp_decode_step_sorted
 
 EXPORTS = (
     "damp_block_bytes", "damp_block_data_bytes", "damp_state_bytes", "damp_state_alloc",
@@ -37,7 +38,7 @@ EXPORTS = (
     "damp_window_flush", "stq_state_bytes", "stq_state_alloc", "stq_state_free",
     "stq_state_head_info", "stq_state_quantize", "stq_state_dequantize", "stq_decode_step",
     "damp_batch_order", "damp_decode_step_ordered", "damp_decode_step_fused_ordered",
-    "damp_window_step_ordered",
+    "damp_window_step_ordered", "damp_decode_step_sorted",
 )
 
 
@@ -112,6 +113,8 @@ def load() -> ctypes.CDLL:
                                             P, P, P], ctypes.c_int),
         "damp_window_step_ordered": ([P, P, I32, P, P, I32, P, P, P, ctypes.c_int, P,
                                       ctypes.c_int, P, P, P], ctypes.c_int),
+        "damp_decode_step_sorted": ([P, P, I32, P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, P],
+                                    ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -323,6 +326,17 @@ class DampState:
         _check(load().damp_decode_step_ordered(self._h, _ptr(slot_idx), _ptr(order), B, _ptr(q),
                                                _ptr(k), _ptr(v), dt, _ptr(alpha), decay,
                                                _ptr(beta), _ptr(out), _stream(stream)))
+
+    def decode_step_sorted(self, slot_idx, q, k, v, alpha, beta, out, stream=None) -> None:
+        """One decode step with the batch listed by slot in the library-held order buffer
+        (damp_decode_step_sorted: no allocation, no workspace; calls on one device must not
+        overlap). At most SORTED_MAX_B requests."""
+        B, dt, decay = _step_vectors(slot_idx, q, k, v, alpha, beta, out, self.num_heads, self.d)
+        if slot_idx.device != self.pool.device:
+            raise ValueError("slot_idx and the pool are on different devices")
+        _check(load().damp_decode_step_sorted(self._h, _ptr(slot_idx), B, _ptr(q), _ptr(k), _ptr(v),
+                                              dt, _ptr(alpha), decay, _ptr(beta), _ptr(out),
+                                              _stream(stream)))
 
     def batch_order(self, slot_idx, out=None, stream=None):
         """The batch positions by ascending slot of this pool (damp_batch_order)."""

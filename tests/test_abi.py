@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.damp_abi_version() == (1 << 16) | 2
+    assert L.damp_abi_version() == (1 << 16) | 3
 
 
 def test_block_accounting_d128():
@@ -257,3 +257,16 @@ def test_order_entry_points_reject_bad_arguments_on_host():
     assert "state is NULL" in lib.last_error()
     assert L.damp_decode_step_fused_ordered(None, a, o, 1, a, a, a, 0, a, 0, a, a, None) == bad
     assert L.damp_window_step_ordered(None, a, 4, a, o, 1, a, a, a, 0, a, 0, a, a, None) == bad
+
+
+def test_sorted_step_rejects_bad_arguments_on_host():
+    """damp_decode_step_sorted checks the batch against its library-held buffer before anything
+    else, then the arguments as damp_decode_step does; none of it needs a GPU."""
+    L = lib.load()
+    a = ctypes.c_void_p(0x100000)
+    assert L.damp_decode_step_sorted(None, a, lib.SORTED_MAX_B + 1, a, a, a, 0, a, 0, a, a,
+                                     None) == lib.DAMP_ERR_UNSUPPORTED
+    assert "order buffer" in lib.last_error()
+    assert L.damp_decode_step_sorted(None, a, lib.SORTED_MAX_B, a, a, a, 0, a, 0, a, a,
+                                     None) == lib.DAMP_ERR_INVALID_ARGUMENT
+    assert "state is NULL" in lib.last_error()
