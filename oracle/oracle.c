@@ -29,12 +29,10 @@
  * Round to nearest, ties to even. Binary32 -> binary64 is exact and scaling by a power of two
  * is exact, so the rounding is done on an exact integer multiple count with nearbyint().
  * ---------------------------------------------------------------------------------------- */
-uint16_t oracle_f16_from_f32(float xf) {
-  uint32_t u;
-  memcpy(&u, &xf, sizeof u);
-  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
-  if (isnan(xf)) return (uint16_t)(sign | 0x7e00u);
-  const double a = fabs((double)xf);
+static uint16_t f16_from_double(double x) {
+  const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  if (isnan(x)) return (uint16_t)(sign | 0x7e00u);
+  const double a = fabs(x);
   /* 65520 = 65504 + half of the last binade's spacing (32); at or above it, RNE overflows. */
   if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u);
   if (a == 0.0) return sign;
@@ -51,6 +49,9 @@ uint16_t oracle_f16_from_f32(float xf) {
   const uint32_t bits = ((uint32_t)(E + 15) << 10) + (uint32_t)n - 1024u;
   return (uint16_t)(sign | bits);
 }
+
+/* binary32 widens to binary64 exactly, so this is the single rounding of x to binary16 */
+uint16_t oracle_f16_from_f32(float xf) { return f16_from_double((double)xf); }
 
 float oracle_f32_from_f16(uint16_t h) {
   const int sign = (h >> 15) & 1;
@@ -581,7 +582,7 @@ static void stq_store_unit(int D, const uint8_t* bits, const float* w, const flo
       const double wi = unweighted ? 1.0 : (double)w[i];
       acc += wi * wi * (double)X[(long)i * D + j] * (double)X[(long)i * D + j];
     }
-    cs[j] = sw > 0.0 ? oracle_f16_from_f32((float)sqrt(acc / sw)) : 0;
+    cs[j] = sw > 0.0 ? f16_from_double(sqrt(acc / sw)) : 0; /* one rounding to binary16 */
   }
   for (int i = 0; i < D; ++i) {
     const float* x = X + (long)i * D;

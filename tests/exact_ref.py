@@ -111,3 +111,116 @@ def step_exact(D, fmt, mask, S32, h, c, s, q, k, v, alpha, beta):
             sn[i] = float(sc)
     res.update(h=hn, c=cn, s=sn)
     return res
+
+
+# ------------------------------------------------------------------------------------------
+# STEPQuant-style state (the STEPQuant page, appendix Table C2 steps 1-6; the fit's formulas
+# are this repository's reading of the page's description): pivot rows in binary16, integer
+# rows of b in {8, 6, 4} bits with a binary16 row factor each and one binary16 column-scale
+# vector per unit, fitted from the new state X (rounded once to binary32) over the non-pivot
+# rows N with squared row-impact weights w_i:
+#   cs_j = the binary16 value nearest to sqrt(sum_N w_i^2 X_ij^2 / sum_N w_i^2)
+#          (all w_i = 0 on N: every weight 1)
+#   rf_i = f16(f32(max over j with cs_j > 0 of f32(|X_ij| / cs_j) / qmax)),  qmax = 2^(b-1) - 1
+#   code = clamp(rne(f32(X_ij / (rf_i cs_j))), -qmax, qmax), 0 where rf_i cs_j = 0
+# Here every quantity is exact (Fraction) up to the roundings the statement names; the square
+# root is rounded to binary16 directly from the exact ratio, by comparing squares.
+# ------------------------------------------------------------------------------------------
+def _isqrt_floor(x: Fraction) -> int:
+    """Largest integer n >= 0 with n^2 <= x."""
+    from math import isqrt
+    return isqrt(x.numerator // x.denominator)
+
+
+def sqrt_round_binary(R: Fraction, p: int, emin: int, emax: int):
+    """The IEEE value with p significand bits nearest to sqrt(R) (R >= 0), ties to even, from
+    the exact R: n = floor(sqrt(R) / quantum) by an integer square root, then the half-way
+    point compared by squares. Returns (value, distance of sqrt(R) to the nearest tie point in
+    units of the quantum, as a float, for callers that want to know how close it came)."""
+    if R == 0:
+        return Fraction(0), float("inf")
+    e = _ilog2(R) // 2      # 2^(2e) <= R < 2^(2e+2) up to the floor: sqrt(R) in [2^e, 2^(e+1))
+    while Fraction(2) ** (2 * e) > R:
+        e -= 1
+    while Fraction(2) ** (2 * e + 2) <= R:
+        e += 1
+    e = max(e, emin)
+    quantum = Fraction(2) ** (e - (p - 1))
+    n = _isqrt_floor(R / (quantum * quantum))
+    mid2 = (Fraction(2 * n + 1, 2) * quantum) ** 2
+    if R > mid2:
+        n += 1
+    elif R == mid2 and n % 2 == 1:
+        n += 1
+    val = n * quantum
+    if val >= Fraction(2) ** (emax + 1):
+        return float("inf"), float("inf")
+    # how far sqrt(R) lies from the tie point (n_floor + 1/2) quantum, relative to the quantum
+    import math
+    s = math.sqrt(float(R / (quantum * quantum)))
+    return val, abs(s - (math.floor(s) + 0.5))
+
+
+def f16_value(bits) -> Fraction:
+    return Fraction(float(np.array([bits], np.uint16).view(np.float16)[0]))
+
+
+def stq_step_exact(D, bits, w, h, c, rf, cs, q, k, v, alpha, beta, cs_near_tie=None):
+    """One STEPQuant-style unit, exact. bits [D] (16 = pivot, 8, 6, 4), w [D] float32 row-impact
+    scores, h uint16 [D, D], c int8 [D, D], rf uint16 [D], cs uint16 [D]; alpha scalar or [D].
+    Returns dict(out float32 [D], h, c, rf, cs (new state), tie [D]: for each column, how close
+    sqrt of its weighted mean square came to a binary16 tie, in quanta).
+    cs_near_tie: optional dict j -> binary16 bits, used for column j instead of the exact value
+    (for a column whose square root lies so close to a tie that binary64 evaluation may take the
+    other side)."""
+    F = Fraction
+    a = [F(float(alpha))] * D if np.ndim(alpha) == 0 else [F(float(x)) for x in alpha]
+    qq = [F(float(x)) for x in q]
+    kk = [F(float(x)) for x in k]
+    vv = [F(float(x)) for x in v]
+    bb = F(float(beta))
+    piv = [int(b) == 16 for b in bits]
+    rfv = [f16_value(x) for x in rf]
+    csv = [f16_value(x) for x in cs]
+    Sh = [[f16_value(h[i, j]) if piv[i] else int(c[i, j]) * rfv[i] * csv[j] for j in range(D)]
+          for i in range(D)]
+    Sp = [[a[i] * Sh[i][j] for j in range(D)] for i in range(D)]
+    u = [sum(kk[i] * Sp[i][j] for i in range(D)) for j in range(D)]
+    delta = [bb * (vv[j] - u[j]) for j in range(D)]
+    X = [[Sp[i][j] + kk[i] * delta[j] for j in range(D)] for i in range(D)]
+    y = [sum(qq[i] * X[i][j] for i in range(D)) for j in range(D)]
+    Xf = [[f32(X[i][j]) for j in range(D)] for i in range(D)]
+    N = [i for i in range(D) if not piv[i]]
+    w2 = {i: F(float(w[i])) ** 2 for i in N}
+    if sum(w2.values()) == 0:
+        w2 = {i: F(1) for i in N}
+    sw = sum(w2.values())
+    cs_new, tie = [], []
+    for j in range(D):
+        if not N:
+            cs_new.append(F(0))
+            tie.append(float("inf"))
+            continue
+        R = sum(w2[i] * Xf[i][j] ** 2 for i in N) / sw
+        val, t = sqrt_round_binary(R, 11, -14, 15)
+        if cs_near_tie and j in cs_near_tie:
+            val = f16_value(cs_near_tie[j])
+        cs_new.append(val)
+        tie.append(t)
+    hn = np.zeros((D, D), np.uint16)
+    cn = np.zeros((D, D), np.int8)
+    rfn = np.zeros(D, np.uint16)
+    for i in range(D):
+        if piv[i]:
+            hn[i] = [f16_bits(f16(x)) for x in Xf[i]]
+            continue
+        qm = 2 ** (int(bits[i]) - 1) - 1
+        m = max([f32(abs(Xf[i][j]) / cs_new[j]) for j in range(D) if cs_new[j] > 0], default=F(0))
+        r = f16(f32(m / qm))
+        rfn[i] = f16_bits(r)
+        for j in range(D):
+            sc = r * cs_new[j]
+            if sc > 0:
+                cn[i, j] = max(-qm, min(qm, rne_int(f32(Xf[i][j] / sc))))
+    return {"out": np.array([float(f32(x)) for x in y], np.float32), "h": hn, "c": cn, "rf": rfn,
+            "cs": np.array([f16_bits(x) for x in cs_new], np.uint16), "tie": np.array(tie)}

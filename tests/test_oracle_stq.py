@@ -6,14 +6,16 @@ repository's reading, written out in oracle.c).
 Pinned by a hand-derived 2x3 fixture (tests/golden/stq_3x3.json), exact rational
 reconstruction, numpy's IEEE float16 on pivot rows, closed forms (a lone integer row codes every
 entry at +-qmax, weight scaling changes nothing, zero weights mean equal weights), invariants of
-the codes (range, half-step error where not clamped), and the step's reduction to the
-all-FP16 DAMP step when every row is a pivot.
+the codes (range, half-step error where not clamped), the step's reduction to the
+all-FP16 DAMP step when every row is a pivot, and the step over several units with integer rows
+against an exact rational model of the fit (tests/exact_ref.py).
 """
 import json
 import os
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 import oracle
 
@@ -149,3 +151,57 @@ def test_step_with_every_row_a_pivot_is_the_all_fp16_damp_step():
     assert np.array_equal(hd, h)
     outd = oracle.step_quant(mask, hd, cd, sd, q, k, v, al, be)
     assert np.array_equal(out, outd) and np.array_equal(h2, hd)
+
+
+def _stq_case(seed, n, D, per_key):
+    """n units with their own precision maps (each has a pivot and rows of all three integer
+    widths), their own row-impact scores (the last unit all zero: equal weights), a heavy row
+    and a heavy column, packed by the oracle; plus one step's inputs."""
+    rng = np.random.default_rng(seed)
+    bits = np.empty((n, D), np.uint8)
+    for u in range(n):
+        kinds = np.array([16, 8, 6, 4] + list(rng.choice(np.array([16, 8, 6, 4], np.uint8), D - 4)), np.uint8)
+        bits[u] = rng.permutation(kinds)
+    w = rng.uniform(0.2, 3.0, (n, D)).astype(np.float32)
+    w[-1] = 0.0
+    S = (rng.standard_normal((n, D, D)) * 0.3).astype(np.float32)
+    S[:, :, 3] *= 12.0
+    S[:, 5, :] *= 7.0
+    st = oracle.stq_quantize(bits, w, S)
+    q = rng.standard_normal((n, D)).astype(np.float32)
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    k = rng.standard_normal((n, D)).astype(np.float32)
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((n, D)).astype(np.float32)
+    al = (rng.uniform(0.3, 1.0, (n, D)) if per_key else rng.uniform(0.3, 1.0, n)).astype(np.float32)
+    be = rng.uniform(0.1, 1.0, n).astype(np.float32)
+    return bits, w, st, (q, k, v, al, be)
+
+
+@pytest.mark.parametrize("per_key", [False, True])
+def test_step_on_integer_rows_matches_exact_rationals_across_units(per_key):
+    """The step over several units with mixed 8/6/4-bit rows, per-unit precision maps and row
+    weights, both gate forms, against exact rational arithmetic of the fit's statement: every
+    readout, pivot value, code, row factor and column scale bit for bit. A column whose square
+    root lies within 1e-9 of a quantum of a binary16 tie (where binary64 evaluation could take
+    the other side) takes the oracle's scale and is counted; there is none in these cases."""
+    import exact_ref
+    n, D = 4, 12
+    bits, w, (h, c, rf, cs), (q, k, v, al, be) = _stq_case(11 + per_key, n, D, per_key)
+    out, (h2, c2, rf2, cs2) = oracle.stq_step(bits, w, h, c, rf, cs, q, k, v, al, be)
+    near = 0
+    for u in range(n):
+        ref = exact_ref.stq_step_exact(D, bits[u], w[u], h[u], c[u], rf[u], cs[u], q[u], k[u], v[u],
+                                       al[u], be[u])
+        ties = {j: int(cs2[u, j]) for j in np.nonzero(ref["tie"] < 1e-9)[0]}
+        if ties:
+            near += len(ties)
+            ref = exact_ref.stq_step_exact(D, bits[u], w[u], h[u], c[u], rf[u], cs[u], q[u], k[u],
+                                           v[u], al[u], be[u], cs_near_tie=ties)
+        assert np.array_equal(cs2[u], ref["cs"]), f"unit {u}: column scales"
+        assert np.array_equal(rf2[u], ref["rf"]), f"unit {u}: row factors"
+        assert np.array_equal(c2[u], ref["c"]), f"unit {u}: codes"
+        assert np.array_equal(h2[u], ref["h"]), f"unit {u}: pivot rows"
+        assert np.array_equal(out[u], ref["out"]), f"unit {u}: readout"
+        assert (c2[u][bits[u] != 16] != 0).any()
+    assert near == 0
