@@ -6,12 +6,12 @@
  *
  * Sources (web pages):
  *  [C2]   "STEPQuant: When and Where Errors Matter in Delta-Rule Recurrent State Quantization"
- *         (thelatestinai.com listing), appendix Table C2, one persistent decode step: inputs
- *         are the compressed state, q_t, k_t, v_t, the gate D_t, beta_t and a frozen precision
- *         map; (1) reconstruct the previous state from integer codes and scales, or FP16 for
- *         pivot units; (2) X = D_t S_hat + beta_t k_t (v_t^T - k_t^T D_t S_hat); (3) emit
- *         y_t = X^T q_t before requantization; (6) pack codes and scales, store pivots in FP16,
- *         keep the old representation valid until its readers finish.
+ *         (thelatestinai.com listing), appendix Table C2, one persistent decode step. It takes
+ *         the compressed state, q_t, k_t, v_t, the gate D_t, beta_t and a frozen precision map.
+ *         Step 1 rebuilds S_hat (codes times scales; FP16 rows as stored); step 2 forms
+ *         X = D_t S_hat + beta_t k_t (v_t^T - k_t^T D_t S_hat); step 3 takes the readout
+ *         y_t = X^T q_t before any requantization; step 6 writes the new codes, scales and FP16
+ *         rows, leaving the previous copy intact for readers that still use it.
  *  [DAMP] "DAMP: Decay-Aware Mixed-Precision Recurrent-State Quantization", abstract (arXiv v1
  *         on news.chathome.org; later version on mlsanity.com): high-risk key channels chosen
  *         offline are kept in FP16, the remaining key channels in INT8, under a fixed storage
@@ -26,13 +26,14 @@
  *
  * INT8 rows (the pages only say "INT8"; this rule is the library's): symmetric, one fp32 scale
  * per row, scale = fl32(max_j |X_ij| / 127), code = round-half-to-even of fl32(X_ij / scale),
- * codes in [-127, 127]; an all-zero row has scale 0 and codes 0. damp_state_quantize and
+ * codes in [-127, 127]; a row whose scale is 0 (an all-zero row, or an absmax below
+ * 127 * 2^-150, where the quotient rounds to zero) has codes 0. A subnormal scale (absmax below
+ * 127 * 2^-126 ~ 1.5e-36) follows the same rule. damp_state_quantize and
  * uniform_int8_quantize follow this rule bit for bit. Inside the decode steps the code is the
  * round-half-to-even of X_ij * rcp(scale) (hardware reciprocal, 1 ulp), which can differ by one
  * from the rule where X_ij / scale lies within ~2e-5 of a half-integer (a few codes in 10^5).
  * FP16 rows: IEEE binary16, round to nearest even. Reconstruction: code * scale, or the
- * binary16 value. Rows whose absmax is below ~1e-36 (subnormal scales) are outside the range
- * the rule is supported for.
+ * binary16 value.
  *
  * Execution model. Every call that takes a `stream` (a hipStream_t, e.g. torch's
  * torch.cuda.current_stream().cuda_stream; NULL = the default stream) only validates its
@@ -109,7 +110,8 @@ size_t damp_block_bytes(const damp_layout* layout);
 /* Data bytes of one block, without the padding (what a step reads and writes), or 0. */
 size_t damp_block_data_bytes(const damp_layout* layout);
 
-/* Device bytes a pool needs: num_slots * num_heads * damp_block_bytes, or 0 if invalid. */
+/* Device bytes a pool needs: num_slots * num_heads * damp_block_bytes, or 0 if invalid.
+ * (Library infrastructure: no page defines it; the storage it counts is [DAMP]'s layout.) */
 size_t damp_state_bytes(const damp_layout* layout);
 
 /* Bind a caller-owned device pool to a layout and a frozen row map.
@@ -126,7 +128,8 @@ damp_status damp_state_alloc(const damp_layout* layout, const int32_t* fp16_rows
                              size_t pool_bytes, damp_state** out);
 
 /* Release the handle and its row-map copy (not the pool). NULL is accepted. Synchronises
- * nothing: the caller must not free while work that uses the handle is still queued. */
+ * nothing: the caller must not free while work that uses the handle is still queued.
+ * (Library infrastructure: no page defines it.) */
 damp_status damp_state_free(damp_state* state);
 
 /* Layout of a handle (copied to *layout). */
@@ -263,10 +266,11 @@ size_t damp_window_bytes(const damp_layout* layout, int32_t window);
  * is appended to the buffer; if it is the window's window-th token, X is stored in the unit's
  * rule (FP16 rows RNE, INT8 rows absmax / 127) and the buffer emptied. Otherwise the pool is only
  * read. window = 1 is the per-token step (the same arithmetic as damp_decode_step up to fp32
- * rounding order). A given buffer must always be used with the same window length and the same
- * decay mode: with DAMP_DECAY_SCALAR the buffer holds the decay as scalars (one for the window,
- * one per buffered key) and the keys as appended, with DAMP_DECAY_PER_KEY as row gains and
- * decayed keys.
+ * rounding order). A given buffer must always be used with the same window length, and within
+ * one window with the same decay mode: with DAMP_DECAY_SCALAR the buffer holds the decay as
+ * scalars (one for the window, one per buffered key) and the keys as appended, with
+ * DAMP_DECAY_PER_KEY as row gains and decayed keys. A flag in the buffer, set by the window's
+ * tokens and cleared when the window ends (or is flushed), tells a flush which form it holds.
  * Errors: INVALID_ARGUMENT, SLOT_INDEX (debug), HIP. */
 damp_status damp_window_step(damp_state* state, void* window_buf, int32_t window,
                              const int32_t* slot_idx, int32_t B, const void* q, const void* k,
@@ -289,7 +293,8 @@ damp_status damp_window_step_ordered(damp_state* state, void* window_buf, int32_
 damp_status damp_window_flush(damp_state* state, void* window_buf, int32_t window,
                               const int32_t* slot_idx, int32_t n, void* stream);
 
-/* The same step on an FP32 state pool (the reference format of the DAMP speedups):
+/* The same step on an FP32 state pool: the format the states are commonly kept in and that the
+ * DAMP storage and kernel speedups are measured against ([DAMP], both abstracts).
  *   pool dev fp32 [num_slots][num_heads][d_k][d_v], 16-byte aligned. Other arguments as in
  *   damp_decode_step. No requantization: X is stored as fp32. */
 damp_status fp32_decode_step(float* pool, int32_t num_slots, int32_t num_heads, int32_t d_k,
@@ -298,7 +303,9 @@ damp_status fp32_decode_step(float* pool, int32_t num_slots, int32_t num_heads, 
                              const float* alpha, damp_decay decay, const float* beta,
                              float* out, void* stream);
 
-/* The same step on a uniform-INT8 state (every key row INT8 with its own fp32 scale):
+/* The same step on a uniform-INT8 state (every key row INT8 with its own fp32 scale): the
+ * uniform quantization DAMP improves on, with no high-risk channels kept at higher precision
+ * ([DAMP], both abstracts: uniform INT8 already costs reasoning accuracy).
  *   codes  dev int8 [num_slots][num_heads][d_k][d_v], 16-byte aligned
  *   scales dev fp32 [num_slots][num_heads][d_k], 16-byte aligned
  * Bit-identical to damp_decode_step with num_fp16_rows = 0 on the same values. */
@@ -453,7 +460,7 @@ damp_status stq_state_dequantize(const stq_state* state, float* S, const int32_t
 /* One decode step on the STEPQuant-style state ([C2] Table C2 steps 1-6): reconstruct, decay,
  * update, readout y = X^T q before requantization, refit and pack. dst_pool: NULL writes the new
  * state in place; otherwise a second pool of the same layout receives it and the state bound to
- * the handle is only read (step 6: the old representation stays valid until its readers finish;
+ * the handle is only read (step 6: the previous copy stays intact while readers still use it;
  * the caller then binds the other pool or copies). Other arguments as in damp_decode_step. */
 damp_status stq_decode_step(stq_state* state, void* dst_pool, const int32_t* slot_idx, int32_t B,
                             const void* q, const void* k, const void* v, damp_dtype qkv_dtype,
@@ -461,10 +468,11 @@ damp_status stq_decode_step(stq_state* state, void* dst_pool, const int32_t* slo
                             void* stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). The string
- * is owned by the library and valid until the thread's next call. */
+ * is owned by the library and valid until the thread's next call. (Library infrastructure: no
+ * page defines it.) */
 const char* damp_last_error(void);
 
-/* ABI version: (major << 16) | minor. */
+/* ABI version: (major << 16) | minor. (Library infrastructure: no page defines it.) */
 int32_t damp_abi_version(void);
 
 #ifdef __cplusplus

@@ -86,12 +86,14 @@ void oracle_quant_row(int D, const float* x, int8_t* c, float* s) {
     const float a = fabsf(x[j]);
     if (a > m) m = a;
   }
-  if (m == 0.0f) {
+  const float sc = m / 127.0f; /* binary32 division, round to nearest even */
+  if (sc == 0.0f) {
+    /* an all-zero row, or one whose absmax is below 127 * 2^-150 so that m / 127 rounds to
+     * zero: scale 0, codes 0 (no code can reconstruct anything else with a zero scale) */
     *s = 0.0f;
     memset(c, 0, (size_t)D);
     return;
   }
-  const float sc = m / 127.0f; /* binary32 division, round to nearest even */
   for (int j = 0; j < D; ++j) {
     const float t = x[j] / sc;   /* binary32 division */
     float r = nearbyintf(t);     /* default rounding mode: to nearest, ties to even */
@@ -549,9 +551,10 @@ int oracle_window_flush(int D, long n_units, const uint8_t* mask, uint16_t* h, i
  * Each key row of a head is a pivot (kept in FP16) or an integer row with its own code width
  * b in {4, 6, 8} (a frozen precision map); the integer rows share one column-scale vector per
  * head and carry one row factor each, both stored in FP16; entry (i, j) of an integer row is
- * code_ij * rf_i * cs_j. The page names the fit (key-row-aware dual-axis fitting; for KDA one
- * shared column-scale vector fitted with squared row-impact factors over all non-pivot integer
- * rows) but not its formulas; the reading taken here, for the non-pivot rows N of a unit:
+ * code_ij * rf_i * cs_j. The page names the fit (a dual-axis fit aware of key rows; for KDA a
+ * single column-scale vector per head, fitted over the integer rows with each row weighted by
+ * the square of its row-impact score) but not its formulas; the reading taken here, for the
+ * non-pivot rows N of a unit:
  *   cs_j = fp16( sqrt( sum_{i in N} w_i^2 X_ij^2 / sum_{i in N} w_i^2 ) )   (binary64, then
  *          binary16 RNE; all w_i = 0 is read as all w_i = 1)
  *   rf_i = fp16( fl32( max_{j: cs_j > 0} fl32(|X_ij| / cs_j) / qmax_i ) ),  qmax = 2^(b-1) - 1

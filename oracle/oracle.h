@@ -42,7 +42,7 @@ void oracle_f32_from_f16_n(const uint16_t* h, float* x, long n);
 
 /* Requantize one row of D binary32 values to symmetric INT8: m = max|x|, s = m/127 (binary32
  * division), c = clamp(round_half_even(x/s), -127, 127) with x/s a binary32 division.
- * m == 0 gives s = 0 and all codes 0. */
+ * s == 0 (m == 0, or m < 127 * 2^-150 so that m/127 rounds to zero) gives all codes 0. */
 void oracle_quant_row(int D, const float* x, int8_t* c, float* s);
 
 /* Pack n_units fp32 states S[n][D][D] into the logical representation (mask[n][D]). */

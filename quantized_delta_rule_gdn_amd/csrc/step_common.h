@@ -383,29 +383,47 @@ struct Row {
       for (int c = 1; c < CPL; ++c) m = fmaxf(m, fabsf(x[c]));
       m = max_row16(m);
       const float s = div127(m);
-      if constexpr (EXACT) {
-        const float inv = m > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
+      // The codes of values xx with scale ss: ss normal, or 0 (an all-zero row, or one whose
+      // absmax is below 127 * 2^-150, where m / 127 rounds to zero): then every code is 0.
+      auto codes = [&](const float* xx, float ss) __attribute__((always_inline)) {
+        if constexpr (EXACT) {
+          const float inv = ss > 0.0f ? __fdiv_rn(1.0f, ss) : 0.0f;
 #pragma unroll
-        for (int i = 0; i < W; ++i) wd[i] = 0;
+          for (int i = 0; i < W; ++i) wd[i] = 0;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const int32_t code = m > 0.0f ? int8_code_exact(x[c], s, inv) : 0;
-          wd[c >> 2] |= (static_cast<uint32_t>(code) & 0xFFu) << (8 * (c & 3));
-        }
-      } else {
-        const float inv = m > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
-        uint32_t f[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) f[c] = int8_code_fast_bits(x[c], inv);
-        if constexpr (CPL >= 4) {
-#pragma unroll
-          for (int i = 0; i < CPL / 4; ++i)
-            wd[i] = pack4_low_bytes(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
-        } else if constexpr (CPL == 2) {
-          wd[0] = __builtin_amdgcn_perm(f[1], f[0], 0x0c0c0400u);
+          for (int c = 0; c < CPL; ++c) {
+            const int32_t code = ss > 0.0f ? int8_code_exact(xx[c], ss, inv) : 0;
+            wd[c >> 2] |= (static_cast<uint32_t>(code) & 0xFFu) << (8 * (c & 3));
+          }
         } else {
-          wd[0] = f[0] & 0xFFu;
+          const float inv = ss > 0.0f ? __builtin_amdgcn_rcpf(ss) : 0.0f;
+          uint32_t f[CPL];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) f[c] = int8_code_fast_bits(xx[c], inv);
+          if constexpr (CPL >= 4) {
+#pragma unroll
+            for (int i = 0; i < CPL / 4; ++i)
+              wd[i] = pack4_low_bytes(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+          } else if constexpr (CPL == 2) {
+            wd[0] = __builtin_amdgcn_perm(f[1], f[0], 0x0c0c0400u);
+          } else {
+            wd[0] = f[0] & 0xFFu;
+          }
         }
+      };
+      // A row whose absmax is below 127 * 2^-126 (~1.5e-36) has a subnormal scale, whose
+      // reciprocal overflows. Its codes are taken on the row and the scale both multiplied by
+      // 2^64, which is exact and leaves every quotient x / s as it is. The branch is
+      // wave-uniform and only waves holding such a row take it; the stored scale is s itself.
+      const bool tiny = s > 0.0f && s < 0x1p-126f;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(tiny) != 0, 0)) {
+        const float k2 = tiny ? 0x1p64f : 1.0f;
+        float xs[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) xs[c] = x[c] * k2;
+        codes(xs, s * k2);
+      } else {
+        codes(x, s);
       }
       if (cg == 0) {
         if constexpr (SC_LDS) {

@@ -41,8 +41,8 @@
 // product its row maximum used, by one fma against 1.5 * 2^23, like the DAMP step's codes. Since
 // |a_j| <= m and rf >= (m / qmax)(1 - 2^-11) for a normal binary16 rf, no such code rounds past
 // qmax; only a row group holding a subnormal or zero row factor clamps.
-// The step may write its new state to another pool than it read (Table C2 step 6: the old
-// representation stays valid until its readers finish).
+// The step may write its new state to another pool than it read (Table C2 step 6: the previous
+// copy stays intact while readers still use it).
 #include <type_traits>
 
 #include "step_common.h"

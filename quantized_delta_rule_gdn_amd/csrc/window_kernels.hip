@@ -23,7 +23,8 @@ namespace {
 // Window buffer of one unit, fp32 words at a.win + (slot * H + head) * a.win_stride bytes:
 //   [0]            t, the tokens applied in the current window (int32; 0 = empty, a = 1)
 //   [1]            scalar gate: a, the product of the window's gates so far
-//   [2]            1 for a window with a scalar gate (written by its tokens), 0 for per-row gates
+//   [2]            1 for a window with a scalar gate, 0 for per-row gates (written by every
+//                  token that leaves the window open; cleared when the window ends)
 //   [4, 4 + D)     per-row gates: a, storage row order
 //                  scalar gate: [4, 4 + W) c[tau], the product of the gates after token tau
 //   [4 + D, ..)    K[tau][p], tau < W, storage row order (per-row gates: decayed; scalar gate:
@@ -292,7 +293,10 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
     if (!ends) {
       // append the token's key (storage order) and count it; the stored state stays as it is
       for (int i = tid; i < D; i += G::NT) wp.K[t * D + i] = srow[i].y;
-      if (tid == 0) *wp.hdr = t + 1;
+      if (tid == 0) {
+        wp.hdr[0] = t + 1;
+        if (!scal) wp.hdr[2] = 0;   // per-row gates (the scalar form set its flag in staging)
+      }
       return;
     }
     terms = t + 1;
@@ -340,7 +344,10 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
     });
   }
   flush_scales<D, G::NT>(up, ssc, r, tid);
-  if (tid == 0) *wp.hdr = 0;
+  if (tid == 0) {   // an empty window, with no gate form yet
+    wp.hdr[0] = 0;
+    wp.hdr[2] = 0;
+  }
 }
 
 template <int D, int PER_KEY, int BF16, int WAVES, int NF, bool FLUSH_ONLY>

@@ -64,11 +64,12 @@ def f16_bits(x: Fraction) -> int:
 
 def quant_row_exact(xf: list[Fraction]):
     """INT8 row rule on binary32 values xf: m = max|x|, s = f32(m/127), c = rne(f32(x/s)),
-    clamped to [-127, 127]; m == 0 -> s = 0, c = 0."""
+    clamped to [-127, 127]; s == 0 (m == 0, or m/127 below half the smallest subnormal) ->
+    c = 0."""
     m = max(abs(x) for x in xf)
-    if m == 0:
-        return [0] * len(xf), Fraction(0)
     s = f32(m / 127)
+    if s == 0:
+        return [0] * len(xf), Fraction(0)
     codes = [max(-127, min(127, rne_int(f32(x / s)))) for x in xf]
     return codes, s
 

@@ -136,6 +136,14 @@ def test_quantize_and_dequantize_kernels_bit_exact(D, r):
     S[0, 0, 3] = 0.0                     # an all-zero row
     S[1, 1, 5, 7] = 127.0                # absmax 127 -> scale exactly 1 ...
     S[1, 1, 5, :7] = np.arange(7) + 0.5  # ... and exact .5 ties
+    # rows whose scale is subnormal (absmax below 127 * 2^-126): 1e-37, 127 * 2^-127, 3e-41,
+    # 2^-140; one at the boundary, absmax 127 * 2^-126 (scale exactly 2^-126);
+    # plus one below 127 * 2^-150, whose scale rounds to zero (codes 0)
+    for (u, hh, i), amax in zip([(2, 0, 4), (2, 1, 6), (3, 2, 9), (4, 0, 11), (4, 1, 1), (4, 2, 13)],
+                                [1e-37, 127 * 2.0 ** -127, 3e-41, 2.0 ** -140, 127 * 2.0 ** -126,
+                                 60 * 2.0 ** -149]):
+        row = S[u, hh, i].astype(np.float64)
+        S[u, hh, i] = (row / np.abs(row).max() * amax).astype(np.float32)
     rows = synth.random_rows(rng, H, D, r)
     mask = synth.rows_to_mask(rows, D)
     maskn = np.broadcast_to(mask, (n, H, D)).reshape(n * H, D)
@@ -254,6 +262,52 @@ print('ok')
     r = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
+
+
+def test_step_rows_with_subnormal_scales():
+    """INT8 rows whose absmax lies below 127 * 2^-126, so that their scale is subnormal, next to
+    ordinary rows, against the oracle; the key entry of those rows is 0, so X keeps them that
+    small. The codes come out as the rule gives them (the reciprocal of a subnormal scale
+    overflows; the kernel takes the codes on the row and the scale scaled by 2^64).
+    Tolerances. The kernel forms X = code * m with the row multiplier m = a * scale, which is
+    subnormal too and rounded to the grid of 2^-149: |dX| <= 127 * 2^-150 + 2^-23 |X|, so
+    |d scale| <= 3 * 2^-150 + 2^-23 scale, inside 1e-6 scale + 2^-148, and codes move by at most
+    127 * 2^-150 / scale + ... < 1 while the scale is above ~1e-41 (rows of absmax 1e-37 and
+    2e-39 here: codes >= 99.9% equal, |delta| <= 1 as everywhere). A row of absmax 5e-42 has a
+    scale of ~28 grid steps, so its codes may move by several; it is held instead to its values:
+    |reconstruction - oracle's| <= |dX| + (scale_gpu + scale_ref) / 2 < 2^-142."""
+    B, H, D, r = 4, 3, 128, 24
+    rows, S, inp = _random_case(91, B, H, D, r, synth.GDN, "bf16")
+    rng = np.random.default_rng(92)
+    tiny_rows, deep_rows = [], []
+    for h in range(H):
+        int8_rows = np.setdiff1d(np.arange(D), rows[h])
+        pick = rng.choice(int8_rows, 3, replace=False)
+        for i, amax in zip(pick, [1e-37, 2e-39, 5e-42]):
+            row = S[:, h, i].astype(np.float64)
+            S[:, h, i] = (row / np.abs(row).max(axis=-1, keepdims=True) * amax).astype(np.float32)
+            inp.k[:, h, i] = 0.0
+            inp.k_bits[:, h, i] = 0
+            (deep_rows if amax < 1e-40 else tiny_rows).append((h, i))
+    mask, out, got, ref_out, ref, _ = _damp_ref_and_gpu(rows, S, inp, np.arange(B), B)
+    check_readout(out, ref_out)
+    keep = np.ones((H, D), bool)            # every row but the deepest ones
+    for h, i in deep_rows:
+        keep[h, i] = False
+    sub = lambda arrs: tuple(np.where(keep[None, :, :, None], x, 0) if x.ndim == 4 else
+                             np.where(keep[None], x, 0) for x in arrs)
+    stats = check_quant(mask, sub(got), sub(ref), scale_abs=2.0 ** -148)
+    _log(f"subnormal scales: {stats}")
+    for h, i in tiny_rows:
+        s_ref = ref[2][:, h, i]
+        assert (s_ref > 0).all() and (s_ref < 2.0 ** -126).all()
+        # the codes span the range as the rule makes them (absmax code 127), not 0
+        assert (np.abs(got[1][:, h, i].astype(int)).max(axis=-1) == 127).all()
+    for h, i in deep_rows:
+        rg = got[1][:, h, i].astype(np.float64) * got[2][:, h, i, None].astype(np.float64)
+        rr = ref[1][:, h, i].astype(np.float64) * ref[2][:, h, i, None].astype(np.float64)
+        assert (np.abs(rg - rr) < 2.0 ** -142).all()
+        assert (np.abs(got[1][:, h, i].astype(int)).max(axis=-1) >= 120).all()
 
 
 @pytest.mark.parametrize("case", ["identity", "full_forget", "zero_rows", "tiny", "large", "zero_v_beta1"])

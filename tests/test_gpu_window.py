@@ -194,3 +194,27 @@ def test_window_full_heads_gdn64_shape():
     torch.cuda.synchronize()
     _log(str(check_quant(mask, pool.logical(), (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D),
                                                 win.s.reshape(B, H, D)))))
+
+
+def test_one_buffer_takes_a_scalar_gate_window_then_a_per_key_one():
+    """A GDN window (scalar gate), a flush, then a KDA window (a gate per key row) and a flush on
+    the same buffers: the flag that tells a flush which form the buffer holds is set by each
+    window's own tokens and cleared when a window ends, so the second flush takes the per-row
+    form. Each flush against the oracle."""
+    B, H, D, r, W = 5, 3, 128, 24, 4
+    rng, rows, mask, maskn, h, c, s = _setup(404, B, H, D, r, synth.GDN)
+    win = oracle.Window(maskn, h.copy(), c.copy(), s.copy(), W)
+    pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), np.arange(B), B)
+    wbuf = pool.state.window_buffer(W)
+    for decay in (synth.GDN, synth.KDA):
+        print(f"window of two tokens, decay {decay}, then a flush", flush=True)
+        for _ in range(2):
+            inp = synth.step_inputs(rng, B, H, D, decay, "bf16")
+            out = _gpu_step(pool, wbuf, W, pool.slot_dev, inp)
+            check_readout(out, win.step(*ref_vectors(inp, B, H, D)).reshape(B, H, D))
+        pool.state.window_flush(wbuf, W, pool.slot_dev)
+        win.flush()
+        torch.cuda.synchronize()
+        got = pool.logical()
+        check_quant(mask, got, (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D), win.s.reshape(B, H, D)))
+        _resync(win, got)

@@ -165,11 +165,17 @@ def test_pool4096_full_size():
 
 
 # ------------------------------------------------------------------------------------------
-DRIFT_SAMPLE_SLOTS = (0, 41)        # oracle free-runs these slots' 32 heads
-DRIFT_CHECK_STEPS = (0, 700, 2047)  # identical-input parity at these steps
+DRIFT_SAMPLE_SLOTS = (0, 41)        # oracle free-runs these slots' 32 heads (fp32 deviation)
+DRIFT_CHECK_SLOTS = (0, 9, 17, 26, 33, 41, 50, 63)   # identical-input parity on these slots ...
+DRIFT_CHECK_STEPS = (0, 700, 2047)                  # ... at these steps, in all three formats
 
 
 def test_drift_2048_steps(gdn64_warm):
+    """The drift workload: 2,048 steps in all three formats from gdn64's warmed state, the
+    readout error of the quantized formats against the fp32 run per step, and identical-input
+    parity along the way: at the check steps each format's GPU state of the check slots (8 slots
+    x 32 heads) is handed to the oracle, which takes the same step; readouts, DAMP and uniform-INT8
+    states (tolerances of gpu_common) and the fp32 state (its error bound) are compared."""
     S_warm, _, rows = gdn64_warm
     w = synth.DRIFT
     B, H, D, T = w.batch, w.heads, w.d, w.steps
@@ -179,41 +185,28 @@ def test_drift_2048_steps(gdn64_warm):
     # GPU states, all 64 slots
     h, c, s = oracle.quantize(maskn, S_warm)
     damp = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), np.arange(B), B)
-    hi, ci, si = oracle.quantize(z, S_warm)
+    _, ci, si = oracle.quantize(z, S_warm)
     codes = to_dev(ci.reshape(B, H, D, D))
     scales = to_dev(si.reshape(B, H, D))
     pool32 = to_dev(S_warm.reshape(B, H, D, D))
     slot_dev = to_dev(np.arange(B, dtype=np.int32))
-    # oracle states for the sampled units
+    # the oracle's free-running fp32 units
     sel = np.concatenate([np.arange(sl * H, (sl + 1) * H) for sl in DRIFT_SAMPLE_SLOTS])
-    n = len(sel)
     o_S = S_warm[sel].copy()
-    o_q = [x[sel].copy() for x in (h, c, s)]
-    o_i = [x[sel].copy() for x in (hi, ci, si)]
-    msel = maskn[sel]
-    zsel = z[sel]
+    chk = list(DRIFT_CHECK_SLOTS)
+    csel = np.concatenate([np.arange(sl * H, (sl + 1) * H) for sl in chk])
+    nc = len(chk)
     outs = {f: torch.empty((B, H, D), dtype=torch.float32, device="cuda") for f in ("f32", "q", "i8")}
     err_q, err_i, dev32, unit_q, unit_i = [], [], [], [], []
     for t in range(T):
         inp = synth.drift_step(t)
         vecs = ref_vectors(inp, B, H, D)
-        vs = tuple(x[sel] for x in vecs)
-        if t in DRIFT_CHECK_STEPS:   # identical-input parity from the oracle's states
-            _log(f"drift step {t}: identical-input check")
-            sl = np.arange(len(DRIFT_SAMPLE_SLOTS))
-            sub = synth.StepInputs(*(x[list(DRIFT_SAMPLE_SLOTS)] for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta)),
-                                   inp.dtype, *(x[list(DRIFT_SAMPLE_SLOTS)] for x in (inp.q_bits, inp.k_bits, inp.v_bits)))
-            ns = len(DRIFT_SAMPLE_SLOTS)
-            p = DampPool(rows, *(x.reshape(ns, H, D, D) for x in o_q[:2]), o_q[2].reshape(ns, H, D), sl, ns)
-            go = p.step(sub)
-            gq = p.logical()
-        # advance the oracle's sampled units
-        r32 = oracle.step_fp32(o_S, *vs)
-        rq = oracle.step_quant(msel, *o_q, *vs)
-        oracle.step_quant(zsel, *o_i, *vs)
-        if t in DRIFT_CHECK_STEPS:
-            check_readout(go, rq)
-            check_quant(mask, gq, tuple(x.reshape(len(DRIFT_SAMPLE_SLOTS), H, *x.shape[1:]) for x in o_q))
+        check = t in DRIFT_CHECK_STEPS
+        if check:   # the GPU's states of the check slots before this step
+            _log(f"drift step {t}: identical-input check, three formats, {nc} slots")
+            gq0 = [x[chk].reshape(nc * H, *x.shape[2:]).copy() for x in damp.logical()]
+            gi0 = (codes[chk].cpu().numpy().reshape(nc * H, D, D), scales[chk].cpu().numpy().reshape(nc * H, D))
+            g320 = pool32[chk].cpu().numpy().reshape(nc * H, D, D)
         # the GPU runs all units in all three formats
         q, k, v, a, b = step_tensors(inp)
         lib.fp32_decode_step(pool32, slot_dev, q, k, v, a, b, outs["f32"])
@@ -222,6 +215,27 @@ def test_drift_2048_steps(gdn64_warm):
         o32 = outs["f32"].cpu().numpy().reshape(B * H, D)
         oq = outs["q"].cpu().numpy().reshape(B * H, D)
         oi = outs["i8"].cpu().numpy().reshape(B * H, D)
+        if check:
+            vc = tuple(x[csel] for x in vecs)
+            hq, cq, sq = (x.copy() for x in gq0)
+            ref_q = oracle.step_quant(maskn[csel], hq, cq, sq, *vc)
+            check_readout(oq[csel], ref_q)
+            got_q = [x[chk] for x in damp.logical()]
+            check_quant(mask, got_q, (hq.reshape(nc, H, D, D), cq.reshape(nc, H, D, D), sq.reshape(nc, H, D)))
+            hz = np.zeros((nc * H, D, D), np.uint16)
+            ci0, si0 = (x.copy() for x in gi0)
+            ref_i = oracle.step_quant(z[csel], hz, ci0, si0, *vc)
+            check_readout(oi[csel], ref_i)
+            hz = hz.reshape(nc, H, D, D)
+            got_i = (hz, codes[chk].cpu().numpy(), scales[chk].cpu().numpy())
+            check_quant(np.zeros((H, D), np.uint8), got_i, (hz, ci0.reshape(nc, H, D, D), si0.reshape(nc, H, D)))
+            S32 = g320.copy()
+            ref_32 = oracle.step_fp32(S32, *vc)
+            check_readout(o32[csel], ref_32)
+            check_fp32_state(pool32[chk].cpu().numpy().reshape(nc * H, D, D), S32,
+                             fp32_state_bound(g320, vc[3], vc[1], vc[2], vc[4], S32))
+        # advance the oracle's free-running fp32 units
+        r32 = oracle.step_fp32(o_S, *(x[sel] for x in vecs))
         assert np.isfinite(oq).all() and np.isfinite(oi).all() and np.isfinite(o32).all()
         nrm = np.linalg.norm(o32)
         err_q.append(np.linalg.norm(oq - o32) / nrm)

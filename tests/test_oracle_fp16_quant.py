@@ -103,6 +103,28 @@ def test_int8_matches_exact_rational_rule():
         assert c.tolist() == ce
 
 
+def test_int8_rule_with_subnormal_scales_matches_exact_rationals():
+    """Rows whose absmax is below 127 * 2^-126, so that the scale is a binary32 subnormal (down
+    to rows of subnormal values themselves): the rule is the same, decided on the subnormal
+    scale, and the largest entry still codes at +-127."""
+    rng = np.random.default_rng(13)
+    for amax in (127 * 2.0 ** -126, 1e-36, 1e-37, 2e-39, 3e-41, 2.0 ** -140, 2.0 ** -142):
+        for _ in range(20):
+            x = rng.standard_normal(16)
+            x = (x / np.abs(x).max() * amax).astype(np.float32)
+            c, s = oracle.quant_row(x)
+            ce, se = exact_ref.quant_row_exact([Fraction(float(v)) for v in x])
+            assert float(s) == float(se) and c.tolist() == ce
+            assert 0 < s < 2.0 ** -126 or amax == 127 * 2.0 ** -126
+            assert np.abs(c).max() == 127
+    # absmax below 127 * 2^-150: m / 127 rounds to zero, so scale 0 and codes 0
+    x = np.zeros(16, np.float32)
+    x[[2, 5]] = np.float32(2.0 ** -149) * np.array([3, -60], np.float32)
+    c, s = oracle.quant_row(x)
+    assert s == 0 and not c.any()
+    assert exact_ref.quant_row_exact([Fraction(float(v)) for v in x]) == ([0] * 16, 0)
+
+
 def test_requantize_is_idempotent():
     rng = np.random.default_rng(13)
     X = (rng.standard_normal((20000, 128)) * rng.lognormal(0, 1, (20000, 1))).astype(np.float32)
