@@ -414,12 +414,13 @@ damp_status damp_allocate_rows(const double* score, int32_t num_heads, int32_t d
  *   cs_j = fp16( sqrt( sum_{i in N} w_i^2 X_ij^2 / sum_{i in N} w_i^2 ) )
  *   rf_i = fp16( max_{j: cs_j > 0} (|X_ij| / cs_j) / qmax_i ),   qmax = 2^(b - 1) - 1
  *   code = clamp(rint(X_ij / (rf_i cs_j)), -qmax, qmax), 0 where rf_i cs_j = 0
- * with w_i the frozen row-impact score (all w_i = 0 in a head means equal weights), binary32
- * divisions and binary16 round-to-nearest-even. The page names this fit (key-row-aware
- * dual-axis fitting, one shared column-scale vector fitted with squared row-impact factors) but
- * prints no formula: the formulas are the library's reading. The device sums the column sums
- * of squares in fp32 (a column scale can land one binary16 step from the binary64 fit where the
- * sum sits at a rounding tie). stq_state_quantize takes every other decision as written; inside
+ * with w_i the frozen row-impact score (all w_i = 0 in a head means equal weights), the column
+ * scales' sums, division and square root in binary64 rounded once to binary16, the other
+ * divisions in binary32, binary16 round-to-nearest-even. The page names this fit (a dual-axis fit
+ * aware of key rows, one column-scale vector per head weighted by squared row-impact scores) but
+ * prints no formula: the formulas are the library's reading. stq_state_quantize takes every
+ * decision as written (its sums add in another order than a sequential loop, which can only
+ * matter within ~1e-15 of a binary16 tie); inside
  * stq_decode_step the row maximum and the codes use products with rounded reciprocals, so a
  * code can differ by one where its quotient lies within a few ulps of a half-integer.
  * Block of (slot, head): storage rows ordered pivots, 8-bit, 6-bit, 4-bit (each by ascending key

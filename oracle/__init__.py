@@ -75,8 +75,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_stq_quantize.restype = I
         L.oracle_stq_dequantize.argtypes = [I, Lg, P, P, P, P, P, P]
         L.oracle_stq_dequantize.restype = I
-        L.oracle_stq_step.argtypes = [I, Lg, P, P, P, P, P, P, P, P, P, P, P, P, P, P, I, P, P, I]
+        L.oracle_stq_step.argtypes = [I, Lg, P, P, P, P, P, P, P, P, P, P, P, P, P, P, I, P, P, P, I]
         L.oracle_stq_step.restype = I
+        L.oracle_stq_fit_rows.argtypes = [I, Lg, P, P, P, P, P, P]
+        L.oracle_stq_fit_rows.restype = I
         _lib = L
     return _lib
 
@@ -310,8 +312,10 @@ def stq_dequantize(bits, h, c, rf, cs):
     return S
 
 
-def stq_step(bits, w, h, c, rf, cs, q, k, v, alpha, beta, nthreads: int | None = None):
-    """One step; returns ``(out [n, D], (h2, c2, rf2, cs2))`` (the inputs are not modified)."""
+def stq_step(bits, w, h, c, rf, cs, q, k, v, alpha, beta, nthreads: int | None = None,
+             return_x: bool = False):
+    """One step; returns ``(out [n, D], (h2, c2, rf2, cs2))`` (the inputs are not modified), and
+    with ``return_x`` also the new states X rounded to binary32 [n, D, D]."""
     h, c = _c(h, np.uint16), _c(c, np.int8)
     rf, cs = _c(rf, np.uint16), _c(cs, np.uint16)
     n, D, _ = c.shape
@@ -320,8 +324,24 @@ def stq_step(bits, w, h, c, rf, cs, q, k, v, alpha, beta, nthreads: int | None =
     q, k, v, alpha, per_key, beta = _vecs(q, k, v, alpha, beta, n, D)
     h2, c2, rf2, cs2 = np.empty_like(h), np.empty_like(c), np.empty_like(rf), np.empty_like(cs)
     out = np.empty((n, D), np.float32)
+    X = np.empty((n, D, D), np.float32) if return_x else None
     rc = lib().oracle_stq_step(D, n, _p(bits), _p(w), _p(h), _p(c), _p(rf), _p(cs), _p(h2), _p(c2),
                                _p(rf2), _p(cs2), _p(q), _p(k), _p(v), _p(alpha), per_key, _p(beta),
-                               _p(out), nthreads or default_threads())
+                               _p(out), _p(X), nthreads or default_threads())
     assert rc == 0
-    return out, (h2, c2, rf2, cs2)
+    return (out, (h2, c2, rf2, cs2), X) if return_x else (out, (h2, c2, rf2, cs2))
+
+
+def stq_fit_rows(bits, X, cs):
+    """The fit's second half for given column scales: ``(h, c, rf)`` of states ``X[n, D, D]``
+    with column scales ``cs[n, D]`` (binary16 bits)."""
+    X = _c(X, np.float32)
+    n, D, _ = X.shape
+    bits = _c(np.broadcast_to(bits, (n, D)), np.uint8)
+    cs = _c(np.broadcast_to(cs, (n, D)), np.uint16)
+    h = np.empty((n, D, D), np.uint16)
+    c = np.empty((n, D, D), np.int8)
+    rf = np.empty((n, D), np.uint16)
+    rc = lib().oracle_stq_fit_rows(D, n, _p(bits), _p(X), _p(cs), _p(h), _p(c), _p(rf))
+    assert rc == 0
+    return h, c, rf

@@ -567,8 +567,9 @@ int oracle_window_flush(int D, long n_units, const uint8_t* mask, uint16_t* h, i
  * ---------------------------------------------------------------------------------------- */
 static int stq_qmax(int b) { return (1 << (b - 1)) - 1; }
 
-static void stq_store_unit(int D, const uint8_t* bits, const float* w, const float* X,
-                           uint16_t* h, int8_t* c, uint16_t* rf, uint16_t* cs) {
+/* The fit's first half: the column scales of one unit from its binary32 state X. */
+static void stq_fit_columns(int D, const uint8_t* bits, const float* w, const float* X,
+                            uint16_t* cs) {
   double sw = 0.0;
   for (int i = 0; i < D; ++i)
     if (bits[i] != 16) sw += (double)w[i] * (double)w[i];
@@ -587,6 +588,11 @@ static void stq_store_unit(int D, const uint8_t* bits, const float* w, const flo
     }
     cs[j] = sw > 0.0 ? f16_from_double(sqrt(acc / sw)) : 0; /* one rounding to binary16 */
   }
+}
+
+/* The fit's second half, given the column scales: pivot values, row factors and codes. */
+static void stq_fit_rows(int D, const uint8_t* bits, const float* X, const uint16_t* cs,
+                         uint16_t* h, int8_t* c, uint16_t* rf) {
   for (int i = 0; i < D; ++i) {
     const float* x = X + (long)i * D;
     if (bits[i] == 16) {
@@ -620,6 +626,12 @@ static void stq_store_unit(int D, const uint8_t* bits, const float* w, const flo
       c[(long)i * D + j] = (int8_t)code;
     }
   }
+}
+
+static void stq_store_unit(int D, const uint8_t* bits, const float* w, const float* X,
+                           uint16_t* h, int8_t* c, uint16_t* rf, uint16_t* cs) {
+  stq_fit_columns(D, bits, w, X, cs);
+  stq_fit_rows(D, bits, X, cs, h, c, rf);
 }
 
 static double stq_recon(int D, const uint8_t* bits, const uint16_t* h, const int8_t* c,
@@ -667,7 +679,7 @@ int oracle_stq_step(int D, long n, const uint8_t* bits, const float* w, const ui
                     const int8_t* c, const uint16_t* rf, const uint16_t* cs, uint16_t* h2,
                     int8_t* c2, uint16_t* rf2, uint16_t* cs2, const float* q, const float* k,
                     const float* v, const float* alpha, int per_key, const float* beta,
-                    float* out, int nthreads) {
+                    float* out, float* x_out, int nthreads) {
   if (D <= 0 || n < 0 || !bits || !w || !h || !c || !rf || !cs || !h2 || !c2 || !rf2 || !cs2 ||
       !q || !k || !v || !alpha || !beta || !out)
     return -1;
@@ -712,10 +724,24 @@ int oracle_stq_step(int D, long n, const uint8_t* bits, const float* w, const ui
         out[un * D + j] = (float)acc;
       }
       for (long e = 0; e < DD; ++e) Xf[e] = (float)X[e];
+      if (x_out) memcpy(x_out + un * DD, Xf, sizeof(float) * (size_t)DD);
       stq_store_unit(D, bt, w + un * D, Xf, h2 + un * DD, c2 + un * DD, rf2 + un * D, cs2 + un * D);
     }
     free(X);
     free(Xf);
   }
   return bad ? -1 : 0;
+}
+
+/* The second half of the fit for given column scales cs [n][D] (binary16 bits): pivot values,
+ * row factors and codes of n units from their binary32 states X [n][D][D]. */
+int oracle_stq_fit_rows(int D, long n, const uint8_t* bits, const float* X, const uint16_t* cs,
+                        uint16_t* h, int8_t* c, uint16_t* rf) {
+  if (D <= 0 || n < 0 || !bits || !X || !cs || !h || !c || !rf) return -1;
+  const long DD = (long)D * D;
+  for (long u = 0; u < n; ++u) {
+    if (!stq_bits_ok(D, bits + u * D)) return -1;
+    stq_fit_rows(D, bits + u * D, X + u * DD, cs + u * D, h + u * DD, c + u * DD, rf + u * D);
+  }
+  return 0;
 }

@@ -112,7 +112,10 @@ int oracle_window_flush(int D, long n_units, const uint8_t* mask, uint16_t* h, i
  * with squared row-impact weights (the fit is written out in oracle.c).
  *   bits [n][D] (16 = pivot, 8, 6, 4), w [n][D] row-impact scores, h [n][D][D] binary16 pivot
  *   values, c [n][D][D] codes, rf [n][D] and cs [n][D] binary16 bits.
- * oracle_stq_step writes the new state to (h2, c2, rf2, cs2), which may alias the inputs. */
+ * oracle_stq_step writes the new state to (h2, c2, rf2, cs2), which may alias the inputs, and,
+ * when x_out is not NULL, the units' new states X rounded to binary32 [n][D][D].
+ * oracle_stq_fit_rows takes the second half of the fit alone: for given column scales cs [n][D]
+ * it writes the pivot values, row factors and codes of the states X [n][D][D]. */
 int oracle_stq_quantize(int D, long n, const uint8_t* bits, const float* w, const float* S,
                         uint16_t* h, int8_t* c, uint16_t* rf, uint16_t* cs);
 int oracle_stq_dequantize(int D, long n, const uint8_t* bits, const uint16_t* h,
@@ -121,7 +124,9 @@ int oracle_stq_step(int D, long n, const uint8_t* bits, const float* w, const ui
                     const int8_t* c, const uint16_t* rf, const uint16_t* cs, uint16_t* h2,
                     int8_t* c2, uint16_t* rf2, uint16_t* cs2, const float* q, const float* k,
                     const float* v, const float* alpha, int per_key, const float* beta,
-                    float* out, int nthreads);
+                    float* out, float* x_out, int nthreads);
+int oracle_stq_fit_rows(int D, long n, const uint8_t* bits, const float* X, const uint16_t* cs,
+                        uint16_t* h, int8_t* c, uint16_t* rf);
 
 #ifdef __cplusplus
 }

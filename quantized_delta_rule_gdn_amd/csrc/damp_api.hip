@@ -258,7 +258,7 @@ damp::StqArgs stq_args(const stq_state* s) {
   a.pool = s->pool;
   a.slot_stride = static_cast<int64_t>(s->slot_bytes);
   a.rowmap = s->table_dev;
-  a.w2 = reinterpret_cast<const float*>(s->table_dev + H * d);
+  a.w1 = reinterpret_cast<const float*>(s->table_dev + H * d);
   a.heads = reinterpret_cast<const int4*>(s->table_dev + H * d + 4 * H * d);
   a.H = s->num_heads;
   a.step.st.rowmap = s->table_dev;
@@ -899,9 +899,9 @@ damp_status stq_state_alloc(int32_t num_slots, int32_t H, int32_t d, const uint8
   if (need == 0) return fail(DAMP_ERR_INVALID_ARGUMENT, "pool size overflows size_t");
   if (pool_bytes < need) return fail(DAMP_ERR_INVALID_ARGUMENT, "pool_bytes %zu < %zu needed", pool_bytes, need);
   const size_t Hs = static_cast<size_t>(H), ds = static_cast<size_t>(d);
-  // device table: rowmap (storage order: pivots, 8-bit, 6-bit, 4-bit, each ascending) | w2 | heads
+  // device table: rowmap (storage order: pivots, 8-bit, 6-bit, 4-bit, each ascending) | w1 | heads
   std::vector<uint8_t> blob(Hs * ds + 4 * Hs * ds + 16 * Hs, 0);
-  float* w2 = reinterpret_cast<float*>(blob.data() + Hs * ds);
+  float* w1 = reinterpret_cast<float*>(blob.data() + Hs * ds);
   int32_t* heads = reinterpret_cast<int32_t*>(blob.data() + Hs * ds + 4 * Hs * ds);
   stq_state* s = new (std::nothrow) stq_state{};
   if (!s) return fail(DAMP_ERR_OUT_OF_MEMORY, "host allocation of the handle failed");
@@ -919,22 +919,19 @@ damp_status stq_state_alloc(int32_t num_slots, int32_t H, int32_t d, const uint8
     for (int32_t i = 0; i < d; ++i)
       if (bits[i] != 16) sw += static_cast<double>(w[i]) * w[i];
     const bool unweighted = !(sw > 0.0);
+    if (unweighted) sw = static_cast<double>(d - cnt[4 * h]);   // every integer row weighs 1
     int p = 0;
-    double swf = 0.0;
     for (int k = 0; k < 4; ++k)
       for (int32_t i = 0; i < d; ++i) {
         if (bits[i] != kWidths[k]) continue;
         blob[static_cast<size_t>(h) * d + p] = static_cast<uint8_t>(i);
-        const float wi = k == 0 ? 0.0f : (unweighted ? 1.0f : w[i]);
-        w2[static_cast<size_t>(h) * d + p] = wi * wi;
-        swf += static_cast<double>(wi) * wi;
+        w1[static_cast<size_t>(h) * d + p] = k == 0 ? 0.0f : (unweighted ? 1.0f : w[i]);
         ++p;
       }
     s->head_off[static_cast<size_t>(h)] = static_cast<int64_t>(off);
     heads[4 * h] = static_cast<int32_t>(off);
     heads[4 * h + 1] = cnt[4 * h] | (cnt[4 * h + 1] << 8) | (cnt[4 * h + 2] << 16) | (cnt[4 * h + 3] << 24);
-    const float swv = static_cast<float>(swf);
-    std::memcpy(&heads[4 * h + 2], &swv, 4);
+    std::memcpy(&heads[4 * h + 2], &sw, 8);   // the binary64 sum of w_i^2 over the integer rows
     off += round_up(stq_block_bytes(d, cnt[4 * h], cnt[4 * h + 1], cnt[4 * h + 2], cnt[4 * h + 3]), kBlockAlign);
   }
   s->slot_bytes = off;

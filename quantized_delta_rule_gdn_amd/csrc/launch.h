@@ -81,16 +81,17 @@ hipError_t launch_batch_order(const int32_t* slot_idx, int32_t B, int32_t num_sl
                               hipStream_t s);
 
 // STEPQuant-style state (stq_kernels.hip). The block of (slot, head) is at pool + slot *
-// slot_stride + heads[head].x; heads[head] = {offset, n16 | n8 << 8 | n6 << 16 | n4 << 24,
-// bits of the fp32 sum of w2 over the head's integer rows, 0}; rowmap [H][d] storage row ->
-// key row; w2 [H][d] squared row-impact weights in storage order (0 on pivot rows).
+// slot_stride + heads[head].x; heads[head] = {offset, n16 | n8 << 8 | n6 << 16 | n4 << 24, and
+// in .z/.w the bits of the binary64 sum of w_i^2 over the head's integer rows}; rowmap [H][d]
+// storage row -> key row; w1 [H][d] row-impact weights in storage order (0 on pivot rows; 1 on
+// every integer row of a head whose weights are all 0).
 struct StqArgs {
   StepArgs step;            // q, k, v, alpha, beta, out and st.rowmap for the step's staging
   uint8_t* pool;            // source state
   uint8_t* dst;             // destination state (nullptr = in place)
   int64_t slot_stride;
   const int4* heads;
-  const float* w2;
+  const float* w1;
   const uint8_t* rowmap;
   const int32_t* slot_idx;
   int32_t B;                // units = B * H

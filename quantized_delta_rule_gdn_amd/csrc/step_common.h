@@ -147,6 +147,16 @@ __device__ __forceinline__ float max_row16(float x) {
   return x;
 }
 
+// Sum over the 16 lanes of a row, by the same DPP pattern as max_row16 (every lane of the row
+// ends with the same sum; the addition order is fixed).
+__device__ __forceinline__ float sum_row16(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
+  return x;
+}
+
 // ---- the INT8 row rule --------------------------------------------------------------------
 // scale = fl(m / 127). q = fl(m * fl(1/127)) followed by one residual correction gives the
 // correctly rounded quotient: checked against IEEE division for every binary32 significand at

@@ -31,9 +31,13 @@
 // (the sign bit moved to bit 7), so every integer row converts with one signed-byte instruction
 // per value; the staged row multiplier carries the exact power-of-two inverse.
 //
-// Arithmetic of the fit. Column scales: fp32 partial sums per lane, added per column in a fixed
-// order, one IEEE division and square root per column; the column thread also forms
-// rcs_j = RN(1 / cs_j). Row factor: the row maximum m of |X_ij| rcs_j (pack: the quotient
+// Arithmetic of the fit. Column scales: binary64, as the fit's reading states it. Each lane
+// forms (w_i X_ij)^2 with w_i X_ij exact in binary64 and adds its rows' terms in order; the
+// column thread adds the lanes' partials in a fixed order, divides by the binary64 sum of w_i^2
+// and takes the square root (IEEE binary64 division and square root), rounded once to binary16
+// (through a round-to-odd binary32 value). Only the order of the sums differs from the oracle's,
+// so from the same X the scales agree unless a square root lies within ~1e-15 of a binary16 tie.
+// The column thread also forms rcs_j = RN(1 / cs_j). Row factor: the row maximum m of |X_ij| rcs_j (pack: the quotient
 // corrected to the IEEE one by one residual step, exact because cs_j has an 11-bit significand),
 // divided by qmax with one multiply and one residual correction (correctly rounded for 7, 31 and
 // 127 at every binary32 significand). Codes: pack takes the IEEE quotient X / (rf cs) for each
@@ -56,12 +60,12 @@ enum StqMode : int { SM_STEP = 0, SM_PACK = 1, SM_UNPACK = 2 };
 struct StqBlock {
   uint32_t o8, o6, o4, orf, ocs, bytes;
   int n16, n8, n6, n4;
-  float sw;
+  double sw;   // the binary64 sum of w_i^2 over the integer rows
 };
 
 template <int D>
 __device__ __forceinline__ StqBlock stq_block(const StqArgs& a, int head) {
-  const int4 hi = a.heads[head];   // {offset, counts n16 | n8 << 8 | n6 << 16 | n4 << 24, sw, 0}
+  const int4 hi = a.heads[head];   // {offset, counts n16 | n8 << 8 | n6 << 16 | n4 << 24, sw (2 words)}
   StqBlock b;
   b.n16 = hi.y & 0xff;
   b.n8 = (hi.y >> 8) & 0xff;
@@ -73,7 +77,7 @@ __device__ __forceinline__ StqBlock stq_block(const StqArgs& a, int head) {
   b.orf = b.o4 + (D / 2) * b.n4;
   b.ocs = b.orf + 2 * (D - b.n16);
   b.bytes = b.ocs + 2 * D;
-  b.sw = __int_as_float(hi.z);
+  b.sw = __hiloint2double(hi.w, hi.z);
   return b;
 }
 
@@ -235,6 +239,21 @@ __device__ __forceinline__ void stq_store(rsrc_t rs, const StqBlock& b, int p, i
   }
 }
 
+// binary64 -> binary16, one rounding (to nearest, ties to even): round to odd into binary32
+// first (keep the truncation, set the last bit when inexact), then v_cvt_f16_f32. Binary32 has
+// more than two bits beyond binary16's significand over binary16's whole range, so the odd
+// intermediate never creates or hides a tie.
+__device__ __forceinline__ uint32_t f16_from_f64(double d) {
+  float f = static_cast<float>(d);   // to nearest
+  const double back = static_cast<double>(f);
+  if (back != d) {
+    uint32_t u = __float_as_uint(f);
+    if (fabs(back) > fabs(d)) u -= 1u;   // rounded away from zero: one step back toward zero
+    f = __uint_as_float(u | 1u);
+  }
+  return float_to_half_bits(f);
+}
+
 // m / qmax correctly rounded: one multiply by RN(1 / qmax) and one residual correction (checked
 // against IEEE division for every binary32 significand at exponents 2^-120 .. 2^127 for qmax in
 // {7, 31, 127}).
@@ -247,9 +266,12 @@ __device__ __forceinline__ float div_qmax(float m, float qm, float inv) {
 template <int D, int NW>
 struct StqSmem {
   float4 srow[D];            // {gate_p, k_p, q_p, rf_p (1 for pivots)}, storage order
-  float sw2[D];              // w_p^2 (0 for pivots), storage order
+  float sw1[D];              // w_p (0 for pivots), storage order
   float sv[D];               // v, then delta
-  float red[2][4 * NW][D];   // partial sums: u and p; then the column-scale sums in red[0]
+  union {
+    float red[2][4 * NW][D];   // partial sums: u and p
+    double red64[4 * NW][D];   // then the column-scale sums (binary64)
+  };
   float redqk[NW];
   float scs[D];              // column scales (binary16 values as fp32)
   float srcs[D];             // RN(1 / cs_j), 0 where cs_j = 0
@@ -259,12 +281,12 @@ struct StqSmem {
 // the state is decoded in between: stq_stage_load issues the loads (k, q, the gate, v, the row
 // map, the fit's row weights and the stored row factors, one element per thread),
 // stq_stage_store writes them to LDS in storage order (srow = {gate_p, k_p, q_p, rf_p / scale_p}
-// with rf = 1 for pivots and scale_p the row kind's decode scale, sv = v, sw2) and returns beta.
+// with rf = 1 for pivots and scale_p the row kind's decode scale, sv = v, sw1) and returns beta.
 template <int D, int NT>
 struct StqStage {
   static constexpr int PER = (D + NT - 1) / NT;
   int src[PER];
-  float kv[PER], qv[PER], gv[PER], vv[PER], w2[PER];
+  float kv[PER], qv[PER], gv[PER], vv[PER], w1[PER];
   uint32_t rf[PER];
   float g0, beta;
 };
@@ -283,7 +305,7 @@ __device__ __forceinline__ StqStage<D, NT> stq_stage_load(const StqArgs& a, rsrc
       st.qv[n] = load_in<BF16>(a.step.q, vec + i);
       st.gv[n] = PER_KEY ? a.step.alpha[vec + i] : 0.0f;
       st.vv[n] = load_in<BF16>(a.step.v, vec + i);
-      st.w2[n] = a.w2[head * D + i];
+      st.w1[n] = a.w1[head * D + i];
       const int ri = i - blk.n16;
       st.rf[n] = 0x3C00u;   // 1.0 for pivots
       if (ri >= 0) buf_load<2>(blk_rs, blk.orf + 2u * static_cast<uint32_t>(ri), 0u, &st.rf[n]);
@@ -297,7 +319,7 @@ __device__ __forceinline__ StqStage<D, NT> stq_stage_load(const StqArgs& a, rsrc
 template <int D, int NT, int PER_KEY>
 __device__ __forceinline__ float stq_stage_store(const StqStage<D, NT>& st, const StqBlock& blk, int tid,
                                                  float4* srow, float* sv,
-                                                 float* sw2, float* tmp) {
+                                                 float* sw1, float* tmp) {
 #pragma unroll
   for (int n = 0; n < StqStage<D, NT>::PER; ++n) {
     const int i = tid + n * NT;
@@ -306,7 +328,7 @@ __device__ __forceinline__ float stq_stage_store(const StqStage<D, NT>& st, cons
       tmp[D + i] = st.qv[n];
       if constexpr (PER_KEY) tmp[2 * D + i] = st.gv[n];
       sv[i] = st.vv[n];
-      sw2[i] = st.w2[n];
+      sw1[i] = st.w1[n];
     }
   }
   __syncthreads();
@@ -357,7 +379,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
       load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(a.S + (int64_t(bh) * D + rowmap[p]) * D + cg * CPL),
                           reinterpret_cast<uint32_t*>(X[t]));
     }
-    for (int i = tid; i < D; i += NT) sm.sw2[i] = a.w2[head * D + i];
+    for (int i = tid; i < D; i += NT) sm.sw1[i] = a.w1[head * D + i];
     __syncthreads();
   } else {
     // (1) the stored state: the lane's words of each row, its row factor, its column scales
@@ -417,7 +439,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
           }
         });
       }
-      const float beta = stq_stage_store<D, NT, PER_KEY>(stage, blk, tid, sm.srow, sm.sv, sm.sw2, &sm.red[0][0][0]);
+      const float beta = stq_stage_store<D, NT, PER_KEY>(stage, blk, tid, sm.srow, sm.sv, sm.sw1, &sm.red[0][0][0]);
       // (3) S' = diag(gate) S_hat (row multiplier gate_p * rf_p), and the partial column sums of
       // u = S'^T k and p = S'^T q
       float pu[CPL], pp[CPL], pqk = 0.0f;
@@ -449,26 +471,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
     }
   }
 
-  // (5) the fit: column scales from the weighted column sums of squares
+  // (5) the fit: column scales from the weighted column sums of squares, in binary64: each
+  // product (w_i X_ij)^2 rounded once, the lane's rows added in order, then the lanes' partials
   {
-    float acc[CPL];
+    double acc[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.0;
 #pragma unroll
     for (int t = 0; t < RPL; ++t) {
-      const float w2 = sm.sw2[t * RPS + w * 4 + rs];
+      const double w1 = sm.sw1[t * RPS + w * 4 + rs];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w2 * X[t][c], X[t][c], acc[c]);
+      for (int c = 0; c < CPL; ++c) {
+        const double y = w1 * static_cast<double>(X[t][c]);   // exact: two 24-bit significands
+        acc[c] = fma(y, y, acc[c]);
+      }
     }
-    store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(&sm.red[0][w * 4 + rs][cg * CPL]),
+    store_bytes<CPL * 8>(reinterpret_cast<uint8_t*>(&sm.red64[w * 4 + rs][cg * CPL]),
                          reinterpret_cast<const uint32_t*>(acc));
   }
   __syncthreads();
   for (int j = tid; j < D; j += NT) {
-    float s = sm.red[0][0][j];
+    double s = sm.red64[0][j];
 #pragma unroll
-    for (int k = 1; k < 4 * NW; ++k) s += sm.red[0][k][j];
-    const uint32_t hb = blk.sw > 0.0f ? float_to_half_bits(sqrtf(__fdiv_rn(s, blk.sw))) : 0u;
+    for (int k = 1; k < 4 * NW; ++k) s += sm.red64[k][j];
+    const uint32_t hb = blk.sw > 0.0 ? f16_from_f64(sqrt(s / blk.sw)) : 0u;
     const float cs = half_bits_to_float(hb);
     sm.scs[j] = cs;
     sm.srcs[j] = cs > 0.0f ? __fdiv_rn(1.0f, cs) : 0.0f;

@@ -34,14 +34,15 @@ constexpr int kMaxWindow = 8;
 
 template <int D, int NW>
 struct WinSmem {
-  static constexpr int RR = 4 * NW > kMaxWindow ? 4 * NW : kMaxWindow;
   float4 srow[D];            // {m_p = scale * a'_p, k_p, q_p, gate_p}
   float sv[D];               // v, then delta
-  float redu[RR][D];         // column partials; at the window's end E[tau][j]
-  float redp[RR][D];         // column partials; at the window's end K'[tau][p]
+  float redu[4 * NW][D];     // column partials
+  float redp[4 * NW][D];
+  float se[kMaxWindow][D];   // the window's deltas E[tau][j] (the token's own last)
+  float sk[kMaxWindow][D];   // the window's keys decayed to this token, K'[tau][p]
   float redqk[NW];
   float ssc[D];
-  float sdot[NW][kMaxWindow][2];   // per wave: K'_tau . k and K'_tau . q
+  float sdot[kMaxWindow][2];  // K'_tau . k and K'_tau . q
 };
 
 struct WinPtr {
@@ -65,50 +66,108 @@ __device__ __forceinline__ bool win_scalar(const WinPtr& wp, int t) {
   return t > 0 && __builtin_amdgcn_readfirstlane(wp.hdr[2]) == 1;
 }
 
-// Staging of a window step (FLUSH_ONLY = false) or of a flush with no token (true). As
-// stage_rows, plus: a'_p = gate_p * a_p (a = 1 when the window is empty), srow.x = scale * a'_p,
-// srow.w = gate_p; every buffered key decayed, K'_tau,p = gate_p K_tau,p, and its dot products
-// with k and q summed per wave into sdot. Unless the window ends here, a' and K' go back to the
-// buffer. Scalar gate (scal): a' = gate a and K'_tau = c'_tau K_tau with c'_tau = gate c_tau,
-// so the dot products are c'_tau (K_tau . k); a', c' and c[t] = 1 go back to the header words.
-// Returns beta.
+// Staging of a window step (FLUSH_ONLY = false) or of a flush with no token (true), in two
+// phases as the step's Stage. load() issues every small global load of the unit into registers,
+// before the caller issues the state loads: the row map and old INT8 scales, k, q, the gate and v
+// of the token, and of the t tokens already in the window their keys K[tau][i], their deltas
+// E[tau][i] (column i) and the decay words (per-row gains a_i, or the scalars c[tau] and a).
+// store() then stages as stage_rows does, plus: a'_p = gate_p * a_p (a = 1 when the window is
+// empty), srow.x = scale * a'_p, srow.w = gate_p; every buffered key decayed, K'_tau,p =
+// gate_p K_tau,p, and its dot products with k and q, all tokens' products first and then their
+// wave sums side by side, summed per wave into sdot. Unless the window ends here, a' and K' go
+// back to the buffer. Scalar gate (scal): a' = gate a and K'_tau = c'_tau K_tau with c'_tau =
+// gate c_tau, so the dot products are c'_tau (K_tau . k); a', c' and c[t] = 1 go back to the
+// header words. The buffered keys and deltas stay in registers for the column pass and for the
+// window's end.
 template <int D, int NT, int PER_KEY, int BF16, bool FLUSH_ONLY>
-__device__ __forceinline__ float stage_rows_win(const StepArgs& a, const WinPtr& wp, int t,
-                                                bool ends, const float* sc_old, int bh, int head,
-                                                int r, int tid, float4* srow, float* sv,
-                                                float* tmp, float (*sdot)[kMaxWindow][2],
-                                                bool scal) {
-  const int64_t vec = int64_t(bh) * D;
-  constexpr int PER = (D + NT - 1) / NT;
-  constexpr int NWS = NT / 64;
-  const bool pre = !FLUSH_ONLY && a.prestep != 0;
-  int src[PER];
-  float sc[PER];
-  float ssq = 0.0f, ssk = 0.0f;
+struct WinStage {
+  static constexpr int PER = (D + NT - 1) / NT;
+  static constexpr int NWS = NT / 64;
+  static constexpr int WM = kMaxWindow;
+  uint32_t src[PER], sc[PER], kv[PER], qv[PER], gv[PER], vv[PER];
+  float A[PER], Kb[WM][PER], Eb[WM][PER], cA[WM];
+  float g0, beta, as;
+
+  __device__ __forceinline__ void load(const StepArgs& a, const WinPtr& wp, int t, bool scal,
+                                       const float* sc_old, int bh, int head, int r, int tid) {
+    const int64_t vec = int64_t(bh) * D;
 #pragma unroll
-  for (int n = 0; n < PER; ++n) {
-    const int i = tid + n * NT;
-    if (i < D) {
-      src[n] = a.st.rowmap ? a.st.rowmap[head * D + i] : i;
-      sc[n] = i >= r ? sc_old[i - r] : 1.0f;
-      if constexpr (!FLUSH_ONLY) {
-        const float kv = load_in<BF16>(a.k, vec + i), qv = load_in<BF16>(a.q, vec + i);
-        tmp[i] = kv;
-        tmp[D + i] = qv;
-        ssk = fmaf(kv, kv, ssk);
-        ssq = fmaf(qv, qv, ssq);
-        if constexpr (PER_KEY) tmp[2 * D + i] = pre ? gate_from_logit(a.alpha[vec + i]) : a.alpha[vec + i];
-        sv[i] = load_in<BF16>(a.v, vec + i);
+    for (int n = 0; n < PER; ++n) {
+      const int i = tid + n * NT;
+      src[n] = static_cast<uint32_t>(i);
+      sc[n] = __float_as_uint(1.0f);
+      kv[n] = qv[n] = gv[n] = vv[n] = 0u;
+      A[n] = 1.0f;
+#pragma unroll
+      for (int tau = 0; tau < WM; ++tau) Kb[tau][n] = Eb[tau][n] = 0.0f;
+      if (PER * NT == D || i < D) {
+        if (a.st.rowmap) src[n] = a.st.rowmap[head * D + i];
+        if (i >= r) sc[n] = reinterpret_cast<const uint32_t*>(sc_old)[i - r];
+        if constexpr (!FLUSH_ONLY) {
+          kv[n] = Stage<D, NT, PER_KEY, BF16, true>::template raw_in<BF16>(a.k, vec + i);
+          qv[n] = Stage<D, NT, PER_KEY, BF16, true>::template raw_in<BF16>(a.q, vec + i);
+          if constexpr (PER_KEY) gv[n] = reinterpret_cast<const uint32_t*>(a.alpha)[vec + i];
+          vv[n] = Stage<D, NT, PER_KEY, BF16, true>::template raw_in<BF16>(a.v, vec + i);
+        }
+        if (!scal && t > 0) A[n] = wp.A[i];
+#pragma unroll
+        for (int tau = 0; tau < WM; ++tau)
+          if (tau < t) {
+            Kb[tau][n] = wp.K[tau * D + i];
+            Eb[tau][n] = wp.E[tau * D + i];
+          }
       }
     }
+    g0 = FLUSH_ONLY ? 1.0f : (PER_KEY ? 0.0f : a.alpha[bh]);
+    beta = FLUSH_ONLY ? 0.0f : a.beta[bh];
+    as = scal && t > 0 ? __int_as_float(wp.hdr[1]) : 1.0f;
+#pragma unroll
+    for (int tau = 0; tau < WM; ++tau) cA[tau] = scal && tau < t ? wp.A[tau] : 1.0f;
   }
-  float g0 = 1.0f, beta = 0.0f;
-  if constexpr (!FLUSH_ONLY) {
-    g0 = PER_KEY ? 0.0f : a.alpha[bh];
-    beta = a.beta[bh];
+
+  __device__ __forceinline__ float store(const StepArgs& a, const WinPtr& wp, int t, bool ends,
+                                         bool scal, int tid, float4* srow, float* sv, float* tmp,
+                                         float (*sdot)[2], float (*se)[D], float (*sk)[D]) {
+    // the loaded registers are used from here on: the caller's state loads are issued above
+#pragma unroll
+    for (int n = 0; n < PER; ++n)
+      asm volatile("" : "+v"(src[n]), "+v"(sc[n]), "+v"(kv[n]), "+v"(qv[n]), "+v"(gv[n]), "+v"(vv[n]), "+v"(A[n]));
+    const bool pre = !FLUSH_ONLY && a.prestep != 0;
+    using S = Stage<D, NT, PER_KEY, BF16, true>;
+    // the buffered terms to LDS first, so their registers are free from here on: E as stored,
+    // K as stored (decayed below, each thread its own entries)
+#pragma unroll
+    for (int n = 0; n < PER; ++n) {
+      const int i = tid + n * NT;
+      if (PER * NT == D || i < D) {
+#pragma unroll
+        for (int tau = 0; tau < WM; ++tau)
+          if (tau < t) {
+            se[tau][i] = Eb[tau][n];
+            sk[tau][i] = Kb[tau][n];
+          }
+      }
+    }
+    float ssq = 0.0f, ssk = 0.0f;
+    if constexpr (!FLUSH_ONLY) {
+#pragma unroll
+      for (int n = 0; n < PER; ++n) {
+        const int i = tid + n * NT;
+        if (PER * NT == D || i < D) {
+          const float kf = S::widen(kv[n]), qf = S::widen(qv[n]), gf = __uint_as_float(gv[n]);
+          tmp[i] = kf;
+          tmp[D + i] = qf;
+          ssk = fmaf(kf, kf, ssk);
+          ssq = fmaf(qf, qf, ssq);
+          if constexpr (PER_KEY) tmp[2 * D + i] = pre ? gate_from_logit(gf) : gf;
+          sv[i] = S::widen(vv[n]);
+        }
+      }
+    }
+    float g = g0, bt = beta;
     if (pre) {
-      if constexpr (!PER_KEY) g0 = gate_from_logit(g0);
-      beta = 1.0f / (1.0f + expf(-beta));
+      if constexpr (!PER_KEY) g = gate_from_logit(g);
+      bt = 1.0f / (1.0f + expf(-bt));
       ssq = wave_sum(ssq);
       ssk = wave_sum(ssk);
       if ((tid & 63) == 0) {
@@ -116,85 +175,93 @@ __device__ __forceinline__ float stage_rows_win(const StepArgs& a, const WinPtr&
         tmp[3 * D + 2 * (tid >> 6) + 1] = ssk;
       }
     }
-  }
-  __syncthreads();
-  float invq = 1.0f, invk = 1.0f;
-  if (pre) {
-    float nq = tmp[3 * D], nk = tmp[3 * D + 1];
+    __syncthreads();
+    float invq = 1.0f, invk = 1.0f;
+    if (pre) {
+      float nq = tmp[3 * D], nk = tmp[3 * D + 1];
 #pragma unroll
-    for (int w2 = 1; w2 < NWS; ++w2) {
-      nq += tmp[3 * D + 2 * w2];
-      nk += tmp[3 * D + 2 * w2 + 1];
-    }
-    invq = nq > 0.0f ? rsqrtf(nq) : 0.0f;
-    invk = nk > 0.0f ? rsqrtf(nk) : 0.0f;
-  }
-  // scalar gate: the gate of this token (1 for a flush) and the window's product before it
-  const float gs = FLUSH_ONLY ? 1.0f : g0;
-  const float as = scal && t > 0 ? __int_as_float(__builtin_amdgcn_readfirstlane(wp.hdr[1])) : 1.0f;
-  float kh[PER], qh[PER], gt[PER];
-#pragma unroll
-  for (int n = 0; n < PER; ++n) {
-    const int i = tid + n * NT;
-    kh[n] = qh[n] = 0.0f;
-    gt[n] = 1.0f;
-    if (i < D) {
-      if constexpr (!FLUSH_ONLY) {
-        gt[n] = PER_KEY ? tmp[2 * D + src[n]] : g0;
-        kh[n] = tmp[src[n]] * invk;
-        qh[n] = tmp[D + src[n]] * invq;
+      for (int w2 = 1; w2 < NWS; ++w2) {
+        nq += tmp[3 * D + 2 * w2];
+        nk += tmp[3 * D + 2 * w2 + 1];
       }
-      const float ap = scal ? gs * as : gt[n] * (t > 0 ? wp.A[i] : 1.0f);
-      srow[i] = make_float4(sc[n] * ap, kh[n], qh[n], gt[n]);
-      if (!FLUSH_ONLY && !ends && !scal) wp.A[i] = ap;
+      invq = nq > 0.0f ? rsqrtf(nq) : 0.0f;
+      invk = nk > 0.0f ? rsqrtf(nk) : 0.0f;
     }
-  }
-  if constexpr (!FLUSH_ONLY) {
-    for (int tau = 0; tau < t; ++tau) {
-      float ck = 0.0f, cq = 0.0f;
+    // scalar gate: the gate of this token (1 for a flush) and the window's product before it
+    const float gs = g;
 #pragma unroll
-      for (int n = 0; n < PER; ++n) {
-        const int i = tid + n * NT;
-        if (i < D) {
-          const float kb = wp.K[tau * D + i];
-          const float kd = scal ? kb : gt[n] * kb;
-          if (!scal && !ends) wp.K[tau * D + i] = kd;
-          ck = fmaf(kd, kh[n], ck);
-          cq = fmaf(kd, qh[n], cq);
+    for (int n = 0; n < PER; ++n) {
+      const int i = tid + n * NT;
+      if (PER * NT == D || i < D) {
+        float gt = 1.0f, kh = 0.0f, qh = 0.0f;
+        if constexpr (!FLUSH_ONLY) {
+          gt = PER_KEY ? tmp[2 * D + src[n]] : g;
+          kh = tmp[src[n]] * invk;
+          qh = tmp[D + src[n]] * invq;
+        }
+        const float ap = scal ? gs * as : gt * A[n];
+        srow[i] = make_float4(__uint_as_float(sc[n]) * ap, kh, qh, gt);
+        if (!FLUSH_ONLY && !ends && !scal) wp.A[i] = ap;
+        // the thread's own entries of the buffered keys, decayed to this token: per-row gates
+        // gate_p K_tau,p (also written back unless the window ends); scalar gate c'_tau K_tau,p
+#pragma unroll
+        for (int tau = 0; tau < WM; ++tau)
+          if (tau < t) {
+            const float kd = (scal ? gs * cA[tau] : gt) * sk[tau][i];
+            sk[tau][i] = kd;
+            if (!FLUSH_ONLY && !ends && !scal) wp.K[tau * D + i] = kd;
+          }
+      }
+    }
+    __syncthreads();
+    if constexpr (!FLUSH_ONLY) {
+      // the dot products K'_tau . k and K'_tau . q: 16 lanes per token, each over every 16th
+      // row, then a sum over the 16 lanes of a row of the wave
+      constexpr int TPP = NT / 16;   // tokens per pass
+      const int part = tid & 15;
+#pragma unroll
+      for (int t0 = 0; t0 < WM; t0 += TPP) {
+        const int tau = t0 + (tid >> 4);
+        float ck = 0.0f, cq = 0.0f;
+        if (tau < t) {
+#pragma unroll
+          for (int i = part; i < D; i += 16) {
+            const float4 rw = srow[i];
+            ck = fmaf(sk[tau][i], rw.y, ck);
+            cq = fmaf(sk[tau][i], rw.z, cq);
+          }
+        }
+        ck = sum_row16(ck);
+        cq = sum_row16(cq);
+        if (part == 0 && tau < t) {
+          sdot[tau][0] = ck;
+          sdot[tau][1] = cq;
         }
       }
-      ck = wave_sum(ck);
-      cq = wave_sum(cq);
-      if (scal) {
-        const float cf = gs * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wp.A[tau])));
-        ck *= cf;
-        cq *= cf;
-      }
-      if ((tid & 63) == 0) {
-        sdot[tid >> 6][tau][0] = ck;
-        sdot[tid >> 6][tau][1] = cq;
-      }
     }
+    // scalar gate: every wave has read the old words (at its start); the next token's go back
+    if (!FLUSH_ONLY && scal && !ends && tid == 0) {
+#pragma unroll
+      for (int tau = 0; tau < WM; ++tau)
+        if (tau < t) wp.A[tau] = gs * cA[tau];
+      wp.A[t] = 1.0f;
+      wp.hdr[1] = __float_as_int(gs * as);
+      wp.hdr[2] = 1;
+    }
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bt)));
   }
-  __syncthreads();
-  // scalar gate: every wave has read the old words above; the next token's words go back now
-  if (!FLUSH_ONLY && scal && !ends && tid == 0) {
-    for (int tau = 0; tau < t; ++tau) wp.A[tau] = gs * wp.A[tau];
-    wp.A[t] = 1.0f;
-    wp.hdr[1] = __float_as_int(gs * as);
-    wp.hdr[2] = 1;
-  }
-  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(beta)));
-}
+};
 
 // finish_columns plus the buffered terms: u_j += sum_tau E_tau,j (K'_tau . k),
-// p_j += sum_tau E_tau,j (K'_tau . q). Unless the window ends here, delta goes to E[t].
+// p_j += sum_tau E_tau,j (K'_tau . q), with E from the LDS copy the staging made. Unless the
+// window ends here, delta goes to E[t].
 template <int D, typename G>
 __device__ __forceinline__ void finish_columns_win(float (*redu)[D], float (*redp)[D], float* redqk,
-                                                   float (*sdot)[kMaxWindow][2], const WinPtr& wp,
-                                                   int t, bool ends, float* sv, float* pu, float* pp,
-                                                   float pqk, float beta, float* out_row, int tid,
-                                                   int w, int rs, int lane, int cg) {
+                                                   float (*sdot)[2], float (*se)[D],
+                                                   const WinPtr& wp, int t, bool ends, float* sv,
+                                                   float* pu, float* pp, float pqk, float beta,
+                                                   float* out_row, int tid, int w, int rs, int lane,
+                                                   int cg) {
   constexpr int CPL = G::CPL, NW = G::NW;
   store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(&redu[w * 4 + rs][cg * CPL]),
                        reinterpret_cast<const uint32_t*>(pu));
@@ -204,30 +271,27 @@ __device__ __forceinline__ void finish_columns_win(float (*redu)[D], float (*red
   if (lane == 0) redqk[w] = pqk;
   __syncthreads();
   for (int j = tid; j < D; j += G::NT) {
-    float uu = redu[0][j], pv = redp[0][j];
+    {
+      float uu = redu[0][j], pv = redp[0][j];
 #pragma unroll
-    for (int k = 1; k < 4 * NW; ++k) {
-      uu += redu[k][j];
-      pv += redp[k][j];
-    }
-    for (int tau = 0; tau < t; ++tau) {
-      float ck = sdot[0][tau][0], cq = sdot[0][tau][1];
-#pragma unroll
-      for (int w2 = 1; w2 < NW; ++w2) {
-        ck += sdot[w2][tau][0];
-        cq += sdot[w2][tau][1];
+      for (int k = 1; k < 4 * NW; ++k) {
+        uu += redu[k][j];
+        pv += redp[k][j];
       }
-      const float e = wp.E[tau * D + j];
-      uu = fmaf(e, ck, uu);
-      pv = fmaf(e, cq, pv);
-    }
-    float qk = redqk[0];
 #pragma unroll
-    for (int w2 = 1; w2 < NW; ++w2) qk += redqk[w2];
-    const float dj = beta * (sv[j] - uu);
-    sv[j] = dj;
-    out_row[j] = fmaf(qk, dj, pv);
-    if (!ends) wp.E[t * D + j] = dj;
+      for (int tau = 0; tau < kMaxWindow; ++tau)
+        if (tau < t) {
+          uu = fmaf(se[tau][j], sdot[tau][0], uu);
+          pv = fmaf(se[tau][j], sdot[tau][1], pv);
+        }
+      float qk = redqk[0];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) qk += redqk[w2];
+      const float dj = beta * (sv[j] - uu);
+      sv[j] = dj;
+      out_row[j] = fmaf(qk, dj, pv);
+      if (!ends) wp.E[t * D + j] = dj;
+    }
   }
   __syncthreads();
 }
@@ -254,6 +318,9 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
   const int r = PLAN == PLAN_FIXED ? NF * G::RPS : ua.r;
   const UnitPtr up = (PLAN != PLAN_ANY && a.st.contiguous) ? unit_ptr<D, FMT_Q, true>(ua, r)
                                                            : unit_ptr<D, FMT_Q>(ua, r);
+  // the staging loads (and the window's buffered terms), then every state load of this lane
+  WinStage<D, G::NT, PER_KEY, BF16, FLUSH_ONLY> ws;
+  ws.load(a, wp, t, scal, reinterpret_cast<const float*>(ua.s), bh, head, r, tid);
   uint32_t raw[RPL][RW];
 #pragma unroll
   for (int tt = 0; tt < RPL; ++tt) {
@@ -262,9 +329,7 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
       load_row_step<D, K>(up, p0, rs, cg, raw[tt]);
     });
   }
-  const float beta = stage_rows_win<D, G::NT, PER_KEY, BF16, FLUSH_ONLY>(
-      a, wp, t, ends, reinterpret_cast<const float*>(ua.s), bh, head, r, tid, srow, sv,
-      &sm.redu[0][0], sm.sdot, scal);
+  const float beta = ws.store(a, wp, t, ends, scal, tid, srow, sv, &sm.redu[0][0], sm.sdot, sm.se, sm.sk);
   const float4* my_rows = srow + (w * 4 + rs);
 
   int terms = t;   // buffered terms in X at the window's end (the token's own one included)
@@ -288,7 +353,7 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
       });
       pqk = fmaf(rw.z, rw.y, pqk);
     }
-    finish_columns_win<D, G>(sm.redu, sm.redp, sm.redqk, sm.sdot, wp, t, ends, sv, pu, pp, pqk,
+    finish_columns_win<D, G>(sm.redu, sm.redp, sm.redqk, sm.sdot, sm.se, wp, t, ends, sv, pu, pp, pqk,
                              beta, a.out + int64_t(bh) * D, tid, w, rs, lane, cg);
     if (!ends) {
       // append the token's key (storage order) and count it; the stored state stays as it is
@@ -301,21 +366,12 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
     }
     terms = t + 1;
   }
-  // the window ends: E[tau][j] and K'[tau][p] of every buffered term into LDS (the token's own
-  // term last: its key and delta)
-  for (int x = tid; x < terms * D; x += G::NT) {
-    const int tau = x / D, i = x - tau * D;
-    if (!FLUSH_ONLY && tau == t) {
-      sm.redu[tau][i] = sv[i];
-      sm.redp[tau][i] = srow[i].y;
-    } else {
-      sm.redu[tau][i] = wp.E[tau * D + i];
-      // K'_tau,p: per-row gates gate_p K_tau,p (K decayed up to the previous token); scalar
-      // gate (gate c_tau) K_tau,p with the key as appended
-      const float g = scal ? srow[i].w * wp.A[tau] : srow[i].w;
-      sm.redp[tau][i] = g * wp.K[tau * D + i];
+  // the window ends: the token's own term joins the buffered ones in LDS (its key and delta)
+  if (!FLUSH_ONLY)
+    for (int i = tid; i < D; i += G::NT) {
+      sm.se[t][i] = sv[i];
+      sm.sk[t][i] = srow[i].y;
     }
-  }
   __syncthreads();
 #pragma unroll
   for (int tt = 0; tt < RPL; ++tt)
@@ -331,9 +387,9 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
 #pragma unroll
       for (int c = 0; c < CPL; ++c) X[c] = decode_row<D, K>(raw[tt], c, p, r) * m;
       for (int tau = 0; tau < terms; ++tau) {
-        const float kp = sm.redp[tau][p];
+        const float kp = sm.sk[tau][p];
         float e[CPL];
-        load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(&sm.redu[tau][cg * CPL]),
+        load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(&sm.se[tau][cg * CPL]),
                             reinterpret_cast<uint32_t*>(e));
 #pragma unroll
         for (int c = 0; c < CPL; ++c) X[c] = fmaf(kp, e[c], X[c]);

@@ -208,20 +208,27 @@ def stq_step_exact(D, bits, w, h, c, rf, cs, q, k, v, alpha, beta, cs_near_tie=N
             val = f16_value(cs_near_tie[j])
         cs_new.append(val)
         tie.append(t)
+    hn, cn, rfn = stq_rows_exact(D, bits, Xf, cs_new)
+    return {"out": np.array([float(f32(x)) for x in y], np.float32), "h": hn, "c": cn, "rf": rfn,
+            "cs": np.array([f16_bits(x) for x in cs_new], np.uint16), "tie": np.array(tie)}
+
+
+def stq_rows_exact(D, bits, Xf, cs_new):
+    """The fit's second half: pivot values, row factors and codes of the binary32 state Xf
+    (Fractions [D][D]) for the column scales cs_new (Fractions, binary16 values)."""
     hn = np.zeros((D, D), np.uint16)
     cn = np.zeros((D, D), np.int8)
     rfn = np.zeros(D, np.uint16)
     for i in range(D):
-        if piv[i]:
+        if int(bits[i]) == 16:
             hn[i] = [f16_bits(f16(x)) for x in Xf[i]]
             continue
         qm = 2 ** (int(bits[i]) - 1) - 1
-        m = max([f32(abs(Xf[i][j]) / cs_new[j]) for j in range(D) if cs_new[j] > 0], default=F(0))
+        m = max([f32(abs(Xf[i][j]) / cs_new[j]) for j in range(D) if cs_new[j] > 0], default=Fraction(0))
         r = f16(f32(m / qm))
         rfn[i] = f16_bits(r)
         for j in range(D):
             sc = r * cs_new[j]
             if sc > 0:
                 cn[i, j] = max(-qm, min(qm, rne_int(f32(Xf[i][j] / sc))))
-    return {"out": np.array([float(f32(x)) for x in y], np.float32), "h": hn, "c": cn, "rf": rfn,
-            "cs": np.array([f16_bits(x) for x in cs_new], np.uint16), "tie": np.array(tie)}
+    return hn, cn, rfn

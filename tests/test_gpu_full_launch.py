@@ -70,10 +70,11 @@ def test_stq_step_pool4096_launch():
     _inactive_untouched(st.slots(), slots)
     out = out.cpu().numpy()
     assert np.isfinite(out).all()
-    ref_out, ref_state = oracle.stq_step(bb, ww, h, c, rf, cs, *_sample(inp))
+    ref_out, ref_state, X_ref = oracle.stq_step(bb, ww, h, c, rf, cs, *_sample(inp), return_x=True)
     check_readout(out[SAMPLE_B], ref_out.reshape(ns, H, D))
     got = layout_ref.stq_unpack(bits, st.slots()[torch.from_numpy(slots[SAMPLE_B]).long().cuda()].cpu().numpy(), D)
-    _log("stq pool4096: " + str(check_stq(bits, got, tuple(x.reshape((ns, H) + x.shape[1:]) for x in ref_state))))
+    _log("stq pool4096: " + str(check_stq(bits, impact, got, tuple(x.reshape((ns, H) + x.shape[1:]) for x in ref_state),
+                                          X_ref.reshape(ns, H, D, D))))
 
 
 def _damp_pool(rows, slots, seed, r_per_head=None, row_map=None):

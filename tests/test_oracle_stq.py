@@ -205,3 +205,28 @@ def test_step_on_integer_rows_matches_exact_rationals_across_units(per_key):
         assert np.array_equal(out[u], ref["out"]), f"unit {u}: readout"
         assert (c2[u][bits[u] != 16] != 0).any()
     assert near == 0
+
+
+def test_fit_rows_for_given_column_scales_matches_exact_rationals():
+    """oracle_stq_fit_rows (the fit's second half with the column scales given, which the GPU
+    tests use to take the row factors and codes from the device's own column scales) against
+    the exact rational rule, on states and column scales drawn at random (some scales 0), and
+    against the whole fit when handed the fit's own column scales."""
+    import exact_ref
+    rng = np.random.default_rng(21)
+    n, D = 3, 12
+    bits = np.stack([rng.permutation(np.array([16, 8, 6, 4] + list(rng.choice(np.array([16, 8, 6, 4], np.uint8), D - 4)), np.uint8))
+                     for _ in range(n)])
+    X = (rng.standard_normal((n, D, D)) * 0.5).astype(np.float32)
+    cs = np.abs(rng.standard_normal((n, D)) * 0.2).astype(np.float16)
+    cs[0, 3] = 0
+    csb = cs.view(np.uint16)
+    h, c, rf = oracle.stq_fit_rows(bits, X, csb)
+    for u in range(n):
+        Xf = [[Fraction(float(X[u, i, j])) for j in range(D)] for i in range(D)]
+        he, ce, rfe = exact_ref.stq_rows_exact(D, bits[u], Xf, [Fraction(float(x)) for x in cs[u]])
+        assert np.array_equal(h[u], he) and np.array_equal(c[u], ce) and np.array_equal(rf[u], rfe)
+    w = rng.uniform(0.5, 2, (n, D)).astype(np.float32)
+    hq, cq, rfq, csq = oracle.stq_quantize(bits, w, X)
+    h2, c2, rf2 = oracle.stq_fit_rows(bits, X, csq)
+    assert np.array_equal(hq, h2) and np.array_equal(cq, c2) and np.array_equal(rfq, rf2)
