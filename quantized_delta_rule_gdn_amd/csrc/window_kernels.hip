@@ -36,8 +36,13 @@ template <int D, int NW>
 struct WinSmem {
   float4 srow[D];            // {m_p = scale * a'_p, k_p, q_p, gate_p}
   float sv[D];               // v, then delta
-  float redu[4 * NW][D];     // column partials
-  float redp[4 * NW][D];
+  union {
+    struct {
+      float redu[4 * NW][D];   // column partials
+      float redp[4 * NW][D];
+    };
+    float skT[D][kMaxWindow];  // at the window's end: every term's key, transposed
+  };
   float se[kMaxWindow][D];   // the window's deltas E[tau][j] (the token's own last)
   float sk[kMaxWindow][D];   // the window's keys decayed to this token, K'[tau][p]
   float redqk[NW];
@@ -366,39 +371,73 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
     }
     terms = t + 1;
   }
-  // the window ends: the token's own term joins the buffered ones in LDS (its key and delta)
-  if (!FLUSH_ONLY)
-    for (int i = tid; i < D; i += G::NT) {
-      sm.se[t][i] = sv[i];
-      sm.sk[t][i] = srow[i].y;
-    }
+  // The window ends. Every term's key goes to LDS transposed, skT[p][tau] (zero past the last
+  // term), over the column partials, which nothing reads any more; the token's own delta joins
+  // the buffered ones.
+  float (*skT)[kMaxWindow] = sm.skT;
+  for (int i = tid; i < D; i += G::NT) {
+    float kt[kMaxWindow];
+#pragma unroll
+    for (int tau = 0; tau < kMaxWindow; ++tau)
+      kt[tau] = tau < t ? sm.sk[tau][i] : (!FLUSH_ONLY && tau == t ? srow[i].y : 0.0f);
+    store_bytes<4 * kMaxWindow>(reinterpret_cast<uint8_t*>(skT[i]), reinterpret_cast<const uint32_t*>(kt));
+    if (!FLUSH_ONLY) sm.se[t][i] = sv[i];
+  }
   __syncthreads();
 #pragma unroll
   for (int tt = 0; tt < RPL; ++tt)
 #pragma unroll
     for (int i = 0; i < RW; ++i) asm volatile("" : "+v"(raw[tt][i]));
-  // X = m_p c_pj + sum_tau K'_tau,p E_tau,j, requantized and stored in place
+  // X = m_p c_pj + sum_tau K'_tau,p E_tau,j, requantized and stored in place, over TM terms
+  // (zero past the last one). The lane's columns of the first TR terms' deltas stay in registers
+  // over all row steps; a row step reads from LDS its row's keys and the lane's columns of the
+  // other TM - TR deltas. (TR < TM keeps the register count within four waves per SIMD.)
+  auto materialise = [&]<int TM, int TR>() __attribute__((always_inline)) {
+    float e[TR][CPL];
 #pragma unroll
-  for (int tt = 0; tt < RPL; ++tt) {
-    const int p0 = tt * G::RPS + w * 4, p = p0 + rs;
-    const float m = my_rows[tt * G::RPS].x;
-    by_plan<PLAN, T16>(tt, p0, r, [&]<int K>() __attribute__((always_inline)) {
-      float X[CPL];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) X[c] = decode_row<D, K>(raw[tt], c, p, r) * m;
-      for (int tau = 0; tau < terms; ++tau) {
-        const float kp = sm.sk[tau][p];
-        float e[CPL];
+    for (int tau = 0; tau < TR; ++tau) {
+      if (tau < terms) {
         load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(&sm.se[tau][cg * CPL]),
-                            reinterpret_cast<uint32_t*>(e));
+                            reinterpret_cast<uint32_t*>(e[tau]));
+      } else {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) X[c] = fmaf(kp, e[c], X[c]);
+        for (int c = 0; c < CPL; ++c) e[tau][c] = 0.0f;
       }
-      each_kind<K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
-        Row<D, K2>::template store<false, MIX, true>(up, p0, rs, cg, X, ssc);
+    }
+#pragma unroll
+    for (int tt = 0; tt < RPL; ++tt) {
+      const int p0 = tt * G::RPS + w * 4, p = p0 + rs;
+      const float m = my_rows[tt * G::RPS].x;
+      by_plan<PLAN, T16>(tt, p0, r, [&]<int K>() __attribute__((always_inline)) {
+        float X[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) X[c] = decode_row<D, K>(raw[tt], c, p, r) * m;
+#pragma unroll
+        for (int tau = 0; tau < TM; ++tau) {
+          const float kp = skT[p][tau];
+          if (tau < TR) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) X[c] = fmaf(kp, e[tau < TR ? tau : 0][c], X[c]);
+          } else if (tau < terms) {
+            float el[CPL];
+            load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(&sm.se[tau][cg * CPL]),
+                                reinterpret_cast<uint32_t*>(el));
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) X[c] = fmaf(kp, el[c], X[c]);
+          }
+        }
+        each_kind<K>([&]<int K2, bool MIX>() __attribute__((always_inline)) {
+          Row<D, K2>::template store<false, MIX, true>(up, p0, rs, cg, X, ssc);
+        });
       });
-    });
-  }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  constexpr int TR8 = PLAN == PLAN_FIXED ? kMaxWindow - 1 : kMaxWindow / 2;
+  if (terms <= kMaxWindow / 2)
+    materialise.template operator()<kMaxWindow / 2, kMaxWindow / 2>();
+  else
+    materialise.template operator()<kMaxWindow, TR8>();
   flush_scales<D, G::NT>(up, ssc, r, tid);
   if (tid == 0) {   // an empty window, with no gate form yet
     wp.hdr[0] = 0;
@@ -418,8 +457,10 @@ __device__ __forceinline__ void window_heads_case(const StepArgs& a, const UnitA
 }
 
 // HEADS: per-head layout whose r are all multiples of the row step (kinds fixed per head's r).
+// At least four waves per SIMD (at most 128 VGPRs): at d = 128 that is every workgroup a CU
+// holds; the window's end keeps its deltas in registers within that bound.
 template <int D, int PER_KEY, int BF16, int PLAN, int WAVES, int NF, bool FLUSH_ONLY, bool HEADS>
-__global__ __launch_bounds__(64 * WAVES) void window_kernel(const StepArgs a) {
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4))) void window_kernel(const StepArgs a) {
   __shared__ WinSmem<D, Geo<D, WAVES>::NW> sm;
   int b, head;
   if (!unit_of(a, b, head)) return;
