@@ -33,6 +33,10 @@ FLAGS = [
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    # a variable read before every path has set it is an error (it becomes an address)
+    "-Werror=uninitialized",
+    "-Werror=sometimes-uninitialized",
+    "-Werror=conditional-uninitialized",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]

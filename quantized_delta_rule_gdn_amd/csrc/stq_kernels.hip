@@ -8,8 +8,9 @@
 //   cs_j = fp16( sqrt( sum_{i in N} w_i^2 X_ij^2 / sum_{i in N} w_i^2 ) )
 //   rf_i = fp16( max_{j: cs_j > 0} (|X_ij| / cs_j) / qmax_i ),   qmax = 2^(b-1) - 1
 //   code = clamp(rint(X_ij / (rf_i cs_j)), -qmax, qmax)   (0 where rf_i cs_j = 0)
-// The page gives the structure (shared column scales fitted with squared row-impact factors, row
-// factors, FP16 scales and pivots) but not these formulas; they are the library's reading.
+// The page gives the structure (per-head column scales whose fit weighs each row by the square of
+// its impact score, row factors, FP16 scales and pivots) but not these formulas; they are the
+// library's reading.
 //
 // Block of one (slot, head), storage rows ordered pivots, 8-bit, 6-bit, 4-bit (each ascending
 // key index): FP16 pivot rows (2 d bytes each) | 8-bit rows (d) | 6-bit rows (3 d / 4: a plane of
@@ -275,6 +276,7 @@ struct StqSmem {
   float redqk[NW];
   float scs[D];              // column scales (binary16 values as fp32)
   float srcs[D];             // RN(1 / cs_j), 0 where cs_j = 0
+  uint16_t srf[D];           // the new row factors (binary16 bits), integer-row order
 };
 
 // The step's per-row scalars in two halves, so that their loads overlap the state loads while
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
         const float m = max_row16(mq);
         const uint32_t rb = float_to_half_bits(div_qmax(m, qm, inv));
         const float rf = half_bits_to_float(rb);
-        if (cg == 0) buf_store<2>(dst, blk.orf + 2u * static_cast<uint32_t>(p - blk.n16), 0u, &rb);
+        if (cg == 0) sm.srf[p - blk.n16] = static_cast<uint16_t>(rb);
         if constexpr (EXACT) {
 #pragma unroll
           for (int c = 0; c < CPL; ++c) {
@@ -554,6 +556,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
       }
       stq_store<D, K>(dst, blk, p, cg, X[t], tb);
     });
+  }
+  // the row factors, gathered in LDS, go out as one contiguous run (scattered 2-byte stores by
+  // one lane per row reached HBM as partial lines)
+  __syncthreads();
+  const int nint = D - blk.n16;
+  for (int i = 2 * tid; i < nint; i += 2 * NT) {
+    const uint32_t two = sm.srf[i] | (i + 1 < nint ? static_cast<uint32_t>(sm.srf[i + 1]) << 16 : 0u);
+    if (i + 1 < nint)
+      buf_store<4>(dst, blk.orf + 2u * static_cast<uint32_t>(i), 0u, &two);
+    else
+      buf_store<2>(dst, blk.orf + 2u * static_cast<uint32_t>(i), 0u, &two);
   }
 }
 
