@@ -40,9 +40,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 # Batches of at least this many (slot, head) units run the step in ascending slot order under
-# --order auto. The step keeps about 3,000 units in flight (12 per CU); a batch that spans many
+# --order auto. The step holds at most 2,048 units at once (8 per CU); a batch that spans many
 # such waves gains from streaming nearby blocks together more than the ordering launch costs
-# (about 2 us), a batch that is resident at once does not.
+# (about 2-5 us), a batch that is resident at once does not.
 ORDER_MIN_UNITS = 16384
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "damp_step_pool4096_hbm_traffic.txt")
 # the DAMP step's kernel source: its building blocks and its kernels

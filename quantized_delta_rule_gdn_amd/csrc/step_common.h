@@ -730,9 +730,10 @@ __device__ __forceinline__ void flush_scales(const UnitPtr& u, const float* sc_l
 }
 
 // Waves per workgroup of the quantized step with the row kinds fixed at compile time: two at
-// d = 128 (80 VGPRs with 24 FP16 rows: 6 waves per SIMD, 12 units per CU), which measured a
-// few percent faster than four waves per unit on the short batches and equal on the long one;
-// one wave per unit (115 VGPRs, 16 units per CU) measured slower everywhere.
+// d = 128 (78 VGPRs with 24 FP16 rows), which measured a few percent faster than four waves per
+// unit on the short batches and equal on the long one; one wave per unit (115 VGPRs) measured
+// slower everywhere. A CU was measured to hold at most 8 workgroups of the step at once
+// whatever their register count, so a unit's two waves may use up to 128 VGPRs at no cost.
 constexpr int kStepWaves = 2;
 template <int D>
 constexpr int kWaves = kStepWaves < Geo<D>::NW ? kStepWaves : Geo<D>::NW;
