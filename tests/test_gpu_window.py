@@ -59,6 +59,11 @@ def _gpu_step(pool, wbuf, W, slots_dev, inp):
     (64, 8, 7, 3, 5, synth.GDN, "fp32", 7),
     (16, 2, 4, 2, 2, synth.KDA, "bf16", 5),
     (128, 24, 5, 2, 1, synth.GDN, "bf16", 3),     # one token per window: the per-token step
+    # compile-time row kinds with windows over 4 tokens: the last token's update holds seven
+    # terms' deltas in registers and reads the eighth from LDS (W = 8), or holds six of eight
+    # with two empty (W = 6); both end mid-window and flush
+    (128, 24, 7, 3, 8, synth.GDN, "bf16", 19),
+    (128, 16, 5, 2, 6, synth.KDA, "fp32", 9),
 ])
 def test_window_steps_and_flush(D, r, B, H, W, decay, dtype, tokens):
     rng, rows, mask, maskn, h, c, s = _setup(D + r + W, B, H, D, r, decay)
