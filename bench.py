@@ -85,22 +85,24 @@ def order_enabled(order: str, units: int, window: int = 0, stq: bool = False) ->
 
 def alg_bytes_window(W: int, d: int = 128, r: int = 24, per_key: bool = False, qkv_bytes: int = 2) -> float:
     """Bytes per (slot, head) update of the windowed step, averaged over the W tokens of a
-    window: every token reads the stored block and its buffered terms (keys and deltas, 4 d bytes
-    each); a token that does not end the window appends its key and delta, the last one writes
-    the block instead. The decay: with a gate per key row (KDA) the row gains (4 d bytes) and
-    every buffered key are read and written back decayed; with one gate per unit (GDN) the decay
-    is one number for the window and one per buffered key, in the buffer's header words."""
+    window: every token reads the stored block and its buffered terms (a key and a delta each);
+    a token that does not end the window appends its key and delta, the last one writes the
+    block instead. Deltas are fp32 (4 d bytes). The decay: with a gate per key row (KDA) the row
+    gains (4 d bytes) and every buffered key (fp32) are read and written back decayed; with one
+    gate per unit (GDN) the decay is one number for the window and one per buffered key, in the
+    buffer's header words, and the keys stay as given: 2 d bytes each from bf16 inputs."""
     block = 2 * r * d + (d - r) * d + 4 * (d - r)
     vecs = 3 * qkv_bytes * d + (4 * d if per_key else 4) + 4 + 4 * d + 4
+    key = 4 * d if per_key or qkv_bytes != 2 else 2 * d
     total = 0
     for t in range(W):
         last = t == W - 1
         if per_key:
             rd = block + 4 + (4 * d if t else 0) + t * 2 * 4 * d
-            wr = block if last else 4 + 4 * d + t * 4 * d + 2 * 4 * d
+            wr = block if last else 12 + 4 * d + t * 4 * d + 2 * 4 * d
         else:
-            rd = block + 4 + (4 + 4 * t if t else 0) + t * 2 * 4 * d
-            wr = block if last else 12 + 4 * (t + 1) + 2 * 4 * d
+            rd = block + 4 + (8 + 4 * t if t else 0) + t * (key + 4 * d)
+            wr = block if last else 16 + 4 * (t + 1) + key + 4 * d
         total += rd + wr + vecs
     return total / W
 

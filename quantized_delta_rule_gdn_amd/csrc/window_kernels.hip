@@ -25,10 +25,13 @@ namespace {
 //   [1]            scalar gate: a, the product of the window's gates so far
 //   [2]            1 for a window with a scalar gate, 0 for per-row gates (written by every
 //                  token that leaves the window open; cleared when the window ends)
+//   [3]            scalar gate: bit tau set when K[tau] is stored as bf16 (the first 2 D bytes
+//                  of its row): the key of a call with bf16 inputs and no fused pre-step is a
+//                  bf16 value, so it is stored exactly in half the bytes; 0 otherwise
 //   [4, 4 + D)     per-row gates: a, storage row order
 //                  scalar gate: [4, 4 + W) c[tau], the product of the gates after token tau
 //   [4 + D, ..)    K[tau][p], tau < W, storage row order (per-row gates: decayed; scalar gate:
-//                  as appended)
+//                  as appended, fp32 or bf16 by word [3])
 //   then           E[tau][j], tau < W
 constexpr int kMaxWindow = 8;
 
@@ -90,12 +93,17 @@ struct WinStage {
   static constexpr int NWS = NT / 64;
   static constexpr int WM = kMaxWindow;
   uint32_t src[PER], sc[PER], kv[PER], qv[PER], gv[PER], vv[PER];
-  float A[PER], Kb[WM][PER], Eb[WM][PER], cA[WM];
+  float A[PER], Eb[WM][PER], cA[WM];
+  uint32_t Kb[WM][PER];   // the buffered keys' words as loaded (decoded in store())
   float g0, beta, as;
+  uint32_t kbf;   // header word [3] of the window so far (scalar gate), else 0
 
+  // hdr3: header word [3], read with the token count (so that its wait is the count's).
   __device__ __forceinline__ void load(const StepArgs& a, const WinPtr& wp, int t, bool scal,
-                                       const float* sc_old, int bh, int head, int r, int tid) {
+                                       uint32_t hdr3, const float* sc_old, int bh, int head, int r,
+                                       int tid) {
     const int64_t vec = int64_t(bh) * D;
+    kbf = scal && t > 0 ? hdr3 : 0u;
 #pragma unroll
     for (int n = 0; n < PER; ++n) {
       const int i = tid + n * NT;
@@ -104,7 +112,10 @@ struct WinStage {
       kv[n] = qv[n] = gv[n] = vv[n] = 0u;
       A[n] = 1.0f;
 #pragma unroll
-      for (int tau = 0; tau < WM; ++tau) Kb[tau][n] = Eb[tau][n] = 0.0f;
+      for (int tau = 0; tau < WM; ++tau) {
+        Kb[tau][n] = 0u;
+        Eb[tau][n] = 0.0f;
+      }
       if (PER * NT == D || i < D) {
         if (a.st.rowmap) src[n] = a.st.rowmap[head * D + i];
         if (i >= r) sc[n] = reinterpret_cast<const uint32_t*>(sc_old)[i - r];
@@ -118,7 +129,10 @@ struct WinStage {
 #pragma unroll
         for (int tau = 0; tau < WM; ++tau)
           if (tau < t) {
-            Kb[tau][n] = wp.K[tau * D + i];
+            // one 4-byte load either way, kept as loaded: a bf16 row's element i is half i & 1
+            // of its word i / 2 (no use of a loaded value here, so no wait before the state loads)
+            const bool hb = (kbf >> tau) & 1u;
+            Kb[tau][n] = reinterpret_cast<const uint32_t*>(wp.K + tau * D)[hb ? (i >> 1) : i];
             Eb[tau][n] = wp.E[tau * D + i];
           }
       }
@@ -140,7 +154,7 @@ struct WinStage {
     const bool pre = !FLUSH_ONLY && a.prestep != 0;
     using S = Stage<D, NT, PER_KEY, BF16, true>;
     // the buffered terms to LDS first, so their registers are free from here on: E as stored,
-    // K as stored (decayed below, each thread its own entries)
+    // K as fp32 from its stored form (decayed below, each thread its own entries)
 #pragma unroll
     for (int n = 0; n < PER; ++n) {
       const int i = tid + n * NT;
@@ -149,7 +163,8 @@ struct WinStage {
         for (int tau = 0; tau < WM; ++tau)
           if (tau < t) {
             se[tau][i] = Eb[tau][n];
-            sk[tau][i] = Kb[tau][n];
+            sk[tau][i] = (kbf >> tau) & 1u ? __uint_as_float((i & 1) ? (Kb[tau][n] & 0xFFFF0000u) : (Kb[tau][n] << 16))
+                                           : __uint_as_float(Kb[tau][n]);
           }
       }
     }
@@ -309,7 +324,8 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
   constexpr int T16 = PLAN == PLAN_FIXED ? NF : G::T16;
   constexpr int CPL = G::CPL, RPL = G::RPL, RW = Words<CPL * 2>::W;
   const WinPtr wp = win_ptr<D>(a, slot, head);
-  const int t = __builtin_amdgcn_readfirstlane(*wp.hdr);
+  const int t = __builtin_amdgcn_readfirstlane(wp.hdr[0]);
+  const uint32_t hdr3 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wp.hdr[3]));
   if (FLUSH_ONLY && t == 0) return;   // nothing pending (uniform over the workgroup)
   const bool ends = FLUSH_ONLY || t + 1 >= a.window;
   const bool scal = win_scalar<PER_KEY, FLUSH_ONLY>(wp, t);
@@ -325,7 +341,7 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
                                                            : unit_ptr<D, FMT_Q>(ua, r);
   // the staging loads (and the window's buffered terms), then every state load of this lane
   WinStage<D, G::NT, PER_KEY, BF16, FLUSH_ONLY> ws;
-  ws.load(a, wp, t, scal, reinterpret_cast<const float*>(ua.s), bh, head, r, tid);
+  ws.load(a, wp, t, scal, hdr3, reinterpret_cast<const float*>(ua.s), bh, head, r, tid);
   uint32_t raw[RPL][RW];
 #pragma unroll
   for (int tt = 0; tt < RPL; ++tt) {
@@ -361,11 +377,20 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
     finish_columns_win<D, G>(sm.redu, sm.redp, sm.redqk, sm.sdot, sm.se, wp, t, ends, sv, pu, pp, pqk,
                              beta, a.out + int64_t(bh) * D, tid, w, rs, lane, cg);
     if (!ends) {
-      // append the token's key (storage order) and count it; the stored state stays as it is
-      for (int i = tid; i < D; i += G::NT) wp.K[t * D + i] = srow[i].y;
+      // append the token's key (storage order) and count it; the stored state stays as it is.
+      // With a scalar gate the key is kept as given: from bf16 inputs without the fused pre-step
+      // it is a bf16 value, stored exactly in 2 bytes.
+      const bool kb = BF16 && scal && a.prestep == 0;
+      for (int i = tid; i < D; i += G::NT) {
+        if (kb)
+          reinterpret_cast<uint16_t*>(wp.K + t * D)[i] = static_cast<uint16_t>(__float_as_uint(srow[i].y) >> 16);
+        else
+          wp.K[t * D + i] = srow[i].y;
+      }
       if (tid == 0) {
         wp.hdr[0] = t + 1;
         if (!scal) wp.hdr[2] = 0;   // per-row gates (the scalar form set its flag in staging)
+        wp.hdr[3] = (ws.kbf & ~(1u << t)) | (kb ? 1u << t : 0u);
       }
       return;
     }
@@ -442,6 +467,7 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
   if (tid == 0) {   // an empty window, with no gate form yet
     wp.hdr[0] = 0;
     wp.hdr[2] = 0;
+    wp.hdr[3] = 0;
   }
 }
 

@@ -29,13 +29,18 @@ def test_window_bytes_reduce_to_the_per_token_step():
         assert w4 < 41036 and w8 < 41036      # the block is written once per window
     # per-row gates: every buffered key is rewritten decayed each token, so the bytes grow with W
     assert bench.alg_bytes_window(8, per_key=True) > bench.alg_bytes_window(4, per_key=True)
-    # one gate per unit, W = 2, by hand: token 0 reads the block and the count (19,872 + 4) and
-    # writes the header words, c[0], its key and its delta (12 + 4 + 512 + 512); token 1 reads the
-    # block, count, a, c[0], one key and one delta (19,872 + 4 + 4 + 4 + 1,024) and writes the
-    # block; each token also moves its 1,292 vector bytes
-    t0 = 19872 + 4 + 12 + 4 + 512 + 512 + 1292
-    t1 = 19872 + 4 + 4 + 4 + 1024 + 19872 + 1292
+    # one gate per unit, W = 2, bf16 inputs, by hand: token 0 reads the block and the count
+    # (19,872 + 4) and writes the header words, c[0], its key as bf16 and its delta
+    # (16 + 4 + 256 + 512); token 1 reads the block, the count, a, the key-format word, c[0], one
+    # bf16 key and one delta (19,872 + 4 + 4 + 4 + 4 + 256 + 512) and writes the block; each token
+    # also moves its 1,292 vector bytes
+    t0 = 19872 + 4 + 16 + 4 + 256 + 512 + 1292
+    t1 = 19872 + 4 + 4 + 4 + 4 + 256 + 512 + 19872 + 1292
     assert abs(bench.alg_bytes_window(2) - (t0 + t1) / 2) < 1e-9
+    # fp32 inputs keep fp32 keys (512 bytes each) and fp32 q, k, v (1,536 bytes)
+    f0 = 19872 + 4 + 16 + 4 + 512 + 512 + 2060
+    f1 = 19872 + 4 + 4 + 4 + 4 + 512 + 512 + 19872 + 2060
+    assert abs(bench.alg_bytes_window(2, qkv_bytes=4) - (f0 + f1) / 2) < 1e-9
 
 
 def test_traffic_is_reported_only_for_the_profiled_source():

@@ -99,6 +99,35 @@ def test_window_steps_and_flush(D, r, B, H, W, decay, dtype, tokens):
     assert torch.equal(pool.state.blocks(), before)
 
 
+@pytest.mark.parametrize("W,tokens", [(4, 10), (8, 13)])
+def test_scalar_gate_window_with_mixed_input_types(W, tokens):
+    """One gate per unit: a key from bf16 inputs is buffered as bf16 (exact), one from fp32
+    inputs as fp32; tokens alternate between the two input types within every window, so each
+    window holds both formats (at W = 8 the last token's update also reads an LDS-held delta)."""
+    D, r, B, H = 128, 24, 6, 3
+    rng, rows, mask, maskn, h, c, s = _setup(500 + W, B, H, D, r, synth.GDN)
+    win = oracle.Window(maskn, h.copy(), c.copy(), s.copy(), W)
+    slots = np.random.default_rng(W).choice(2 * B, B, replace=False)
+    pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), slots, 2 * B)
+    wbuf = pool.state.window_buffer(W)
+    for tok in range(tokens):
+        dtype = "bf16" if tok % 3 != 1 else "fp32"
+        inp = synth.step_inputs(rng, B, H, D, synth.GDN, dtype)
+        out = _gpu_step(pool, wbuf, W, pool.slot_dev, inp)
+        ref = win.step(*ref_vectors(inp, B, H, D))
+        check_readout(out, ref.reshape(B, H, D))
+        if (tok + 1) % W == 0:
+            got = pool.logical()
+            check_quant(mask, got, (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D),
+                                    win.s.reshape(B, H, D)))
+            _resync(win, got)
+    pool.state.window_flush(wbuf, W, pool.slot_dev)
+    win.flush()
+    torch.cuda.synchronize()
+    check_quant(mask, pool.logical(), (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D),
+                                       win.s.reshape(B, H, D)))
+
+
 def test_requests_at_different_window_positions():
     D, r, H, W = 128, 24, 3, 4
     B = 8
