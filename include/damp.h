@@ -250,7 +250,9 @@ damp_status damp_decode_step_sorted(damp_state* state, const int32_t* slot_idx, 
  * both, and the state is quantized once at the window's end). Within a window the state of a
  * unit is diag(a) S_hat + sum over the window's tokens of K_tau E_tau^T: S_hat the stored DAMP
  * state (not written until the window ends), a its cumulative row decay, K_tau the token's key
- * decayed by the later gates and E_tau its delta, all fp32 in a window buffer. Each unit has its
+ * decayed by the later gates and E_tau its delta, held in a window buffer in fp32 (a key of the
+ * DAMP_DECAY_SCALAR form that came from bf16 inputs is a bf16 value, and is held as bf16, which
+ * is exact). Each unit has its
  * own window position, so the requests of one batch may be at different points of their windows.
  * ------------------------------------------------------------------------------------- */
 
@@ -268,8 +270,8 @@ size_t damp_window_bytes(const damp_layout* layout, int32_t window);
  * read. window = 1 is the per-token step (the same arithmetic as damp_decode_step up to fp32
  * rounding order). A given buffer must always be used with the same window length, and within
  * one window with the same decay mode: with DAMP_DECAY_SCALAR the buffer holds the decay as
- * scalars (one for the window, one per buffered key) and the keys as appended, with
- * DAMP_DECAY_PER_KEY as row gains and decayed keys. A flag in the buffer, set by the window's
+ * scalars (one for the window, one per buffered key) and the keys as appended (bf16 or fp32, as
+ * each call's inputs give them), with DAMP_DECAY_PER_KEY as row gains and decayed keys. A flag in the buffer, set by the window's
  * tokens and cleared when the window ends (or is flushed), tells a flush which form it holds.
  * Errors: INVALID_ARGUMENT, SLOT_INDEX (debug), HIP. */
 damp_status damp_window_step(damp_state* state, void* window_buf, int32_t window,
