@@ -673,14 +673,6 @@ struct Stage {
   }
 };
 
-template <int D, int NT, int PER_KEY, int BF16, bool Q>
-__device__ __forceinline__ float stage_rows(const StepArgs& a, const float* sc_old, int bh, int head,
-                                            int r, int tid, float4* srow, float* sv, float* tmp) {
-  Stage<D, NT, PER_KEY, BF16, Q> sg;
-  sg.load(a, sc_old, bh, head, r, tid);
-  return sg.store(a, tid, srow, sv, tmp);
-}
-
 // Column sums over the key rows, shared by the step kernels. Every lane writes its CPL partial
 // sums of u = S'^T k and p = S'^T q (over its RPL rows) to LDS; thread j then adds the 4*NW
 // partials of column j in a fixed order, forms delta_j = beta (v_j - u_j) (left in sv[j]) and

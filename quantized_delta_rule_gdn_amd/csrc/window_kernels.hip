@@ -79,7 +79,7 @@ __device__ __forceinline__ bool win_scalar(const WinPtr& wp, int t) {
 // before the caller issues the state loads: the row map and old INT8 scales, k, q, the gate and v
 // of the token, and of the t tokens already in the window their keys K[tau][i], their deltas
 // E[tau][i] (column i) and the decay words (per-row gains a_i, or the scalars c[tau] and a).
-// store() then stages as stage_rows does, plus: a'_p = gate_p * a_p (a = 1 when the window is
+// store() then stages as Stage::store does, plus: a'_p = gate_p * a_p (a = 1 when the window is
 // empty), srow.x = scale * a'_p, srow.w = gate_p; every buffered key decayed, K'_tau,p =
 // gate_p K_tau,p, and its dot products with k and q, all tokens' products first and then their
 // wave sums side by side, summed per wave into sdot. Unless the window ends here, a' and K' go
