@@ -8,7 +8,9 @@
 * pool4096: the benchmark's configuration: a 4,096-slot DAMP pool, 1,024 random active slots,
             one step with the benchmark's first input set, launched as the benchmark launches it
             (damp_batch_order, then the step in slot order); every active unit compared, every
-            inactive block checked bit-identical.
+            inactive block checked bit-identical. Then every slot of that pool at once (131,072
+            units, the largest batch it takes): 64 sampled slots against the oracle, every unit
+            against the properties a correct step leaves.
 * drift:    the 64-slot state run for 2,048 steps in all three formats on the GPU; the oracle runs
             the same steps for a sample of units, and at sampled steps the GPU restarts from the
             oracle's state for one step (identical-input parity). The per-step readout error of
@@ -162,6 +164,64 @@ def test_pool4096_full_size():
     eq = min(x["code_eq_frac"] for x in stats)
     _log(f"pool4096: min code_eq_frac over chunks {eq:.6f}, max fp16 ulp "
          f"{max(x['fp16_max_ulp'] for x in stats)}, max scale rel {max(x['scale_max_rel'] for x in stats):.3g}")
+
+
+def test_pool4096_every_slot_active():
+    """The largest batch the benchmark's pool takes: all 4,096 slots (131,072 units) in one
+    ordered launch, the slots in a seeded random order. The pool starts from random blocks made
+    on the device (FP16 rows ~N(0, 0.05^2), INT8 codes uniform in [-100, 100], scales uniform in
+    [1e-3, 2e-3)). 64 sampled slots are compared with the oracle element by element; every unit
+    is checked for what any correct step leaves: each INT8 row with a nonzero scale holds a code
+    of magnitude 127 (a block left unwritten still stops at 100), scales finite and >= 0, FP16
+    rows and readouts finite."""
+    w = synth.POOL4096
+    n_slots, H, D, r = w.pool_slots, w.heads, w.d, w.fp16_rows
+    rows = synth.pool4096_rows()
+    mask = synth.rows_to_mask(rows, D)
+    st = lib.DampState(n_slots, H, D, rows)
+    blocks = st.blocks()
+    o1, o2 = 2 * r * D, 2 * r * D + (D - r) * D
+    g = torch.Generator(device="cuda").manual_seed(40960)
+    blocks[:, :, :o1] = (torch.randn((n_slots, H, r * D), generator=g, device="cuda") * 0.05).half().view(torch.uint8)
+    blocks[:, :, o1:o2] = torch.randint(-100, 101, (n_slots, H, (D - r) * D), generator=g, device="cuda",
+                                        dtype=torch.int8).view(torch.uint8)
+    blocks[:, :, o2:o2 + 4 * (D - r)] = (torch.rand((n_slots, H, D - r), generator=g, device="cuda") * 1e-3
+                                         + 1e-3).view(torch.uint8)
+    rng = np.random.default_rng([w.seed, 40])
+    slots = rng.permutation(n_slots).astype(np.int32)
+    B = n_slots
+    inp = synth.step_inputs(rng, B, H, D, synth.GDN, "bf16")
+    pick = np.sort(rng.choice(B, 64, replace=False))
+    sel = torch.from_numpy(slots[pick]).long().cuda()
+    h, c, s = layout_ref.unpack(rows, blocks[sel].cpu().numpy(), D)
+    q, k, v, a, b = step_tensors(inp)
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    slots_dev = to_dev(slots)
+    _log(f"pool4096, every slot: {B * H} units")
+    st.decode_step(slots_dev, q, k, v, a, b, out, order=st.batch_order(slots_dev))
+    torch.cuda.synchronize()
+
+    n = len(pick) * H
+    maskn = np.broadcast_to(mask, (len(pick), H, D)).reshape(n, D)
+    vecs = tuple(x[pick] for x in (inp.q, inp.k, inp.v, inp.alpha, inp.beta))
+    ref_out = oracle.step_quant(maskn, h.reshape(n, D, D), c.reshape(n, D, D), s.reshape(n, D),
+                                *(x.reshape(n, -1) if x.ndim == 3 else x.reshape(n) for x in vecs))
+    check_readout(out[torch.from_numpy(pick).long().cuda()].cpu().numpy(), ref_out)
+    stats = check_quant(mask, layout_ref.unpack(rows, blocks[sel].cpu().numpy(), D), (h, c, s))
+
+    codes = blocks[:, :, o1:o2].contiguous().view(torch.int8).view(n_slots, H, D - r, D)
+    scales = blocks[:, :, o2:o2 + 4 * (D - r)].contiguous().view(torch.float32)
+    f16 = blocks[:, :, :o1].contiguous().view(torch.float16)
+    peak = codes.to(torch.int16).abs().amax(dim=-1)
+    assert bool(torch.isfinite(scales).all()) and bool((scales >= 0).all()), "a scale is negative or not finite"
+    live = scales > 0
+    assert bool((peak[live] == 127).all()), \
+        f"{int((peak[live] != 127).sum())} INT8 rows with a nonzero scale have no code of magnitude 127"
+    assert bool((peak[~live] == 0).all()), "an INT8 row with scale 0 has a nonzero code"
+    assert bool(torch.isfinite(f16).all()), "an FP16 row holds a non-finite value"
+    assert bool(torch.isfinite(out).all()), "a readout is not finite"
+    _log(f"pool4096, every slot: sample code_eq_frac {stats['code_eq_frac']:.6f}, "
+         f"{int(live.sum())} live INT8 rows checked")
 
 
 # ------------------------------------------------------------------------------------------
