@@ -5,7 +5,7 @@ tolerances the tests state.
 Tolerances (GPU vs oracle, from identical input states):
   readout                elementwise |got - ref| <= 1e-5 + 1e-3 |ref|
   INT8 codes             >= 99.9% equal, |delta| <= 1 everywhere
-  FP16 rows              <= 1 ulp of binary16
+  FP16 rows              <= 1 ulp of binary16; infinities bit for bit
   INT8 scales            |got - ref| <= 1e-6 |ref| (exact when ref == 0)
   fp32 state             |got - ref| <= the worst-case binary32 error bound of the step's
                          arithmetic (fp32_state_bound below), computed per element
@@ -134,6 +134,11 @@ def check_quant(mask, got, ref, scale_abs=0.0):
         ulp = np.abs(_f16_ord(hg[m]) - _f16_ord(hr[m]))
         stats["fp16_max_ulp"] = int(ulp.max())
         assert ulp.max() <= 1, f"FP16 rows: max {ulp.max()} ulp"
+        # an infinity is one step from the largest finite value in that order: where either side
+        # is not finite, the bits must agree
+        nf = ((hg[m] & 0x7C00) == 0x7C00) | ((hr[m] & 0x7C00) == 0x7C00)
+        stats["fp16_nonfinite"] = int(nf.sum())
+        assert np.array_equal(hg[m][nf], hr[m][nf]), "FP16 rows: a non-finite value differs"
     if (~m).any():
         d = np.abs(cg[~m].astype(np.int32) - cr[~m].astype(np.int32))
         eq = float((d == 0).mean())

@@ -310,11 +310,14 @@ def test_step_rows_with_subnormal_scales():
         assert (np.abs(got[1][:, h, i].astype(int)).max(axis=-1) >= 120).all()
 
 
-@pytest.mark.parametrize("case", ["identity", "full_forget", "zero_rows", "tiny", "large", "zero_v_beta1"])
+@pytest.mark.parametrize("case", ["identity", "full_forget", "zero_rows", "tiny", "large", "zero_v_beta1",
+                                  "fp16_overflow", "fp16_subnormal"])
 def test_degenerate_inputs(case):
     """Degenerate steps against the oracle: alpha = 1 with beta = 0 (the state must come back
     unchanged), alpha = 0 (the state is replaced by beta k v^T), all-zero rows (scale 0), very
-    small and large magnitudes, and v = 0 with beta = 1 (the key direction is erased)."""
+    small and large magnitudes, v = 0 with beta = 1 (the key direction is erased), v scaled by
+    2^20 so that many FP16 entries round to infinity, and a state scaled by 1e-5 with v = 0 so
+    that the FP16 rows land in binary16's subnormal range."""
     B, H, D, r = 4, 3, 128, 24
     rows, S, inp = _random_case(77, B, H, D, r, synth.GDN, "bf16")
     if case == "identity":
@@ -333,10 +336,25 @@ def test_degenerate_inputs(case):
         inp = synth.StepInputs(inp.q, inp.k, np.zeros_like(inp.v), inp.alpha,
                                np.ones_like(inp.beta), inp.dtype, inp.q_bits, inp.k_bits,
                                np.zeros_like(inp.v_bits))
+    elif case == "fp16_overflow":
+        v = (inp.v * np.float32(2.0 ** 20)).astype(np.float32)   # exact: a power of two
+        inp = synth.StepInputs(inp.q, inp.k, v, inp.alpha, inp.beta, inp.dtype, inp.q_bits,
+                               inp.k_bits, (v.view(np.uint32) >> 16).astype(np.uint16))
+    elif case == "fp16_subnormal":
+        S *= np.float32(1e-5)
+        inp = synth.StepInputs(inp.q, inp.k, np.zeros_like(inp.v), inp.alpha, inp.beta,
+                               inp.dtype, inp.q_bits, inp.k_bits, np.zeros_like(inp.v_bits))
     mask, out, got, ref_out, ref, _ = _damp_ref_and_gpu(rows, S, inp, np.arange(B), B)
     check_readout(out, ref_out)
     stats = check_quant(mask, got, ref)
     _log(f"{case}: {stats}")
+    f16 = np.broadcast_to(mask, (B, H, D)).astype(bool)
+    if case == "fp16_overflow":
+        inf = (ref[0][f16] & 0x7FFF) == 0x7C00
+        assert 0 < inf.sum() < inf.size, "the case should round some FP16 entries, not all, to infinity"
+    if case == "fp16_subnormal":
+        e = ref[0][f16] & 0x7FFF
+        assert ((e > 0) & (e < 0x0400)).mean() > 0.5, "most FP16 entries should be subnormal"
     if case == "identity":
         # the oracle's state came back unchanged; the GPU's codes equal the input codes exactly
         m = np.broadcast_to(mask, (B, H, D)).reshape(B * H, D)

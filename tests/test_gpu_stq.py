@@ -67,6 +67,8 @@ def check_stq(bits, impact, got, ref, X_ref):
     piv = np.broadcast_to(bits == 16, (n, H, D))
     ulp = np.abs(_f16_ord(hg[piv]) - _f16_ord(hr[piv])) if piv.any() else np.zeros(1)
     assert ulp.max() <= 1, f"pivots: {ulp.max()} ulp"
+    nf = ((hg[piv] & 0x7C00) == 0x7C00) | ((hr[piv] & 0x7C00) == 0x7C00)
+    assert np.array_equal(hg[piv][nf], hr[piv][nf]), "pivots: a non-finite value differs"
     dcs = np.abs(_f16_ord(sg) - _f16_ord(sr))
     cs_eq = float((dcs == 0).mean())
     assert dcs.max() <= 1 and cs_eq >= 0.99, f"column scales: max {dcs.max()}, eq {cs_eq}"
