@@ -32,12 +32,13 @@
 // (the sign bit moved to bit 7), so every integer row converts with one signed-byte instruction
 // per value; the staged row multiplier carries the exact power-of-two inverse.
 //
-// Arithmetic of the fit. Column scales: binary64, as the fit's reading states it. Each lane
-// forms (w_i X_ij)^2 with w_i X_ij exact in binary64 and adds its rows' terms in order; the
-// column thread adds the lanes' partials in a fixed order, divides by the binary64 sum of w_i^2
-// and takes the square root (IEEE binary64 division and square root), rounded once to binary16
-// (through a round-to-odd binary32 value). Only the order of the sums differs from the oracle's,
-// so from the same X the scales agree unless a square root lies within ~1e-15 of a binary16 tie.
+// Arithmetic of the fit. Column scales: each lane sums (w_i X_ij)^2 over its rows in order
+// (pack: in binary64, w_i X_ij exact, so only the order of the sums differs from the oracle's
+// and pack's scales agree unless a square root lies within ~1e-15 of a binary16 tie; the step:
+// in binary32, within 5 binary32 ulps of the binary64 fit at d = 128, see the fit below); the
+// column thread adds the lanes' partials in binary64 in a fixed order, divides by the binary64
+// sum of w_i^2 and takes the square root (IEEE binary64 division and square root), rounded once
+// to binary16 (through a round-to-odd binary32 value).
 // The column thread also forms rcs_j = RN(1 / cs_j). Row factor: the row maximum m of |X_ij| rcs_j (pack: the quotient
 // corrected to the IEEE one by one residual step, exact because cs_j has an 11-bit significand),
 // divided by qmax with one multiply and one residual correction (correctly rounded for 7, 31 and
@@ -473,20 +474,42 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
     }
   }
 
-  // (5) the fit: column scales from the weighted column sums of squares, in binary64: each
-  // product (w_i X_ij)^2 rounded once, the lane's rows added in order, then the lanes' partials
+  // (5) the fit: column scales from the weighted column sums of squares. Each lane sums its rows'
+  // (w_i X_ij)^2 in order; the column thread adds the lanes' partials in binary64. Pack forms
+  // the lane sums in binary64 too (each w_i X_ij exact, each square-and-add rounded once). The
+  // step forms them in binary32 (w_i X_ij rounded, then one fma per row): for RPL positive
+  // terms that is within (RPL + 2) u of the exact sum (u = 2^-24), so the column scale before
+  // its binary16 rounding is within (RPL + 2) u / 2 = 5u (d = 128) of the binary64 fit of the
+  // same X, and the two can differ only where that value lies so close to a binary16 tie.
   {
     double acc[CPL];
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = 0.0;
+      for (int c = 0; c < CPL; ++c) acc[c] = 0.0;
 #pragma unroll
-    for (int t = 0; t < RPL; ++t) {
-      const double w1 = sm.sw1[t * RPS + w * 4 + rs];
+      for (int t = 0; t < RPL; ++t) {
+        const double w1 = sm.sw1[t * RPS + w * 4 + rs];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const double y = w1 * static_cast<double>(X[t][c]);   // exact: two 24-bit significands
-        acc[c] = fma(y, y, acc[c]);
+        for (int c = 0; c < CPL; ++c) {
+          const double y = w1 * static_cast<double>(X[t][c]);   // exact: two 24-bit significands
+          acc[c] = fma(y, y, acc[c]);
+        }
       }
+    } else {
+      float accf[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) accf[c] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < RPL; ++t) {
+        const float w1 = sm.sw1[t * RPS + w * 4 + rs];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const float y = w1 * X[t][c];
+          accf[c] = fmaf(y, y, accf[c]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = static_cast<double>(accf[c]);
     }
     store_bytes<CPL * 8>(reinterpret_cast<uint8_t*>(&sm.red64[w * 4 + rs][cg * CPL]),
                          reinterpret_cast<const uint32_t*>(acc));
