@@ -423,7 +423,9 @@ damp_status damp_allocate_rows(const double* score, int32_t num_heads, int32_t d
  * prints no formula: the formulas are the library's reading. stq_state_quantize takes every
  * decision as written (its sums add in another order than a sequential loop, which can only
  * matter within ~1e-15 of a binary16 tie); inside
- * stq_decode_step the row maximum and the codes use products with rounded reciprocals, so a
+ * stq_decode_step each thread's partial sum of w_i^2 X_ij^2 over its 8 rows is binary32 (a column
+ * scale within 5 binary32 ulps of the binary64 value, so it can differ only that close to a
+ * binary16 tie), and the row maximum and the codes use products with rounded reciprocals, so a
  * code can differ by one where its quotient lies within a few ulps of a half-integer.
  * Block of (slot, head): storage rows ordered pivots, 8-bit, 6-bit, 4-bit (each by ascending key
  * index): FP16 pivot rows (2 d bytes each) | 8-bit rows (d bytes) | 6-bit rows (3 d / 4 bytes: d / 2
