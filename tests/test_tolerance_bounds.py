@@ -1,0 +1,95 @@
+"""CPU checks of the error bounds the GPU tests take as tolerance windows (no GPU, no library).
+
+The STEPQuant-style step sums each lane's rows of (w_i X_ij)^2 in binary32 (w_i X_ij rounded,
+then one fused multiply-add per row, 8 rows per lane at d = 128 and d = 64) and adds the 16 lane
+partials, divides by the sum of w_i^2 and takes the square root in binary64. For positive terms
+that lane sum is within (8 + 2) u of the exact one (u = 2^-24), so the column scale before its
+binary16 rounding is within 5u (relative) of the binary64 fit of the same X. The GPU test allows
+a column scale to differ from the oracle's only where the oracle's value lies within 1e-6 of a
+binary16 tie, which needs this 5u (3e-7) plus the few ulps by which the device's X differs.
+Here the device's arithmetic is emulated exactly (each binary32 product and fused
+multiply-add rounded once from its exact rational value) on random and adversarial columns,
+against exact sums.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+
+U = 2.0 ** -24
+ROWS_PER_LANE = 8
+LANES = 16
+
+
+def _round32(q):
+    """The binary32 value nearest the rational q, ties to even (one rounding)."""
+    f = np.float32(float(q))
+    best = None
+    for g in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        d = abs(Fraction(float(g)) - q)
+        even = (int(np.array(g, np.float32).view(np.uint32)) & 1) == 0
+        if best is None or d < best[0] or (d == best[0] and even):
+            best = (d, g)
+    return best[1]
+
+
+def _fma32(a, b, c):
+    """fl32(a * b + c), rounded once from the exact value."""
+    return _round32(Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c)))
+
+
+def _device_scale(w, x):
+    """w [128], x [128] (binary32): the column scale before its binary16 rounding, as the step
+    forms it: partial l (a lane's row slot) holds rows l, l + 16, ..., l + 112 in that order, and
+    the column thread adds the partials in index order."""
+    parts = []
+    for lane in range(LANES):
+        acc = np.float32(0.0)
+        for t in range(ROWS_PER_LANE):
+            i = t * LANES + lane
+            y = _round32(Fraction(float(w[i])) * Fraction(float(x[i])))
+            acc = _fma32(y, y, acc)
+        parts.append(float(acc))
+    s = 0.0
+    for p in parts:
+        s += p
+    sw = math.fsum(float(v) ** 2 for v in w)
+    return math.sqrt(s / sw)
+
+
+def _exact_scale(w, x):
+    num = math.fsum((float(a) * float(b)) ** 2 for a, b in zip(w, x))
+    sw = math.fsum(float(v) ** 2 for v in w)
+    return math.sqrt(num / sw)
+
+
+def _columns(rng):
+    n = LANES * ROWS_PER_LANE
+    yield rng.lognormal(0, 1, n).astype(np.float32), rng.normal(0, 0.1, n).astype(np.float32)
+    w = rng.lognormal(0, 2, n).astype(np.float32)
+    x = rng.normal(0, 1, n).astype(np.float32)
+    x[rng.choice(n, 4, replace=False)] *= 300          # heavy rows
+    yield w, x
+    x = np.sort(np.abs(rng.normal(0, 1, n))).astype(np.float32)   # ascending, then descending
+    yield np.ones(n, np.float32), x
+    yield np.ones(n, np.float32), x[::-1].copy()
+    x = (2.0 ** rng.uniform(-30, 30, n)).astype(np.float32)        # magnitudes spread wide
+    yield rng.lognormal(0, 1, n).astype(np.float32), x
+    x = np.full(n, np.float32(1.0) + np.float32(U) * 3, np.float32)   # equal terms, every add rounds
+    yield np.ones(n, np.float32), x
+
+
+def test_stq_binary32_lane_sums_stay_within_five_ulps_of_the_binary64_fit():
+    rng = np.random.default_rng(20260)
+    worst = 0.0
+    for _ in range(40):
+        for w, x in _columns(rng):
+            exact = _exact_scale(w, x)
+            if exact == 0.0:
+                continue
+            rel = abs(_device_scale(w, x) - exact) / exact
+            worst = max(worst, rel)
+            assert rel <= 5 * U, f"relative error {rel:.3g} above 5u"
+    # the tolerance window of the GPU test holds this bound with room for the X differences
+    assert 5 * U < 1e-6 / 2
+    assert worst > 0.0
