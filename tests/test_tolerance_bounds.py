@@ -1,4 +1,5 @@
-"""CPU checks of the error bounds the GPU tests take as tolerance windows (no GPU, no library).
+"""CPU checks of the error bounds the GPU tests take as tolerance windows (no GPU): the
+STEPQuant-style fit's binary32 lane sums, and the fp32-state step's per-element bound.
 
 The STEPQuant-style step sums each lane's rows of (w_i X_ij)^2 in binary32 (w_i X_ij rounded,
 then one fused multiply-add per row, 8 rows per lane at d = 128 and d = 64) and adds the 16 lane
@@ -93,3 +94,47 @@ def test_stq_binary32_lane_sums_stay_within_five_ulps_of_the_binary64_fit():
     # the tolerance window of the GPU test holds this bound with room for the X differences
     assert 5 * U < 1e-6 / 2
     assert worst > 0.0
+
+
+def _fp32_step_emulated(S, alpha, k, v, beta):
+    """The fp32-state step in binary32, every operation rounded on its own (no fused
+    multiply-add, sums in row order): S' = a S, u = sum_i k_i S'_i, delta = beta (v - u),
+    X = S' + k delta^T."""
+    n, D, _ = S.shape
+    a = alpha.reshape(n, -1, 1) if alpha.ndim == 2 else alpha.reshape(n, 1, 1)
+    Sp = (a.astype(np.float32) * S).astype(np.float32)
+    u = np.zeros((n, D), np.float32)
+    for i in range(D):
+        u = (u + (k[:, i:i + 1] * Sp[:, i, :]).astype(np.float32)).astype(np.float32)
+    delta = (beta.reshape(n, 1).astype(np.float32) * (v - u).astype(np.float32)).astype(np.float32)
+    return (Sp + (k[:, :, None] * delta[:, None, :]).astype(np.float32)).astype(np.float32)
+
+
+def test_fp32_state_error_bound_covers_binary32_arithmetic():
+    """gpu_common.fp32_state_bound, the GPU tests' tolerance for the fp32-state step, holds for
+    binary32 arithmetic in a plain order against the oracle's binary64 step, on GDN and KDA
+    gates, on random states and on columns where v nearly cancels u."""
+    import oracle
+    from gpu_common import fp32_state_bound
+    rng = np.random.default_rng(31)
+    n, D = 6, 128
+    for per_key in (False, True):
+        for cancel in (False, True):
+            S = rng.normal(0, 0.3, (n, D, D)).astype(np.float32)
+            k = rng.normal(0, 1, (n, D))
+            k = (k / np.linalg.norm(k, axis=1, keepdims=True)).astype(np.float32)
+            q = rng.normal(0, 1, (n, D)).astype(np.float32)
+            alpha = rng.uniform(0.2, 1.0, (n, D) if per_key else n).astype(np.float32)
+            beta = rng.uniform(0.0, 1.0, n).astype(np.float32)
+            v = rng.normal(0, 1, (n, D)).astype(np.float32)
+            if cancel:   # v = the exact u, rounded: delta is all rounding
+                a = alpha.reshape(n, -1, 1) if per_key else alpha.reshape(n, 1, 1)
+                v = np.einsum("ni,nij->nj", k.astype(np.float64),
+                              a.astype(np.float64) * S.astype(np.float64)).astype(np.float32)
+            X_ref = S.copy()
+            oracle.step_fp32(X_ref, q, k, v, alpha, beta)
+            X = _fp32_step_emulated(S, alpha, k, v, beta)
+            bound = fp32_state_bound(S, alpha, k, v, beta, X_ref)
+            err = np.abs(X.astype(np.float64) - X_ref.astype(np.float64))
+            assert (err <= bound).all(), f"per_key={per_key} cancel={cancel}: {(err > bound).sum()} above"
+            assert err.max() > 0
