@@ -122,10 +122,12 @@ def _f16_ord(bits):
     return np.where(b & 0x8000, -(b & 0x7FFF), b)
 
 
-def check_quant(mask, got, ref, scale_abs=0.0):
+def check_quant(mask, got, ref, scale_abs=0.0, min_code_eq=0.999):
     """mask broadcastable to [n, H, D] (1 = FP16 row); got/ref = (h, c, s) logical arrays.
     scale_abs: an absolute allowance added to the scales' relative bound, for rows whose
-    arithmetic runs in the binary32 subnormal range (where rounding errors are absolute)."""
+    arithmetic runs in the binary32 subnormal range (where rounding errors are absolute).
+    min_code_eq: the equal-code fraction; a caller whose INT8 rows share one code pattern (a
+    rank-one state) lowers it and checks instead that every differing code sits at a tie."""
     hg, cg, sg = got
     hr, cr, sr = ref
     m = np.broadcast_to(mask, sr.shape).astype(bool)
@@ -145,7 +147,7 @@ def check_quant(mask, got, ref, scale_abs=0.0):
         stats["code_eq_frac"] = eq
         stats["code_max_abs"] = int(d.max())
         assert d.max() <= 1, f"INT8 codes differ by {d.max()}"
-        assert eq >= 0.999, f"INT8 codes equal on {eq:.6f} < 0.999"
+        assert eq >= min_code_eq, f"INT8 codes equal on {eq:.6f} < {min_code_eq}"
         sgv, srv = sg[~m].astype(np.float64), sr[~m].astype(np.float64)
         zero = srv == 0
         assert np.array_equal(sgv[zero], srv[zero]), "scale of an all-zero row is not 0"
