@@ -241,6 +241,55 @@ def test_step_edge_maps(name, D, decay, inplace):
     _log(f"{name} D={D}: " + str(_step_case(D, H, B, decay, "bf16", 0, 7 * D + len(name), inplace, bits, impact)))
 
 
+@pytest.mark.parametrize("case", ["zero", "zero_columns", "identity"])
+def test_step_degenerate(case):
+    """Degenerate STEPQuant-style steps: a zero state with v = 0 (every stored number and the
+    readout exactly 0), value columns that are zero in the state and in v (their column scales
+    exactly 0 on both sides, so those columns code 0 and the row factors come from the others),
+    and alpha = 1 with beta = 0 (the refit of the reconstructed state)."""
+    D, H, B = 128, 4, 6
+    rng, bits, impact, S = _state(91, B, H, D, 2)
+    inp = synth.step_inputs(rng, B, H, D, synth.KDA, "fp32")
+    zc = np.zeros(D, bool)
+    if case == "zero":
+        S[:] = 0.0
+        inp.v[:] = 0.0
+    elif case == "zero_columns":
+        zc[rng.choice(D, 9, replace=False)] = True
+        S[..., zc] = 0.0
+        inp.v[..., zc] = 0.0
+    else:
+        inp.alpha[:] = 1.0
+        inp.beta[:] = 0.0
+    st = lib.StqState(B, H, D, bits, impact)
+    sl = torch.arange(B, dtype=torch.int32, device="cuda")
+    st.quantize(to_dev(S), sl)
+    torch.cuda.synchronize()
+    start = layout_ref.stq_unpack(bits, st.slots()[sl.long()].cpu().numpy(), D)
+    q, k, v, a, be = step_tensors(inp)
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    st.decode_step(sl, q, k, v, a, be, out)
+    torch.cuda.synchronize()
+    got = layout_ref.stq_unpack(bits, st.slots()[sl.long()].cpu().numpy(), D)
+    n = B * H
+    bb = np.broadcast_to(bits, (B, H, D)).reshape(n, D)
+    ww = np.broadcast_to(impact, (B, H, D)).reshape(n, D)
+    ref_out, ref_state, X_ref = oracle.stq_step(bb, ww, *(x.reshape((n,) + x.shape[2:]) for x in start),
+                                                *ref_vectors(inp, B, H, D), return_x=True)
+    ref = tuple(x.reshape((B, H) + x.shape[1:]) for x in ref_state)
+    o = out.cpu().numpy()
+    check_readout(o, ref_out.reshape(B, H, D))
+    stats = check_stq(bits, impact, got, ref, X_ref.reshape(B, H, D, D))
+    _log(f"{case}: {stats}")
+    if case == "zero":
+        assert not o.any() and all(not x.any() for x in got) and all(not x.any() for x in ref)
+    if case == "zero_columns":
+        for x in (got[3], ref[3]):          # column scales, binary16 bits
+            assert not x[..., zc].any() and x[..., ~zc].all()
+        ints = np.broadcast_to(bits != 16, (B, H, D))
+        assert not got[1][ints][:, zc].any(), "a code in a zero column is not 0"
+
+
 def test_empty_batch_is_a_no_op():
     D, H = 128, 2
     rng, bits, impact, S = _state(3, 2, H, D)
