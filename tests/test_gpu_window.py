@@ -99,6 +99,51 @@ def test_window_steps_and_flush(D, r, B, H, W, decay, dtype, tokens):
     assert torch.equal(pool.state.blocks(), before)
 
 
+@pytest.mark.parametrize("case,decay", [("identity", synth.GDN), ("identity", synth.KDA),
+                                        ("full_forget", synth.GDN), ("mixed_gates", synth.KDA)])
+def test_window_degenerate(case, decay):
+    """One window of W = 4 tokens with degenerate gates: alpha = 1 and beta = 0 on every token
+    (the window end stores the codes and FP16 rows it started from, bit for bit); alpha = 0 on
+    every token (the state at the window end is k delta^T of its last token, rank one, so every
+    differing code must sit at a rounding tie, X in closed form); per key row gates of exactly 0
+    and 1 mixed with drawn ones."""
+    B, H, D, r, W = 5, 3, 128, 24, 4
+    rng, rows, mask, maskn, h, c, s = _setup(606, B, H, D, r, decay)
+    win = oracle.Window(maskn, h.copy(), c.copy(), s.copy(), W)
+    pool = DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D), np.arange(B), B)
+    wbuf = pool.state.window_buffer(W)
+    for tok in range(W):
+        inp = synth.step_inputs(rng, B, H, D, decay, "bf16")
+        if case == "identity":
+            inp.alpha[:] = 1.0
+            inp.beta[:] = 0.0
+        elif case == "full_forget":
+            inp.alpha[:] = 0.0
+        else:
+            sel = rng.integers(0, 3, inp.alpha.shape)
+            inp.alpha[sel == 0] = 0.0
+            inp.alpha[sel == 1] = 1.0
+        out = _gpu_step(pool, wbuf, W, pool.slot_dev, inp)
+        check_readout(out, win.step(*ref_vectors(inp, B, H, D)).reshape(B, H, D))
+    got = pool.logical()
+    ref = (win.h.reshape(B, H, D, D), win.c.reshape(B, H, D, D), win.s.reshape(B, H, D))
+    stats = check_quant(mask, got, ref, min_code_eq=0.0 if case == "full_forget" else 0.999)
+    _log(f"{case} (decay {decay}): {stats}")
+    f16 = np.broadcast_to(mask, (B, H, D)).astype(bool)
+    if case == "identity":
+        assert np.array_equal(got[1][~f16], c.reshape(B, H, D, D)[~f16])
+        assert np.array_equal(got[0][f16], h.reshape(B, H, D, D)[f16])
+    if case == "full_forget":
+        dl = inp.beta.reshape(B, H, 1).astype(np.float64) * inp.v.astype(np.float64)
+        X = (inp.k.astype(np.float64)[:, :, :, None] * dl[:, :, None, :]).astype(np.float32)
+        with np.errstate(divide="ignore", invalid="ignore"):   # FP16 rows carry scale 0 here
+            qt = X.astype(np.float64) / ref[2].astype(np.float64)[..., None]
+            tie = np.abs(np.abs(qt - np.floor(qt)) - 0.5)
+        differ = (got[1] != ref[1]) & ~f16[..., None]
+        assert (tie[differ] <= 1e-4).all(), "a code of the rank-one state differs away from a tie"
+        assert stats["code_eq_frac"] >= 0.99
+
+
 @pytest.mark.parametrize("W,tokens", [(4, 10), (8, 13)])
 def test_scalar_gate_window_with_mixed_input_types(W, tokens):
     """One gate per unit: a key from bf16 inputs is buffered as bf16 (exact), one from fp32
