@@ -259,7 +259,9 @@ damp_status damp_decode_step_sorted(damp_state* state, const int32_t* slot_idx, 
 /* Bytes of the window buffers of a whole pool (num_slots * num_heads units) for windows of
  * `window` tokens, 1 <= window <= 8; 0 if invalid. Per unit: round_up(4 (4 + d + 2 window d), 256).
  * The caller allocates them (256-byte aligned) and fills them with zero bytes once: a zero buffer
- * is a unit at the start of a window. */
+ * is a unit at the start of a window. A buffer whose token count lies outside [0, window) (not
+ * zero-filled, or last used with another window length) is read as a unit at the start of a
+ * window; no access leaves the unit's buffer whatever the buffer holds. */
 size_t damp_window_bytes(const damp_layout* layout, int32_t window);
 
 /* One token of a window for B requests, same arguments as damp_decode_step plus the window

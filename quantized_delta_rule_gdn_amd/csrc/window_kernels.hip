@@ -324,7 +324,11 @@ __device__ __forceinline__ void window_q_unit(const StepArgs& a, const UnitAddr&
   constexpr int T16 = PLAN == PLAN_FIXED ? NF : G::T16;
   constexpr int CPL = G::CPL, RPL = G::RPL, RW = Words<CPL * 2>::W;
   const WinPtr wp = win_ptr<D>(a, slot, head);
-  const int t = __builtin_amdgcn_readfirstlane(wp.hdr[0]);
+  // A count outside [0, window) (a buffer that was never zero-filled, or one last used with
+  // another window length) reads as an empty window: every term index then stays inside the
+  // unit's buffer, and t = 0 reads nothing else from it.
+  int t = __builtin_amdgcn_readfirstlane(wp.hdr[0]);
+  if (t < 0 || t >= a.window) t = 0;
   const uint32_t hdr3 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wp.hdr[3]));
   if (FLUSH_ONLY && t == 0) return;   // nothing pending (uniform over the workgroup)
   const bool ends = FLUSH_ONLY || t + 1 >= a.window;

@@ -144,6 +144,34 @@ def test_window_degenerate(case, decay):
         assert stats["code_eq_frac"] >= 0.99
 
 
+@pytest.mark.parametrize("decay", [synth.GDN, synth.KDA])
+def test_window_count_out_of_range_reads_as_an_empty_window(decay):
+    """A window buffer whose token count lies outside [0, W) (never zero-filled, or last used with
+    another window length), the rest of it random bytes, behaves as a zero buffer: three tokens
+    and a flush give the same readouts and the same pool, bit for bit."""
+    B, H, D, r, W = 6, 3, 128, 24, 4
+    rng, rows, mask, maskn, h, c, s = _setup(707, B, H, D, r, decay)
+    pools = [DampPool(rows, h.reshape(B, H, D, D), c.reshape(B, H, D, D), s.reshape(B, H, D),
+                      np.arange(B), B) for _ in range(2)]
+    zero = pools[0].state.window_buffer(W)
+    junk = pools[1].state.window_buffer(W)
+    g = torch.Generator(device="cuda").manual_seed(708)
+    junk.copy_(torch.randint(0, 256, junk.shape, generator=g, device="cuda", dtype=torch.int32).to(torch.uint8))
+    words = junk.view(torch.int32).view(B * H, -1)        # one row of words per unit's buffer
+    counts = [W, W + 1, 1000, -1, -5, 2 ** 31 - 1, -2 ** 31]
+    words[:, 0] = torch.tensor([counts[u % len(counts)] for u in range(B * H)], dtype=torch.int32,
+                               device="cuda")
+    for tok in range(3):
+        inp = synth.step_inputs(rng, B, H, D, decay, "bf16")
+        o0 = _gpu_step(pools[0], zero, W, pools[0].slot_dev, inp)
+        o1 = _gpu_step(pools[1], junk, W, pools[1].slot_dev, inp)
+        assert np.array_equal(o0, o1), f"token {tok}: readouts differ"
+    for p, wb in zip(pools, (zero, junk)):
+        p.state.window_flush(wb, W, p.slot_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(pools[0].state.blocks(), pools[1].state.blocks())
+
+
 @pytest.mark.parametrize("W,tokens", [(4, 10), (8, 13)])
 def test_scalar_gate_window_with_mixed_input_types(W, tokens):
     """One gate per unit: a key from bf16 inputs is buffered as bf16 (exact), one from fp32
