@@ -270,3 +270,46 @@ def test_sorted_step_rejects_bad_arguments_on_host():
     assert L.damp_decode_step_sorted(None, a, lib.SORTED_MAX_B, a, a, a, 0, a, 0, a, a,
                                      None) == lib.DAMP_ERR_INVALID_ARGUMENT
     assert "state is NULL" in lib.last_error()
+
+
+def test_header_is_plain_c99_and_the_library_links_from_c(tmp_path):
+    """tests/c/abi_from_c.c, built with gcc -std=c99 -pedantic -Werror against include/damp.h and
+    linked with libdamp.so, prints the host-side results of a few calls; each must equal the
+    same call made through the Python binding (no GPU involved)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc is not on PATH")
+    libdir = os.path.dirname(lib.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    src = os.path.join(os.path.dirname(__file__), "c", "abi_from_c.c")
+    subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-I",
+                    os.path.join(ROOT, "include"), src, "-L", libdir, "-ldamp",
+                    f"-Wl,-rpath,{libdir}", "-o", exe], check=True, capture_output=True, text=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.splitlines()
+    got = {ln.split(" ", 1)[0]: ln.split(" ", 1)[1] for ln in out}
+
+    L = lib.load()
+    big, small, bad = lib.layout(4096, 32, 128, 24), lib.layout(64, 2, 16, 2), lib.layout(0, 32, 128, 24)
+    r_per_head = np.array([2, 5], np.int32)
+    bits = np.array([16 if i % 16 < 2 else (8 if i % 16 < 6 else (6 if i % 16 < 11 else 4))
+                     for i in range(32)], np.uint8)
+    st = ctypes.c_void_p()
+    rc_alloc = L.damp_state_alloc(ctypes.byref(bad), None, None, 0, ctypes.byref(st))
+    err_alloc = L.damp_last_error().decode()
+    rc_step = L.damp_decode_step(None, None, 1, None, None, None, 1, None, 0, None, None, None)
+    err_step = L.damp_last_error().decode()
+    want = {
+        "block_bytes": str(L.damp_block_bytes(ctypes.byref(big))),
+        "block_data_bytes": str(L.damp_block_data_bytes(ctypes.byref(big))),
+        "state_bytes": str(L.damp_state_bytes(ctypes.byref(big))),
+        "window_bytes_8": str(L.damp_window_bytes(ctypes.byref(big), 8)),
+        "window_bytes_9": str(L.damp_window_bytes(ctypes.byref(big), 9)),
+        "state_bytes_per_head": str(L.damp_state_bytes_per_head(
+            ctypes.byref(small), r_per_head.ctypes.data_as(ctypes.c_void_p))),
+        "stq_state_bytes": str(L.stq_state_bytes(64, 2, 16, bits.ctypes.data_as(ctypes.c_void_p))),
+        "alloc_bad": f"{rc_alloc} {err_alloc}",
+        "step_null": f"{rc_step} {err_step}",
+    }
+    assert got == want
+    assert want["window_bytes_9"] == "0" and rc_alloc == lib.DAMP_ERR_INVALID_ARGUMENT
