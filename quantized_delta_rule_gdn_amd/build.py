@@ -82,7 +82,38 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
         if res.returncode != 0:
             raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
     os.replace(tmp, LIB)
+    build_c_callers()
     return LIB
+
+
+# C programs the tests run against the library (tests/c): one that includes the header as
+# pedantic C99 and calls the host-side entry points, one that takes a GPU step through the C ABI
+# with the HIP runtime only. Built next to their sources; skipped where gcc is missing.
+C_DIR = os.path.join(ROOT, "tests", "c")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_c_callers() -> list[str]:
+    import shutil
+    if shutil.which("gcc") is None:
+        return []
+    rpath = "-Wl,-rpath,$ORIGIN/../../quantized_delta_rule_gdn_amd"
+    inc = ["-I", os.path.join(ROOT, "include")]
+    jobs = [
+        ("abi_from_c", ["-std=c99", "-pedantic"], []),
+        ("step_from_c", ["-std=gnu11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include")],
+         ["-L", os.path.join(ROCM, "lib"), "-lamdhip64", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"]),
+    ]
+    built = []
+    for name, cflags, libs in jobs:
+        exe = os.path.join(C_DIR, name)
+        cmd = ["gcc", *cflags, "-Wall", "-Wextra", "-Werror", *inc, os.path.join(C_DIR, name + ".c"),
+               "-L", PKG, "-ldamp", *libs, rpath, "-o", exe]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"gcc failed on {name}.c:\n" + res.stdout + res.stderr)
+        built.append(exe)
+    return built
 
 
 if __name__ == "__main__":
