@@ -41,8 +41,10 @@
  * covers host-side validation and launch errors; a fault inside a kernel surfaces at the next
  * synchronisation of that stream (as a HIP error of the caller's runtime). States are updated
  * in place: within one call each listed slot must appear once (duplicates race; the result is
- * undefined), and only listed slots are read or written. With the environment variable
- * DAMP_DEBUG=1 the step calls copy slot_idx to the host first (synchronising the stream) and
+ * undefined), and only listed slots are read or written. A slot index outside [0, num_slots) is
+ * skipped by the kernels: nothing of that request is read or written (its readout rows are left
+ * as they were), so a bad index cannot send an access outside the pool. With the environment
+ * variable DAMP_DEBUG=1 the calls copy slot_idx to the host first (synchronising the stream) and
  * return DAMP_ERR_SLOT_INDEX for an index outside [0, num_slots) or a repeated one.
  *
  * Pointers. "dev" pointers are device (HBM) addresses, "host" pointers host memory. The caller

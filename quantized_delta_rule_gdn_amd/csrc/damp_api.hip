@@ -256,6 +256,7 @@ damp::StqArgs stq_args(const stq_state* s) {
   damp::StqArgs a{};
   const size_t H = static_cast<size_t>(s->num_heads), d = static_cast<size_t>(s->d);
   a.pool = s->pool;
+  a.num_slots = s->num_slots;
   a.slot_stride = static_cast<int64_t>(s->slot_bytes);
   a.rowmap = s->table_dev;
   a.w1 = reinterpret_cast<const float*>(s->table_dev + H * d);
@@ -330,6 +331,7 @@ damp_status run_step(int fmt, const damp::StateRef& ref, int32_t d, int32_t H, i
   damp::StepArgs a{};
   a.order = order;
   a.st = ref;
+  a.st.num_slots = num_slots;
   a.slot_idx = slot_idx;
   a.B = B;
   a.H = H;
@@ -570,6 +572,7 @@ damp_status damp_state_quantize(damp_state* s, const float* S, const int32_t* sl
   if (r != DAMP_OK) return r;
   damp::PackArgs a{};
   a.st = damp_ref(s);
+  a.st.num_slots = s->layout.num_slots;
   a.slot_idx = slot_idx;
   a.n = n;
   a.H = s->layout.num_heads;
@@ -590,6 +593,7 @@ damp_status damp_state_dequantize(const damp_state* s, float* S, const int32_t* 
   if (r != DAMP_OK) return r;
   damp::PackArgs a{};
   a.st = damp_ref(s);
+  a.st.num_slots = s->layout.num_slots;
   a.slot_idx = slot_idx;
   a.n = n;
   a.H = s->layout.num_heads;
@@ -812,6 +816,7 @@ damp_status uniform_int8_quantize(int8_t* codes, float* scales, int32_t num_slot
   if (r != DAMP_OK) return r;
   damp::PackArgs a{};
   a.st = int8_ref(codes, scales, d_k);
+  a.st.num_slots = num_slots;
   a.slot_idx = slot_idx;
   a.n = n;
   a.H = H;

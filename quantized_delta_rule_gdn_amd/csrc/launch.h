@@ -35,6 +35,7 @@ struct StateRef {
   int64_t slot_stride;
   int32_t heads_r_or;
   int32_t heads_r_max;
+  int32_t num_slots;          // slots in the pool: a slot index outside [0, num_slots) is skipped
 };
 
 struct StepArgs {
@@ -94,6 +95,7 @@ struct StqArgs {
   const float* w1;
   const uint8_t* rowmap;
   const int32_t* slot_idx;
+  int32_t num_slots;        // a slot index outside [0, num_slots) is skipped
   int32_t B;                // units = B * H
   int32_t H;
   float* S;                 // pack / unpack: fp32 [B][H][d][d], key rows in original order

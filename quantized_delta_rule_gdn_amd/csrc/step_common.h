@@ -549,6 +549,14 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Whether a slot index addresses the pool. Distinct indices in [0, num_slots) are the caller's
+// contract (DAMP_DEBUG checks it on the host); a workgroup whose slot lies outside returns before
+// it touches the pool, its window buffer or its readout, so a bad index cannot send an access
+// outside them.
+__device__ __forceinline__ bool slot_in_pool(int64_t slot, int32_t num_slots) {
+  return static_cast<uint64_t>(slot) < static_cast<uint64_t>(static_cast<uint32_t>(num_slots));
+}
+
 // The unit of this workgroup: head = w mod H of batch position order[w / H] (w / H without an
 // order). False for an order entry outside [0, B): the workgroup then does nothing.
 __device__ __forceinline__ bool unit_of(const StepArgs& a, int& b, int& head) {

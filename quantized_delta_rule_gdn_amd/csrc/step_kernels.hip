@@ -24,7 +24,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void step_kernel_f32(const StepArgs a) 
   const int bh = __builtin_amdgcn_workgroup_id_x();  // b * H + head
   const int b = bh / a.H;
   const int head = bh - b * a.H;
-  const UnitAddr ua = unit_addr<D, FMT_F32>(a.st, a.slot_idx[b], head, a.H);
+  const int64_t slot = a.slot_idx[b];
+  const UnitAddr ua = unit_addr<D, FMT_F32>(a.st, slot, head, a.H);   // arithmetic only
+  if (!slot_in_pool(slot, a.st.num_slots)) return;
   const UnitPtr up = unit_ptr<D, FMT_F32>(ua, 0);
 
   // (1) the staging loads (per-row scalars, v), then every state load of this lane, so the
@@ -189,7 +191,9 @@ __global__ __launch_bounds__(64 * WAVES) void step_kernel_q(const StepArgs a) {
   int b, head;
   if (!unit_of(a, b, head)) return;
   const int bh = b * a.H + head;
-  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, a.slot_idx[b], head, a.H);
+  const int64_t slot = a.slot_idx[b];
+  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, slot, head, a.H);   // arithmetic only
+  if (!slot_in_pool(slot, a.st.num_slots)) return;
   step_q_unit<D, PER_KEY, BF16, PLAN, WAVES, NF>(a, ua, bh, head, sm);
 }
 
@@ -212,7 +216,9 @@ __global__ __launch_bounds__(64 * WAVES) void step_kernel_q_heads(const StepArgs
   int b, head;
   if (!unit_of(a, b, head)) return;
   const int bh = b * a.H + head;
-  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, a.slot_idx[b], head, a.H);
+  const int64_t slot = a.slot_idx[b];
+  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, slot, head, a.H);   // arithmetic only
+  if (!slot_in_pool(slot, a.st.num_slots)) return;
   step_q_heads_case<D, PER_KEY, BF16, WAVES, Geo<D, WAVES>::T16>(a, ua, bh, head, sm);
 }
 
@@ -227,7 +233,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void quantize_kernel(const PackArgs a) 
   const int ih = __builtin_amdgcn_workgroup_id_x();  // i * H + head
   const int i = ih / a.H;
   const int head = ih - i * a.H;
-  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, a.slot_idx[i], head, a.H);
+  const int64_t slot = a.slot_idx[i];
+  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, slot, head, a.H);   // arithmetic only
+  if (!slot_in_pool(slot, a.st.num_slots)) return;
   const int r = ua.r;
   const UnitPtr up = unit_ptr<D, FMT_Q>(ua, r);
 #pragma unroll
@@ -256,7 +264,9 @@ __global__ __launch_bounds__(Geo<D>::NT) void dequantize_kernel(const PackArgs a
   const int ih = __builtin_amdgcn_workgroup_id_x();
   const int i = ih / a.H;
   const int head = ih - i * a.H;
-  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, a.slot_idx[i], head, a.H);
+  const int64_t slot = a.slot_idx[i];
+  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, slot, head, a.H);   // arithmetic only
+  if (!slot_in_pool(slot, a.st.num_slots)) return;
   const int r = ua.r;
   const UnitPtr up = unit_ptr<D, FMT_Q>(ua, r);
 #pragma unroll

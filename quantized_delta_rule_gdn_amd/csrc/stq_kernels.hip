@@ -372,6 +372,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const int64_t boff = slot * a.slot_stride + a.heads[head].x;
   const rsrc_t src = make_rsrc(a.pool + boff, blk.bytes);
   const rsrc_t dst = make_rsrc((a.dst ? a.dst : a.pool) + boff, blk.bytes);
+  if (!slot_in_pool(slot, a.num_slots)) return;   // before any access through src or dst
   const uint8_t* rowmap = a.rowmap + head * D;
 
   float X[RPL][CPL];

@@ -496,7 +496,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4)))
   if (!unit_of(a, b, head)) return;
   const int bh = b * a.H + head;
   const int64_t slot = a.slot_idx[b];
-  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, slot, head, a.H);
+  const UnitAddr ua = unit_addr<D, FMT_Q>(a.st, slot, head, a.H);   // arithmetic only
+  if (!slot_in_pool(slot, a.st.num_slots)) return;
   if constexpr (HEADS)
     window_heads_case<D, PER_KEY, BF16, WAVES, Geo<D, WAVES>::T16, FLUSH_ONLY>(a, ua, slot, bh, head, sm);
   else
