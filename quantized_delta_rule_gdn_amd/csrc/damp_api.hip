@@ -35,6 +35,7 @@ struct stq_state {
   size_t slot_bytes;
   std::vector<int64_t> head_off;
   uint8_t* table_dev;   // rowmap [H][d] (uint8) | w2 [H][d] (fp32) | heads [H] (int4)
+  int32_t max_pivots;   // the largest number of pivot rows in one head
 };
 
 // The library-held order buffer of damp_decode_step_sorted: one copy of this file-scope device
@@ -264,6 +265,7 @@ damp::StqArgs stq_args(const stq_state* s) {
   a.H = s->num_heads;
   a.step.st.rowmap = s->table_dev;
   a.step.H = s->num_heads;
+  a.max_pivots = s->max_pivots;
   return a;
 }
 
@@ -934,6 +936,7 @@ damp_status stq_state_alloc(int32_t num_slots, int32_t H, int32_t d, const uint8
         ++p;
       }
     s->head_off[static_cast<size_t>(h)] = static_cast<int64_t>(off);
+    s->max_pivots = std::max(s->max_pivots, cnt[4 * h]);
     heads[4 * h] = static_cast<int32_t>(off);
     heads[4 * h + 1] = cnt[4 * h] | (cnt[4 * h + 1] << 8) | (cnt[4 * h + 2] << 16) | (cnt[4 * h + 3] << 24);
     std::memcpy(&heads[4 * h + 2], &sw, 8);   // the binary64 sum of w_i^2 over the integer rows

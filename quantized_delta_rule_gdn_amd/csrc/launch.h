@@ -99,6 +99,7 @@ struct StqArgs {
   int32_t B;                // units = B * H
   int32_t H;
   float* S;                 // pack / unpack: fp32 [B][H][d][d], key rows in original order
+  int32_t max_pivots;       // the largest number of pivot rows in one head
 };
 // mode 0 = decode step, 1 = pack, 2 = unpack; d is 64 or 128.
 hipError_t launch_stq(int mode, int d, int per_key, int bf16, const StqArgs& a, hipStream_t s);

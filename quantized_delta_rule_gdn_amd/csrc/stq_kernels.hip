@@ -49,6 +49,7 @@
 // qmax; only a row group holding a subnormal or zero row factor clamps.
 // The step may write its new state to another pool than it read (Table C2 step 6: the previous
 // copy stays intact while readers still use it).
+#include <cstdlib>
 #include <type_traits>
 
 #include "step_common.h"
@@ -129,6 +130,12 @@ __device__ __forceinline__ void by_kind(const StqBlock& blk, int p0, int p, F&& 
   on_kind<SK_I4>(k0, k3, mine, f);
 }
 
+// r 6-bit rows of 3 d / 4 bytes, as two shifts and an add (no quarter-rate integer multiply).
+template <int D>
+__device__ __forceinline__ int i6_row_bytes(int r) {
+  return r * (D / 2) + r * (D / 4);
+}
+
 // Byte offset of the lane's part of storage row p (kind K) in the block; I6: of its nibbles (its
 // top bits: stq_top_off).
 template <int D, int K>
@@ -137,14 +144,14 @@ __device__ __forceinline__ uint32_t stq_off(const StqBlock& b, int p, int cg) {
   if constexpr (K == SK_F16) return static_cast<uint32_t>(p * 2 * D + cg * 2 * CPL);
   if constexpr (K == SK_I8) return b.o8 + static_cast<uint32_t>((p - b.n16) * D + cg * CPL);
   if constexpr (K == SK_I6)
-    return b.o6 + static_cast<uint32_t>((p - b.n16 - b.n8) * (3 * D / 4) + cg * (CPL / 2));
+    return b.o6 + static_cast<uint32_t>(i6_row_bytes<D>(p - b.n16 - b.n8) + cg * (CPL / 2));
   return b.o4 + static_cast<uint32_t>((p - b.n16 - b.n8 - b.n6) * (D / 2) + cg * (CPL / 2));
 }
 
 template <int D>
 __device__ __forceinline__ uint32_t stq_top_off(const StqBlock& b, int p, int cg) {
   constexpr int CPL = D / 16;
-  return b.o6 + static_cast<uint32_t>((p - b.n16 - b.n8) * (3 * D / 4) + D / 2 + cg * (CPL / 4));
+  return b.o6 + static_cast<uint32_t>(i6_row_bytes<D>(p - b.n16 - b.n8) + D / 2 + cg * (CPL / 4));
 }
 
 // The lane's stored words of row p (kind K): F16 CPL halves, I8 CPL bytes, I6 / I4 CPL nibbles
@@ -594,6 +601,515 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   }
 }
 
+// ---- the decode step at d = 128 with the codes held ------------------------------------------
+// The kernel above holds the whole fp32 X of a unit (64 VGPRs per lane at d = 128), so a CU fits
+// four units, and issues ~21 VALU instructions per state element. This one keeps each row's
+// codes as they were stored (2 words per lane and row, FP16 pivot rows 4) until the update is
+// known, and takes the two column sums of Table C2 step 2 on the matrix cores:
+//  - Projections. For an integer row, S'_ij = gate_i rf_i cs_j c_ij, so
+//    u_j = cs_j sum_i z_i c_ij + (pivot rows) with z_i = gate_i rf_i k_i (q_i for p). The codes
+//    are exact int8 (6- and 4-bit codes as 4 c and 16 c, their factor in rf); each wave splits
+//    its 32 rows' z into four int8 pieces of 7 bits below a per-wave power of two (z = 2^-S
+//    (P0 + P1 2^-7 + P2 2^-14 + P3 2^-21) + e, |e| <= 2^-27 max|z|), so one v_mfma_i32_16x16x64_i8
+//    per pair of columns gives exact integer sums of pieces times codes for both k and q; the
+//    lanes then recombine the pieces (three roundings) and scale by 2^-S cs_j. Pivot rows are
+//    summed on the VALU.
+//  - The update in the old column scale's units: Y_ij = X_ij / g_j = gate_i rf_i c_ij +
+//    k_i delta_j / g_j, with g_j = cs_j (1 where cs_j = 0; the codes of such a column are
+//    masked to zero, which is what they reconstruct to). Pivot rows hold X_ij itself.
+//  - The fit reads Y: sum_i (w_i Y_ij)^2 in binary32 per lane, the column thread adds the
+//    partials in binary64 and multiplies by g_j^2 (exact); a row's maximum and codes use
+//    a_ij = Y_ij * RN(g_j / cs'_j), the quotient X_ij / cs'_j up to a few binary32 ulps.
+// Y is recomputed from the held codes for the codes (3 VALU instructions per element) rather than
+// kept: holding it takes 64 more VGPRs, four units per CU instead of six, and measured slower
+// (392 against 352 us on the pool of 1,024 active slots x 32 heads).
+// NP: row steps that may hold pivot rows (the host picks NP >= ceil(max pivots per head / 16)).
+typedef int stq_v4i __attribute__((ext_vector_type(4)));
+
+struct Stq2Smem {
+  float4 srow[128];   // {gate_p, k_p, q_p, rf_p / scale_p}, storage order
+  float sw1[128];     // w_p (0 for pivots)
+  float sv[128];      // v, then delta
+  float sd[128];      // delta / g_j
+  union {
+    float red[2][4][128];   // u and p: one partial per wave
+    float red2[16][128];    // the fit's lane partials (binary32), one per wave and row slot
+    float tmp[3 * 128];     // the staging's permutation to storage order
+  };
+  uint8_t apc[4][2][4][32];   // pieces of z: [wave][k | q][piece][g * 8 + t]
+  float redqk[4];
+  float sratio[128];  // g_j / cs'_j, 0 where cs'_j = 0
+  uint16_t srf[128];  // the new row factors (binary16 bits), integer-row order
+};
+
+// Row-kind dispatch for the codes-held step: a row group of one kind (nearly all of them) takes
+// a scalar branch on that kind, with no per-lane compare or exec-mask change; only a group that
+// straddles two kinds forms each lane's kind and runs the kinds under exec masks. F16OK = false
+// for row steps that cannot hold pivot rows.
+template <bool F16OK, typename F>
+__device__ __forceinline__ void by_kind2(const StqBlock& blk, int p0, int p, F&& f) {
+  const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3);
+  if (k0 == k3) {
+    if (F16OK && k0 == SK_F16) {
+      if constexpr (F16OK) f(std::integral_constant<int, SK_F16>{});
+    } else if (k0 == SK_I8) {
+      f(std::integral_constant<int, SK_I8>{});
+    } else if (k0 == SK_I6) {
+      f(std::integral_constant<int, SK_I6>{});
+    } else {
+      f(std::integral_constant<int, SK_I4>{});
+    }
+  } else {
+    int mine = stq_kind(blk, p);
+    asm volatile("" : "+v"(mine));
+    if constexpr (F16OK) on_kind<SK_F16>(k0, k3, mine, f);
+    on_kind<SK_I8>(k0, k3, mine, f);
+    on_kind<SK_I6>(k0, k3, mine, f);
+    on_kind<SK_I4>(k0, k3, mine, f);
+  }
+}
+
+// Where the lane's words of storage row p lie in the block, for a row of kind k: off = the
+// codes (pivot rows: the halves; 6-bit rows: the nibbles), offt = the 6-bit top bits.
+template <int D>
+__device__ __forceinline__ void stq_row_at(const StqBlock& b, int k, int p, int cg, uint32_t& off, uint32_t& offt) {
+  constexpr int CPL = D / 16;
+  const int b1 = b.n16, b2 = b1 + b.n8, b3 = b2 + b.n6;
+  const uint32_t base = k == SK_F16 ? 0u : (k == SK_I8 ? b.o8 : (k == SK_I6 ? b.o6 : b.o4));
+  const int first = k == SK_F16 ? 0 : (k == SK_I8 ? b1 : (k == SK_I6 ? b2 : b3));
+  const int stride = k == SK_F16 ? 2 * D : (k == SK_I8 ? D : (k == SK_I6 ? 3 * D / 4 : D / 2));
+  const int lw = k == SK_F16 ? 2 * CPL : (k == SK_I8 ? CPL : CPL / 2);
+  // 24-bit products: full-rate v_mad_u32_u24 (the row index and the stride are small and
+  // non-negative for the lane's own kind; offt is used only by 6-bit rows)
+  off = base + __umul24(static_cast<uint32_t>(p - first), static_cast<uint32_t>(stride)) + static_cast<uint32_t>(cg * lw);
+  offt = b.o6 + static_cast<uint32_t>(i6_row_bytes<D>(p - b2) + D / 2 + cg * (CPL / 4));
+}
+
+// The step's per-row scalars for the codes-held kernel (d = 128, 256 threads): every thread
+// issues the same loads (thread i and i + 128 the same row), none of them under a branch, before
+// the state loads; the raw words stay opaque until store(), so no wait for them lands between
+// the state loads. store() writes srow / sv / sw1 in storage order (two barriers) and returns
+// beta in a scalar register.
+template <int PER_KEY, int BF16>
+struct Stq2Stage {
+  static constexpr int D = 128;
+  uint32_t src, kv, qv, gv, vv, w1, rf, csj;
+  float g0, beta;
+
+  __device__ __forceinline__ void load(const StqArgs& a, rsrc_t rs, const StqBlock& blk, int bh, int head,
+                                       int tid) {
+    const int i = tid & (D - 1);
+    const int64_t vec = int64_t(bh) * D;
+    auto raw = [](const void* base, int64_t j) -> uint32_t {
+      if constexpr (BF16) return reinterpret_cast<const uint16_t*>(base)[j];
+      else return reinterpret_cast<const uint32_t*>(base)[j];
+    };
+    src = a.rowmap[head * D + i];
+    kv = raw(a.step.k, vec + i);
+    qv = raw(a.step.q, vec + i);
+    gv = PER_KEY ? reinterpret_cast<const uint32_t*>(a.step.alpha)[vec + i] : 0u;
+    vv = raw(a.step.v, vec + i);
+    w1 = __float_as_uint(a.w1[head * D + i]);
+    const int ri = i - blk.n16;
+    buf_load<2>(rs, blk.orf + 2u * static_cast<uint32_t>(ri < 0 ? 0 : ri), 0u, &rf);
+    buf_load<2>(rs, blk.ocs + 2u * static_cast<uint32_t>(i), 0u, &csj);
+    g0 = PER_KEY ? 0.0f : a.step.alpha[bh];
+    beta = a.step.beta[bh];
+  }
+
+  __device__ __forceinline__ void fence() {
+    asm volatile("" : "+v"(src), "+v"(kv), "+v"(qv), "+v"(gv), "+v"(vv), "+v"(w1), "+v"(rf), "+v"(csj));
+  }
+
+  __device__ __forceinline__ float store(const StqBlock& blk, int tid, float4* srow, float* sv, float* sw1,
+                                         float* tmp) {
+    fence();
+    auto widen = [](uint32_t w) { return BF16 ? __uint_as_float(w << 16) : __uint_as_float(w); };
+    if (tid < D) {
+      tmp[tid] = widen(kv);
+      tmp[D + tid] = widen(qv);
+      if constexpr (PER_KEY) tmp[2 * D + tid] = __uint_as_float(gv);
+      sv[tid] = widen(vv);
+      sw1[tid] = __uint_as_float(w1);
+    }
+    __syncthreads();
+    if (tid < D) {
+      const int j = static_cast<int>(src);
+      const int kind = stq_kind(blk, tid);   // exact: a power-of-two division of a binary16 value
+      const float rfs = tid < blk.n16 ? 1.0f
+                                      : half_bits_to_float(rf) *
+                                            (kind == SK_I6 ? 1.0f / kDecodeScale<SK_I6>
+                                                           : (kind == SK_I4 ? 1.0f / kDecodeScale<SK_I4> : 1.0f));
+      srow[tid] = make_float4(PER_KEY ? tmp[2 * D + j] : g0, tmp[j], tmp[D + j], rfs);
+    }
+    __syncthreads();
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(beta)));
+  }
+};
+
+// Signed byte k of x as a float (v_cvt_f32_i32 with a sign-extended byte select).
+__device__ __forceinline__ float sbyte_f(uint32_t x, int k) {
+  return static_cast<float>(static_cast<int8_t>(x >> (8 * k)));
+}
+
+// Canonical code words of a row: E holds the codes of the lane's even columns 0, 2, 4, 6 in
+// bytes 0..3, O those of the odd columns (6- and 4-bit codes as 4 c and 16 c).
+template <int K>
+__device__ __forceinline__ void stq_canon(uint32_t* w, uint32_t top) {
+  if constexpr (K == SK_I8) {
+    const uint32_t e = __builtin_amdgcn_perm(w[1], w[0], 0x06040200u);
+    const uint32_t o = __builtin_amdgcn_perm(w[1], w[0], 0x07050301u);
+    w[0] = e;
+    w[1] = o;
+  } else if constexpr (K == SK_I4) {
+    const uint32_t x = w[0];
+    w[0] = (x << 4) & 0xF0F0F0F0u;
+    w[1] = x & 0xF0F0F0F0u;
+  } else if constexpr (K == SK_I6) {
+    const uint32_t x = w[0];
+    const uint32_t y = __builtin_amdgcn_perm(0u, top, 0x01010000u);   // bytes t0 t0 t1 t1
+    const uint32_t t = (y & 0x000F000Fu) | ((y >> 4) & 0x0F000F00u);
+    w[0] = ((x << 2) & 0x3C3C3C3Cu) | ((t << 6) & 0xC0C0C0C0u);
+    w[1] = ((x >> 2) & 0x3C3C3C3Cu) | ((t << 4) & 0xC0C0C0C0u);
+  }
+}
+
+// The first of the two lane columns MFMA i reads (the second is 2 further): E bytes 0, 1 are
+// columns 0, 2; E bytes 2, 3 columns 4, 6; O bytes 0, 1 columns 1, 3; O bytes 2, 3 columns 5, 7.
+__device__ constexpr int kColOfMfma[4] = {0, 4, 1, 5};
+
+template <int PER_KEY, int BF16, int NP>
+__global__ __launch_bounds__(256) void stq_step2_kernel(const StqArgs a) {
+  constexpr int D = 128, NT = 256, CPL = 8, RPS = 16, RPL = 8;
+  constexpr float kMagic = 0x1.8p23f;
+  __shared__ Stq2Smem sm;
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, rs = lane >> 4, cg = lane & 15;
+  const int bh = __builtin_amdgcn_workgroup_id_x();
+  const int b = bh / a.H;
+  const int head = bh - b * a.H;
+  const int64_t slot = a.slot_idx[b];
+  const StqBlock blk = stq_block<D>(a, head);
+  const int64_t boff = slot * a.slot_stride + a.heads[head].x;
+  const rsrc_t src = make_rsrc(a.pool + boff, blk.bytes);
+  const rsrc_t dst = make_rsrc((a.dst ? a.dst : a.pool) + boff, blk.bytes);
+  if (!slot_in_pool(slot, a.num_slots)) return;   // before any access through src or dst
+
+  // (1) the per-row scalars' loads, then the stored state: each row step's words (pivot rows:
+  // 4 words of halves) and the lane's 8 old column scales
+  Stq2Stage<PER_KEY, BF16> stage;
+  stage.load(a, src, blk, bh, head, tid);
+  uint32_t csw[CPL / 2];   // before the state loads: the in-order counter then lets its wait pass them
+  buf_load<2 * CPL>(src, blk.ocs + 2u * cg * CPL, 0u, csw);
+  uint32_t cw[RPL][4];
+  uint32_t top[RPL];
+  // The loads are the same instructions for every kind (no load sits in a branch: the
+  // compiler would then wait for each row step's loads at the branches' join): 16 bytes in row
+  // steps that may hold pivot rows, else 8 (the codes of an 8-bit row; a 6- or 4-bit row uses
+  // the first 4, the rest is the next lane's part of the same lines), and the 2 bytes of a
+  // 6-bit row's top bits. Only the offsets depend on the kind: scalar for a group of one kind.
+#pragma unroll
+  for (int t = 0; t < RPL; ++t) {
+    const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
+    const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3);
+    uint32_t off, offt;
+    if (k0 == k3) {
+      stq_row_at<D>(blk, k0, p, cg, off, offt);
+    } else {
+      int mine = stq_kind(blk, p);
+      asm volatile("" : "+v"(mine));
+      stq_row_at<D>(blk, mine, p, cg, off, offt);
+    }
+    if (t < NP) {
+      buf_load<16>(src, off, 0u, cw[t]);
+    } else {
+      buf_load<8>(src, off, 0u, cw[t]);
+      cw[t][2] = cw[t][3] = 0u;
+    }
+    buf_load<2>(src, offt, 0u, &top[t]);
+  }
+
+  // (2) the codes put in canonical form as they arrive
+  float csf[CPL];
+  uint32_t mE = 0u, mO = 0u;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    csf[c] = half_bits_to_float(csw[c >> 1] >> (16 * (c & 1)));
+    const uint32_t nz = csf[c] > 0.0f ? 0xFFu : 0u;
+    if (c & 1) mO |= nz << (8 * (c >> 1));
+    else mE |= nz << (8 * (c >> 1));
+  }
+  const bool zero_cols = __any((mE & mO) != 0xFFFFFFFFu);   // wave-uniform
+  float cso[4];   // the old scales of the columns this lane's MFMA outputs land in
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cso[i] = (rs & 1) ? csf[kColOfMfma[i] + 2] : csf[kColOfMfma[i]];
+#pragma unroll
+  for (int t = 0; t < RPL; ++t) {
+    const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
+    auto canon = [&](auto KC) {
+      constexpr int K = decltype(KC)::value;
+      if constexpr (K != SK_F16) {
+        stq_canon<K>(cw[t], top[t]);
+        if (zero_cols) {
+          cw[t][0] &= mE;
+          cw[t][1] &= mO;
+        }
+      }
+    };
+    if (t < NP) by_kind2<true>(blk, p0, p, canon);
+    else by_kind2<false>(blk, p0, p, canon);
+  }
+  const uint32_t csj = stage.csj;
+  const float beta = stage.store(blk, tid, sm.srow, sm.sv, sm.sw1, sm.tmp);
+
+  // (3) the projection weights of this wave's 32 rows in int8 pieces: lane (k | q, j) takes
+  // row 16 (j / 4) + 4 w + j % 4; S = the wave's power of two for its half (k or q)
+  const int kq = lane >> 5;
+  int S;
+  {
+    const int j = lane & 31, tz = j >> 2, gz = j & 3;
+    const int row = tz * RPS + w * 4 + gz;
+    const float4 r4 = sm.srow[row];
+    const float z = row < blk.n16 ? 0.0f : r4.x * r4.w * (kq ? r4.z : r4.y);
+    // q.k over the wave's rows (the k half's lanes hold all 32 rows)
+    float qk = sum_row16(r4.y * r4.z);
+    {
+      const uint32_t u = __float_as_uint(qk);
+      const auto sw2 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      qk = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+    }
+    if (lane == 0) sm.redqk[w] = qk;
+    float zm = max_row16(fabsf(z));
+    {
+      const uint32_t u = __float_as_uint(zm);
+      const auto sw2 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      zm = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
+    }
+    S = zm > 0.0f ? 6 - __builtin_amdgcn_frexp_expf(zm) : 0;   // |z| 2^S < 64
+    float r = ldexpf(z, S);
+    uint32_t pc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float pk = rintf(r);
+      pc[k] = static_cast<uint32_t>(static_cast<int32_t>(pk)) & 0xFFu;
+      r = (r - pk) * 128.0f;   // exact
+    }
+    uint8_t* ap = &sm.apc[w][kq][0][gz * 8 + tz];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ap[32 * k] = static_cast<uint8_t>(pc[k]);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // A operand: lane (m = cg, g = rs), m = (k | q) * 8 + cc * 4 + piece; byte 2 t + cc' holds
+  // the piece of row 16 t + 4 w + g when cc' = cc, else 0
+  int aw[4];
+  {
+    const int kqa = cg >> 3, cca = (cg >> 2) & 1, pa = cg & 3;
+    uint32_t xw[2];
+    load_bytes<8>(&sm.apc[w][kqa][pa][rs * 8], xw);
+    const uint32_t s_even = cca ? 0x010c000cu : 0x0c010c00u;
+    const uint32_t s_odd = cca ? 0x030c020cu : 0x0c030c02u;
+    aw[0] = static_cast<int>(__builtin_amdgcn_perm(0u, xw[0], s_even));
+    aw[1] = static_cast<int>(__builtin_amdgcn_perm(0u, xw[0], s_odd));
+    aw[2] = static_cast<int>(__builtin_amdgcn_perm(0u, xw[1], s_even));
+    aw[3] = static_cast<int>(__builtin_amdgcn_perm(0u, xw[1], s_odd));
+  }
+  const stq_v4i Av = {aw[0], aw[1], aw[2], aw[3]};
+  // B operands: MFMA i takes two columns of the lane's 8 (i = 0: E bytes 0, 1 = columns 0, 2;
+  // 1: E bytes 2, 3 = 4, 6; 2: O bytes 0, 1 = 1, 3; 3: O bytes 2, 3 = 5, 7) for rows t = 0..7
+  stq_v4i acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int wd = i >> 1;
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+    int bw[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      bw[d] = static_cast<int>(__builtin_amdgcn_perm(cw[2 * d + 1][wd], cw[2 * d][wd], sel));
+    const stq_v4i Bv = {bw[0], bw[1], bw[2], bw[3]};
+    const stq_v4i zero = {0, 0, 0, 0};
+    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Av, Bv, zero, 0, 0, 0);
+  }
+  // recombine: lane (g = rs, cg) holds, for MFMA i, the four pieces of (k | q = g / 2) at
+  // column 8 cg + col(i, cc = g % 2)
+  const int kqo = rs >> 1, cco = rs & 1;
+  float vo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = fmaf(static_cast<float>(acc[i][3]), 0x1p-7f, static_cast<float>(acc[i][2]));
+    v = fmaf(v, 0x1p-7f, static_cast<float>(acc[i][1]));
+    v = fmaf(v, 0x1p-7f, static_cast<float>(acc[i][0]));
+    vo[i] = ldexpf(v, -S) * cso[i];
+  }
+  // pivot rows on the VALU, summed over the wave's row slots
+  bool wpiv = false;
+#pragma unroll
+  for (int t = 0; t < NP; ++t) wpiv |= t * RPS + w * 4 < blk.n16;
+  if (wpiv) {
+    float pvu[CPL], pvp[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) pvu[c] = pvp[c] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NP; ++t) {
+      const int p = t * RPS + w * 4 + rs;
+      if (p < blk.n16) {
+        const float4 r4 = sm.srow[p];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const float x = r4.x * half_bits_to_float(cw[t][c >> 1] >> (16 * (c & 1)));
+          pvu[c] = fmaf(r4.y, x, pvu[c]);
+          pvp[c] = fmaf(r4.z, x, pvp[c]);
+        }
+      }
+    }
+    // every column's sum over the row slots first: the lanes of different row slots select
+    // different columns afterwards
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      pvu[c] = sum_row_slots(pvu[c]);
+      pvp[c] = sum_row_slots(pvp[c]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c0 = kColOfMfma[i];
+      const float pu = cco ? pvu[c0 + 2] : pvu[c0];
+      const float pq = cco ? pvp[c0 + 2] : pvp[c0];
+      vo[i] += kqo ? pq : pu;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sm.red[kqo][w][cg * CPL + kColOfMfma[i] + 2 * cco] = vo[i];
+  __syncthreads();
+  // (4) columns: u, p, delta, the readout; delta / g_j for the integer rows
+  float gj = 1.0f;
+  if (tid < D) {
+    const int j = tid;
+    const float uu = ((sm.red[0][0][j] + sm.red[0][1][j]) + sm.red[0][2][j]) + sm.red[0][3][j];
+    const float pv = ((sm.red[1][0][j] + sm.red[1][1][j]) + sm.red[1][2][j]) + sm.red[1][3][j];
+    const float qk = ((sm.redqk[0] + sm.redqk[1]) + sm.redqk[2]) + sm.redqk[3];
+    const float dj = beta * (sm.sv[j] - uu);
+    a.step.out[int64_t(bh) * D + j] = fmaf(qk, dj, pv);
+    const float cs = half_bits_to_float(csj);
+    gj = cs > 0.0f ? cs : 1.0f;
+    sm.sv[j] = dj;
+    sm.sd[j] = __fdiv_rn(dj, gj);
+  }
+  __syncthreads();
+
+  // (5) the update and the fit's lane sums of (w_i Y_ij)^2. The held words are made opaque
+  // before each use, so the compiler cannot keep their decoded values (64 floats) from this
+  // pass to the next.
+#pragma unroll
+  for (int t = 0; t < RPL; ++t) asm volatile("" : "+v"(cw[t][0]), "+v"(cw[t][1]), "+v"(cw[t][2]), "+v"(cw[t][3]));
+  float dl[CPL];
+  load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sm.sd + cg * CPL), reinterpret_cast<uint32_t*>(dl));
+  float accf[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) accf[c] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < RPL; ++t) {
+    const int p = t * RPS + w * 4 + rs;
+    const float4 r4 = sm.srow[p];
+    const float wt = sm.sw1[p];
+    const bool piv_grp = t < NP && fresh_s(t * RPS + w * 4) < blk.n16;   // wave-uniform
+    // pivot rows (w = 0) take no part in the fit
+    if (!(piv_grp && p < blk.n16)) {
+      // w_i Y_ij = (w_i k_i) delta'_j + (w_i gate_i rf_i) c_ij: the weight folded into the row's
+      // two factors
+      const float wm = wt * (r4.x * r4.w), wk = wt * r4.y;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float yw = fmaf(wk, dl[c], wm * sbyte_f(cw[t][c & 1], c >> 1));
+        accf[c] = fmaf(yw, yw, accf[c]);
+      }
+    }
+  }
+  store_bytes<CPL * 4>(reinterpret_cast<uint8_t*>(&sm.red2[w * 4 + rs][cg * CPL]),
+                       reinterpret_cast<const uint32_t*>(accf));
+  __syncthreads();
+  if (tid < D) {
+    const int j = tid;
+    double s = static_cast<double>(sm.red2[0][j]);
+#pragma unroll
+    for (int k = 1; k < 16; ++k) s += static_cast<double>(sm.red2[k][j]);
+    const double g = static_cast<double>(gj);
+    const uint32_t hb = blk.sw > 0.0 ? f16_from_f64(sqrt(s * (g * g) / blk.sw)) : 0u;
+    const float cs = half_bits_to_float(hb);
+    sm.sratio[j] = cs > 0.0f ? __fdiv_rn(gj, cs) : 0.0f;
+    buf_store<2>(dst, blk.ocs + 2u * j, 0u, &hb);
+  }
+  __syncthreads();
+
+  // (6) per row: row factor, codes, store, with the row kind (and so qmax) known at compile time
+#pragma unroll
+  for (int t = 0; t < RPL; ++t) asm volatile("" : "+v"(cw[t][0]), "+v"(cw[t][1]), "+v"(cw[t][2]), "+v"(cw[t][3]));
+  float ratio[CPL];
+  load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sm.sratio + cg * CPL), reinterpret_cast<uint32_t*>(ratio));
+#pragma unroll
+  for (int t = 0; t < RPL; ++t) {
+    const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
+    float yr[CPL];
+    {
+      const float4 r4 = sm.srow[p];
+      const bool piv_grp = t < NP && p0 < blk.n16;
+      if (piv_grp && p < blk.n16) {
+        float dv[CPL];
+        load_bytes<CPL * 4>(reinterpret_cast<const uint8_t*>(sm.sv + cg * CPL), reinterpret_cast<uint32_t*>(dv));
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          yr[c] = fmaf(r4.y, dv[c], r4.x * half_bits_to_float(cw[t][c >> 1] >> (16 * (c & 1))));
+      } else {
+        const float m = r4.x * r4.w;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) yr[c] = fmaf(r4.y, dl[c], m * sbyte_f(cw[t][c & 1], c >> 1));
+      }
+    }
+    auto rowf = [&](auto KC) {
+      constexpr int K = decltype(KC)::value;
+      uint32_t tb[CPL];
+      if constexpr (K != SK_F16) {
+        constexpr float qm = K == SK_I8 ? 127.0f : (K == SK_I6 ? 31.0f : 7.0f);
+        constexpr float inv = 1.0f / qm;
+        float av[CPL];
+        float mq = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          av[c] = yr[c] * ratio[c];
+          mq = fmaxf(mq, fabsf(av[c]));
+        }
+        const float m = max_row16(mq);
+        const uint32_t rb = float_to_half_bits(div_qmax(m, qm, inv));
+        const float rf = half_bits_to_float(rb);
+        if (cg == 0) sm.srf[p - blk.n16] = static_cast<uint16_t>(rb);
+        // rf = 0 only where every a_j is 0, which then codes 0 with any finite factor
+        const float rrf = __builtin_amdgcn_rcpf(fmaxf(rf, 0x1p-126f));
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) tb[c] = __float_as_uint(fmaf(av[c], rrf, kMagic));
+        if (__any(rf < 0x1p-14f)) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+            tb[c] = __float_as_uint(__builtin_amdgcn_fmed3f(__uint_as_float(tb[c]), kMagic - qm, kMagic + qm));
+        }
+      }
+      stq_store<D, K>(dst, blk, p, cg, yr, tb);
+    };
+    if (t < NP) by_kind2<true>(blk, p0, p, rowf);
+    else by_kind2<false>(blk, p0, p, rowf);
+  }
+  // the row factors, gathered in LDS, go out as one contiguous run
+  __syncthreads();
+  const int nint = D - blk.n16;
+  for (int i = 2 * tid; i < nint; i += 2 * NT) {
+    const uint32_t two = sm.srf[i] | (i + 1 < nint ? static_cast<uint32_t>(sm.srf[i + 1]) << 16 : 0u);
+    if (i + 1 < nint)
+      buf_store<4>(dst, blk.orf + 2u * static_cast<uint32_t>(i), 0u, &two);
+    else
+      buf_store<2>(dst, blk.orf + 2u * static_cast<uint32_t>(i), 0u, &two);
+  }
+}
+
 template <int D, int NW, int MODE>
 hipError_t stq_launch_mode(int per_key, int bf16, const StqArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H)), block(NW * 64);
@@ -613,9 +1129,36 @@ hipError_t stq_launch_mode(int per_key, int bf16, const StqArgs& a, hipStream_t 
 template <int D>
 constexpr int kStqWaves = D >= 128 ? 4 : 2;
 
+template <int NP>
+hipError_t stq_step2_launch(int per_key, int bf16, const StqArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H)), block(256);
+  if (per_key) {
+    if (bf16) hipLaunchKernelGGL((stq_step2_kernel<1, 1, NP>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stq_step2_kernel<1, 0, NP>), grid, block, 0, s, a);
+  } else {
+    if (bf16) hipLaunchKernelGGL((stq_step2_kernel<0, 1, NP>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stq_step2_kernel<0, 0, NP>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// The d = 128 step runs the codes-held kernel; DAMP_STQ_STEP=x (read once) selects the X-held
+// kernel instead, for comparisons.
+bool stq_step_x_held() {
+  static const bool x = [] {
+    const char* e = getenv("DAMP_STQ_STEP");
+    return e && e[0] == 'x';
+  }();
+  return x;
+}
+
 template <int D>
 hipError_t stq_d(int mode, int per_key, int bf16, const StqArgs& a, hipStream_t s) {
   constexpr int NW = kStqWaves<D>;
+  if constexpr (D == 128) {
+    if (mode == SM_STEP && !stq_step_x_held())
+      return a.max_pivots <= 16 ? stq_step2_launch<1>(per_key, bf16, a, s) : stq_step2_launch<8>(per_key, bf16, a, s);
+  }
   if (mode == SM_STEP) return stq_launch_mode<D, NW, SM_STEP>(per_key, bf16, a, s);
   if (mode == SM_PACK) return stq_launch_mode<D, NW, SM_PACK>(per_key, bf16, a, s);
   return stq_launch_mode<D, NW, SM_UNPACK>(per_key, bf16, a, s);
