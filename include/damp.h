@@ -436,7 +436,9 @@ damp_status damp_allocate_rows(const double* score, int32_t num_heads, int32_t d
  * bytes of low nibbles, then d / 4 bytes of the top two bits: column c at bits 4 (c mod 2) of byte
  * c / 2 and 2 (c mod 4) of byte c / 4) | 4-bit rows (d / 2 bytes, nibbles as in the 6-bit rows' low
  * plane) | FP16 row factors of the integer rows (storage order) | FP16 column scales (d) | zero
- * padding to 256 bytes; codes are two's complement. A slot is its heads' blocks in order.
+ * padding to 256 bytes; each region after the pivots starts at the next multiple of 128 bytes
+ * (padding never read or written, so no cache line holds two regions); codes are two's
+ * complement. A slot is its heads' blocks in order.
  * Supported: d_k = d_v = d in {64, 128}.
  * ------------------------------------------------------------------------------------- */
 typedef struct stq_state stq_state;

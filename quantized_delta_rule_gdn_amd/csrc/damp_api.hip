@@ -225,9 +225,14 @@ damp_status launched(hipError_t e, const char* what) {
 // ---- STEPQuant-style layout (stq_*) ----------------------------------------------------------
 bool stq_supported_d(int32_t d) { return d == 64 || d == 128; }
 
+// The block's regions (pivots, 8-, 6-, 4-bit rows, row factors, column scales) each start on a
+// 128-byte line; the result is the end of the column scales (before the 256-byte rounding).
 size_t stq_block_bytes(int32_t d_, int n16, int n8, int n6, int n4) {
   const size_t d = static_cast<size_t>(d_);
-  return 2 * d * n16 + d * n8 + (3 * d / 4) * n6 + (d / 2) * n4 + 2 * (d - n16) + 2 * d;
+  auto up = [](size_t x) { return (x + 127) / 128 * 128; };
+  const size_t o8 = up(2 * d * n16), o6 = up(o8 + d * n8), o4 = up(o6 + (3 * d / 4) * n6);
+  const size_t orf = up(o4 + (d / 2) * n4), ocs = up(orf + 2 * (d - n16));
+  return ocs + 2 * d;
 }
 
 // Per-head counts of each code width; row_bits must hold 16, 8, 6 or 4.

@@ -15,7 +15,8 @@
 // Block of one (slot, head), storage rows ordered pivots, 8-bit, 6-bit, 4-bit (each ascending
 // key index): FP16 pivot rows (2 d bytes each) | 8-bit rows (d) | 6-bit rows (3 d / 4: a plane of
 // the low nibbles, d / 2 bytes, then a plane of the top two bits, d / 4 bytes) | 4-bit rows
-// (d / 2) | FP16 row factors of the integer rows | FP16 column scales (d) | zero padding to 256 B.
+// (d / 2) | FP16 row factors of the integer rows | FP16 column scales (d) | zero padding to 256 B;
+// each region after the pivots starts at the next multiple of 128 bytes (never-touched padding).
 // Codes are two's complement in their width. A lane owns CPL = d / 16 columns of a row, so its
 // codes of a row are CPL bytes (8-bit), CPL / 2 + CPL / 4 bytes (6-bit) or CPL / 2 bytes (4-bit):
 // d is 64 or 128.
@@ -74,11 +75,14 @@ __device__ __forceinline__ StqBlock stq_block(const StqArgs& a, int head) {
   b.n8 = (hi.y >> 8) & 0xff;
   b.n6 = (hi.y >> 16) & 0xff;
   b.n4 = (hi.y >> 24) & 0xff;
-  b.o8 = 2u * D * b.n16;
-  b.o6 = b.o8 + D * b.n8;
-  b.o4 = b.o6 + (3 * D / 4) * b.n6;
-  b.orf = b.o4 + (D / 2) * b.n4;
-  b.ocs = b.orf + 2 * (D - b.n16);
+  // every region starts on a 128-byte line, so no line holds two regions (a store never writes
+  // part of a line another store completes)
+  auto up = [](uint32_t x) { return (x + 127u) & ~127u; };
+  b.o8 = up(2u * D * b.n16);
+  b.o6 = up(b.o8 + D * b.n8);
+  b.o4 = up(b.o6 + (3 * D / 4) * b.n6);
+  b.orf = up(b.o4 + (D / 2) * b.n4);
+  b.ocs = up(b.orf + 2 * (D - b.n16));
   b.bytes = b.ocs + 2 * D;
   b.sw = __hiloint2double(hi.w, hi.z);
   return b;
@@ -804,27 +808,67 @@ __global__ __launch_bounds__(256) void stq_step2_kernel(const StqArgs a) {
   buf_load<2 * CPL>(src, blk.ocs + 2u * cg * CPL, 0u, csw);
   uint32_t cw[RPL][4];
   uint32_t top[RPL];
-  // The loads are the same instructions for every kind (no load sits in a branch: the
-  // compiler would then wait for each row step's loads at the branches' join): 16 bytes in row
-  // steps that may hold pivot rows, else 8 (the codes of an 8-bit row; a 6- or 4-bit row uses
-  // the first 4, the rest is the next lane's part of the same lines), and the 2 bytes of a
-  // 6-bit row's top bits. Only the offsets depend on the kind: scalar for a group of one kind.
+  // The loads are the same instructions for every kind: no load sits in a branch (the
+  // compiler would then wait for each row step's loads at the branches' join). Each reads
+  // exactly the bytes of its kind, and a lane whose row does not need it gets an offset past
+  // the block (the buffer's range check returns 0 without a memory access), so no line is
+  // fetched twice: 4 bytes at the row (every kind), 4 more (8-bit and pivot rows), 8 more
+  // (pivot rows, only in row steps that may hold them) and the 2 bytes of a 6-bit row's top
+  // bits. For a group of one kind the offsets are a scalar row base plus the lane's part for
+  // that kind (precomputed); a group that straddles two kinds forms them per lane.
+  constexpr uint32_t kOut = 0x80000000u;   // past any block: no access
+  const int b2 = blk.n16 + blk.n8;
+  uint32_t lp[4];   // the lane's byte offset within a row group of each kind: rs rows + cg parts
+  lp[SK_F16] = __umul24(rs, 2 * D) + cg * (2 * CPL);
+  lp[SK_I8] = __umul24(rs, D) + cg * CPL;
+  lp[SK_I6] = __umul24(rs, 3 * D / 4) + cg * (CPL / 2);
+  lp[SK_I4] = __umul24(rs, D / 2) + cg * (CPL / 2);
+  const uint32_t lpt = __umul24(rs, 3 * D / 4) + D / 2 + cg * (CPL / 4);
 #pragma unroll
   for (int t = 0; t < RPL; ++t) {
     const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
     const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3);
-    uint32_t off, offt;
+    const uint32_t sT = blk.o6 + static_cast<uint32_t>((p0 - b2) * (3 * D / 4));
+    uint32_t off, off4, off8 = kOut, offt;   // 4 bytes at off (all), 4 at off4, 8 at off8, 2 at offt
     if (k0 == k3) {
-      stq_row_at<D>(blk, k0, p, cg, off, offt);
+      // a scalar branch per kind; the empty volatile statements keep the compiler from turning
+      // them into per-lane selects
+      if (k0 == SK_F16) {
+        asm volatile("");
+        off = static_cast<uint32_t>(p0 * 2 * D) + lp[SK_F16];
+        off4 = off + 4u;
+        off8 = off + 8u;
+        offt = kOut;
+      } else if (k0 == SK_I8) {
+        asm volatile("");
+        off = blk.o8 + static_cast<uint32_t>((p0 - blk.n16) * D) + lp[SK_I8];
+        off4 = off + 4u;
+        offt = kOut;
+      } else if (k0 == SK_I6) {
+        asm volatile("");
+        off = sT + lp[SK_I6];
+        off4 = kOut;
+        offt = sT + lpt;
+      } else {
+        asm volatile("");
+        off = blk.o4 + static_cast<uint32_t>((p0 - b2 - blk.n6) * (D / 2)) + lp[SK_I4];
+        off4 = kOut;
+        offt = kOut;
+      }
     } else {
       int mine = stq_kind(blk, p);
       asm volatile("" : "+v"(mine));
-      stq_row_at<D>(blk, mine, p, cg, off, offt);
+      uint32_t ot;
+      stq_row_at<D>(blk, mine, p, cg, off, ot);
+      off4 = mine == SK_F16 || mine == SK_I8 ? off + 4u : kOut;
+      off8 = mine == SK_F16 ? off + 8u : kOut;
+      offt = mine == SK_I6 ? ot : kOut;
     }
+    buf_load<4>(src, off, 0u, &cw[t][0]);
+    buf_load<4>(src, off4, 0u, &cw[t][1]);
     if (t < NP) {
-      buf_load<16>(src, off, 0u, cw[t]);
+      buf_load<8>(src, off8, 0u, &cw[t][2]);
     } else {
-      buf_load<8>(src, off, 0u, cw[t]);
       cw[t][2] = cw[t][3] = 0u;
     }
     buf_load<2>(src, offt, 0u, &top[t]);

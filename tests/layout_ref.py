@@ -128,10 +128,25 @@ def stq_storage(row_bits_h: np.ndarray) -> np.ndarray:
     return np.concatenate([np.flatnonzero(row_bits_h == b) for b in STQ_WIDTHS])
 
 
-def stq_block_bytes(D: int, row_bits_h: np.ndarray) -> int:
+def _up128(x: int) -> int:
+    return (x + 127) // 128 * 128
+
+
+def stq_regions(D: int, row_bits_h: np.ndarray) -> dict:
+    """Byte offsets of a block's regions: each after the pivots starts on a 128-byte line."""
     n = {b: int((row_bits_h == b).sum()) for b in STQ_WIDTHS}
-    raw = 2 * D * n[16] + D * n[8] + 3 * D // 4 * n[6] + D // 2 * n[4] + 2 * (D - n[16]) + 2 * D
-    return (raw + 255) // 256 * 256
+    o = {16: 0}
+    o[8] = _up128(2 * D * n[16])
+    o[6] = _up128(o[8] + D * n[8])
+    o[4] = _up128(o[6] + 3 * D // 4 * n[6])
+    o["rf"] = _up128(o[4] + D // 2 * n[4])
+    o["cs"] = _up128(o["rf"] + 2 * (D - n[16]))
+    o["end"] = o["cs"] + 2 * D
+    return o
+
+
+def stq_block_bytes(D: int, row_bits_h: np.ndarray) -> int:
+    return (stq_regions(D, row_bits_h)["end"] + 255) // 256 * 256
 
 
 def _nibbles(codes: np.ndarray) -> np.ndarray:
@@ -154,26 +169,26 @@ def stq_pack(row_bits, h, c, rf, cs) -> np.ndarray:
     for hh in range(H):
         rb = row_bits[hh]
         order = stq_storage(rb)
-        parts = []
+        reg = stq_regions(D, rb)
         for u in range(n):
-            seg = []
+            blk = out[u, off:off + sizes[hh]]
             for b in STQ_WIDTHS:
                 rows = order[rb[order] == b]
                 if b == 16:
-                    seg.append(np.ascontiguousarray(h[u, hh][rows]).view(np.uint8).ravel())
+                    seg = np.ascontiguousarray(h[u, hh][rows]).view(np.uint8).ravel()
                 elif b == 8:
-                    seg.append(c[u, hh][rows].view(np.uint8).ravel())
+                    seg = c[u, hh][rows].view(np.uint8).ravel()
                 elif b == 6:
                     cc = c[u, hh][rows]
-                    seg.append(np.concatenate([_nibbles(cc), _tops(cc)], axis=1).ravel())
+                    seg = np.concatenate([_nibbles(cc), _tops(cc)], axis=1).ravel()
                 else:
-                    seg.append(_nibbles(c[u, hh][rows]).ravel())
+                    seg = _nibbles(c[u, hh][rows]).ravel()
+                blk[reg[b]:reg[b] + seg.size] = seg
             ints = order[rb[order] != 16]
-            seg.append(np.ascontiguousarray(rf[u, hh][ints]).view(np.uint8).ravel())
-            seg.append(np.ascontiguousarray(cs[u, hh]).view(np.uint8).ravel())
-            parts.append(np.concatenate(seg))
-        blk = np.stack(parts)
-        out[:, off:off + blk.shape[1]] = blk
+            seg = np.ascontiguousarray(rf[u, hh][ints]).view(np.uint8).ravel()
+            blk[reg["rf"]:reg["rf"] + seg.size] = seg
+            seg = np.ascontiguousarray(cs[u, hh]).view(np.uint8).ravel()
+            blk[reg["cs"]:reg["cs"] + seg.size] = seg
         off += sizes[hh]
     return out
 
@@ -205,8 +220,9 @@ def stq_unpack(row_bits, slots: np.ndarray, D: int):
     for hh in range(H):
         rb = row_bits[hh]
         order = stq_storage(rb)
-        o = off
+        reg = stq_regions(D, rb)
         for b in STQ_WIDTHS:
+            o = off + reg[b]
             rows = order[rb[order] == b]
             m = len(rows)
             if b == 16:
@@ -226,10 +242,10 @@ def stq_unpack(row_bits, slots: np.ndarray, D: int):
                 v = _from_nibbles(slots[:, o:o + nb].reshape(n * m, D // 2))
                 v = np.where(v >= 8, v - 16, v)
                 c[:, hh][:, rows, :] = v.reshape(n, m, D).astype(np.int8)
-            o += nb
         ints = order[rb[order] != 16]
+        o = off + reg["rf"]
         rf[:, hh][:, ints] = slots[:, o:o + 2 * len(ints)].copy().view(np.uint16).reshape(n, len(ints))
-        o += 2 * len(ints)
+        o = off + reg["cs"]
         cs[:, hh] = slots[:, o:o + 2 * D].copy().view(np.uint16).reshape(n, D)
         off += stq_block_bytes(D, rb)
     return h, c, rf, cs
