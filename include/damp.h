@@ -426,19 +426,25 @@ damp_status damp_allocate_rows(const double* score, int32_t num_heads, int32_t d
  * aware of key rows, one column-scale vector per head weighted by squared row-impact scores) but
  * prints no formula: the formulas are the library's reading. stq_state_quantize takes every
  * decision as written (its sums add in another order than a sequential loop, which can only
- * matter within ~1e-15 of a binary16 tie); inside
- * stq_decode_step each thread's partial sum of w_i^2 X_ij^2 over its 8 rows is binary32 (a column
- * scale within 5 binary32 ulps of the binary64 value, so it can differ only that close to a
- * binary16 tie), and the row maximum and the codes use products with rounded reciprocals, so a
- * code can differ by one where its quotient lies within a few ulps of a half-integer.
+ * matter within ~1e-15 of a binary16 tie). Inside stq_decode_step (d = 128) the column sums
+ * u = S'^T k and p = S'^T q are exact integer sums on the matrix cores of the codes times the row
+ * weights gate_i rf_i k_i (q_i), each split into four 7-bit pieces below a power of two (weights
+ * kept to 2^-27 of the largest in their wave), recombined in binary32; X is formed in units of
+ * the old column scale, Y_ij = X_ij / cs_j; each thread's partial sum of (w_i Y_ij)^2 over its 8
+ * rows is binary32 and the column thread multiplies the binary64 total by cs_j^2, so a column
+ * scale can differ from the binary64 fit of the same X only within a few binary32 ulps of a
+ * binary16 tie; the row maximum and the codes use Y_ij RN(cs_j / cs'_j) and a rounded reciprocal
+ * of the row factor, so a code can differ by one where its quotient lies within a few ulps of a
+ * half-integer. At d = 64 X is formed directly and the same bounds hold.
  * Block of (slot, head): storage rows ordered pivots, 8-bit, 6-bit, 4-bit (each by ascending key
  * index): FP16 pivot rows (2 d bytes each) | 8-bit rows (d bytes) | 6-bit rows (3 d / 4 bytes: d / 2
  * bytes of low nibbles, then d / 4 bytes of the top two bits: column c at bits 4 (c mod 2) of byte
  * c / 2 and 2 (c mod 4) of byte c / 4) | 4-bit rows (d / 2 bytes, nibbles as in the 6-bit rows' low
  * plane) | FP16 row factors of the integer rows (storage order) | FP16 column scales (d) | zero
- * padding to 256 bytes; each region after the pivots starts at the next multiple of 128 bytes
- * (padding never read or written, so no cache line holds two regions); codes are two's
- * complement. A slot is its heads' blocks in order.
+ * padding to 256 bytes. Each region after the pivots starts at the next multiple of 128 bytes,
+ * and the 6- and 4-bit rows start at the group of 4 storage rows holding their first row (lead
+ * rows of padding before it); padding is never read or written. Codes are two's complement. A
+ * slot is its heads' blocks in order.
  * Supported: d_k = d_v = d in {64, 128}.
  * ------------------------------------------------------------------------------------- */
 typedef struct stq_state stq_state;
@@ -472,7 +478,10 @@ damp_status stq_state_dequantize(const stq_state* state, float* S, const int32_t
  * update, readout y = X^T q before requantization, refit and pack. dst_pool: NULL writes the new
  * state in place; otherwise a second pool of the same layout receives it and the state bound to
  * the handle is only read (step 6: the previous copy stays intact while readers still use it;
- * the caller then binds the other pool or copies). Other arguments as in damp_decode_step. */
+ * the caller then binds the other pool or copies). Other arguments as in damp_decode_step.
+ * At d = 128 the step holds the stored codes and forms X twice (environment variable
+ * DAMP_STQ_STEP=x, read once per process, selects the kernel that holds X instead; both
+ * satisfy the bounds above). */
 damp_status stq_decode_step(stq_state* state, void* dst_pool, const int32_t* slot_idx, int32_t B,
                             const void* q, const void* k, const void* v, damp_dtype qkv_dtype,
                             const float* alpha, damp_decay decay, const float* beta, float* out,

@@ -230,8 +230,10 @@ bool stq_supported_d(int32_t d) { return d == 64 || d == 128; }
 size_t stq_block_bytes(int32_t d_, int n16, int n8, int n6, int n4) {
   const size_t d = static_cast<size_t>(d_);
   auto up = [](size_t x) { return (x + 127) / 128 * 128; };
-  const size_t o8 = up(2 * d * n16), o6 = up(o8 + d * n8), o4 = up(o6 + (3 * d / 4) * n6);
-  const size_t orf = up(o4 + (d / 2) * n4), ocs = up(orf + 2 * (d - n16));
+  // the 6- and 4-bit regions begin at the 4-row group of their first storage row
+  const size_t r6 = n6 > 0 ? n6 + (n16 + n8) % 4 : 0, r4 = n4 > 0 ? n4 + (n16 + n8 + n6) % 4 : 0;
+  const size_t o8 = up(2 * d * n16), o6 = up(o8 + d * n8), o4 = up(o6 + (3 * d / 4) * r6);
+  const size_t orf = up(o4 + (d / 2) * r4), ocs = up(orf + 2 * (d - n16));
   return ocs + 2 * d;
 }
 

@@ -15,8 +15,10 @@
 // Block of one (slot, head), storage rows ordered pivots, 8-bit, 6-bit, 4-bit (each ascending
 // key index): FP16 pivot rows (2 d bytes each) | 8-bit rows (d) | 6-bit rows (3 d / 4: a plane of
 // the low nibbles, d / 2 bytes, then a plane of the top two bits, d / 4 bytes) | 4-bit rows
-// (d / 2) | FP16 row factors of the integer rows | FP16 column scales (d) | zero padding to 256 B;
-// each region after the pivots starts at the next multiple of 128 bytes (never-touched padding).
+// (d / 2) | FP16 row factors of the integer rows | FP16 column scales (d) | zero padding to 256 B.
+// Each region after the pivots starts at the next multiple of 128 bytes, and the 6- and 4-bit
+// regions at the 4-row group of their first storage row (never-touched padding): the 4 rows a
+// wave stores together then cover whole 128-byte lines.
 // Codes are two's complement in their width. A lane owns CPL = d / 16 columns of a row, so its
 // codes of a row are CPL bytes (8-bit), CPL / 2 + CPL / 4 bytes (6-bit) or CPL / 2 bytes (4-bit):
 // d is 64 or 128.
@@ -64,6 +66,7 @@ enum StqMode : int { SM_STEP = 0, SM_PACK = 1, SM_UNPACK = 2 };
 struct StqBlock {
   uint32_t o8, o6, o4, orf, ocs, bytes;
   int n16, n8, n6, n4;
+  int f6, f4;  // the storage row at the start of the 6- / 4-bit region (first row rounded down to 4)
   double sw;   // the binary64 sum of w_i^2 over the integer rows
 };
 
@@ -77,11 +80,16 @@ __device__ __forceinline__ StqBlock stq_block(const StqArgs& a, int head) {
   b.n4 = (hi.y >> 24) & 0xff;
   // every region starts on a 128-byte line, so no line holds two regions (a store never writes
   // part of a line another store completes)
+  // and the 6- and 4-bit regions begin at the row group (4 storage rows) of their first row, so
+  // that the 4 rows a wave stores together cover whole lines (4 x 3d/4 and 4 x d/2 bytes)
   auto up = [](uint32_t x) { return (x + 127u) & ~127u; };
+  const int b2 = b.n16 + b.n8, b3 = b2 + b.n6;
+  b.f6 = b2 & ~3;
+  b.f4 = b3 & ~3;
   b.o8 = up(2u * D * b.n16);
   b.o6 = up(b.o8 + D * b.n8);
-  b.o4 = up(b.o6 + (3 * D / 4) * b.n6);
-  b.orf = up(b.o4 + (D / 2) * b.n4);
+  b.o4 = up(b.o6 + (3 * D / 4) * (b.n6 > 0 ? b.n6 + (b2 & 3) : 0));
+  b.orf = up(b.o4 + (D / 2) * (b.n4 > 0 ? b.n4 + (b3 & 3) : 0));
   b.ocs = up(b.orf + 2 * (D - b.n16));
   b.bytes = b.ocs + 2 * D;
   b.sw = __hiloint2double(hi.w, hi.z);
@@ -148,14 +156,14 @@ __device__ __forceinline__ uint32_t stq_off(const StqBlock& b, int p, int cg) {
   if constexpr (K == SK_F16) return static_cast<uint32_t>(p * 2 * D + cg * 2 * CPL);
   if constexpr (K == SK_I8) return b.o8 + static_cast<uint32_t>((p - b.n16) * D + cg * CPL);
   if constexpr (K == SK_I6)
-    return b.o6 + static_cast<uint32_t>(i6_row_bytes<D>(p - b.n16 - b.n8) + cg * (CPL / 2));
-  return b.o4 + static_cast<uint32_t>((p - b.n16 - b.n8 - b.n6) * (D / 2) + cg * (CPL / 2));
+    return b.o6 + static_cast<uint32_t>(i6_row_bytes<D>(p - b.f6) + cg * (CPL / 2));
+  return b.o4 + static_cast<uint32_t>((p - b.f4) * (D / 2) + cg * (CPL / 2));
 }
 
 template <int D>
 __device__ __forceinline__ uint32_t stq_top_off(const StqBlock& b, int p, int cg) {
   constexpr int CPL = D / 16;
-  return b.o6 + static_cast<uint32_t>(i6_row_bytes<D>(p - b.n16 - b.n8) + D / 2 + cg * (CPL / 4));
+  return b.o6 + static_cast<uint32_t>(i6_row_bytes<D>(p - b.f6) + D / 2 + cg * (CPL / 4));
 }
 
 // The lane's stored words of row p (kind K): F16 CPL halves, I8 CPL bytes, I6 / I4 CPL nibbles
@@ -680,13 +688,13 @@ __device__ __forceinline__ void stq_row_at(const StqBlock& b, int k, int p, int 
   constexpr int CPL = D / 16;
   const int b1 = b.n16, b2 = b1 + b.n8, b3 = b2 + b.n6;
   const uint32_t base = k == SK_F16 ? 0u : (k == SK_I8 ? b.o8 : (k == SK_I6 ? b.o6 : b.o4));
-  const int first = k == SK_F16 ? 0 : (k == SK_I8 ? b1 : (k == SK_I6 ? b2 : b3));
+  const int first = k == SK_F16 ? 0 : (k == SK_I8 ? b1 : (k == SK_I6 ? b.f6 : b.f4));
   const int stride = k == SK_F16 ? 2 * D : (k == SK_I8 ? D : (k == SK_I6 ? 3 * D / 4 : D / 2));
   const int lw = k == SK_F16 ? 2 * CPL : (k == SK_I8 ? CPL : CPL / 2);
   // 24-bit products: full-rate v_mad_u32_u24 (the row index and the stride are small and
   // non-negative for the lane's own kind; offt is used only by 6-bit rows)
   off = base + __umul24(static_cast<uint32_t>(p - first), static_cast<uint32_t>(stride)) + static_cast<uint32_t>(cg * lw);
-  offt = b.o6 + static_cast<uint32_t>(i6_row_bytes<D>(p - b2) + D / 2 + cg * (CPL / 4));
+  offt = b.o6 + static_cast<uint32_t>(i6_row_bytes<D>(p - b.f6) + D / 2 + cg * (CPL / 4));
 }
 
 // The step's per-row scalars for the codes-held kernel (d = 128, 256 threads): every thread
@@ -828,7 +836,7 @@ __global__ __launch_bounds__(256) void stq_step2_kernel(const StqArgs a) {
   for (int t = 0; t < RPL; ++t) {
     const int p0 = fresh_s(t * RPS + w * 4), p = p0 + fresh(rs);
     const int k0 = stq_kind(blk, p0), k3 = stq_kind(blk, p0 + 3);
-    const uint32_t sT = blk.o6 + static_cast<uint32_t>((p0 - b2) * (3 * D / 4));
+    const uint32_t sT = blk.o6 + static_cast<uint32_t>((p0 - blk.f6) * (3 * D / 4));
     uint32_t off, off4, off8 = kOut, offt;   // 4 bytes at off (all), 4 at off4, 8 at off8, 2 at offt
     if (k0 == k3) {
       // a scalar branch per kind; the empty volatile statements keep the compiler from turning
@@ -851,7 +859,7 @@ __global__ __launch_bounds__(256) void stq_step2_kernel(const StqArgs a) {
         offt = sT + lpt;
       } else {
         asm volatile("");
-        off = blk.o4 + static_cast<uint32_t>((p0 - b2 - blk.n6) * (D / 2)) + lp[SK_I4];
+        off = blk.o4 + static_cast<uint32_t>((p0 - blk.f4) * (D / 2)) + lp[SK_I4];
         off4 = kOut;
         offt = kOut;
       }

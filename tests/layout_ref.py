@@ -135,11 +135,16 @@ def _up128(x: int) -> int:
 def stq_regions(D: int, row_bits_h: np.ndarray) -> dict:
     """Byte offsets of a block's regions: each after the pivots starts on a 128-byte line."""
     n = {b: int((row_bits_h == b).sum()) for b in STQ_WIDTHS}
+    b2, b3 = n[16] + n[8], n[16] + n[8] + n[6]
     o = {16: 0}
+    # the 6- and 4-bit regions begin at the 4-row group of their first storage row: "lead" rows
+    # of padding come before the first row
+    o["lead6"] = b2 % 4 if n[6] else 0
+    o["lead4"] = b3 % 4 if n[4] else 0
     o[8] = _up128(2 * D * n[16])
     o[6] = _up128(o[8] + D * n[8])
-    o[4] = _up128(o[6] + 3 * D // 4 * n[6])
-    o["rf"] = _up128(o[4] + D // 2 * n[4])
+    o[4] = _up128(o[6] + 3 * D // 4 * (n[6] + o["lead6"]))
+    o["rf"] = _up128(o[4] + D // 2 * (n[4] + o["lead4"]))
     o["cs"] = _up128(o["rf"] + 2 * (D - n[16]))
     o["end"] = o["cs"] + 2 * D
     return o
@@ -183,7 +188,8 @@ def stq_pack(row_bits, h, c, rf, cs) -> np.ndarray:
                     seg = np.concatenate([_nibbles(cc), _tops(cc)], axis=1).ravel()
                 else:
                     seg = _nibbles(c[u, hh][rows]).ravel()
-                blk[reg[b]:reg[b] + seg.size] = seg
+                at = reg[b] + (reg["lead6"] * 3 * D // 4 if b == 6 else (reg["lead4"] * D // 2 if b == 4 else 0))
+                blk[at:at + seg.size] = seg
             ints = order[rb[order] != 16]
             seg = np.ascontiguousarray(rf[u, hh][ints]).view(np.uint8).ravel()
             blk[reg["rf"]:reg["rf"] + seg.size] = seg
@@ -222,7 +228,7 @@ def stq_unpack(row_bits, slots: np.ndarray, D: int):
         order = stq_storage(rb)
         reg = stq_regions(D, rb)
         for b in STQ_WIDTHS:
-            o = off + reg[b]
+            o = off + reg[b] + (reg["lead6"] * 3 * D // 4 if b == 6 else (reg["lead4"] * D // 2 if b == 4 else 0))
             rows = order[rb[order] == b]
             m = len(rows)
             if b == 16:

@@ -23,11 +23,13 @@ def test_block_accounting_of_the_nominal_map():
     # FP16 pivots 2 x 256 | 31 x 128 | 63 x 96 | 32 x 64 | 126 row factors x 2 | 128 column scales x 2
     data = 512 + 3968 + 6048 + 2048 + 252 + 256
     assert data == 13084
-    # each region on a 128-byte line: 8-bit rows at 512, 6-bit at 4480, 4-bit at 10528 -> 10624,
-    # row factors at 12672, column scales at 12924 -> 12928, end 13184 (13312 with the 256-byte
-    # rounding, the same stride as without the line padding)
+    # each region on a 128-byte line, the 6-bit region from the row group of its first row (row
+    # 33: one lead row of 96 bytes): 8-bit rows at 512, 6-bit at 4480 (first row at 4576), 4-bit
+    # at 10624 (row 96 starts a group: no lead), row factors at 12672, column scales at 12924 ->
+    # 12928, end 13184 (13312 with the 256-byte rounding, the same stride as without padding)
     reg = layout_ref.stq_regions(128, bits[0])
     assert (reg[8], reg[6], reg[4], reg["rf"], reg["cs"], reg["end"]) == (512, 4480, 10624, 12672, 12928, 13184)
+    assert (reg["lead6"], reg["lead4"]) == (1, 0)
     assert layout_ref.stq_block_bytes(128, bits[0]) == 13312
     assert abs(8 * data / (128 * 128) - 6.389) < 5e-4
     assert _bytes(1, 32, 128, bits) == 32 * 13312         # each block rounded up to 256 bytes
@@ -44,13 +46,16 @@ def test_block_accounting_of_edge_maps():
     assert _bytes(1, 1, d, all4) == -(-(d * d // 2 + 2 * d + 2 * d) // 256) * 256
     assert _bytes(1, 1, d, all8) == -(-(d * d + 2 * d + 2 * d) // 256) * 256
     mixed = np.array([[16, 6, 4, 8] * (d // 4)], np.uint8)   # any row order: rows are stored by kind
-    # 16 rows of each kind at d = 64: pivots 2048 @0, 8-bit 1024 @2048, 6-bit 768 @3072, 4-bit 512
-    # @3840, 48 row factors 96 @4352, column scales 128 @4480 (4448 rounded to a line): end 4608
+    # 16 rows of each kind at d = 64 (every region starts a row group): pivots 2048 @0, 8-bit 1024
+    # @2048, 6-bit 768 @3072, 4-bit 512 @3840, 48 row factors 96 @4352, column scales 128 @4480
+    # (4448 rounded to a line): end 4608
     assert _bytes(3, 1, d, mixed) == 3 * 4608
     odd = np.array([[16] * 3 + [8] * 5 + [6] * 7 + [4] * (d - 15)], np.uint8)
-    # pivots 384 @0, 8-bit 320 @384, 6-bit 336 @768 (704 rounded), 4-bit 1568 @1152 (1104 rounded),
-    # 61 row factors 122 @2816 (2720 rounded), column scales 128 @2944 (2938 rounded): end 3072
-    assert layout_ref.stq_regions(d, odd[0])["end"] == 3072
+    # pivots 384 @0, 8-bit 320 @384; 6-bit from row 8 (no lead) 7 x 48 = 336 @768 (704 rounded);
+    # 4-bit from row 15: lead 3 rows, (3 + 49) x 32 = 1664 @1152 (1104 rounded); 61 row factors
+    # 122 @2816; column scales 128 @2944 (2938 rounded): end 3072
+    reg = layout_ref.stq_regions(d, odd[0])
+    assert (reg[6], reg[4], reg["rf"], reg["cs"], reg["end"], reg["lead6"], reg["lead4"]) == (768, 1152, 2816, 2944, 3072, 0, 3)
     assert _bytes(2, 1, d, odd) == 2 * 3072
 
 

@@ -4,8 +4,10 @@ Pack fits the column scales from binary64 sums of w_i^2 X_ij^2 as the oracle doe
 order), so from the same binary32 X they agree except where a scale's square root lies within
 ~1e-15 of a binary16 tie; pack starts from the caller's binary32 states and is checked byte for
 byte. In the step the device's X differs from the oracle's by a few binary32 ulps (relative
-~2e-7), and its lane sums of (w_i X_ij)^2 are binary32 (a column scale within 5 binary32 ulps,
-3e-7, of the binary64 fit of the same X), so a column scale or a row factor whose exact value
+~2e-7; at d = 128 it is formed as X / cs_j from the codes, with the column sums u and p taken
+as exact integer sums of codes times 7-bit pieces of the row weights), and its lane sums of
+(w_i X_ij)^2 are binary32 (a column scale within 5 binary32 ulps, 3e-7, of the binary64 fit of
+the same values), so a column scale or a row factor whose exact value
 lies that close to a binary16 tie can take either neighbour, and the row factors and codes that
 follow it move with it. The step is therefore checked over every unit and every row, with each
 disagreement required to be such a tie:

@@ -1,13 +1,17 @@
 """CPU checks of the error bounds the GPU tests take as tolerance windows (no GPU): the
 STEPQuant-style fit's binary32 lane sums, and the fp32-state step's per-element bound.
 
-The STEPQuant-style step sums each lane's rows of (w_i X_ij)^2 in binary32 (w_i X_ij rounded,
-then one fused multiply-add per row, 8 rows per lane at d = 128 and d = 64) and adds the 16 lane
-partials, divides by the sum of w_i^2 and takes the square root in binary64. For positive terms
-that lane sum is within (8 + 2) u of the exact one (u = 2^-24), so the column scale before its
-binary16 rounding is within 5u (relative) of the binary64 fit of the same X. The GPU test allows
-a column scale to differ from the oracle's only where the oracle's value lies within 1e-6 of a
-binary16 tie, which needs this 5u (3e-7) plus the few ulps by which the device's X differs.
+The STEPQuant-style step sums each lane's rows of (w_i X_ij)^2 in binary32 (one binary32 value
+per element, then one fused multiply-add per row, 8 rows per lane at d = 128 and d = 64) and adds
+the 16 lane partials, divides by the sum of w_i^2 and takes the square root in binary64. At
+d = 128 the value is w_i Y_ij = w_i X_ij / cs_j formed from the codes (its binary64 total is then
+multiplied by cs_j^2, exactly); at d = 64 it is w_i X_ij rounded once. Either is within a few
+ulps of the exact product, the same few ulps by which the device's X differs; emulated here as
+one rounding. For positive terms the lane sum is within (8 + 2) u of the exact one (u = 2^-24),
+so the column scale before its binary16 rounding is within 5u (relative) of the binary64 fit of
+the same values. The GPU test allows a column scale to differ from the oracle's only where the
+oracle's value lies within 1e-6 of a binary16 tie, which needs this 5u (3e-7) plus the few ulps
+by which the device's X (or w Y) differs.
 Here the device's arithmetic is emulated exactly (each binary32 product and fused
 multiply-add rounded once from its exact rational value) on random and adversarial columns,
 against exact sums.
