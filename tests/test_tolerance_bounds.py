@@ -1,5 +1,6 @@
 """CPU checks of the error bounds the GPU tests take as tolerance windows (no GPU): the
-STEPQuant-style fit's binary32 lane sums, and the fp32-state step's per-element bound.
+STEPQuant-style fit's binary32 lane sums, the codes-held STEPQuant-style step's column sums
+from int8 pieces of the row weights, and the fp32-state step's per-element bound.
 
 The STEPQuant-style step sums each lane's rows of (w_i X_ij)^2 in binary32 (one binary32 value
 per element, then one fused multiply-add per row, 8 rows per lane at d = 128 and d = 64) and adds
@@ -142,3 +143,61 @@ def test_fp32_state_error_bound_covers_binary32_arithmetic():
             err = np.abs(X.astype(np.float64) - X_ref.astype(np.float64))
             assert (err <= bound).all(), f"per_key={per_key} cancel={cancel}: {(err > bound).sum()} above"
             assert err.max() > 0
+
+
+# ---- the codes-held step's column sums: int8 pieces of the row weights on the matrix cores ----
+def _pieces_sum(z, c):
+    """u_j = sum_i z_i c_ij as the step forms it: z (binary32, one wave's rows) scaled by 2^S so
+    that max |z| 2^S lies in [32, 64), split into four pieces P_k = rint of the remainder times
+    128^k (each in [-64, 64]), exact integer sums A_k = sum_i P_k,i c_ij, then
+    ((A_3 2^-7 + A_2) 2^-7 + A_1) 2^-7 + A_0 in binary32 (each step one rounding, the 2^-7
+    products exact) and the result times 2^-S (exact)."""
+    zm = max(abs(float(x)) for x in z)
+    if zm == 0:
+        return [0.0] * len(c[0])
+    S = 6 - math.frexp(zm)[1]
+    r = [Fraction(float(x)) * Fraction(2) ** S for x in z]
+    P = []
+    for _ in range(4):
+        p = [round(x) for x in r]     # Python rounds halves to even, as v_rndne_f32 does
+        assert all(abs(q) <= 64 for q in p)
+        P.append(p)
+        r = [(x - q) * 128 for x, q in zip(r, p)]
+    out = []
+    for j in range(len(c[0])):
+        A = [sum(P[k][i] * int(c[i][j]) for i in range(len(z))) for k in range(4)]
+        v = _round32(Fraction(A[3]) / 128 + A[2])
+        v = _round32(Fraction(float(v)) / 128 + A[1])
+        v = _round32(Fraction(float(v)) / 128 + A[0])
+        out.append(Fraction(float(v)) / Fraction(2) ** S)
+    return out
+
+
+def test_piece_split_column_sums_stay_within_their_bound():
+    """|u_j - exact| <= 3u sum_i |z_i c_ij| + 2^-27 max|z| sum_i |c_ij| (+ margin for the second
+    order): the pieces keep each z_i to 2^-22 of the scaled unit (2^-27 of max|z|), the integer
+    sums are exact and the recombination rounds three times. On these draws (GDN and KDA row
+    weights, a row-factor outlier, a row of small codes) the error stays near the binary32
+    summation error of the same sums."""
+    rng = np.random.default_rng(11)
+    worst = 0.0
+    for trial in range(24):
+        n = 32
+        k = rng.standard_normal(n) / math.sqrt(128)
+        gate = 1 / (1 + np.exp(-(rng.standard_normal(n) * (0 if trial % 2 else 3) + 2)))
+        rf = np.abs(rng.standard_normal(n)) * 0.01 + 0.001
+        rf[rng.integers(0, n)] *= (100 if trial % 3 == 0 else 8)
+        z = (gate * rf * k).astype(np.float32)
+        c = rng.integers(-127, 128, size=(n, 16))
+        c[rng.integers(0, n)] = rng.integers(-2, 3, size=16)
+        got = _pieces_sum(z, c)
+        zmax = Fraction(float(np.abs(z).max()))
+        for j in range(c.shape[1]):
+            exact = sum(Fraction(float(z[i])) * int(c[i][j]) for i in range(n))
+            sabs = sum(abs(Fraction(float(z[i])) * int(c[i][j])) for i in range(n))
+            bound = 3 * Fraction(U) * sabs * (1 + 4 * Fraction(U)) + Fraction(2) ** -27 * zmax * sum(abs(int(x)) for x in c[:, j])
+            err = abs(got[j] - exact)
+            assert err <= bound, (trial, j, float(err), float(bound))
+            if sabs:
+                worst = max(worst, float(err / sabs))
+    assert worst < 2e-6, worst   # the binary32 summation bound of 32 terms is ~34u = 2e-6
