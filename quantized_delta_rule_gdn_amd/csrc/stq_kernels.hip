@@ -638,18 +638,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 // NP: row steps that may hold pivot rows (the host picks NP >= ceil(max pivots per head / 16)).
 typedef int stq_v4i __attribute__((ext_vector_type(4)));
 
+template <int NW>
 struct Stq2Smem {
+  static constexpr int HZ = 128 / (4 * NW) / 8;   // halves of 8 row steps per lane
   float4 srow[128];   // {gate_p, k_p, q_p, rf_p / scale_p}, storage order
   float sw1[128];     // w_p (0 for pivots)
   float sv[128];      // v, then delta
   float sd[128];      // delta / g_j
   union {
-    float red[2][4][128];   // u and p: one partial per wave
-    float red2[16][128];    // the fit's lane partials (binary32), one per wave and row slot
-    float tmp[3 * 128];     // the staging's permutation to storage order
+    float red[2][NW][128];      // u and p: one partial per wave
+    float red2[4 * NW][128];    // the fit's lane partials (binary32), one per wave and row slot
+    float tmp[3 * 128];         // the staging's permutation to storage order
   };
-  uint8_t apc[4][2][4][32];   // pieces of z: [wave][k | q][piece][g * 8 + t]
-  float redqk[4];
+  uint8_t apc[NW][2][4][HZ][32];   // pieces of z: [wave][k | q][piece][half][g * 8 + t]
+  float redqk[NW];
   float sratio[128];  // g_j / cs'_j, 0 where cs'_j = 0
   uint16_t srf[128];  // the new row factors (binary16 bits), integer-row order
 };
@@ -790,11 +792,13 @@ __device__ __forceinline__ void stq_canon(uint32_t* w, uint32_t top) {
 // columns 0, 2; E bytes 2, 3 columns 4, 6; O bytes 0, 1 columns 1, 3; O bytes 2, 3 columns 5, 7.
 __device__ constexpr int kColOfMfma[4] = {0, 4, 1, 5};
 
-template <int PER_KEY, int BF16, int NP>
-__global__ __launch_bounds__(256) void stq_step2_kernel(const StqArgs a) {
-  constexpr int D = 128, NT = 256, CPL = 8, RPS = 16, RPL = 8;
+template <int PER_KEY, int BF16, int NP, int NW>
+__global__ __launch_bounds__(64 * NW) void stq_step2_kernel(const StqArgs a) {
+  constexpr int D = 128, NT = 64 * NW, CPL = 8, RPS = 4 * NW, RPL = D / RPS;
+  constexpr int HZ = RPL / 8;   // halves of 8 row steps: one MFMA K-block each
+  static_assert(RPL % 8 == 0, "8 or 16 row steps per lane");
   constexpr float kMagic = 0x1.8p23f;
-  __shared__ Stq2Smem sm;
+  __shared__ Stq2Smem<NW> sm;
   const int tid = __builtin_amdgcn_workitem_id_x();
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, rs = lane >> 4, cg = lane & 15;
@@ -915,74 +919,91 @@ __global__ __launch_bounds__(256) void stq_step2_kernel(const StqArgs a) {
   const uint32_t csj = stage.csj;
   const float beta = stage.store(blk, tid, sm.srow, sm.sv, sm.sw1, sm.tmp);
 
-  // (3) the projection weights of this wave's 32 rows in int8 pieces: lane (k | q, j) takes
-  // row 16 (j / 4) + 4 w + j % 4; S = the wave's power of two for its half (k or q)
+  // (3) the projection weights of this wave's rows (32 per half of 8 row steps) in int8 pieces:
+  // lane (k | q, j) takes row (8 h + j / 4) RPS + 4 w + j % 4 of each half h; S = the wave's power
+  // of two for its k or q weights
   const int kq = lane >> 5;
   int S;
   {
     const int j = lane & 31, tz = j >> 2, gz = j & 3;
-    const int row = tz * RPS + w * 4 + gz;
-    const float4 r4 = sm.srow[row];
-    const float z = row < blk.n16 ? 0.0f : r4.x * r4.w * (kq ? r4.z : r4.y);
-    // q.k over the wave's rows (the k half's lanes hold all 32 rows)
-    float qk = sum_row16(r4.y * r4.z);
+    float z[HZ], qk = 0.0f, zm = 0.0f;
+#pragma unroll
+    for (int h = 0; h < HZ; ++h) {
+      const int row = (tz + 8 * h) * RPS + w * 4 + gz;
+      const float4 r4 = sm.srow[row];
+      z[h] = row < blk.n16 ? 0.0f : r4.x * r4.w * (kq ? r4.z : r4.y);
+      qk = fmaf(r4.y, r4.z, qk);
+      zm = fmaxf(zm, fabsf(z[h]));
+    }
+    // q.k over the wave's rows (each 32-lane half holds all of them)
+    qk = sum_row16(qk);
     {
       const uint32_t u = __float_as_uint(qk);
       const auto sw2 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
       qk = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
     }
     if (lane == 0) sm.redqk[w] = qk;
-    float zm = max_row16(fabsf(z));
+    zm = max_row16(zm);
     {
       const uint32_t u = __float_as_uint(zm);
       const auto sw2 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
       zm = fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
     }
     S = zm > 0.0f ? 6 - __builtin_amdgcn_frexp_expf(zm) : 0;   // |z| 2^S < 64
-    float r = ldexpf(z, S);
-    uint32_t pc[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float pk = rintf(r);
-      pc[k] = static_cast<uint32_t>(static_cast<int32_t>(pk)) & 0xFFu;
-      r = (r - pk) * 128.0f;   // exact
+    for (int h = 0; h < HZ; ++h) {
+      float r = ldexpf(z[h], S);
+      uint32_t pc[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float pk = rintf(r);
+        pc[k] = static_cast<uint32_t>(static_cast<int32_t>(pk)) & 0xFFu;
+        r = (r - pk) * 128.0f;   // exact
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sm.apc[w][kq][k][h][gz * 8 + tz] = static_cast<uint8_t>(pc[k]);
     }
-    uint8_t* ap = &sm.apc[w][kq][0][gz * 8 + tz];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) ap[32 * k] = static_cast<uint8_t>(pc[k]);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // A operand: lane (m = cg, g = rs), m = (k | q) * 8 + cc * 4 + piece; byte 2 t + cc' holds
-  // the piece of row 16 t + 4 w + g when cc' = cc, else 0
-  int aw[4];
+  // A operands (one per half): lane (m = cg, g = rs), m = (k | q) * 8 + cc * 4 + piece; byte
+  // 2 t + cc' holds the piece of row (8 h + t) RPS + 4 w + g when cc' = cc, else 0
+  stq_v4i Av[HZ];
   {
     const int kqa = cg >> 3, cca = (cg >> 2) & 1, pa = cg & 3;
-    uint32_t xw[2];
-    load_bytes<8>(&sm.apc[w][kqa][pa][rs * 8], xw);
     const uint32_t s_even = cca ? 0x010c000cu : 0x0c010c00u;
     const uint32_t s_odd = cca ? 0x030c020cu : 0x0c030c02u;
-    aw[0] = static_cast<int>(__builtin_amdgcn_perm(0u, xw[0], s_even));
-    aw[1] = static_cast<int>(__builtin_amdgcn_perm(0u, xw[0], s_odd));
-    aw[2] = static_cast<int>(__builtin_amdgcn_perm(0u, xw[1], s_even));
-    aw[3] = static_cast<int>(__builtin_amdgcn_perm(0u, xw[1], s_odd));
+#pragma unroll
+    for (int h = 0; h < HZ; ++h) {
+      uint32_t xw[2];
+      load_bytes<8>(&sm.apc[w][kqa][pa][h][rs * 8], xw);
+      const stq_v4i a4 = {static_cast<int>(__builtin_amdgcn_perm(0u, xw[0], s_even)),
+                          static_cast<int>(__builtin_amdgcn_perm(0u, xw[0], s_odd)),
+                          static_cast<int>(__builtin_amdgcn_perm(0u, xw[1], s_even)),
+                          static_cast<int>(__builtin_amdgcn_perm(0u, xw[1], s_odd))};
+      Av[h] = a4;
+    }
   }
-  const stq_v4i Av = {aw[0], aw[1], aw[2], aw[3]};
   // B operands: MFMA i takes two columns of the lane's 8 (i = 0: E bytes 0, 1 = columns 0, 2;
-  // 1: E bytes 2, 3 = 4, 6; 2: O bytes 0, 1 = 1, 3; 3: O bytes 2, 3 = 5, 7) for rows t = 0..7
+  // 1: E bytes 2, 3 = 4, 6; 2: O bytes 0, 1 = 1, 3; 3: O bytes 2, 3 = 5, 7) for the row steps
+  // of a half; the halves accumulate in one integer sum
   stq_v4i acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int wd = i >> 1;
     const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-    int bw[4];
+    stq_v4i c4 = {0, 0, 0, 0};
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-      bw[d] = static_cast<int>(__builtin_amdgcn_perm(cw[2 * d + 1][wd], cw[2 * d][wd], sel));
-    const stq_v4i Bv = {bw[0], bw[1], bw[2], bw[3]};
-    const stq_v4i zero = {0, 0, 0, 0};
-    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Av, Bv, zero, 0, 0, 0);
+    for (int h = 0; h < HZ; ++h) {
+      int bw[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        bw[d] = static_cast<int>(__builtin_amdgcn_perm(cw[8 * h + 2 * d + 1][wd], cw[8 * h + 2 * d][wd], sel));
+      const stq_v4i Bv = {bw[0], bw[1], bw[2], bw[3]};
+      c4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Av[h], Bv, c4, 0, 0, 0);
+    }
+    acc[i] = c4;
   }
   // recombine: lane (g = rs, cg) holds, for MFMA i, the four pieces of (k | q = g / 2) at
   // column 8 cg + col(i, cc = g % 2)
@@ -1038,9 +1059,13 @@ __global__ __launch_bounds__(256) void stq_step2_kernel(const StqArgs a) {
   float gj = 1.0f;
   if (tid < D) {
     const int j = tid;
-    const float uu = ((sm.red[0][0][j] + sm.red[0][1][j]) + sm.red[0][2][j]) + sm.red[0][3][j];
-    const float pv = ((sm.red[1][0][j] + sm.red[1][1][j]) + sm.red[1][2][j]) + sm.red[1][3][j];
-    const float qk = ((sm.redqk[0] + sm.redqk[1]) + sm.redqk[2]) + sm.redqk[3];
+    float uu = sm.red[0][0][j], pv = sm.red[1][0][j], qk = sm.redqk[0];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) {
+      uu += sm.red[0][w2][j];
+      pv += sm.red[1][w2][j];
+      qk += sm.redqk[w2];
+    }
     const float dj = beta * (sm.sv[j] - uu);
     a.step.out[int64_t(bh) * D + j] = fmaf(qk, dj, pv);
     const float cs = half_bits_to_float(csj);
@@ -1085,7 +1110,7 @@ __global__ __launch_bounds__(256) void stq_step2_kernel(const StqArgs a) {
     const int j = tid;
     double s = static_cast<double>(sm.red2[0][j]);
 #pragma unroll
-    for (int k = 1; k < 16; ++k) s += static_cast<double>(sm.red2[k][j]);
+    for (int k = 1; k < 4 * NW; ++k) s += static_cast<double>(sm.red2[k][j]);
     const double g = static_cast<double>(gj);
     const uint32_t hb = blk.sw > 0.0 ? f16_from_f64(sqrt(s * (g * g) / blk.sw)) : 0u;
     const float cs = half_bits_to_float(hb);
@@ -1181,15 +1206,15 @@ hipError_t stq_launch_mode(int per_key, int bf16, const StqArgs& a, hipStream_t 
 template <int D>
 constexpr int kStqWaves = D >= 128 ? 4 : 2;
 
-template <int NP>
+template <int NP, int NW>
 hipError_t stq_step2_launch(int per_key, int bf16, const StqArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H)), block(256);
+  const dim3 grid(static_cast<unsigned>(a.B) * static_cast<unsigned>(a.H)), block(64 * NW);
   if (per_key) {
-    if (bf16) hipLaunchKernelGGL((stq_step2_kernel<1, 1, NP>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stq_step2_kernel<1, 0, NP>), grid, block, 0, s, a);
+    if (bf16) hipLaunchKernelGGL((stq_step2_kernel<1, 1, NP, NW>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stq_step2_kernel<1, 0, NP, NW>), grid, block, 0, s, a);
   } else {
-    if (bf16) hipLaunchKernelGGL((stq_step2_kernel<0, 1, NP>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stq_step2_kernel<0, 0, NP>), grid, block, 0, s, a);
+    if (bf16) hipLaunchKernelGGL((stq_step2_kernel<0, 1, NP, NW>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stq_step2_kernel<0, 0, NP, NW>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -1208,8 +1233,11 @@ template <int D>
 hipError_t stq_d(int mode, int per_key, int bf16, const StqArgs& a, hipStream_t s) {
   constexpr int NW = kStqWaves<D>;
   if constexpr (D == 128) {
+    // four waves per unit (16-row steps; NP = row steps that may hold pivot rows): with two
+    // (the kernel's NW = 2, 103 VGPRs, four waves per SIMD) the step measured 342-344 us
+    // against 330 us on the 1,024-slot pool, 102 against 95.5 us on 256 KDA slots
     if (mode == SM_STEP && !stq_step_x_held())
-      return a.max_pivots <= 16 ? stq_step2_launch<1>(per_key, bf16, a, s) : stq_step2_launch<8>(per_key, bf16, a, s);
+      return a.max_pivots <= 16 ? stq_step2_launch<1, 4>(per_key, bf16, a, s) : stq_step2_launch<8, 4>(per_key, bf16, a, s);
   }
   if (mode == SM_STEP) return stq_launch_mode<D, NW, SM_STEP>(per_key, bf16, a, s);
   if (mode == SM_PACK) return stq_launch_mode<D, NW, SM_PACK>(per_key, bf16, a, s);
