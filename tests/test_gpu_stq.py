@@ -213,6 +213,9 @@ def _edge_map(name, H, D, rng):
             counts = (D, 0, 0, 0)
         elif name == "all4":
             counts = (0, 0, 0, D)
+        elif name == "many_pivots":      # more pivot rows than one 16-row step holds
+            n16 = 17 + 5 * h
+            counts = (n16, 13, (D - n16 - 13) // 2, D - n16 - 13 - (D - n16 - 13) // 2)
         elif name == "ragged":           # different counts in every head, none a multiple of 4
             n16 = (3 + 2 * h) % 11
             n8 = ((5 + 7 * h) % 37 + 1) * D // 128
@@ -236,6 +239,7 @@ def _edge_map(name, H, D, rng):
     ("all4", 128, synth.GDN, False),
     ("ragged", 128, synth.KDA, True),
     ("ragged", 64, synth.GDN, False),
+    ("many_pivots", 128, synth.KDA, True),
 ])
 def test_step_edge_maps(name, D, decay, inplace):
     H, B = 5, 6
@@ -243,12 +247,15 @@ def test_step_edge_maps(name, D, decay, inplace):
     _log(f"{name} D={D}: " + str(_step_case(D, H, B, decay, "bf16", 0, 7 * D + len(name), inplace, bits, impact)))
 
 
-@pytest.mark.parametrize("case", ["zero", "zero_columns", "identity"])
+@pytest.mark.parametrize("case", ["zero", "zero_columns", "identity", "wide_range"])
 def test_step_degenerate(case):
     """Degenerate STEPQuant-style steps: a zero state with v = 0 (every stored number and the
     readout exactly 0), value columns that are zero in the state and in v (their column scales
     exactly 0 on both sides, so those columns code 0 and the row factors come from the others),
-    and alpha = 1 with beta = 0 (the refit of the reconstructed state)."""
+    alpha = 1 with beta = 0 (the refit of the reconstructed state), and row weights of the
+    column sums gate_i rf_i k_i spread over ~5 decades (per-key gates from 1e-3 to 1, one row
+    of each head 100 times the others), which the step's 7-bit pieces below the wave's largest
+    weight must still carry."""
     D, H, B = 128, 4, 6
     rng, bits, impact, S = _state(91, B, H, D, 2)
     inp = synth.step_inputs(rng, B, H, D, synth.KDA, "fp32")
@@ -260,9 +267,13 @@ def test_step_degenerate(case):
         zc[rng.choice(D, 9, replace=False)] = True
         S[..., zc] = 0.0
         inp.v[..., zc] = 0.0
-    else:
+    elif case == "identity":
         inp.alpha[:] = 1.0
         inp.beta[:] = 0.0
+    else:
+        inp.alpha[:] = (10.0 ** rng.uniform(-3, 0, size=inp.alpha.shape)).astype(np.float32)
+        for h in range(H):
+            S[:, h, rng.integers(0, D), :] *= 100
     st = lib.StqState(B, H, D, bits, impact)
     sl = torch.arange(B, dtype=torch.int32, device="cuda")
     st.quantize(to_dev(S), sl)
