@@ -128,3 +128,16 @@ def test_entry_points_reject_a_null_handle():
     st = L.stq_decode_step(None, None, p, 1, p, p, p, lib.DAMP_BF16, p, 0, p, p, None)
     assert st == lib.DAMP_ERR_INVALID_ARGUMENT
     assert "state is NULL" in lib.last_error()
+
+
+def test_block_bytes_of_random_maps_match_the_layout_reference():
+    """The library's block size (stq_state_bytes) equals the layout written from the header's
+    description (every region on a 128-byte line, the 6- and 4-bit rows from the 4-row group of
+    their first row, the block rounded to 256 bytes) for random precision maps."""
+    rng = np.random.default_rng(2718)
+    for _ in range(60):
+        d = int(rng.choice([64, 128]))
+        H = int(rng.integers(1, 4))
+        bits = rng.choice(np.array([16, 8, 6, 4], np.uint8), size=(H, d), p=rng.dirichlet(np.ones(4)))
+        want = sum(layout_ref.stq_block_bytes(d, bits[h]) for h in range(H))
+        assert _bytes(3, H, d, bits) == 3 * want
